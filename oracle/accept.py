@@ -1,0 +1,147 @@
+"""The p/q accept/reject rule with residual resampling (oracle; test
+infrastructure only).
+
+Source: *Optimizing DeepSeek-V4-Flash on a single NVIDIA GB10/GX10 with DSpark
+speculative decoding*, post 1, the paragraph under the analyzer output: the
+drafts are sampled from q, the target model defines p, a draft x is accepted
+with probability min(1, p(x)/q(x)), and a rejected draft is replaced by a
+sample of the positive residual distribution (normalised max(0, p - q)).  The
+verifier pushes K+1 rows -- the committed position plus the K drafts -- through
+the target (page 2 of the same thread, the author's verifier post; *ds4-on-spark*
+README, "The break-even law": one committed row plus four draft rows), so when
+every draft passes, row K yields one more token (the bonus token).
+
+The steps, per sequence, with uniforms u_0 .. u_K given as inputs:
+
+  for i = 0 .. K-1, d = draft i:
+      accept iff u_i * q_i(d) < p_i(d)                (exact comparison)
+      on reject: r = max(0, p_i - q_i); emit the first x (vocabulary order) whose
+                 running sum C(x) = sum_{y <= x} r(y) exceeds u_K * Z, Z = C(V-1);
+                 if Z == 0 sample p_i the same way instead; stop
+  all K accepted: emit the same inverse-CDF sample of p_K (the bonus token)
+
+Readings where the pages are silent (listed in the design notes): the uniform
+budget (K accept uniforms plus one sampling uniform), inverse-CDF order
+(vocabulary index, strict ">"), equality rejects, the Z == 0 fallback, and the
+bonus row.
+
+``p`` and ``q`` come either from logits (softmax at temperature T, fp64) or are
+given as probabilities.  ``accept_sequence`` also runs on ``fractions.Fraction``
+inputs, where every step is exact; the parity pins enumerate it that way.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+from itertools import accumulate
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+LOGITS, PROBS = 0, 1
+
+
+def softmax_t(z, temperature: float) -> np.ndarray:
+    """p = exp(z/T - max) / sum, fp64, for one row of fp32 logits."""
+    a = np.asarray(z, np.float32).astype(np.float64) / np.float64(np.float32(temperature))
+    e = np.exp(a - a.max())
+    return e / e.sum()
+
+
+def first_exceeding(weights, u):
+    """Index of the first x with sum_{y<=x} w(y) > u * Z, Z = total mass.
+
+    Runs on an fp64 numpy row (running sum in index order, fp64) or on a list
+    of Fractions (exact).  Returns None when Z <= 0.
+    """
+    if isinstance(weights, np.ndarray):
+        c = np.cumsum(weights, dtype=np.float64)
+        z = c[-1]
+        if not z > 0.0:
+            return None
+        t = np.float64(u) * z
+        return int(np.argmax(c > t))
+    c = list(accumulate(weights))
+    z = c[-1]
+    if not z > 0:
+        return None
+    t = Fraction(u) * z
+    for x, cx in enumerate(c):
+        if cx > t:
+            return x
+    return None   # unreachable for u < 1
+
+
+def _lt_exact(a, b, c) -> bool:
+    """a * b < c, evaluated exactly."""
+    return Fraction(a) * Fraction(b) < Fraction(c)
+
+
+def _residual(p, q):
+    if isinstance(p, np.ndarray):
+        return np.maximum(p - q, 0.0)
+    return [max(Fraction(0), pi - qi) for pi, qi in zip(p, q)]
+
+
+def accept_sequence(p_rows: Sequence, q_rows: Sequence, drafts: Sequence[int],
+                    u: Sequence) -> Tuple[int, List[int]]:
+    """One sequence: p_rows K+1 distributions, q_rows K, drafts K, u K+1.
+
+    Returns (n_accepted, emitted tokens: n_accepted drafts then one more)."""
+    K = len(drafts)
+    out: List[int] = []
+    for i in range(K):
+        d = int(drafts[i])
+        if _lt_exact(u[i], q_rows[i][d], p_rows[i][d]):
+            out.append(d)
+            continue
+        tok = first_exceeding(_residual(p_rows[i], q_rows[i]), u[K])
+        if tok is None:
+            tok = first_exceeding(p_rows[i], u[K])
+        out.append(tok)
+        return i, out
+    out.append(first_exceeding(p_rows[K], u[K]))
+    return K, out
+
+
+def _row_valid(v: np.ndarray, kind: int) -> bool:
+    if not np.all(np.isfinite(v)):
+        return False
+    if kind == PROBS:
+        return bool(np.all(v >= 0)) and float(v.astype(np.float64).sum()) > 0.0
+    return True
+
+
+def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float,
+                draft, draft_kind: int, t_q: float, drafts, uniforms):
+    """Batched form with the library's argument order.
+
+    target [S*(K+1), V] fp32 (row s*(K+1)+i), draft [S*K, V] fp32, drafts
+    [S, K] int32, uniforms [S, K+1] fp32.  Returns (out_tokens int32 [S, K+1]
+    padded with -1, n_accepted int32 [S]); a sequence whose inputs are invalid
+    (a token outside [0, V), a uniform outside [0, 1), a non-finite value, or a
+    negative / all-zero probability row) gets -1 everywhere.
+    """
+    target = np.asarray(target, np.float32).reshape(S, K + 1, V)
+    draft = np.asarray(draft, np.float32).reshape(S, K, V) if K else np.zeros((S, 0, V), np.float32)
+    drafts = np.asarray(drafts, np.int64).reshape(S, K)
+    uniforms = np.asarray(uniforms, np.float32).reshape(S, K + 1)
+    toks = np.full((S, K + 1), -1, np.int32)
+    nacc = np.full(S, -1, np.int32)
+    for s in range(S):
+        ok = all(_row_valid(target[s, i], target_kind) for i in range(K + 1))
+        ok = ok and all(_row_valid(draft[s, i], draft_kind) for i in range(K))
+        ok = ok and bool(np.all((drafts[s] >= 0) & (drafts[s] < V)))
+        ok = ok and bool(np.all((uniforms[s] >= 0) & (uniforms[s] < 1)))
+        if not ok:
+            continue
+
+        def dist(row, kind, t):
+            return softmax_t(row, t) if kind == LOGITS else row.astype(np.float64)
+
+        p_rows = [dist(target[s, i], target_kind, t_p) for i in range(K + 1)]
+        q_rows = [dist(draft[s, i], draft_kind, t_q) for i in range(K)]
+        n, out = accept_sequence(p_rows, q_rows, drafts[s].tolist(),
+                                 [float(x) for x in uniforms[s]])
+        nacc[s] = n
+        toks[s, :len(out)] = out
+    return toks, nacc
