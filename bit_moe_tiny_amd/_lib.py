@@ -1,0 +1,208 @@
+"""ctypes binding of libspecverify (argument marshalling only).
+
+Every function here forwards to the C ABI declared in ``include/specverify.h``
+with the same name; all computation happens in the HIP kernels.  Tensors are
+PyTorch device tensors (PyTorch provides device memory and streams); their
+pointers and the current HIP stream are passed through unchanged.  There is no
+fallback: if the shared library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = range(5)
+SV_F32, SV_BF16 = 0, 1
+SV_FFN_PLAIN, SV_FFN_SWIGLU = 0, 1
+SV_LOGITS, SV_PROBS = 0, 1
+
+EXPORTS = [
+    "sv_api_version", "sv_status_str", "sv_q2_matrix_bytes", "sv_q8_matrix_bytes",
+    "sv_moe_workspace_bytes", "vq2_moe_gemm", "sv_lmhead_workspace_bytes", "vq8_lmhead_gemm",
+    "sv_accept_workspace_bytes", "spec_accept", "vq2_dequant", "vq8_dequant",
+]
+
+
+class SvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("ffn", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_SIGS = {
+    "sv_api_version": ([], ctypes.c_int),
+    "sv_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "sv_q2_matrix_bytes": ([_i32, _i32], _sz),
+    "sv_q8_matrix_bytes": ([_i32, _i32], _sz),
+    "sv_moe_workspace_bytes": ([ctypes.POINTER(MoeDesc), _i32], _sz),
+    "vq2_moe_gemm": ([ctypes.POINTER(MoeDesc), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                     ctypes.c_int),
+    "sv_lmhead_workspace_bytes": ([_i32, _i32], _sz),
+    "vq8_lmhead_gemm": ([_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sv_accept_workspace_bytes": ([_i32, _i32, _i32], _sz),
+    "spec_accept": ([_i32, _i32, _i32, _vp, _i32, _f32, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
+                     _sz, _vp], ctypes.c_int),
+    "vq2_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "vq8_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m bit_moe_tiny_amd.build` "
+                          "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().sv_status_str(int(status)).decode()
+
+
+def api_version() -> int:
+    return load().sv_api_version()
+
+
+def _check(fn: str, st: int):
+    if st != SV_OK:
+        raise SvError(fn, st)
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _act_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"activation rows must be float32 or bfloat16, not {t.dtype}")
+
+
+def _dev_check(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _workspace(nbytes: int, like):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+# -------------------------------------------------------------------- sizes
+def sv_q2_matrix_bytes(n_out: int, k_in: int) -> int:
+    return load().sv_q2_matrix_bytes(n_out, k_in)
+
+
+def sv_q8_matrix_bytes(n_out: int, k_in: int) -> int:
+    return load().sv_q8_matrix_bytes(n_out, k_in)
+
+
+def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_gate, w_up=None,
+             w_down=None, s_gate=None, s_up=None, s_down=None) -> MoeDesc:
+    """Layer description over device weight tensors (uint8 byte buffers)."""
+    _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
+    d = MoeDesc(ffn, hidden, inter, n_experts, top_k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                _ptr(s_gate), _ptr(s_up), _ptr(s_down))
+    d._keep = (w_gate, w_up, w_down, s_gate, s_up, s_down)   # keep tensors alive
+    return d
+
+
+def sv_moe_workspace_bytes(desc: MoeDesc, R: int) -> int:
+    return load().sv_moe_workspace_bytes(ctypes.byref(desc), R)
+
+
+def sv_lmhead_workspace_bytes(hidden: int, R: int) -> int:
+    return load().sv_lmhead_workspace_bytes(hidden, R)
+
+
+def sv_accept_workspace_bytes(S: int, K: int, V: int) -> int:
+    return load().sv_accept_workspace_bytes(S, K, V)
+
+
+# ------------------------------------------------------------------- calls
+def vq2_moe_gemm(desc: MoeDesc, x, router_logits, y, topk_idx=None, topk_w=None, ws=None,
+                 stream=None):
+    """y[R, hidden] (PLAIN: [R, inter]) from rows x[R, hidden] (fp32 or bf16)."""
+    _dev_check(x, router_logits, y, topk_idx, topk_w, ws)
+    R = x.shape[0]
+    if ws is None:
+        ws = _workspace(sv_moe_workspace_bytes(desc, R), x)
+    st = load().vq2_moe_gemm(ctypes.byref(desc), _ptr(x), _act_dtype(x), R, _ptr(router_logits),
+                             _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
+                             _stream(stream))
+    _check("vq2_moe_gemm", st)
+    return y
+
+
+def vq8_lmhead_gemm(w, vocab: int, hidden: int, h, logits, ws=None, stream=None):
+    """logits[R, vocab] from hidden rows h[R, hidden] (fp32 or bf16)."""
+    _dev_check(w, h, logits, ws)
+    R = h.shape[0]
+    if ws is None:
+        ws = _workspace(sv_lmhead_workspace_bytes(hidden, R), h)
+    st = load().vq8_lmhead_gemm(_ptr(w), vocab, hidden, _ptr(h), _act_dtype(h), R, _ptr(logits),
+                                _ptr(ws), ws.numel(), _stream(stream))
+    _check("vq8_lmhead_gemm", st)
+    return logits
+
+
+def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float, draft,
+                draft_kind: int, t_q: float, draft_tokens, uniforms, out_tokens, out_n_accepted,
+                ws=None, stream=None):
+    """Accept/reject for S sequences of K drafts; fills out_tokens [S, K+1] and
+    out_n_accepted [S] (int32)."""
+    _dev_check(target, draft, draft_tokens, uniforms, out_tokens, out_n_accepted, ws)
+    if ws is None:
+        ws = _workspace(sv_accept_workspace_bytes(S, K, V), target)
+    st = load().spec_accept(S, K, V, _ptr(target), target_kind, t_p, _ptr(draft), draft_kind, t_q,
+                            _ptr(draft_tokens), _ptr(uniforms), _ptr(out_tokens),
+                            _ptr(out_n_accepted), _ptr(ws), ws.numel(), _stream(stream))
+    _check("spec_accept", st)
+    return out_tokens, out_n_accepted
+
+
+def vq2_dequant(w, n_out: int, k_in: int, out, stream=None):
+    _dev_check(w, out)
+    _check("vq2_dequant", load().vq2_dequant(_ptr(w), n_out, k_in, _ptr(out), _stream(stream)))
+    return out
+
+
+def vq8_dequant(w, n_out: int, k_in: int, out, stream=None):
+    _dev_check(w, out)
+    _check("vq8_dequant", load().vq8_dequant(_ptr(w), n_out, k_in, _ptr(out), _stream(stream)))
+    return out

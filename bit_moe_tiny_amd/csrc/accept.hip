@@ -1,0 +1,376 @@
+// The p/q accept/reject rule with residual resampling, on the GPU.
+//
+// Rule (GB10/GX10 DSpark thread, post 1): drafts are sampled from q, the
+// target defines p, a draft is accepted with probability min(1, p/q), a
+// rejected draft is replaced from the normalised positive residual
+// max(0, p - q); the verifier's K+1 rows give a bonus token when every draft
+// passes.  Decided here with explicit uniforms: accept iff u_i q_i(d_i) <
+// p_i(d_i), tested exactly as the sign of fma(u, q, -p); the replacement or
+// bonus token is the first x whose running sum exceeds u_K times the total.
+//
+// Two launches, no host sync:
+//   k_acc_stats  grid (chunk, row): per 2048-entry chunk of every target and
+//                draft row, the chunk max of z/T and sum exp(z/T - max) in
+//                fp64 (or the plain sum for probability rows), plus a
+//                validity flag.  Spreads the vocabulary-wide reductions over
+//                many CUs.
+//   k_acc_resid  grid (chunk, sequence): every block recombines its
+//                sequence's row statistics (same order in every block, so all
+//                agree bit for bit), replays the accept chain, and sums the
+//                sampling weights of its chunk (residual, or p_K for the
+//                bonus).  The last block of a sequence to finish (device-scope
+//                counter) prefix-sums the chunk totals, finds the chunk that
+//                holds u_K * Z, scans it and writes the outputs.
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int ACC_CHUNK = 2048;
+constexpr int ACC_PER = ACC_CHUNK / 256;
+constexpr int ACC_MAX_CH = 256;   // V <= 524288
+
+struct AccWs {
+  double* cmax;     // [rows, CH]
+  double* csum;     // [rows, CH]
+  int* cbad;        // [rows, CH]
+  double* rsum;     // [S, CH]
+  unsigned* ctr;    // [S]
+};
+
+static inline int acc_chunks(int V) { return (V + ACC_CHUNK - 1) / ACC_CHUNK; }
+
+static AccWs acc_carve(void* base, int S, int K, int V) {
+  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V);
+  uint8_t* p = (uint8_t*)base;
+  AccWs w;
+  w.cmax = (double*)p;
+  p += up256(rows * CH * 8);
+  w.csum = (double*)p;
+  p += up256(rows * CH * 8);
+  w.cbad = (int*)p;
+  p += up256(rows * CH * 4);
+  w.rsum = (double*)p;
+  p += up256((size_t)S * CH * 8);
+  w.ctr = (unsigned*)p;
+  return w;
+}
+
+size_t accept_ws_bytes(int S, int K, int V) {
+  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V);
+  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256((size_t)S * CH * 8) +
+         up256((size_t)S * 4);
+}
+
+__device__ inline double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide fixed-order reductions (256 threads); `sh` holds 4 doubles.
+__device__ inline double block_sum_d(double v, double* sh) {
+  v = wave_sum_d(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+__device__ inline double block_max_d(double v, double* sh) {
+  v = wave_max_d(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+}
+
+struct RowSrc {
+  const float* p;   // row start
+  int kind;         // SV_LOGITS / SV_PROBS
+  double T;
+};
+
+__device__ inline RowSrc row_src(int r, int S, int K, int V, const float* target, int tkind,
+                                 float Tp, const float* draft, int dkind, float Tq) {
+  RowSrc s;
+  const int nt = S * (K + 1);
+  if (r < nt) {
+    s.p = target + (size_t)r * V;
+    s.kind = tkind;
+    s.T = (double)Tp;
+  } else {
+    s.p = draft + (size_t)(r - nt) * V;
+    s.kind = dkind;
+    s.T = (double)Tq;
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const float* target,
+                                                   int tkind, float Tp, const float* draft,
+                                                   int dkind, float Tq, AccWs ws) {
+  __shared__ double sh[4];
+  __shared__ int shb[4];
+  const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
+  if (c == 0 && r == 0)
+    for (int s = threadIdx.x; s < S; s += 256) ws.ctr[s] = 0u;
+  const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
+  const int x0 = c * ACC_CHUNK;
+  double a[ACC_PER];
+  int bad = 0;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < ACC_PER; ++i) {
+    const int x = x0 + threadIdx.x + 256 * i;
+    a[i] = -INFINITY;
+    if (x < V) {
+      const float v = src.p[x];
+      if (src.kind == SV_LOGITS) {
+        bad |= !(fabsf(v) <= 3.402823466e38f);
+        a[i] = (double)v / src.T;
+      } else {
+        bad |= !(v >= 0.f && v <= 3.402823466e38f);
+        a[i] = (double)v;
+      }
+      mx = fmax(mx, a[i]);
+    }
+  }
+  double sum = 0.0;
+  if (src.kind == SV_LOGITS) {
+    mx = block_max_d(mx, sh);
+#pragma unroll
+    for (int i = 0; i < ACC_PER; ++i)
+      if (x0 + threadIdx.x + 256 * i < V && !bad) sum += exp(a[i] - mx);
+  } else {
+    mx = 0.0;
+#pragma unroll
+    for (int i = 0; i < ACC_PER; ++i)
+      if (x0 + threadIdx.x + 256 * i < V) sum += a[i];
+  }
+  sum = block_sum_d(sum, sh);
+  bad = __any(bad) ? 1 : 0;
+  if ((threadIdx.x & 63) == 0) shb[threadIdx.x >> 6] = bad;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const size_t o = (size_t)r * CH + c;
+    ws.cmax[o] = mx;
+    ws.csum[o] = sum;
+    ws.cbad[o] = shb[0] | shb[1] | shb[2] | shb[3];
+  }
+}
+
+// Distribution value of entry x of a row, given its recombined statistics.
+__device__ inline double dist_val(const RowSrc& s, double m, double z, int x) {
+  const float v = s.p[x];
+  if (s.kind == SV_LOGITS) return exp((double)v / s.T - m) / z;
+  return (double)v;
+}
+
+enum { MODE_RESID = 0, MODE_BONUS = 1, MODE_FALLBACK = 2 };
+
+__device__ inline double sample_weight(int mode, const RowSrc& P, double pm, double pz,
+                                       const RowSrc& Q, double qm, double qz, int x) {
+  const double p = dist_val(P, pm, pz, x);
+  if (mode != MODE_RESID) return p;
+  const double q = dist_val(Q, qm, qz, x);
+  return fmax(p - q, 0.0);
+}
+
+__global__ __launch_bounds__(256) void k_acc_resid(int S, int K, int V, const float* target,
+                                                   int tkind, float Tp, const float* draft,
+                                                   int dkind, float Tq, const int32_t* drafts,
+                                                   const float* uni, int32_t* out_tokens,
+                                                   int32_t* out_n, AccWs ws) {
+  __shared__ double rm[2 * SV_MAX_DRAFTS + 1], rz[2 * SV_MAX_DRAFTS + 1];
+  __shared__ int rbad[2 * SV_MAX_DRAFTS + 1];
+  __shared__ int s_nacc, s_invalid, s_last;
+  __shared__ double sh[4];
+  __shared__ double s_csum[ACC_MAX_CH];
+  __shared__ double tsum[256];
+  __shared__ int s_pick, s_lastpos;
+  const int c = blockIdx.x, s = blockIdx.y, CH = gridDim.x;
+  const int nrows = 2 * K + 1;
+  const int tid = threadIdx.x;
+  // 1. recombine the sequence's row statistics (fixed chunk order)
+  if (tid < nrows) {
+    const int r = tid <= K ? s * (K + 1) + tid : S * (K + 1) + s * K + (tid - K - 1);
+    const bool logits = (tid <= K ? tkind : dkind) == SV_LOGITS;
+    double m = -INFINITY, z = 0.0;
+    int bad = 0;
+    for (int cc = 0; cc < CH; ++cc) {
+      m = fmax(m, ws.cmax[(size_t)r * CH + cc]);
+      bad |= ws.cbad[(size_t)r * CH + cc];
+    }
+    if (!logits) m = 0.0;
+    for (int cc = 0; cc < CH; ++cc) {
+      const double cs = ws.csum[(size_t)r * CH + cc];
+      z += logits ? cs * exp(ws.cmax[(size_t)r * CH + cc] - m) : cs;
+    }
+    rm[tid] = m;
+    rz[tid] = z;
+    rbad[tid] = bad | (logits ? 0 : !(z > 0.0));
+  }
+  __syncthreads();
+  // 2. validity and 3. the accept chain (thread 0)
+  if (tid == 0) {
+    int inv = 0;
+    for (int i = 0; i < nrows; ++i) inv |= rbad[i];
+    for (int i = 0; i < K; ++i) {
+      const int d = drafts[s * K + i];
+      inv |= !(d >= 0 && d < V);
+    }
+    for (int i = 0; i <= K; ++i) {
+      const float u = uni[s * (K + 1) + i];
+      inv |= !(u >= 0.f && u < 1.f);
+    }
+    int n = 0;
+    if (!inv) {
+      for (; n < K; ++n) {
+        const int d = drafts[s * K + n];
+        const RowSrc P = row_src(s * (K + 1) + n, S, K, V, target, tkind, Tp, draft, dkind, Tq);
+        const RowSrc Q = row_src(S * (K + 1) + s * K + n, S, K, V, target, tkind, Tp, draft,
+                                 dkind, Tq);
+        const double p = dist_val(P, rm[n], rz[n], d);
+        const double q = dist_val(Q, rm[K + 1 + n], rz[K + 1 + n], d);
+        const double u = (double)uni[s * (K + 1) + n];
+        if (!(fma(u, q, -p) < 0.0)) break;   // reject: u*q >= p
+      }
+    }
+    s_nacc = n;
+    s_invalid = inv;
+  }
+  __syncthreads();
+  const int nacc = s_nacc, invalid = s_invalid;
+  const int mode = nacc < K ? MODE_RESID : MODE_BONUS;
+  const RowSrc P = row_src(s * (K + 1) + nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq);
+  const RowSrc Q = nacc < K ? row_src(S * (K + 1) + s * K + nacc, S, K, V, target, tkind, Tp,
+                                      draft, dkind, Tq)
+                           : P;
+  const double pm = rm[nacc], pz = rz[nacc];
+  const double qm = nacc < K ? rm[K + 1 + nacc] : 0.0, qz = nacc < K ? rz[K + 1 + nacc] : 1.0;
+  // 4. this chunk's total sampling weight
+  const int x0 = c * ACC_CHUNK;
+  double w = 0.0;
+  if (!invalid) {
+#pragma unroll
+    for (int i = 0; i < ACC_PER; ++i) {
+      const int x = x0 + tid * ACC_PER + i;
+      if (x < V) w += sample_weight(mode, P, pm, pz, Q, qm, qz, x);
+    }
+  }
+  w = block_sum_d(w, sh);
+  if (tid == 0) {
+    ws.rsum[(size_t)s * CH + c] = w;
+    __threadfence();
+    const unsigned prev = atomicAdd(&ws.ctr[s], 1u);
+    s_last = (prev == (unsigned)CH - 1);
+    if (s_last) ws.ctr[s] = 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  // 5. last block of the sequence: inverse CDF over the chunk totals, then in-chunk
+  int32_t* out = out_tokens + (size_t)s * (K + 1);
+  if (invalid) {
+    for (int i = tid; i <= K; i += 256) out[i] = -1;
+    if (tid == 0) out_n[s] = -1;
+    return;
+  }
+  int smode = mode;
+  if (tid < CH) s_csum[tid] = ws.rsum[(size_t)s * CH + tid];
+  __syncthreads();
+  double Z = 0.0;
+  for (int cc = 0; cc < CH; ++cc) Z += s_csum[cc];
+  if (!(Z > 0.0)) {
+    // residual vanished (only through rounding): sample p_i itself
+    smode = MODE_FALLBACK;
+    for (int cc = 0; cc < CH; ++cc) {
+      double t = 0.0;
+#pragma unroll
+      for (int i = 0; i < ACC_PER; ++i) {
+        const int x = cc * ACC_CHUNK + tid * ACC_PER + i;
+        if (x < V) t += sample_weight(smode, P, pm, pz, Q, qm, qz, x);
+      }
+      t = block_sum_d(t, sh);
+      if (tid == 0) s_csum[cc] = t;
+    }
+    __syncthreads();
+    Z = 0.0;
+    for (int cc = 0; cc < CH; ++cc) Z += s_csum[cc];
+  }
+  const double target_t = (double)uni[s * (K + 1) + K] * Z;
+  // chunk holding the target (sequential prefix over chunk totals)
+  int hit = -1, lastpos = -1;
+  double base = 0.0, run = 0.0;
+  for (int cc = 0; cc < CH; ++cc) {
+    if (s_csum[cc] > 0.0) lastpos = cc;
+    if (hit < 0 && run + s_csum[cc] > target_t) {
+      hit = cc;
+      base = run;
+    }
+    run += s_csum[cc];
+  }
+  const bool found_chunk = hit >= 0;
+  if (!found_chunk) {   // rounding pushed the target past the total: take the last positive entry
+    hit = lastpos >= 0 ? lastpos : 0;
+    base = 0.0;
+  }
+  // in-chunk inclusive scan, 8 consecutive entries per thread
+  double loc[ACC_PER];
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < ACC_PER; ++i) {
+    const int x = hit * ACC_CHUNK + tid * ACC_PER + i;
+    loc[i] = x < V ? sample_weight(smode, P, pm, pz, Q, qm, qz, x) : 0.0;
+    tot += loc[i];
+  }
+  tsum[tid] = tot;
+  if (tid == 0) {
+    s_pick = 0x7fffffff;
+    s_lastpos = -1;
+  }
+  __syncthreads();
+  double excl = base;
+  for (int j = 0; j < tid; ++j) excl += tsum[j];   // fixed order; 256 entries at most
+  int mine = 0x7fffffff, lastmine = -1;
+  double run2 = excl;
+#pragma unroll
+  for (int i = 0; i < ACC_PER; ++i) {
+    const int x = hit * ACC_CHUNK + tid * ACC_PER + i;
+    run2 += loc[i];
+    if (loc[i] > 0.0) lastmine = x;
+    if (found_chunk && mine == 0x7fffffff && run2 > target_t) mine = x;
+  }
+  if (mine != 0x7fffffff) atomicMin(&s_pick, mine);
+  if (lastmine >= 0) atomicMax(&s_lastpos, lastmine);
+  __syncthreads();
+  if (tid == 0) {
+    // none crossed (rounding, or no chunk held the target): last positive entry of the chunk
+    const int tok = s_pick != 0x7fffffff ? s_pick : s_lastpos;
+    for (int i = 0; i < nacc; ++i) out[i] = drafts[s * K + i];
+    out[nacc] = tok;
+    for (int i = nacc + 1; i <= K; ++i) out[i] = -1;
+    out_n[s] = nacc;
+  }
+}
+
+hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, float Tp,
+                         const float* draft, int dkind, float Tq, const int32_t* drafts,
+                         const float* u, int32_t* out_tokens, int32_t* out_n, void* wsp,
+                         hipStream_t s) {
+  const AccWs ws = acc_carve(wsp, S, K, V);
+  const int CH = acc_chunks(V);
+  hipLaunchKernelGGL(k_acc_stats, dim3(CH, S * (2 * K + 1)), dim3(256), 0, s, S, K, V, target,
+                     tkind, Tp, draft, dkind, Tq, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_acc_resid, dim3(CH, S), dim3(256), 0, s, S, K, V, target, tkind, Tp,
+                     draft, dkind, Tq, drafts, u, out_tokens, out_n, ws);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,166 @@
+// Internal declarations shared by the HIP translation units of libspecverify.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__host__ __device__ inline size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- formats
+// Two-bit matrix [n_out x k_in]: planes codes / nibbles / d / dmin, each at a
+// 256-byte aligned offset (layout documented in specverify.h).
+struct Q2View {
+  const uint8_t* qs;   // nblk*64
+  const uint8_t* sc;   // nblk*16
+  const uint16_t* d;   // nblk fp16 bits
+  const uint16_t* dm;  // nblk fp16 bits
+  int nb;              // blocks per output row = k_in / 256
+  int n_out;
+};
+
+__host__ __device__ inline size_t q2_bytes(size_t n_out, size_t k_in) {
+  size_t nblk = n_out * (k_in / 256);
+  return up256(nblk * 64) + up256(nblk * 16) + 2 * up256(nblk * 2);
+}
+
+__host__ __device__ inline Q2View q2_view(const void* base, int n_out, int k_in) {
+  const uint8_t* p = (const uint8_t*)base;
+  size_t nblk = (size_t)n_out * (k_in / 256);
+  Q2View v;
+  v.qs = p;
+  v.sc = p + up256(nblk * 64);
+  v.d = (const uint16_t*)(v.sc + up256(nblk * 16));
+  v.dm = (const uint16_t*)((const uint8_t*)v.d + up256(nblk * 2));
+  v.nb = k_in / 256;
+  v.n_out = n_out;
+  return v;
+}
+
+// Eight-bit matrix: codes nblk*32 int8, then d nblk fp16.
+struct Q8View {
+  const int8_t* qs;
+  const uint16_t* d;
+  int nb;  // k_in / 32
+  int n_out;
+};
+
+__host__ __device__ inline size_t q8_bytes(size_t n_out, size_t k_in) {
+  size_t nblk = n_out * (k_in / 32);
+  return up256(nblk * 32) + up256(nblk * 2);
+}
+
+__host__ __device__ inline Q8View q8_view(const void* base, int n_out, int k_in) {
+  const uint8_t* p = (const uint8_t*)base;
+  size_t nblk = (size_t)n_out * (k_in / 32);
+  Q8View v;
+  v.qs = (const int8_t*)p;
+  v.d = (const uint16_t*)(p + up256(nblk * 32));
+  v.nb = k_in / 32;
+  v.n_out = n_out;
+  return v;
+}
+
+// ------------------------------------------------------- activation images
+// Rows of activations prepared for the fp16 matrix cores: each row scaled by
+// a power of two (2^e, chosen so the row's largest magnitude lies in
+// [2^10, 2^11)) and split into an fp16 high part and an fp16 remainder.
+//  layout PERM (two-bit kernels): element order matches the register order in
+//    which the two-bit kernel unpacks codes, with the 4^-j factor of each
+//    position folded in; plus per-16-element sums (for the min term).
+//  layout PLAIN (eight-bit kernel): natural order.
+struct XImg {
+  _Float16* hi;      // [rows, K]
+  _Float16* lo;      // [rows, K]
+  _Float16* sxh;     // [rows, K/16]  (PERM only)
+  _Float16* sxl;     // [rows, K/16]
+  float* rscale;     // [rows]  2^-e, multiplies the result
+  int K;
+};
+
+enum { XL_PERM = 0, XL_PLAIN = 1 };
+
+__host__ __device__ inline size_t ximg_bytes(size_t rows, size_t K, int layout) {
+  size_t b = 2 * up256(rows * K * 2) + up256(rows * 4);
+  if (layout == XL_PERM) b += 2 * up256(rows * (K / 16) * 2);
+  return b;
+}
+
+inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
+  uint8_t* p = (uint8_t*)base;
+  XImg x;
+  x.K = K;
+  x.hi = (_Float16*)p;
+  p += up256(rows * K * 2);
+  x.lo = (_Float16*)p;
+  p += up256(rows * K * 2);
+  if (layout == XL_PERM) {
+    x.sxh = (_Float16*)p;
+    p += up256(rows * (K / 16) * 2);
+    x.sxl = (_Float16*)p;
+    p += up256(rows * (K / 16) * 2);
+  } else {
+    x.sxh = x.sxl = nullptr;
+  }
+  x.rscale = (float*)p;
+  return x;
+}
+
+// ----------------------------------------------------------- MoE workspace
+// Device-side routing/grouping results written by the prep kernel.
+struct MoeMeta {
+  int n_units;    // touched routed experts + shared
+  int n_assign;   // (row, slot) assignments incl. shared rows
+};
+
+struct MoeWs {
+  MoeMeta* meta;
+  int* unit_expert;   // [max_units]  expert id, -1 = shared
+  int* unit_off;      // [max_units]  first assignment of the unit
+  int* unit_cnt;      // [max_units]
+  int* arow;          // [max_assign] activation row of assignment a
+  int* amap;          // [R, top_k+1]  assignment of (row, slot); slot top_k = shared
+  int* topk_idx;      // [R, top_k]
+  float* topk_w;      // [R, top_k]
+  unsigned* ctr;      // [n_down_groups] combine counters
+  float* h;           // [max_assign, inter]  SwiGLU output
+  float* part;        // [max_assign, hidden] per-assignment down outputs
+  XImg x_img;         // staged x  [R, hidden]
+  XImg h_img;         // staged h  [max_assign, inter]
+  int max_units, max_assign, n_down_groups;
+};
+
+size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out);
+
+// ------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error.
+hipError_t launch_stage(const void* src, int dtype, int rows, int K, int layout,
+                        const int* n_rows_dev, XImg img, hipStream_t s);
+hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logits,
+                           const void* x, int x_dtype, int32_t* topk_idx_out,
+                           float* topk_w_out, MoeWs ws, hipStream_t s);
+hipError_t launch_q2_plain(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, float* y,
+                           hipStream_t s);
+hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws,
+                            hipStream_t s);
+hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
+hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo,
+                            XImg img, float* logits, hipStream_t s);
+hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, float Tp,
+                         const float* draft, int dkind, float Tq, const int32_t* drafts,
+                         const float* u, int32_t* out_tokens, int32_t* out_n, void* ws,
+                         hipStream_t s);
+size_t accept_ws_bytes(int S, int K, int V);
+hipError_t launch_q2_dequant(const void* w, int n_out, int k_in, float* out, hipStream_t s);
+hipError_t launch_q8_dequant(const void* w, int n_out, int k_in, float* out, hipStream_t s);
+
+}  // namespace sv

@@ -1,0 +1,209 @@
+/*
+ * libspecverify -- the target-model verifier step of lossless speculative
+ * decoding over a two-bit mixture-of-experts model, as hand-written HIP kernels
+ * for AMD MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *  [T1] "Optimizing DeepSeek-V4-Flash on a single NVIDIA GB10/GX10 with DSpark
+ *       speculative decoding", forum thread, page 1 (post 1: the p/q rule,
+ *       the verifier as the bottleneck; post 20: per-session RNG and state in
+ *       multi-session cohorts) and page 2 (the author's verifier post: K+1
+ *       rows through routed MoE, projections and the vocabulary head).
+ *  [T3] "ds4-on-spark" README (introduction: block formats of the weights,
+ *       expert dedup; "Roofline": decode is weight-streaming bound; "Under the
+ *       hood": routed experts stay quantised with inline dequantisation; "The
+ *       break-even law": one committed row plus four draft rows per verify).
+ *  [T4] "1x Spark tuned DSpark for DeepSeek-V4-Flash: 35 tok/s, 800+ prefill,
+ *       and fast multi-agent serving", forum thread (Q&A answer 3: fused
+ *       gate+up+SwiGLU MoE decode, fused router).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *    memory, including workspaces; the library never allocates, frees or
+ *    synchronises, and keeps no mutable global state.
+ *  - Work is enqueued on `stream` (0 = the null stream).  Calls on different
+ *    streams are independent when their workspaces and outputs are distinct.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failure returns SV_EINVAL (or SV_EWORKSPACE) and changes nothing.  A
+ *    failed launch returns SV_EHIP.  Bad *device data* (e.g. a draft token out
+ *    of range) cannot be reported synchronously; spec_accept marks the affected
+ *    sequence with -1 outputs instead.  No kernel traps.
+ *  - Row-major layouts throughout.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#if defined(__GNUC__)
+#define SV_API __attribute__((visibility("default")))
+#else
+#define SV_API
+#endif
+
+enum sv_status {
+  SV_OK = 0,
+  SV_EINVAL = 1,        /* invalid argument; nothing enqueued */
+  SV_EUNSUPPORTED = 2,  /* valid but outside what this build implements */
+  SV_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() */
+  SV_EHIP = 4           /* a HIP launch failed */
+};
+
+enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };   /* element type of activation rows */
+
+enum sv_ffn {
+  SV_FFN_PLAIN = 0,   /* y = W x with W = w_gate [inter x hidden]; n_experts = top_k = 1 */
+  SV_FFN_SWIGLU = 1   /* y = W_d (silu(W_g x) * (W_u x)) per expert, routed + optional shared */
+};
+
+enum sv_dist { SV_LOGITS = 0, SV_PROBS = 1 };  /* how a distribution row is given */
+
+#define SV_API_VERSION 1
+#define SV_MAX_ROWS 64        /* R limit of the GEMM calls */
+#define SV_MAX_TOPK 16
+#define SV_MAX_EXPERTS 1024
+#define SV_MAX_DRAFTS 31      /* K limit of spec_accept */
+
+SV_API int sv_api_version(void);
+SV_API const char* sv_status_str(int status);
+
+/*
+ * Two-bit block matrix ("Q2_K" is named for routed-expert weights in [T3],
+ * introduction; the pages give no bit layout -- this is the library's own).
+ * [n_out x k_in], k_in % 256 == 0; nb = k_in/256 blocks per output row; block
+ * index b = n*nb + kb.  Four planes, each at a 256-byte-aligned offset from the
+ * start of the matrix:
+ *   codes   nblk*64 B : element e of block b = (codes[64b + e/4] >> 2*(e%4)) & 3
+ *   nibbles nblk*16 B : byte j <-> elements 16j..16j+15; low nibble scale sc,
+ *                       high nibble min m
+ *   d       nblk fp16 : block scale
+ *   dmin    nblk fp16 : block min-scale
+ * weight = d*sc*q - dmin*m.  Returns the matrix size in bytes (sum of the
+ * 256-aligned plane sizes), or 0 for invalid shapes.  Matrices of one tensor
+ * (e.g. all experts' gate matrices) are stored back to back, each this long.
+ */
+SV_API size_t sv_q2_matrix_bytes(int32_t n_out, int32_t k_in);
+
+/*
+ * Eight-bit block matrix ("Q8_0" for the output head in [T3], introduction):
+ * [n_out x k_in], k_in % 32 == 0; blocks of 32 int8 codes with one fp16 scale;
+ * block b = n*(k_in/32) + kb.  Planes: codes nblk*32 int8, then d nblk fp16,
+ * each 256-byte aligned.  weight = d*q.  Returns the size in bytes, or 0.
+ */
+SV_API size_t sv_q8_matrix_bytes(int32_t n_out, int32_t k_in);
+
+/*
+ * Description of one MoE layer (host struct, read only during the call).
+ *  SV_FFN_SWIGLU: w_gate, w_up: n_experts matrices [inter x hidden] each;
+ *    w_down: n_experts matrices [hidden x inter]; s_gate/s_up/s_down: the
+ *    shared expert (always on, combine weight 1) or all NULL.
+ *  SV_FFN_PLAIN: w_gate is one [inter x hidden] matrix; the other five NULL;
+ *    n_experts = top_k = 1.
+ *  hidden % 256 == 0 and inter % 256 == 0 for SWIGLU; PLAIN needs
+ *  hidden % 256 == 0 and inter >= 1.
+ */
+typedef struct {
+  int32_t ffn, hidden, inter, n_experts, top_k;
+  const void *w_gate, *w_up, *w_down;
+  const void *s_gate, *s_up, *s_down;
+} sv_moe_desc;
+
+/* Workspace bytes vq2_moe_gemm needs for this layer and R rows (0 if invalid). */
+SV_API size_t sv_moe_workspace_bytes(const sv_moe_desc* d, int32_t R);
+
+/*
+ * Routed two-bit MoE layer for R verifier rows (steps: activation staging,
+ * router top-k, expert grouping with dedup ([T3] introduction, "MoE gate_up
+ * expert dedup"), fused gate+up+SwiGLU ([T4] Q&A 3), down projection and the
+ * weighted combine).  Weights stay quantised in HBM and are dequantised in
+ * registers ([T3] "Under the hood"); each weight tile is read once for all rows
+ * routed to its expert.
+ *
+ *  x             [R, hidden], x_dtype SV_F32 or SV_BF16; 1 <= R <= SV_MAX_ROWS
+ *  router_logits [R, n_experts] fp32; may be NULL only when n_experts == 1
+ *  y             [R, hidden] fp32 (PLAIN: [R, inter])
+ *  topk_idx      [R, top_k] int32 output or NULL: the top_k experts by router
+ *                logit, largest first, ties to the lower index
+ *  topk_w        [R, top_k] fp32 output or NULL: softmax probability of each
+ *                chosen expert over all n_experts (not renormalised)
+ *  ws, ws_bytes  device workspace of at least sv_moe_workspace_bytes(d, R)
+ *
+ *  y_r = sum_s topk_w[r,s] * FFN_{topk_idx[r,s]}(x_r) + FFN_shared(x_r), with
+ *  FFN(x) = W_d(silu(W_g x) * (W_u x)) and fp32 intermediates.  Summation
+ *  order is fixed, so results are run-to-run deterministic.
+ */
+SV_API int vq2_moe_gemm(const sv_moe_desc* d, const void* x, int32_t x_dtype, int32_t R,
+                 const float* router_logits, float* y, int32_t* topk_idx, float* topk_w,
+                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes vq8_lmhead_gemm needs (0 if invalid). */
+SV_API size_t sv_lmhead_workspace_bytes(int32_t hidden, int32_t R);
+
+/*
+ * Vocabulary head in eight-bit blocks: logits[r, v] = sum_k W[v, k] h[r, k],
+ * W an eight-bit matrix [vocab x hidden] (hidden % 32 == 0), h [R, hidden] in
+ * h_dtype, logits [R, vocab] fp32.  Each weight tile is read once and reused
+ * for all R rows (the "Q8 tiny-batch reuse" of [T1] post 1).
+ */
+SV_API int vq8_lmhead_gemm(const void* w, int32_t vocab, int32_t hidden, const void* h,
+                    int32_t h_dtype, int32_t R, float* logits, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes spec_accept needs (0 if invalid). */
+SV_API size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V);
+
+/*
+ * The p/q accept/reject rule with residual resampling ([T1] post 1: drafts are
+ * sampled from q, the target defines p, accept with probability
+ * min(1, p(x)/q(x)), a rejected draft is replaced from the normalised positive
+ * residual max(0, p - q)), for S independent sequences of K drafts each
+ * (cohorts with per-session state: [T1] post 20).
+ *
+ *  target        [S*(K+1), V] fp32; row s*(K+1)+i is position i of sequence s
+ *                (the K+1 verifier rows: [T1] page 2; [T3] "The break-even law")
+ *  target_kind   SV_LOGITS: p = softmax(row / T_p); SV_PROBS: p = row as given
+ *  draft         [S*K, V] fp32, row s*K+i; q likewise with draft_kind / T_q;
+ *                may be NULL when K == 0
+ *  draft_tokens  [S, K] int32
+ *  uniforms      [S, K+1] fp32 in [0, 1): u[s][i] decides draft i, u[s][K]
+ *                drives the one inverse-CDF sample
+ *  out_tokens    [S, K+1] int32: the n accepted drafts, then the correction
+ *                token (on a rejection) or the bonus token from row K (when all
+ *                K pass), then -1 padding
+ *  out_n_accepted [S] int32
+ *
+ *  Per sequence, for i = 0..K-1: accept iff u_i*q_i(d_i) < p_i(d_i), evaluated
+ *  exactly; on the first reject emit the first x (vocabulary order) whose
+ *  running sum of r = max(0, p_i - q_i) exceeds u_K * sum(r) (if sum(r) == 0,
+ *  sample p_i the same way) and stop; if all pass, sample p_K the same way.
+ *  Distributions are evaluated in fp64.  A sequence with a draft token outside
+ *  [0, V), a uniform outside [0, 1), a non-finite value, or (SV_PROBS) a
+ *  negative value or an all-zero row gets -1 in every output slot.
+ *  T_p / T_q must be finite and > 0 for SV_LOGITS rows.  1 <= S, 0 <= K <=
+ *  SV_MAX_DRAFTS, 1 <= V.
+ */
+SV_API int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
+                float T_p, const float* draft, int32_t draft_kind, float T_q,
+                const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
+                int32_t* out_n_accepted, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Test exports: the dequantised weights [n_out, k_in] fp32.  Two-bit: the exact
+ * value d*sc*q - dmin*m rounded once to fp32 (nearest, ties to even);
+ * eight-bit: d*q (exact).
+ */
+SV_API int vq2_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream);
+SV_API int vq8_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every declared symbol, and validates
+arguments on the host (CPU only: every call here returns before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_moe_tiny_amd as sv
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return re.findall(r"SV_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sv.load()
+    names = _declared()
+    assert len(names) == 12
+    assert set(names) == set(sv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    # nothing beyond the C ABI is exported
+    out = os.popen(f"nm -D --defined-only {sv.LIB_PATH}").read()
+    text_syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert text_syms == set(names)
+
+
+def test_version_and_status_strings():
+    assert sv.api_version() == 1
+    assert sv.status_str(sv.SV_OK) == "ok"
+    assert "workspace" in sv.status_str(sv.SV_EWORKSPACE)
+    assert sv.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (512, 256), (1, 256), (13, 768)])
+def test_q2_matrix_bytes_agree_with_oracle(n, k):
+    assert sv.sv_q2_matrix_bytes(n, k) == oracle.q2_matrix_bytes(n, k)
+
+
+@pytest.mark.parametrize("n,k", [(129280, 7168), (1, 32), (7, 64)])
+def test_q8_matrix_bytes_agree_with_oracle(n, k):
+    assert sv.sv_q8_matrix_bytes(n, k) == oracle.q8_matrix_bytes(n, k)
+
+
+def test_invalid_shapes_give_zero_sizes():
+    assert sv.sv_q2_matrix_bytes(10, 100) == 0 and sv.sv_q2_matrix_bytes(0, 256) == 0
+    assert sv.sv_q8_matrix_bytes(10, 33) == 0
+    assert sv.sv_lmhead_workspace_bytes(7168, 0) == 0 and sv.sv_lmhead_workspace_bytes(7168, 65) == 0
+    assert sv.sv_lmhead_workspace_bytes(100, 4) == 0
+    assert sv.sv_accept_workspace_bytes(1, 32, 100) == 0 and sv.sv_accept_workspace_bytes(0, 4, 100) == 0
+    assert sv.sv_accept_workspace_bytes(1, 4, 600000) == 0
+    assert sv.sv_accept_workspace_bytes(3, 4, 129280) > 0
+
+
+def _desc(**kw):
+    base = dict(ffn=sv.SV_FFN_SWIGLU, hidden=7168, inter=2048, n_experts=256, top_k=8)
+    base.update(kw)
+    d = sv.MoeDesc(base["ffn"], base["hidden"], base["inter"], base["n_experts"], base["top_k"],
+                   base.get("w_gate", 0x1000), base.get("w_up", 0x1000), base.get("w_down", 0x1000),
+                   base.get("s_gate"), base.get("s_up"), base.get("s_down"))
+    return d
+
+
+def test_moe_workspace_sizes():
+    assert sv.sv_moe_workspace_bytes(_desc(), 5) > 0
+    assert sv.sv_moe_workspace_bytes(_desc(s_gate=1, s_up=1, s_down=1), 16) > sv.sv_moe_workspace_bytes(_desc(), 16)
+    assert sv.sv_moe_workspace_bytes(_desc(), 0) == 0
+    assert sv.sv_moe_workspace_bytes(_desc(), 65) == 0
+    assert sv.sv_moe_workspace_bytes(_desc(hidden=7000), 5) == 0
+    assert sv.sv_moe_workspace_bytes(_desc(top_k=17), 5) == 0
+    assert sv.sv_moe_workspace_bytes(_desc(top_k=9, n_experts=8), 5) == 0
+    assert sv.sv_moe_workspace_bytes(_desc(s_gate=1), 5) == 0          # shared expert all-or-none
+    assert sv.sv_moe_workspace_bytes(_desc(ffn=sv.SV_FFN_PLAIN, inter=512, hidden=256, n_experts=1,
+                                           top_k=1, w_up=None, w_down=None), 4) > 0
+    assert sv.sv_moe_workspace_bytes(_desc(ffn=7), 4) == 0
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    lib = sv.load()
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    # R out of range, missing router, null output, bad dtype: all EINVAL, no launch
+    assert lib.vq2_moe_gemm(ctypes.byref(d), fake, 1, 0, fake, fake, None, None, fake, 1 << 30, None) == sv.SV_EINVAL
+    assert lib.vq2_moe_gemm(ctypes.byref(d), fake, 1, 5, None, fake, None, None, fake, 1 << 30, None) == sv.SV_EINVAL
+    assert lib.vq2_moe_gemm(ctypes.byref(d), fake, 1, 5, fake, None, None, None, fake, 1 << 30, None) == sv.SV_EINVAL
+    assert lib.vq2_moe_gemm(ctypes.byref(d), fake, 7, 5, fake, fake, None, None, fake, 1 << 30, None) == sv.SV_EINVAL
+    # undersized workspace
+    assert lib.vq2_moe_gemm(ctypes.byref(d), fake, 1, 5, fake, fake, None, None, fake, 16, None) == sv.SV_EWORKSPACE
+    assert lib.vq8_lmhead_gemm(fake, 129280, 7168, fake, 1, 5, fake, fake, 16, None) == sv.SV_EWORKSPACE
+    assert lib.vq8_lmhead_gemm(fake, 0, 7168, fake, 1, 5, fake, fake, 1 << 30, None) == sv.SV_EINVAL
+    assert lib.vq8_lmhead_gemm(fake, 100, 7168, fake, 1, 65, fake, fake, 1 << 30, None) == sv.SV_EINVAL
+    # accept: bad temperature, bad kind, missing drafts, undersized workspace
+    args = lambda **k: [k.get("S", 1), k.get("K", 4), k.get("V", 32), fake, k.get("tk", 0),
+                        k.get("tp", 1.0), k.get("draft", fake), k.get("dk", 0), k.get("tq", 1.0),
+                        k.get("tok", fake), fake, fake, fake, fake, k.get("wsb", 1 << 20), None]
+    assert lib.spec_accept(*args(tp=0.0)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(tq=float("nan"))) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(tk=3)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(draft=None)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(tok=None)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(K=32)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(wsb=8)) == sv.SV_EWORKSPACE
+    assert lib.vq2_dequant(fake, 10, 100, fake, None) == sv.SV_EINVAL
+    assert lib.vq8_dequant(fake, 10, 33, fake, None) == sv.SV_EINVAL
+
+
+def test_binding_has_no_fallback(tmp_path):
+    from bit_moe_tiny_amd import _lib
+    saved = _lib._lib
+    _lib._lib = None
+    try:
+        with pytest.raises(ImportError):
+            _lib.load(str(tmp_path / "missing.so"))
+    finally:
+        _lib._lib = saved

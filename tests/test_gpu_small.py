@@ -1,0 +1,187 @@
+"""GPU parity at sizes the oracle finishes in seconds: dequantisation
+(bit-exact), the one-matrix two-bit product (the tiny configuration and ragged
+shapes), a small routed MoE layer, a small vocabulary head, and the accept
+rule on the tiny configuration.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.accept import LOGITS, PROBS
+from tests.gpu_util import dev, empty, host, say
+from tests.parity import accept_flags, assert_close, sample_flag
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import bit_moe_tiny_amd as m
+    m.load()
+    return m
+
+
+# ------------------------------------------------------------ dequant
+@pytest.mark.parametrize("n,k", [(512, 256), (2048, 7168), (33, 768)])
+def test_q2_dequant_bit_exact(sv, n, k):
+    p = synth.q2_random(synth.generator(100, n, k), n, k, 0.02)
+    buf = p.packed()
+    say("vq2_dequant", n, k)
+    out = empty((n, k), "f32")
+    sv.vq2_dequant(dev(buf), n, k, out)
+    got = host(out)
+    want = oracle.q2_dequant_f32(buf, n, k)
+    bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))
+    if bad[0].size:
+        q, sc, m, du, dmu = oracle.q2_fields(buf, n, k)
+        rows, cols = bad
+        info = [(int(r), int(c), int(q[r, c]), int(sc[r, c // 16]), int(m[r, c // 16]),
+                 int(du[r, c // 256]), int(dmu[r, c // 256]), float(got[r, c]), float(want[r, c]))
+                for r, c in list(zip(rows, cols))[:8]]
+        pytest.fail(f"{rows.size} mismatches; (n,k,q,sc,m,d*2^24,dmin*2^24,got,want): {info}")
+
+
+@pytest.mark.parametrize("n,k", [(777, 1024), (16, 7168)])
+def test_q8_dequant_bit_exact(sv, n, k):
+    p = synth.q8_random(synth.generator(101, n, k), n, k, 0.01)
+    buf = p.packed()
+    say("vq8_dequant", n, k)
+    out = empty((n, k), "f32")
+    sv.vq8_dequant(dev(buf), n, k, out)
+    assert np.array_equal(host(out).view(np.uint32), oracle.q8_dequant_f32(buf, n, k).view(np.uint32))
+
+
+# --------------------------------------------------------------- plain
+def _plain(sv, buf, n_out, k_in, x):
+    d = sv.moe_desc(sv.SV_FFN_PLAIN, k_in, n_out, 1, 1, dev(buf))
+    y = empty((x.shape[0], n_out), "f32")
+    sv.vq2_moe_gemm(d, x, None, y)
+    return host(y)
+
+
+def test_tiny_plain_layer(sv):
+    t = synth.tiny()
+    buf = t.w.packed()
+    say("vq2_moe_gemm PLAIN tiny 512x256 R=4 f32")
+    y = _plain(sv, buf, 512, 256, dev(t.x))
+    want = oracle.plain_layer(buf, 512, 256, t.x, "f32")
+    assert_close(y, want, what="tiny plain")
+
+
+@pytest.mark.parametrize("n_out,k_in,R,dt", [(520, 768, 3, "f32"), (64, 256, 17, "bf16"),
+                                            (1000, 1024, 33, "f32"), (7, 256, 1, "bf16")])
+def test_plain_ragged(sv, n_out, k_in, R, dt):
+    p = synth.q2_random(synth.generator(102, n_out, k_in), n_out, k_in, 0.02)
+    buf = p.packed()
+    g = synth.generator(103, R, k_in)
+    x = synth.normal_bf16(g, (R, k_in)) if dt == "bf16" else synth.normal_f32(g, (R, k_in))
+    say("vq2_moe_gemm PLAIN", n_out, k_in, R, dt)
+    y = _plain(sv, buf, n_out, k_in, dev(x))
+    want = oracle.plain_layer(buf, n_out, k_in, x, dt)
+    assert_close(y, want, what=f"plain {n_out}x{k_in} R={R} {dt}")
+
+
+# ----------------------------------------------------------------- MoE
+def _small_moe(E, hidden, inter, shared, seed):
+    mats = [synth.expert_matrices(seed, e, 0.02, hidden, inter) for e in range(E + (1 if shared else 0))]
+    cat = lambda m: np.concatenate([mats[e][m].packed() for e in range(E)])
+    ws = (cat(synth.M_GATE), cat(synth.M_UP), cat(synth.M_DOWN))
+    sh = tuple(mats[E][m].packed() for m in (synth.M_GATE, synth.M_UP, synth.M_DOWN)) if shared else (None,) * 3
+    return ws, sh
+
+
+@pytest.mark.parametrize("E,k,hidden,inter,R,shared,dt", [
+    (16, 4, 512, 256, 5, True, "bf16"),
+    (8, 2, 256, 512, 3, False, "f32"),
+    (32, 8, 1024, 256, 16, True, "bf16"),
+    (4, 4, 256, 256, 20, True, "bf16"),
+])
+def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
+    (g, u, d), (sg, su, sd) = _small_moe(E, hidden, inter, shared, 104 + E)
+    gen = synth.generator(105, E, R)
+    x = synth.normal_bf16(gen, (R, hidden)) if dt == "bf16" else synth.normal_f32(gen, (R, hidden))
+    logits = synth.normal_f32(synth.generator(106, E, R), (R, E))
+    tens = [dev(a) if a is not None else None for a in (g, u, d, sg, su, sd)]
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, hidden, inter, E, k, *tens)
+    y = empty((R, hidden), "f32")
+    ti = empty((R, k), "i32")
+    tw = empty((R, k), "f32")
+    say("vq2_moe_gemm SWIGLU", E, k, hidden, inter, R, shared, dt)
+    sv.vq2_moe_gemm(desc, dev(x), dev(logits), y, ti, tw)
+    want, widx, ww = oracle.moe_layer(g, u, d, sg, su, sd, E, k, hidden, inter, x, dt, logits)
+    assert np.array_equal(host(ti), widx)
+    assert_close(host(tw), ww, what="topk_w")
+    assert_close(host(y), want, what="moe y")
+
+
+# ------------------------------------------------------------ lm head
+@pytest.mark.parametrize("vocab,hidden,R,dt", [(1000, 1024, 5, "bf16"), (77, 256, 3, "f32"),
+                                              (4096, 7168, 16, "bf16"), (33, 32, 40, "f32")])
+def test_small_lm_head(sv, vocab, hidden, R, dt):
+    p = synth.q8_random(synth.generator(107, vocab, hidden), vocab, hidden, 0.01)
+    buf = p.packed()
+    gen = synth.generator(108, R, hidden)
+    h = synth.normal_bf16(gen, (R, hidden)) if dt == "bf16" else synth.normal_f32(gen, (R, hidden))
+    out = empty((R, vocab), "f32")
+    say("vq8_lmhead_gemm", vocab, hidden, R, dt)
+    sv.vq8_lmhead_gemm(dev(buf), vocab, hidden, dev(h), out)
+    want = oracle.lm_head_logits(buf, vocab, hidden, h, dt)
+    assert_close(host(out), want, what="lm head")
+
+
+# ------------------------------------------------------------- accept
+def _run_accept(sv, S, K, V, target, tk, tp, draft, dk, tq, drafts, u):
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    say("spec_accept", S, K, V, tk, dk)
+    sv.spec_accept(S, K, V, dev(target), tk, tp, dev(draft) if K else None, dk, tq,
+                   dev(drafts) if K else None, dev(u), toks, nacc)
+    return host(toks), host(nacc)
+
+
+def test_tiny_accept_probs_bit_exact(sv):
+    """Identical fp32 p, q and u: decisions and tokens must match exactly."""
+    t = synth.tiny()
+    p = np.stack([oracle.softmax_t(r, 1.0) for r in t.target_logits]).astype(np.float32)
+    q = np.stack([oracle.softmax_t(r, 1.0) for r in t.draft_logits]).astype(np.float32)
+    toks, nacc = _run_accept(sv, 1, 4, 32, p, PROBS, 1.0, q, PROBS, 1.0, t.drafts, t.uniforms)
+    wt, wn = oracle.spec_accept(1, 4, 32, p, PROBS, 1.0, q, PROBS, 1.0, t.drafts, t.uniforms)
+    assert np.array_equal(nacc, wn) and np.array_equal(toks, wt)
+
+
+def test_tiny_accept_logits(sv):
+    t = synth.tiny()
+    toks, nacc = _run_accept(sv, 1, 4, 32, t.target_logits, LOGITS, 1.0, t.draft_logits, LOGITS,
+                             1.0, t.drafts, t.uniforms)
+    wt, wn = oracle.spec_accept(1, 4, 32, t.target_logits, LOGITS, 1.0, t.draft_logits, LOGITS,
+                                1.0, t.drafts, t.uniforms)
+    p_rows = [oracle.softmax_t(r, 1.0) for r in t.target_logits]
+    q_rows = [oracle.softmax_t(r, 1.0) for r in t.draft_logits]
+    if not accept_flags(p_rows, q_rows, t.drafts[0], t.uniforms[0], int(wn[0])):
+        assert nacc[0] == wn[0]
+        assert np.array_equal(toks, wt)
+
+
+def test_accept_many_sequences_probs(sv):
+    """Random p, q (zeros included) over many sequences: exact agreement."""
+    rng = np.random.default_rng(9)
+    S, K, V = 200, 5, 50
+    def rows(n):
+        w = rng.random((n, V)) * (rng.random((n, V)) > 0.3)
+        w[:, 0] += 1e-3
+        return (w / w.sum(1, keepdims=True)).astype(np.float32)
+    p, q = rows(S * (K + 1)), rows(S * K)
+    drafts = np.stack([[rng.choice(V, p=q[s * K + i] / q[s * K + i].sum()) for i in range(K)]
+                       for s in range(S)]).astype(np.int32)
+    u = synth.uniform24(synth.generator(110), S * (K + 1)).reshape(S, K + 1)
+    toks, nacc = _run_accept(sv, S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    wt, wn = oracle.spec_accept(S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    assert np.array_equal(nacc, wn)
+    bad = [s for s in range(S) if not np.array_equal(toks[s], wt[s])]
+    # tokens may differ only where the sampling target sits on a CDF boundary
+    for s in bad:
+        n = wn[s]
+        w = (np.maximum(p[s * (K + 1) + n].astype(np.float64) - q[s * K + n], 0) if n < K
+             else p[s * (K + 1) + K].astype(np.float64))
+        assert sample_flag(w, u[s, K]), s
+    assert set(np.unique(wn).tolist()) > {0}      # the cases mix accepts and rejects
