@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Verifier-step benchmark on one MI355X.
+
+One step = the whole verifier hot path on one batch of synthetic input:
+  vq2_moe_gemm     one routed MoE layer: 256 two-bit SwiGLU experts + 1 shared
+                   (7168 <-> 2048), router top-8, R verifier rows (bf16);
+  vq8_lmhead_gemm  the eight-bit vocabulary head 129280 x 7168 on R rows;
+  spec_accept      p/q accept/reject with residual resampling for S sequences
+                   of K = R/S - 1 drafts at T = 0.8.
+Inputs for several batches are generated up front (seeded, synth) and stay
+resident in HBM; steps rotate through them.  The timed region is K steps
+between two device synchronisations; value = algorithmic weight bytes of the
+timed steps (the routed experts each batch actually touches, the shared
+expert, the vocabulary head) / elapsed time.
+
+Prints ONE JSON line (rank 0, N = 1).  --sweep prints one line per R instead.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+Q2_EXPERT_BYTES = 3 * 4816896          # gate + up + down of one 7168 <-> 2048 expert
+Q8_HEAD_BYTES = 984596480             # 129280 x 7168 eight-bit blocks
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", type=int, default=5, help="verifier rows R (default 5 = 1 + 4 drafts)")
+    ap.add_argument("--seqs", type=int, default=1, help="sequences S sharing the rows (R %% S == 0)")
+    ap.add_argument("--batches", type=int, default=8, help="distinct input batches rotated over")
+    ap.add_argument("--temperature", type=float, default=0.8)
+    ap.add_argument("--sweep", default="", help="comma list of R values: one JSON line per R")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=3, help="routed experts in the oracle sample")
+    ap.add_argument("--cpu-vocab", type=int, default=16384, help="vocab rows in the oracle sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ inputs
+def gen_moe_weights(threads: int = 8):
+    """All 257 experts (seeded per expert), expert-major byte buffers."""
+    E = synth.N_ROUTED
+
+    def one(e):
+        mats = synth.expert_matrices(synth.CFG_MOE, e)
+        return e, [mats[m].packed() for m in (synth.M_GATE, synth.M_UP, synth.M_DOWN)]
+
+    bufs = [None] * (E + 1)
+    with cf.ThreadPoolExecutor(threads) as ex:
+        for e, b in ex.map(one, range(E + 1)):
+            bufs[e] = b
+    routed = [np.concatenate([bufs[e][m] for e in range(E)]) for m in range(3)]
+    return routed, bufs[E]
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+class Step:
+    """Device-resident inputs, outputs and workspaces for one R/S setting."""
+
+    def __init__(self, sv, desc, wq8, R, S, n_batches, temperature):
+        import torch
+        self.sv, self.desc, self.wq8 = sv, desc, wq8
+        self.R, self.S, self.K = R, S, R // S - 1
+        self.T = temperature
+        V, H = synth.VOCAB, synth.HIDDEN
+        self.batches = []
+        for b in range(n_batches):
+            rows = synth.moe_rows(R, synth.CFG_MOE, sub=100 * R + b)
+            h = synth.lm_head_hidden(R, synth.CFG_LMHEAD, sub=100 * R + b)
+            self.batches.append(dict(x=to_dev(rows.x_bf16), logits=to_dev(rows.router_logits),
+                                     h=to_dev(h)))
+        self.y = torch.empty((R, H), dtype=torch.float32, device="cuda")
+        self.tidx = [torch.empty((R, synth.TOP_K), dtype=torch.int32, device="cuda") for _ in range(n_batches)]
+        self.tw = torch.empty((R, synth.TOP_K), dtype=torch.float32, device="cuda")
+        self.z = torch.empty((R, V), dtype=torch.float32, device="cuda")
+        self.toks = torch.empty((S, self.K + 1), dtype=torch.int32, device="cuda")
+        self.nacc = torch.empty((S,), dtype=torch.int32, device="cuda")
+        self.ws_moe = torch.empty(sv.sv_moe_workspace_bytes(desc, R), dtype=torch.uint8, device="cuda")
+        self.ws_lm = torch.empty(sv.sv_lmhead_workspace_bytes(H, R), dtype=torch.uint8, device="cuda")
+        self.ws_acc = torch.empty(sv.sv_accept_workspace_bytes(S, self.K, V), dtype=torch.uint8, device="cuda")
+        # draft side: target logits of each batch (one untimed head call), then
+        # draft logits = target + N(0, 1.5^2) noise, drafts ~ softmax(draft / T)
+        for b, bt in enumerate(self.batches):
+            sv.vq8_lmhead_gemm(wq8, V, H, bt["h"], self.z, ws=self.ws_lm)
+            torch.cuda.synchronize()
+            acc = synth.accept_inputs(self.z.cpu().numpy(), S, self.K, 1.5, temperature,
+                                      synth.CFG_LMHEAD, sub=100 * R + b)
+            bt["draft"] = to_dev(acc.draft_logits) if self.K else None
+            bt["drafts"] = to_dev(acc.drafts) if self.K else None
+            bt["u"] = to_dev(acc.uniforms)
+
+    def run(self, b, ev=None):
+        sv, bt = self.sv, self.batches[b % len(self.batches)]
+        V, H = synth.VOCAB, synth.HIDDEN
+        if ev:
+            ev[0].record()
+        sv.vq2_moe_gemm(self.desc, bt["x"], bt["logits"], self.y, self.tidx[b % len(self.batches)],
+                        self.tw, ws=self.ws_moe)
+        if ev:
+            ev[1].record()
+        sv.vq8_lmhead_gemm(self.wq8, V, H, bt["h"], self.z, ws=self.ws_lm)
+        if ev:
+            ev[2].record()
+        sv.spec_accept(self.S, self.K, V, self.z, sv.SV_LOGITS, self.T, bt["draft"], sv.SV_LOGITS,
+                       self.T, bt["drafts"], bt["u"], self.toks, self.nacc, ws=self.ws_acc)
+        if ev:
+            ev[3].record()
+
+    def moe_bytes(self, b):
+        """Touched expert bytes of batch b (distinct routed experts + shared)."""
+        idx = self.tidx[b % len(self.batches)].cpu().numpy()
+        return (len(np.unique(idx)) + 1) * Q2_EXPERT_BYTES
+
+
+def measure(step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step.run(i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    moe = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    lm = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    acc = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    moe_b = np.array([step.moe_bytes(i) for i in range(steps)], np.float64)
+    return dict(total_ms=total_ms, wall_s=wall, moe_ms=moe, lm_ms=lm, acc_ms=acc, step_ms=step_ms,
+                moe_bytes=moe_b)
+
+
+def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
+    """The oracle, unchanged, on a bounded sample of the same workload."""
+    import threadpoolctl
+    import oracle
+    x_rows = synth.moe_rows(R, synth.CFG_MOE, sub=100 * R)
+    idx, _ = oracle.route_topk(x_rows.router_logits, synth.TOP_K)
+    experts = sorted(set(idx.reshape(-1).tolist()))[:n_experts]
+    x64 = oracle.linalg._exact_rows(x_rows.x_bf16, "bf16")
+    mats = {e: synth.expert_matrices(synth.CFG_MOE, e) for e in experts + [synth.N_ROUTED]}
+    packed = {e: [mats[e][m].packed() for m in range(3)] for e in mats}
+    q8 = synth.q8_random(synth.generator(synth.CFG_LMHEAD, synth.S_WEIGHTS), n_vocab, synth.HIDDEN, 0.01).packed()
+    h = synth.lm_head_hidden(R, synth.CFG_LMHEAD, sub=100 * R)
+    # warm the BLAS pool (untimed)
+    oracle.swiglu_expert(*packed[experts[0]], synth.HIDDEN, synth.INTER, x64[:1])
+    t0 = time.perf_counter()
+    for e in experts:
+        rows = sorted(set(np.nonzero(idx == e)[0].tolist()))
+        oracle.swiglu_expert(*packed[e], synth.HIDDEN, synth.INTER, x64[rows])
+    oracle.swiglu_expert(*packed[synth.N_ROUTED], synth.HIDDEN, synth.INTER, x64)
+    z = oracle.lm_head_logits(q8, n_vocab, synth.HIDDEN, h, "bf16")
+    S, K = 1, R - 1
+    tl = z.astype(np.float32)
+    acc_in = synth.accept_inputs(tl, S, K, 1.5, 0.8, synth.CFG_LMHEAD, sub=0)
+    oracle.spec_accept(S, K, n_vocab, tl, 0, 0.8, acc_in.draft_logits, 0, 0.8, acc_in.drafts,
+                       acc_in.uniforms)
+    dt = time.perf_counter() - t0
+    nbytes = (len(experts) + 1) * Q2_EXPERT_BYTES + n_vocab * synth.HIDDEN * 34 // 32
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    gbs = nbytes / dt / 1e9
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{len(experts)} routed experts (their routed rows) + the shared expert on "
+                       f"{R} rows, vocabulary head over {n_vocab} of {synth.VOCAB} rows, and "
+                       f"spec_accept (S=1, K={K}) over those {n_vocab} logits; {nbytes / 1e6:.1f} MB "
+                       f"of weights in {dt:.2f} s"),
+            "seconds": round(dt, 3),
+            "est_step_s": round(step_bytes_mean / (gbs * 1e9), 2),
+            "cpu": platform.processor() or platform.machine()}
+
+
+def result_line(args, R, S, m, cpu=None):
+    steps = len(m["step_ms"])
+    total_s = m["total_ms"] / 1e3
+    head_act = R * synth.HIDDEN * 2 + R * synth.VOCAB * 4
+    step_bytes = m["moe_bytes"] + Q8_HEAD_BYTES
+    gbs = float(step_bytes.sum() / total_s / 1e9)
+    lm_ms = float(m["lm_ms"].mean())
+    lm_bytes = Q8_HEAD_BYTES + head_act
+    achieved = lm_bytes / (lm_ms / 1e3) / 1e9
+    line = {
+        "metric": "verifier-step µs and weight HBM GB/s (Q2 MoE + Q8 lm_head, R=1..16)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_s * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"verifier step: MoE layer (256 routed + 1 shared two-bit SwiGLU experts, "
+                         f"7168<->2048, top-8) + eight-bit vocabulary head 129280x7168 + "
+                         f"spec_accept, R={R} rows, S={S} sequence(s) x K={R // S - 1} drafts, T=0.8"),
+            "R": R, "S": S, "K": R // S - 1, "batches": args.batches,
+        },
+        "step_us": {"median": round(float(np.median(m["step_ms"])) * 1e3, 2),
+                    "p10": round(float(np.percentile(m["step_ms"], 10)) * 1e3, 2),
+                    "p90": round(float(np.percentile(m["step_ms"], 90)) * 1e3, 2)},
+        "call_us": {"vq2_moe_gemm": round(float(m["moe_ms"].mean()) * 1e3, 2),
+                    "vq8_lmhead_gemm": round(lm_ms * 1e3, 2),
+                    "spec_accept": round(float(m["acc_ms"].mean()) * 1e3, 2)},
+        "weight_bytes_per_step": int(step_bytes.mean()),
+        "moe_gbs": round(float(m["moe_bytes"].sum() / (m["moe_ms"].sum() / 1e3) / 1e9), 1),
+        "hbm_frac_step": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "vq8_lmhead_gemm (staging + k_q8_lmhead)",
+                     "bytes_per_launch": lm_bytes},
+        "wall_s": round(m["wall_s"], 3),
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the verifier step "
+              "is measured per GPU and nothing here spans several GPUs.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_moe_tiny_amd as sv
+    sv.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    t = time.time()
+    log("generating 257 two-bit experts (3.7 GB) ...")
+    (g, u, d), (sg, su, sd) = gen_moe_weights()
+    wg, wu, wd, wsg, wsu, wsd = (to_dev(a) for a in (g, u, d, sg, su, sd))
+    del g, u, d
+    log(f"experts resident ({time.time() - t:.1f} s); generating the vocabulary head (985 MB) ...")
+    wq8 = to_dev(synth.lm_head_weights().packed())
+    log(f"head resident ({time.time() - t:.1f} s)")
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, synth.N_ROUTED, synth.TOP_K,
+                       wg, wu, wd, wsg, wsu, wsd)
+    rs = [int(r) for r in args.sweep.split(",")] if args.sweep else [args.rows]
+    for R in rs:
+        S = args.seqs if R % args.seqs == 0 else 1
+        step = Step(sv, desc, wq8, R, S, args.batches, args.temperature)
+        log(f"R={R} S={S}: {args.warmup} warmup + {args.steps} timed steps")
+        m = measure(step, args.steps, args.warmup)
+        cpu = None
+        if not args.no_cpu_baseline and not args.sweep:
+            log("cpu_baseline: timing the oracle on a bounded sample ...")
+            cpu = cpu_baseline(float((m["moe_bytes"] + Q8_HEAD_BYTES).mean()), R, args.cpu_experts,
+                               args.cpu_vocab)
+        print(json.dumps(result_line(args, R, S, m, cpu)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
