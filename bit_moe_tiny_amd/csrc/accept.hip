@@ -8,19 +8,19 @@
 // p_i(d_i), tested exactly as the sign of fma(u, q, -p); the replacement or
 // bonus token is the first x whose running sum exceeds u_K times the total.
 //
-// Two launches, no host sync:
+// Three launches, no host sync, no block waiting on another:
 //   k_acc_stats  grid (chunk, row): per 2048-entry chunk of every target and
 //                draft row, the chunk max of z/T and sum exp(z/T - max) in
 //                fp64 (or the plain sum for probability rows), plus a
 //                validity flag.  Spreads the vocabulary-wide reductions over
 //                many CUs.
-//   k_acc_resid  grid (chunk, sequence): every block recombines its
+//   k_acc_chunk  grid (chunk, sequence): every block recombines its
 //                sequence's row statistics (same order in every block, so all
 //                agree bit for bit), replays the accept chain, and sums the
 //                sampling weights of its chunk (residual, or p_K for the
-//                bonus).  The last block of a sequence to finish (device-scope
-//                counter) prefix-sums the chunk totals, finds the chunk that
-//                holds u_K * Z, scans it and writes the outputs.
+//                bonus).
+//   k_acc_pick   one block per sequence: prefix over the chunk totals, the
+//                chunk that holds u_K * Z, a block scan inside it, outputs.
 #include "sv_internal.h"
 
 namespace sv {
@@ -33,8 +33,9 @@ struct AccWs {
   double* cmax;     // [rows, CH]
   double* csum;     // [rows, CH]
   int* cbad;        // [rows, CH]
-  double* rsum;     // [S, CH]
-  unsigned* ctr;    // [S]
+  double* rsum;     // [S, CH]   sampling weight per chunk
+  double* sst;      // [S, 4]    pm, pz, qm, qz of the sampled row pair
+  int* sinfo;       // [S, 2]    n accepted, invalid
 };
 
 static inline int acc_chunks(int V) { return (V + ACC_CHUNK - 1) / ACC_CHUNK; }
@@ -51,14 +52,16 @@ static AccWs acc_carve(void* base, int S, int K, int V) {
   p += up256(rows * CH * 4);
   w.rsum = (double*)p;
   p += up256((size_t)S * CH * 8);
-  w.ctr = (unsigned*)p;
+  w.sst = (double*)p;
+  p += up256((size_t)S * 4 * 8);
+  w.sinfo = (int*)p;
   return w;
 }
 
 size_t accept_ws_bytes(int S, int K, int V) {
   const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V);
   return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256((size_t)S * CH * 8) +
-         up256((size_t)S * 4);
+         up256((size_t)S * 4 * 8) + up256((size_t)S * 2 * 4);
 }
 
 __device__ inline double wave_sum_d(double v) {
@@ -86,6 +89,25 @@ __device__ inline double block_max_d(double v, double* sh) {
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+}
+
+// Block-wide exclusive prefix sum in a fixed order (256 threads); returns the
+// exclusive prefix and sets *total.  `sh` holds 4 doubles.
+__device__ inline double block_excl_scan_d(double v, double* sh, double* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) sh[wv] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wv; ++w) base += sh[w];
+  *total = ((sh[0] + sh[1]) + sh[2]) + sh[3];
+  return base + inc - v;
 }
 
 struct RowSrc {
@@ -116,8 +138,6 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
   __shared__ double sh[4];
   __shared__ int shb[4];
   const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
-  if (c == 0 && r == 0)
-    for (int s = threadIdx.x; s < S; s += 256) ws.ctr[s] = 0u;
   const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
   const int x0 = c * ACC_CHUNK;
   double a[ACC_PER];
@@ -170,7 +190,7 @@ __device__ inline double dist_val(const RowSrc& s, double m, double z, int x) {
   return (double)v;
 }
 
-enum { MODE_RESID = 0, MODE_BONUS = 1, MODE_FALLBACK = 2 };
+enum { MODE_RESID = 0, MODE_P = 1 };
 
 __device__ inline double sample_weight(int mode, const RowSrc& P, double pm, double pz,
                                        const RowSrc& Q, double qm, double qz, int x) {
@@ -180,18 +200,22 @@ __device__ inline double sample_weight(int mode, const RowSrc& P, double pm, dou
   return fmax(p - q, 0.0);
 }
 
-__global__ __launch_bounds__(256) void k_acc_resid(int S, int K, int V, const float* target,
+// The row pair a sequence samples from, once n accepted drafts are known.
+__device__ inline void sample_rows(int s, int n, int S, int K, int V, const float* target,
+                                   int tkind, float Tp, const float* draft, int dkind, float Tq,
+                                   RowSrc& P, RowSrc& Q) {
+  P = row_src(s * (K + 1) + n, S, K, V, target, tkind, Tp, draft, dkind, Tq);
+  Q = n < K ? row_src(S * (K + 1) + s * K + n, S, K, V, target, tkind, Tp, draft, dkind, Tq) : P;
+}
+
+__global__ __launch_bounds__(256) void k_acc_chunk(int S, int K, int V, const float* target,
                                                    int tkind, float Tp, const float* draft,
                                                    int dkind, float Tq, const int32_t* drafts,
-                                                   const float* uni, int32_t* out_tokens,
-                                                   int32_t* out_n, AccWs ws) {
+                                                   const float* uni, AccWs ws) {
   __shared__ double rm[2 * SV_MAX_DRAFTS + 1], rz[2 * SV_MAX_DRAFTS + 1];
   __shared__ int rbad[2 * SV_MAX_DRAFTS + 1];
-  __shared__ int s_nacc, s_invalid, s_last;
+  __shared__ int s_nacc, s_invalid;
   __shared__ double sh[4];
-  __shared__ double s_csum[ACC_MAX_CH];
-  __shared__ double tsum[256];
-  __shared__ int s_pick, s_lastpos;
   const int c = blockIdx.x, s = blockIdx.y, CH = gridDim.x;
   const int nrows = 2 * K + 1;
   const int tid = threadIdx.x;
@@ -231,9 +255,8 @@ __global__ __launch_bounds__(256) void k_acc_resid(int S, int K, int V, const fl
     if (!inv) {
       for (; n < K; ++n) {
         const int d = drafts[s * K + n];
-        const RowSrc P = row_src(s * (K + 1) + n, S, K, V, target, tkind, Tp, draft, dkind, Tq);
-        const RowSrc Q = row_src(S * (K + 1) + s * K + n, S, K, V, target, tkind, Tp, draft,
-                                 dkind, Tq);
+        RowSrc P, Q;
+        sample_rows(s, n, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
         const double p = dist_val(P, rm[n], rz[n], d);
         const double q = dist_val(Q, rm[K + 1 + n], rz[K + 1 + n], d);
         const double u = (double)uni[s * (K + 1) + n];
@@ -242,20 +265,26 @@ __global__ __launch_bounds__(256) void k_acc_resid(int S, int K, int V, const fl
     }
     s_nacc = n;
     s_invalid = inv;
+    if (c == 0) {
+      ws.sinfo[2 * s] = n;
+      ws.sinfo[2 * s + 1] = inv;
+      ws.sst[4 * s + 0] = rm[n];
+      ws.sst[4 * s + 1] = rz[n];
+      ws.sst[4 * s + 2] = n < K ? rm[K + 1 + n] : 0.0;
+      ws.sst[4 * s + 3] = n < K ? rz[K + 1 + n] : 1.0;
+    }
   }
   __syncthreads();
-  const int nacc = s_nacc, invalid = s_invalid;
-  const int mode = nacc < K ? MODE_RESID : MODE_BONUS;
-  const RowSrc P = row_src(s * (K + 1) + nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq);
-  const RowSrc Q = nacc < K ? row_src(S * (K + 1) + s * K + nacc, S, K, V, target, tkind, Tp,
-                                      draft, dkind, Tq)
-                           : P;
+  const int nacc = s_nacc;
+  // 4. this chunk's total sampling weight (residual, or p_K for the bonus)
+  RowSrc P, Q;
+  sample_rows(s, nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
   const double pm = rm[nacc], pz = rz[nacc];
   const double qm = nacc < K ? rm[K + 1 + nacc] : 0.0, qz = nacc < K ? rz[K + 1 + nacc] : 1.0;
-  // 4. this chunk's total sampling weight
-  const int x0 = c * ACC_CHUNK;
+  const int mode = nacc < K ? MODE_RESID : MODE_P;
   double w = 0.0;
-  if (!invalid) {
+  if (!s_invalid) {
+    const int x0 = c * ACC_CHUNK;
 #pragma unroll
     for (int i = 0; i < ACC_PER; ++i) {
       const int x = x0 + tid * ACC_PER + i;
@@ -263,94 +292,94 @@ __global__ __launch_bounds__(256) void k_acc_resid(int S, int K, int V, const fl
     }
   }
   w = block_sum_d(w, sh);
-  if (tid == 0) {
-    ws.rsum[(size_t)s * CH + c] = w;
-    __threadfence();
-    const unsigned prev = atomicAdd(&ws.ctr[s], 1u);
-    s_last = (prev == (unsigned)CH - 1);
-    if (s_last) ws.ctr[s] = 0u;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // 5. last block of the sequence: inverse CDF over the chunk totals, then in-chunk
+  if (tid == 0) ws.rsum[(size_t)s * CH + c] = w;
+}
+
+__global__ __launch_bounds__(256) void k_acc_pick(int S, int K, int V, int CH,
+                                                  const float* target, int tkind, float Tp,
+                                                  const float* draft, int dkind, float Tq,
+                                                  const int32_t* drafts, const float* uni,
+                                                  int32_t* out_tokens, int32_t* out_n, AccWs ws) {
+  __shared__ double sh[4];
+  __shared__ double s_base;
+  __shared__ int s_hit, s_pick, s_last;
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int nacc = ws.sinfo[2 * s], invalid = ws.sinfo[2 * s + 1];
   int32_t* out = out_tokens + (size_t)s * (K + 1);
   if (invalid) {
     for (int i = tid; i <= K; i += 256) out[i] = -1;
     if (tid == 0) out_n[s] = -1;
     return;
   }
-  int smode = mode;
-  if (tid < CH) s_csum[tid] = ws.rsum[(size_t)s * CH + tid];
-  __syncthreads();
-  double Z = 0.0;
-  for (int cc = 0; cc < CH; ++cc) Z += s_csum[cc];
+  RowSrc P, Q;
+  sample_rows(s, nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
+  const double pm = ws.sst[4 * s], pz = ws.sst[4 * s + 1], qm = ws.sst[4 * s + 2],
+               qz = ws.sst[4 * s + 3];
+  int mode = nacc < K ? MODE_RESID : MODE_P;
+  double cw = tid < CH ? ws.rsum[(size_t)s * CH + tid] : 0.0;
+  double Z;
+  double pre = block_excl_scan_d(cw, sh, &Z);
   if (!(Z > 0.0)) {
-    // residual vanished (only through rounding): sample p_i itself
-    smode = MODE_FALLBACK;
+    // the residual vanished (only through rounding): sample p_i itself
+    mode = MODE_P;
+    cw = 0.0;
     for (int cc = 0; cc < CH; ++cc) {
       double t = 0.0;
 #pragma unroll
       for (int i = 0; i < ACC_PER; ++i) {
         const int x = cc * ACC_CHUNK + tid * ACC_PER + i;
-        if (x < V) t += sample_weight(smode, P, pm, pz, Q, qm, qz, x);
+        if (x < V) t += sample_weight(mode, P, pm, pz, Q, qm, qz, x);
       }
       t = block_sum_d(t, sh);
-      if (tid == 0) s_csum[cc] = t;
+      if (tid == cc) cw = t;
     }
-    __syncthreads();
-    Z = 0.0;
-    for (int cc = 0; cc < CH; ++cc) Z += s_csum[cc];
+    pre = block_excl_scan_d(cw, sh, &Z);
   }
   const double target_t = (double)uni[s * (K + 1) + K] * Z;
-  // chunk holding the target (sequential prefix over chunk totals)
-  int hit = -1, lastpos = -1;
-  double base = 0.0, run = 0.0;
-  for (int cc = 0; cc < CH; ++cc) {
-    if (s_csum[cc] > 0.0) lastpos = cc;
-    if (hit < 0 && run + s_csum[cc] > target_t) {
-      hit = cc;
-      base = run;
-    }
-    run += s_csum[cc];
+  // chunk holding the target: the first whose running total exceeds it
+  if (tid == 0) {
+    s_hit = 0x7fffffff;
+    s_last = -1;
+    s_pick = 0x7fffffff;
   }
-  const bool found_chunk = hit >= 0;
-  if (!found_chunk) {   // rounding pushed the target past the total: take the last positive entry
-    hit = lastpos >= 0 ? lastpos : 0;
-    base = 0.0;
-  }
-  // in-chunk inclusive scan, 8 consecutive entries per thread
+  __syncthreads();
+  if (tid < CH && pre + cw > target_t) atomicMin(&s_hit, tid);
+  if (tid < CH && cw > 0.0) atomicMax(&s_last, tid);
+  __syncthreads();
+  const bool found_chunk = s_hit != 0x7fffffff;
+  // no chunk crossed (rounding): fall back to the last chunk with weight
+  const int hit = found_chunk ? s_hit : (s_last >= 0 ? s_last : 0);
+  if (tid == hit) s_base = pre;   // exclusive prefix of chunk `hit`
+  __syncthreads();
+  const double base = found_chunk ? s_base : 0.0;
+  // in-chunk scan, 8 consecutive entries per thread
   double loc[ACC_PER];
   double tot = 0.0;
+  int lastmine = -1;
 #pragma unroll
   for (int i = 0; i < ACC_PER; ++i) {
     const int x = hit * ACC_CHUNK + tid * ACC_PER + i;
-    loc[i] = x < V ? sample_weight(smode, P, pm, pz, Q, qm, qz, x) : 0.0;
+    loc[i] = x < V ? sample_weight(mode, P, pm, pz, Q, qm, qz, x) : 0.0;
     tot += loc[i];
+    if (loc[i] > 0.0) lastmine = x;
   }
-  tsum[tid] = tot;
-  if (tid == 0) {
-    s_pick = 0x7fffffff;
-    s_lastpos = -1;
-  }
-  __syncthreads();
-  double excl = base;
-  for (int j = 0; j < tid; ++j) excl += tsum[j];   // fixed order; 256 entries at most
-  int mine = 0x7fffffff, lastmine = -1;
-  double run2 = excl;
+  double dummy;
+  double run = base + block_excl_scan_d(tot, sh, &dummy);
+  int mine = 0x7fffffff;
 #pragma unroll
   for (int i = 0; i < ACC_PER; ++i) {
-    const int x = hit * ACC_CHUNK + tid * ACC_PER + i;
-    run2 += loc[i];
-    if (loc[i] > 0.0) lastmine = x;
-    if (found_chunk && mine == 0x7fffffff && run2 > target_t) mine = x;
+    run += loc[i];
+    if (found_chunk && mine == 0x7fffffff && run > target_t) mine = hit * ACC_CHUNK + tid * ACC_PER + i;
   }
+  __syncthreads();
+  if (tid == 0) s_last = -1;
+  __syncthreads();
   if (mine != 0x7fffffff) atomicMin(&s_pick, mine);
-  if (lastmine >= 0) atomicMax(&s_lastpos, lastmine);
+  if (lastmine >= 0) atomicMax(&s_last, lastmine);
   __syncthreads();
   if (tid == 0) {
-    // none crossed (rounding, or no chunk held the target): last positive entry of the chunk
-    const int tok = s_pick != 0x7fffffff ? s_pick : s_lastpos;
+    // none crossed (rounding): the last positive entry of the chunk
+    const int tok = s_pick != 0x7fffffff ? s_pick : s_last;
     for (int i = 0; i < nacc; ++i) out[i] = drafts[s * K + i];
     out[nacc] = tok;
     for (int i = nacc + 1; i <= K; ++i) out[i] = -1;
@@ -368,8 +397,12 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
                      tkind, Tp, draft, dkind, Tq, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_acc_resid, dim3(CH, S), dim3(256), 0, s, S, K, V, target, tkind, Tp,
-                     draft, dkind, Tq, drafts, u, out_tokens, out_n, ws);
+  hipLaunchKernelGGL(k_acc_chunk, dim3(CH, S), dim3(256), 0, s, S, K, V, target, tkind, Tp, draft,
+                     dkind, Tq, drafts, u, ws);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_acc_pick, dim3(S), dim3(256), 0, s, S, K, V, CH, target, tkind, Tp, draft,
+                     dkind, Tq, drafts, u, out_tokens, out_n, ws);
   return hipGetLastError();
 }
 

@@ -16,11 +16,13 @@ namespace sv {
 
 __device__ inline float f16b_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// bytes 0,1 (or 2,3) of u under the exponent byte of 1024.0: v_perm_b32 picks
+// bytes 0-3 from its second operand and 4-7 from its first.
 __device__ inline h2_t bytes01_to_h2(uint32_t u) {
-  return __builtin_bit_cast(h2_t, (u & 0xFFu) | ((u & 0xFF00u) << 8) | 0x64006400u);
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
 }
 __device__ inline h2_t bytes23_to_h2(uint32_t u) {
-  return __builtin_bit_cast(h2_t, ((u >> 16) & 0xFFu) | ((u >> 8) & 0xFF0000u) | 0x64006400u);
+  return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
 }
 
 __device__ inline h8_t q8_bop(uint2 q) {
@@ -32,42 +34,133 @@ __device__ inline h8_t q8_bop(uint2 q) {
   return r;
 }
 
-template <bool USE_LO, int T>
+// One wave: T tiles of 16 vocabulary rows over all of K, in groups of 8 blocks
+// (256 k, one activation-image scale per column).
+//
+// Loads: a lane reads 16 contiguous code bytes, so the 4 lanes of a row cover
+// 64 bytes -- two blocks -- per instruction (32-byte pieces per row measure
+// ~25% below the streaming read rate on this part; 64-byte pieces match it).
+// One v_permlane32_swap per dword pair then gives every lane 8 bytes of each
+// of the two blocks: lanes of k-group g hold block bytes 8*kofs(g)..+7 with
+// kofs = (0, 2, 1, 3) for g = 0..3, and the activation operand is read at the
+// same offsets.  Weight groups are double buffered: the loads of group j+1
+// are issued before group j is computed.
+template <int T, bool DVEC>
+struct Q8Grp {
+  uint4 q[T][4];     // 4 block pairs
+  uint4 dv[T];
+  uint16_t dd[T][DVEC ? 1 : 8];
+};
+
+template <int T, bool DVEC>
+__device__ inline void q8_grp_load(const Q8View& W, const size_t* rowb, int kg, int nblk, int g,
+                                   Q8Grp<T, DVEC>& G) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      if (DVEC || 2 * p < nblk) G.q[t][p] = *(const uint4*)(W.qs + (rowb[t] + kg + 2 * p) * 32 + 16 * g);
+    if (DVEC) {
+      G.dv[t] = *(const uint4*)(W.d + rowb[t] + kg);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < nblk) G.dd[t][DVEC ? 0 : i] = W.d[rowb[t] + kg + i];
+    }
+  }
+}
+
+// Regroup one pair: returns (block A bytes, block B bytes) of this lane as uint2 each.
+__device__ inline void q8_regroup(uint4 v, uint2& a, uint2& b) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(v.x, v.z, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(v.y, v.w, false, false);
+  a = make_uint2(s0[0], s1[0]);
+  b = make_uint2(s0[1], s1[1]);
+}
+
+// DVEC: the block count is a multiple of 8, so every group is full -- no
+// guards at all, and a group's 8 block scales come in one 16-byte load.
+template <bool USE_LO, int T, bool DVEC>
 __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, float* logits) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int tile0 = (blockIdx.x * 4 + wv) * T;
-  const int vocab = W.n_out, K = W.nb * 32;
+  const int vocab = W.n_out, K = W.nb * 32, nb = W.nb;
   if (tile0 * 16 >= vocab) return;
   const int nl = lane & 15, g = lane >> 4, cg = blockIdx.z;
-  const int c = cg * 16 + nl;
-  const _Float16* xh = c < R ? img.hi + (size_t)c * K : nullptr;
-  const _Float16* xl = c < R ? img.lo + (size_t)c * K : nullptr;
-  int nrow[T];
+  const int kofs = 8 * (((g & 1) << 1) | (g >> 1));   // k offset of this lane's 8 values in a block
+  // padding columns read row R-1: an output column depends only on its own
+  // operand row and padding columns are never stored, so every load stays
+  // unconditional (branches around loads would serialise the memory waits)
+  const int c = min(cg * 16 + nl, R - 1);
+  const _Float16* xh = img.hi + (size_t)c * K + kofs;
+  const _Float16* xl = img.lo + (size_t)c * K + kofs;
+  const float* bs = img.bscale + (size_t)c * img.nbk;
+  size_t rowb[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int n = (tile0 + t) * 16 + nl;
-    nrow[t] = n < vocab ? n : vocab - 1;   // ragged tail: valid row, result dropped
+    rowb[t] = (size_t)(n < vocab ? n : vocab - 1) * nb;   // ragged tail: valid row, result dropped
   }
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const h8_t z8 = {0, 0, 0, 0, 0, 0, 0, 0};
   f4_t acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = zero;
-  for (int kb = 0; kb < W.nb; ++kb) {
-    const h8_t a = xh ? *(const h8_t*)(xh + kb * 32 + 8 * g) : z8;
-    h8_t al = z8;
-    if (USE_LO) al = xl ? *(const h8_t*)(xl + kb * 32 + 8 * g) : z8;
+  Q8Grp<T, DVEC> cur, nxt;
+  q8_grp_load<T, DVEC>(W, rowb, 0, min(8, nb), g, cur);
+  for (int kg = 0; kg < nb; kg += 8) {
+    const int nblk = min(8, nb - kg);
+    // issue order = use order: the loads retire in order, so the activation
+    // operands of this group go out before the weights of the next one
+    h8_t xa[8], xb[USE_LO ? 8 : 1];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const size_t b = (size_t)nrow[t] * W.nb + kb;
-      const uint2 q = *(const uint2*)(W.qs + b * 32 + 8 * g);
-      const float d = f16b_to_f32(W.d[b]);
-      const h8_t bw = q8_bop(q);
-      f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw, zero, 0, 0, 0);
-      if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bw, dt, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(d, dt[e], acc[t][e]);
+    for (int i = 0; i < 8; ++i) {
+      if (DVEC || i < nblk) {
+        xa[i] = *(const h8_t*)(xh + (kg + i) * 32);
+        if (USE_LO) xb[USE_LO ? i : 0] = *(const h8_t*)(xl + (kg + i) * 32);
+      }
     }
+    if (kg + 8 < nb) q8_grp_load<T, DVEC>(W, rowb, kg + 8, min(8, nb - kg - 8), g, nxt);
+    const float s_own = bs[kg >> 3];
+    f4_t xs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) xs[e] = __shfl(s_own, 4 * g + e, 64);
+    f4_t gacc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) gacc[t] = zero;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (DVEC || 2 * p < nblk) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          uint2 qa, qb;
+          q8_regroup(cur.q[t][p], qa, qb);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int i = 2 * p + h;
+            if (DVEC || i < nblk) {
+              const h8_t bw = q8_bop(h == 0 ? qa : qb);
+              f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[i], bw, zero, 0, 0, 0);
+              if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xb[USE_LO ? i : 0], bw, dt, 0, 0, 0);
+              uint16_t db;
+              if (DVEC) {
+                const uint32_t w32 = p == 0 ? cur.dv[t].x : p == 1 ? cur.dv[t].y : p == 2 ? cur.dv[t].z : cur.dv[t].w;
+                db = (uint16_t)(w32 >> (16 * h));
+              } else {
+                db = cur.dd[t][DVEC ? 0 : i];
+              }
+              const float d = f16b_to_f32(db);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) gacc[t][e] = fmaf(d, dt[e], gacc[t][e]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(xs[e], gacc[t][e], acc[t][e]);
+    cur = nxt;
   }
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -76,23 +169,31 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int cc = cg * 16 + 4 * g + e;
-      if (cc < R) logits[(size_t)cc * vocab + n] = acc[t][e] * img.rscale[cc];
+      if (cc < R) logits[(size_t)cc * vocab + n] = acc[t][e];
     }
   }
 }
 
-constexpr int LM_T = 2;
+// two tiles per wave: with double-buffered weight groups this keeps two waves
+// per SIMD resident; 129280 rows then run in two full rounds of waves
+template <bool USE_LO, int T>
+static void launch_lm(int R, hipStream_t s, const Q8View& W, const XImg& img, float* logits) {
+  const int tiles = (W.n_out + 15) / 16;
+  const int waves = (tiles + T - 1) / T;
+  const dim3 grid((waves + 3) / 4, 1, (R + 15) / 16);
+  if (W.nb % 8 == 0)
+    hipLaunchKernelGGL((k_q8_lmhead<USE_LO, T, true>), grid, dim3(256), 0, s, W, R, img, logits);
+  else
+    hipLaunchKernelGGL((k_q8_lmhead<USE_LO, T, false>), grid, dim3(256), 0, s, W, R, img, logits);
+}
 
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo, XImg img,
                             float* logits, hipStream_t s) {
   const Q8View W = q8_view(w, vocab, hidden);
-  const int tiles = (vocab + 15) / 16;
-  const int waves = (tiles + LM_T - 1) / LM_T;
-  const dim3 grid((waves + 3) / 4, 1, (R + 15) / 16);
   if (use_lo)
-    hipLaunchKernelGGL((k_q8_lmhead<true, LM_T>), grid, dim3(256), 0, s, W, R, img, logits);
+    launch_lm<true, 2>(R, s, W, img, logits);
   else
-    hipLaunchKernelGGL((k_q8_lmhead<false, LM_T>), grid, dim3(256), 0, s, W, R, img, logits);
+    launch_lm<false, 2>(R, s, W, img, logits);
   return hipGetLastError();
 }
 

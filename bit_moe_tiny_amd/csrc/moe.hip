@@ -5,7 +5,7 @@
 //   k_moe_prep    block 0 routes all rows (top-k on logits, softmax weights)
 //                 and groups (row, slot) pairs by expert so each touched
 //                 expert's weights are read once ("MoE gate_up expert dedup",
-//                 ds4-on-spark README, introduction); blocks 1..R stage x.
+//                 ds4-on-spark README, introduction); the other blocks stage x.
 //   k_q2_gateup   grid (n-tile of inter, unit, column group): 4 waves split K,
 //                 one pass computes gate and up and applies SwiGLU ("fused
 //                 gate+up+swiglu MoE decode", 1x Spark tuned DSpark thread,
@@ -13,8 +13,12 @@
 //   k_stage       stages h per (row, slot) assignment.
 //   k_q2_down     grid (64-row group of hidden, unit, column group); each wave
 //                 one 16-row tile over all of inter; per-assignment outputs go
-//                 to the workspace and the last block of each row group
-//                 combines them in a fixed order: slots 0..k-1, then shared.
+//                 to the workspace.
+//   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
+//                 slots 0..k-1, then the shared expert.
+// Blocks never wait on each other inside a kernel: on a part whose L2 is split
+// across dies, a device-wide fence per block would cost far more than the
+// extra launch.
 #include "sv_internal.h"
 #include "sv_q2.h"
 #include "sv_stage.h"
@@ -28,7 +32,6 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   const int has_shared = (!plain && d->s_gate) ? 1 : 0;
   const int max_units = plain ? 1 : (R * k < d->n_experts ? R * k : d->n_experts) + has_shared;
   const int max_assign = plain ? R : R * k + has_shared * R;
-  const int n_groups = plain ? 0 : d->hidden / 64;
   uint8_t* p = (uint8_t*)base;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -45,7 +48,6 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.amap = (int*)take(sizeof(int) * R * (k + 1));
   w.topk_idx = (int*)take(sizeof(int) * R * k);
   w.topk_w = (float*)take(sizeof(float) * R * k);
-  w.ctr = (unsigned*)take(sizeof(unsigned) * (n_groups ? n_groups : 1));
   w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
   void* xb = take(ximg_bytes(R, d->hidden, XL_PERM));
@@ -56,7 +58,6 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   }
   w.max_units = max_units;
   w.max_assign = max_assign;
-  w.n_down_groups = n_groups;
   if (out) *out = w;
   return off;
 }
@@ -78,6 +79,12 @@ __device__ inline void wave_argmax(float& bv, int& bi) {
   }
 }
 
+__device__ inline float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
 __device__ inline float wave_sum_f(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -86,13 +93,12 @@ __device__ inline float wave_sum_f(float v) {
 
 // Block 0: top-k + grouping.  256 threads.
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
-                                int n_ctr, int32_t* idx_out, float* w_out, MoeWs ws) {
+                                int32_t* idx_out, float* w_out, MoeWs ws) {
   __shared__ int s_idx[SV_MAX_ROWS * SV_MAX_TOPK];
   __shared__ int cnt[SV_MAX_EXPERTS];
   __shared__ int eoff[SV_MAX_EXPERTS];
   __shared__ int s_nu;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int i = tid; i < n_ctr; i += 256) ws.ctr[i] = 0u;
   for (int e = tid; e < E; e += 256) cnt[e] = 0;
   if (logits == nullptr) {  // one expert, no router: weight 1
     for (int i = tid; i < R * k; i += 256) {
@@ -146,7 +152,7 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
         for (int i = 0; i < PER; ++i)
           if (lane + 64 * i == bi) taken |= 1u << i;
         if (lane == 0) {
-          const float w = expf(logits[(size_t)r * E + bi] - mx) / sum;
+          const float w = expf(bv - mx) / sum;
           s_idx[r * k + s] = bi;
           ws.topk_idx[r * k + s] = bi;
           ws.topk_w[r * k + s] = w;
@@ -213,18 +219,15 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   }
 }
 
+template <int DT>
 __global__ __launch_bounds__(256) void k_moe_prep(const float* logits, int R, int E, int k,
-                                                  int has_shared, int n_ctr, int32_t* idx_out,
-                                                  float* w_out, const void* x, int x_dtype,
-                                                  int hidden, MoeWs ws) {
-  extern __shared__ float xs[];
-  __shared__ float red[4];
-  __shared__ int flag[4];
+                                                  int has_shared, int32_t* idx_out, float* w_out,
+                                                  const void* x, MoeWs ws) {
   if (blockIdx.x == 0) {
-    route_and_group(logits, R, E, k, has_shared, n_ctr, idx_out, w_out, ws);
+    route_and_group(logits, R, E, k, has_shared, idx_out, w_out, ws);
   } else {
-    const int row = blockIdx.x - 1;
-    stage_row(x, x_dtype, (size_t)row * hidden, row, hidden, XL_PERM, ws.x_img, xs, red, flag);
+    stage_gid<DT>(x, R, XL_PERM, ws.x_img, (blockIdx.x - 1) * 8 + (threadIdx.x >> 5),
+                  threadIdx.x & 31);
   }
 }
 
@@ -232,9 +235,14 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            const void* x, int x_dtype, int32_t* topk_idx_out,
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
   const int has_shared = d->s_gate ? 1 : 0;
-  hipLaunchKernelGGL(k_moe_prep, dim3(1 + R), dim3(256), (size_t)d->hidden * sizeof(float), s,
-                     router_logits, R, d->n_experts, d->top_k, has_shared, ws.n_down_groups,
-                     topk_idx_out, topk_w_out, x, x_dtype, d->hidden, ws);
+  const int groups = R * (d->hidden / 256);
+  const dim3 grid(1 + (groups + 7) / 8);
+  if (x_dtype == SV_BF16)
+    hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(256), 0, s, router_logits, R, d->n_experts,
+                       d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
+  else
+    hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(256), 0, s, router_logits, R, d->n_experts,
+                       d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
   return hipGetLastError();
 }
 
@@ -252,24 +260,20 @@ __global__ __launch_bounds__(256) void k_q2_gateup(ExpertPtrs P, int hidden, int
   const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
   const int c0 = cg * 16;
   if (c0 >= cnt) return;
-  const Q2View G = q2_view(e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg, inter, hidden);
-  const Q2View U = q2_view(e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su, inter, hidden);
+  Q2View W[2];
+  W[0] = q2_view(e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg, inter, hidden);
+  W[1] = q2_view(e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su, inter, hidden);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int n = nt * 16 + nl;
-  const XRow x = xrow(ws.x_img, (c0 + nl < cnt) ? ws.arow[off + c0 + nl] : -1);
+  const XRow x = xrow(ws.x_img, (c0 + nl < cnt) ? ws.arow[off + c0 + nl] : -1, ws.arow[off]);
   const int nb = hidden / 256;
-  const int kb0 = nb * wv / 4, kb1 = nb * (wv + 1) / 4;
-  f4_t ag = {0.f, 0.f, 0.f, 0.f}, au = ag;
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const Q2Blk bg = q2_load(G, n, kb, g);
-    const Q2Blk bu = q2_load(U, n, kb, g);
-    q2_block<USE_LO>(bg, x, kb, g, ag);
-    q2_block<USE_LO>(bu, x, kb, g, au);
-  }
+  const int kb0 = nb * wv / 4;
+  f4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  q2_run<2, USE_LO>(W, n, kb0, nb * (wv + 1) / 4 - kb0, x, lane, acc);
   __shared__ f4_t red[2][4][64];
-  red[0][wv][lane] = ag;
-  red[1][wv][lane] = au;
+  red[0][wv][lane] = acc[0];
+  red[1][wv][lane] = acc[1];
   __syncthreads();
   if (wv != 0) return;
   f4_t sg = red[0][0][lane], su = red[1][0][lane];
@@ -282,11 +286,8 @@ __global__ __launch_bounds__(256) void k_q2_gateup(ExpertPtrs P, int hidden, int
   for (int i = 0; i < 4; ++i) {
     const int c = c0 + 4 * g + i;
     if (c >= cnt) continue;
-    const int a = off + c;
-    const float rs = ws.x_img.rscale[ws.arow[a]];
-    const float gv = sg[i] * rs, uv = su[i] * rs;
-    const float hv = gv / (1.f + expf(-gv)) * uv;
-    ws.h[(size_t)a * inter + n] = hv;
+    const float gv = sg[i], uv = su[i];
+    ws.h[(size_t)(off + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
   }
 }
 
@@ -320,57 +321,106 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws,
 }
 
 // ------------------------------------------------------------------ down
-__global__ __launch_bounds__(256) void k_q2_down(ExpertPtrs P, int hidden, int inter, int R,
-                                                 int k, int has_shared, MoeWs ws, float* y) {
+// Grid (64-row group of hidden, unit, group of 4 columns).  The block's (up
+// to 4) h rows are staged in LDS once -- all 4 waves use the same rows over
+// all of inter -- then each wave streams one 16-row tile of the down matrix.
+constexpr int DOWN_COLS = 4;
+
+__host__ __device__ inline size_t down_lds_bytes(int inter) {
+  return (size_t)DOWN_COLS * inter * 2 * 2 + (size_t)DOWN_COLS * (inter / 16) * 2 * 2 +
+         (size_t)DOWN_COLS * (inter / 256) * 4;
+}
+
+__global__ __launch_bounds__(256) void k_q2_down(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
+  extern __shared__ __align__(16) uint8_t lds[];
   const int grp = blockIdx.x, u = blockIdx.y, cg = blockIdx.z;
-  const int n_units = ws.meta->n_units;
-  if (u >= n_units) return;
+  if (u >= ws.meta->n_units) return;
   const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
-  const int c0 = cg * 16;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
+  const int c0 = cg * DOWN_COLS;
+  if (c0 >= cnt) return;
+  const int ncols = min(DOWN_COLS, cnt - c0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nl = lane & 15;
   const int n = grp * 64 + wv * 16 + nl;
-  if (c0 < cnt) {
-    const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
-    const XRow x = xrow(ws.h_img, (c0 + nl < cnt) ? off + c0 + nl : -1);
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const int nb = inter / 256;
-    for (int kb = 0; kb < nb; ++kb) {
-      const Q2Blk b = q2_load(D, n, kb, g);
-      q2_block<true>(b, x, kb, g, acc);
+  const int nbk = inter / 256;
+  XLds X;
+  X.K = inter;
+  X.nbk = nbk;
+  _Float16* hi = (_Float16*)lds;
+  _Float16* lo = hi + DOWN_COLS * inter;
+  _Float16* sxh = lo + DOWN_COLS * inter;
+  _Float16* sxl = sxh + DOWN_COLS * (inter / 16);
+  float* bs = (float*)(sxl + DOWN_COLS * (inter / 16));
+  X.hi = hi;
+  X.lo = lo;
+  X.sxh = sxh;
+  X.sxl = sxl;
+  X.bs = bs;
+  // stage the rows of assignments off+c0 .. off+c0+ncols-1 (16-byte pieces)
+  const XImg& H = ws.h_img;
+  for (int c = 0; c < ncols; ++c) {
+    const size_t a = (size_t)(off + c0 + c);
+    for (int i = tid; i < inter / 8; i += 256) {
+      *(uint4*)(hi + c * inter + 8 * i) = *(const uint4*)(H.hi + a * inter + 8 * i);
+      *(uint4*)(lo + c * inter + 8 * i) = *(const uint4*)(H.lo + a * inter + 8 * i);
     }
+    for (int i = tid; i < inter / 16; i += 256) {
+      sxh[c * (inter / 16) + i] = H.sxh[a * (inter / 16) + i];
+      sxl[c * (inter / 16) + i] = H.sxl[a * (inter / 16) + i];
+    }
+    for (int i = tid; i < nbk; i += 256) bs[c * nbk + i] = H.bscale[a * nbk + i];
+  }
+  __syncthreads();
+  const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // lane column c = nl reads LDS row nl & 3; columns >= ncols are padding (not stored)
+  q2_run_lds(D, n, nbk, X, nl & 3, lane, acc);
+  const int g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = c0 + 4 * g + i;
-      if (c < cnt) ws.part[(size_t)(off + c) * hidden + n] = acc[i] * ws.h_img.rscale[off + c];
-    }
-  }
-  // fixed-order combine by the last block of this row group
-  __shared__ int last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const unsigned total = (unsigned)n_units * gridDim.z;
-    const unsigned prev = atomicAdd(&ws.ctr[grp], 1u);
-    last = (prev == total - 1);
-    if (last) ws.ctr[grp] = 0u;
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < R * 64; i += 256) {
-    const int r = i / 64, nn = grp * 64 + (i & 63);
-    float acc = 0.f;
-    for (int s = 0; s < k; ++s)
-      acc = fmaf(ws.topk_w[r * k + s], ws.part[(size_t)ws.amap[r * (k + 1) + s] * hidden + nn], acc);
-    if (has_shared) acc += ws.part[(size_t)ws.amap[r * (k + 1) + k] * hidden + nn];
-    y[(size_t)r * hidden + nn] = acc;
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * g + i;   // tile column; only 0..ncols-1 are real
+    if (c < ncols) ws.part[(size_t)(off + c0 + c) * hidden + n] = acc[i];
   }
 }
 
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const dim3 grid(d->hidden / 64, ws.max_units, (R + 15) / 16);
-  hipLaunchKernelGGL(k_q2_down, grid, dim3(256), 0, s, expert_ptrs(d), d->hidden, d->inter, R,
+  const dim3 grid(d->hidden / 64, ws.max_units, (R + DOWN_COLS - 1) / DOWN_COLS);
+  hipLaunchKernelGGL(k_q2_down, grid, dim3(256), down_lds_bytes(d->inter), s, expert_ptrs(d),
+                     d->hidden, d->inter, ws);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_moe_combine(d, R, ws, y, s);
+}
+
+// --------------------------------------------------------------- combine
+// y[r, n] = sum_{s<k} w[r, s] * part[a(r, s), n] (+ part[a(r, shared), n]), in slot order.
+// Grid (hidden/256, R): the row's slot map goes to LDS first, then all of its
+// partial loads are issued together.
+__global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_shared, MoeWs ws,
+                                                     float* y) {
+  __shared__ int s_a[SV_MAX_TOPK + 1];
+  __shared__ float s_w[SV_MAX_TOPK];
+  const int r = blockIdx.y, tid = threadIdx.x;
+  if (tid <= k) s_a[tid] = ws.amap[r * (k + 1) + tid];
+  if (tid < k) s_w[tid] = ws.topk_w[r * k + tid];
+  __syncthreads();
+  const int n = blockIdx.x * 256 + tid;
+  if (n >= hidden) return;
+  const int ns = k + has_shared;
+  float v[SV_MAX_TOPK + 1];
+#pragma unroll
+  for (int s = 0; s <= SV_MAX_TOPK; ++s)
+    if (s < ns) v[s] = ws.part[(size_t)s_a[s] * hidden + n];
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < SV_MAX_TOPK; ++s)
+    if (s < k) acc = fmaf(s_w[s], v[s], acc);
+  if (has_shared) acc += v[k];
+  y[(size_t)r * hidden + n] = acc;
+}
+
+hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden + 255) / 256, R), dim3(256), 0, s, d->hidden,
                      d->top_k, d->s_gate ? 1 : 0, ws, y);
   return hipGetLastError();
 }
@@ -388,17 +438,14 @@ __global__ __launch_bounds__(256) void k_q2_plain(const uint8_t* w, int n_out, i
   const int nld = n < n_out ? n : n_out - 1;   // ragged tail: load a valid row, drop the result
   const Q2View W = q2_view(w, n_out, k_in);
   const int c = cg * 16 + nl;
-  const XRow x = xrow(img, c < R ? c : -1);
+  const XRow x = xrow(img, c < R ? c : -1, 0);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < W.nb; ++kb) {
-    const Q2Blk b = q2_load(W, nld, kb, g);
-    q2_block<USE_LO>(b, x, kb, g, acc);
-  }
+  q2_run<1, USE_LO>(&W, nld, 0, W.nb, x, lane, &acc);
   if (n >= n_out) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int cc = cg * 16 + 4 * g + i;
-    if (cc < R) y[(size_t)cc * n_out + n] = acc[i] * img.rscale[cc];
+    if (cc < R) y[(size_t)cc * n_out + n] = acc[i];
   }
 }
 

@@ -71,9 +71,12 @@ __host__ __device__ inline Q8View q8_view(const void* base, int n_out, int k_in)
 }
 
 // ------------------------------------------------------- activation images
-// Rows of activations prepared for the fp16 matrix cores: each row scaled by
-// a power of two (2^e, chosen so the row's largest magnitude lies in
-// [2^10, 2^11)) and split into an fp16 high part and an fp16 remainder.
+// Rows of activations prepared for the fp16 matrix cores.  Every 256-element
+// block of a row is scaled by its own power of two 2^e (its largest magnitude
+// lands in [2^10, 2^11), far from fp16 overflow even after 16-element sums)
+// and split into an fp16 high part and an fp16 remainder (~22 significant
+// bits together).  bscale holds 2^-e per (row, block); consumers multiply
+// each block's partial result by it, so the scaling is exact end to end.
 //  layout PERM (two-bit kernels): element order matches the register order in
 //    which the two-bit kernel unpacks codes, with the 4^-j factor of each
 //    position folded in; plus per-16-element sums (for the min term).
@@ -83,14 +86,16 @@ struct XImg {
   _Float16* lo;      // [rows, K]
   _Float16* sxh;     // [rows, K/16]  (PERM only)
   _Float16* sxl;     // [rows, K/16]
-  float* rscale;     // [rows]  2^-e, multiplies the result
+  float* bscale;     // [rows, nbk]  2^-e per 256-element block
   int K;
+  int nbk;           // ceil(K / 256)
 };
 
 enum { XL_PERM = 0, XL_PLAIN = 1 };
 
 __host__ __device__ inline size_t ximg_bytes(size_t rows, size_t K, int layout) {
-  size_t b = 2 * up256(rows * K * 2) + up256(rows * 4);
+  size_t nbk = (K + 255) / 256;
+  size_t b = 2 * up256(rows * K * 2) + up256(rows * nbk * 4);
   if (layout == XL_PERM) b += 2 * up256(rows * (K / 16) * 2);
   return b;
 }
@@ -99,6 +104,7 @@ inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
   uint8_t* p = (uint8_t*)base;
   XImg x;
   x.K = K;
+  x.nbk = (K + 255) / 256;
   x.hi = (_Float16*)p;
   p += up256(rows * K * 2);
   x.lo = (_Float16*)p;
@@ -111,7 +117,7 @@ inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
   } else {
     x.sxh = x.sxl = nullptr;
   }
-  x.rscale = (float*)p;
+  x.bscale = (float*)p;
   return x;
 }
 
@@ -131,12 +137,11 @@ struct MoeWs {
   int* amap;          // [R, top_k+1]  assignment of (row, slot); slot top_k = shared
   int* topk_idx;      // [R, top_k]
   float* topk_w;      // [R, top_k]
-  unsigned* ctr;      // [n_down_groups] combine counters
   float* h;           // [max_assign, inter]  SwiGLU output
   float* part;        // [max_assign, hidden] per-assignment down outputs
   XImg x_img;         // staged x  [R, hidden]
   XImg h_img;         // staged h  [max_assign, inter]
-  int max_units, max_assign, n_down_groups;
+  int max_units, max_assign;
 };
 
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out);
@@ -153,6 +158,7 @@ hipError_t launch_q2_plain(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, f
 hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws,
                             hipStream_t s);
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
+hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo,
                             XImg img, float* logits, hipStream_t s);
 hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, float Tp,

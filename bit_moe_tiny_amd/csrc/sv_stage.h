@@ -1,28 +1,28 @@
-// Device routine that stages one activation row into an XImg (see stage.hip).
+// Device routine that stages one 256-element block of an activation row into
+// an XImg (layout and scaling described in sv_internal.h).  32 lanes -- half a
+// wave -- share one block: each lane converts 8 elements, the block's scale
+// comes from a 32-lane max, so a whole row set is staged in one parallel pass.
 #pragma once
 
 #include "sv_internal.h"
 
 namespace sv {
 
-__device__ inline float load_act(const void* src, int dtype, size_t idx) {
-  if (dtype == SV_BF16) {
-    uint32_t b = ((const uint16_t*)src)[idx];
-    return __uint_as_float(b << 16);
+template <int DT>
+__device__ inline void load4_act(const void* src, size_t idx, float* v) {
+  if (DT == SV_BF16) {
+    const uint2 b = *(const uint2*)((const uint16_t*)src + idx);
+    v[0] = __uint_as_float(b.x << 16);
+    v[1] = __uint_as_float(b.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(b.y << 16);
+    v[3] = __uint_as_float(b.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *(const float4*)((const float*)src + idx);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
   }
-  return ((const float*)src)[idx];
-}
-
-__device__ inline float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ inline int wave_or_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
 }
 
 __device__ inline void split16(float v, _Float16& hi, _Float16& lo) {
@@ -30,76 +30,95 @@ __device__ inline void split16(float v, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(v - (float)hi);
 }
 
-// Stage source row `src[base .. base+K)` into image row `row`.  256 threads;
-// `xs` is K floats of LDS, `red`/`flag` 4 entries each.
-__device__ inline void stage_row(const void* src, int dtype, size_t base, int row, int K,
-                                 int layout, XImg img, float* xs, float* red, int* flag) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// Stage block kb of image row `row`, whose source elements start at
+// src[src_base].  l = lane index within the half-wave (0..31).
+template <int DT>
+__device__ inline void stage_block(const void* src, size_t src_base, int row, int kb, int layout,
+                                   const XImg& img, int l) {
+  const int K = img.K;
+  const int k0 = kb * 256;
+  float v[8];
+  size_t dst;
+  if (layout == XL_PERM) {
+    // lane = chunk (t, g) of the block: element e = 2j + hb <-> k = 16 s + 4 hs + j + 8 hb
+    const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
+    float a[4], b[4];
+    load4_act<DT>(src, src_base + k0 + 16 * s + 4 * hs, a);
+    load4_act<DT>(src, src_base + k0 + 16 * s + 4 * hs + 8, b);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = a[j];
+      v[2 * j + 1] = b[j];
+    }
+    dst = (size_t)row * K + (size_t)(kb * 32 + l) * 8;
+  } else {
+    const int ka = k0 + 8 * l;
+    if (ka < K) {
+      load4_act<DT>(src, src_base + ka, v);
+      load4_act<DT>(src, src_base + ka + 4, v + 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    }
+    dst = (size_t)row * K + ka;
+  }
   float mx = 0.f;
   int bad = 0;
-  for (int k = tid; k < K; k += 256) {
-    float v = load_act(src, dtype, base + k);
-    xs[k] = v;
-    float a = fabsf(v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float a = fabsf(v[e]);
     bad |= !(a <= 3.402823466e38f);   // inf or NaN
     mx = fmaxf(mx, a);
   }
-  mx = wave_max_f(mx);
-  bad = wave_or_i(bad);
-  if (lane == 0) {
-    red[wv] = mx;
-    flag[wv] = bad;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    bad |= __shfl_xor(bad, o, 32);
   }
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  bad = flag[0] | flag[1] | flag[2] | flag[3];
   int esc = 0;
   if (!bad && mx > 0.f) {
     int E;
     frexpf(mx, &E);          // mx in [2^(E-1), 2^E)
-    esc = 11 - E;            // mx * 2^esc in [2^10, 2^11)
+    esc = 11 - E;            // block max lands in [2^10, 2^11)
     esc = esc < -120 ? -120 : (esc > 120 ? 120 : esc);
   }
-  const size_t rb = (size_t)row * K;
-  if (layout == XL_PERM) {
-    // chunk = 8 halves read by one lane for one matrix-core step:
-    // ch = (kb*8 + t)*4 + g; element e = 2j + hb <-> k = kb*256 + 16*s + 4*hs + j + 8*hb,
-    // s = 4g + (t>>1), hs = t&1, scaled by 4^-j.
-    for (int ch = tid; ch < K / 8; ch += 256) {
-      const int kb = ch >> 5, t = (ch >> 2) & 7, g = ch & 3;
-      const int s = 4 * g + (t >> 1), hs = t & 1;
-      h8_t hv, lv;
+  if (layout == XL_PLAIN && k0 + 8 * l >= K) return;
+  h8_t hv, lv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = e >> 1, hb = e & 1;
-        const int k = kb * 256 + 16 * s + 4 * hs + j + 8 * hb;
-        _Float16 h, l;
-        split16(ldexpf(xs[k], esc - 2 * j), h, l);
-        hv[e] = h;
-        lv[e] = l;
-      }
-      *(h8_t*)(img.hi + rb + (size_t)ch * 8) = hv;
-      *(h8_t*)(img.lo + rb + (size_t)ch * 8) = lv;
-    }
-    const size_t sb0 = (size_t)row * (K / 16);
-    for (int sb = tid; sb < K / 16; sb += 256) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc += ldexpf(xs[16 * sb + i], esc);
-      _Float16 h, l;
-      split16(acc, h, l);
-      img.sxh[sb0 + sb] = h;
-      img.sxl[sb0 + sb] = l;
-    }
-  } else {
-    for (int k = tid; k < K; k += 256) {
-      _Float16 h, l;
-      split16(ldexpf(xs[k], esc), h, l);
-      img.hi[rb + k] = h;
-      img.lo[rb + k] = l;
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int sh = layout == XL_PERM ? esc - 2 * (e >> 1) : esc;   // 4^-j folded in (PERM)
+    _Float16 h, lo;
+    split16(ldexpf(v[e], sh), h, lo);
+    hv[e] = h;
+    lv[e] = lo;
   }
-  if (tid == 0) img.rscale[row] = ldexpf(1.f, -esc);
+  *(h8_t*)(img.hi + dst) = hv;
+  *(h8_t*)(img.lo + dst) = lv;
+  if (layout == XL_PERM && l < 16) {   // sum of sub-block l (the min term)
+    float a[4], acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      load4_act<DT>(src, src_base + k0 + 16 * l + 4 * q, a);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += ldexpf(a[i], esc);
+    }
+    _Float16 h, lo;
+    split16(acc, h, lo);
+    const size_t so = (size_t)row * (K / 16) + kb * 16 + l;
+    img.sxh[so] = h;
+    img.sxl[so] = lo;
+  }
+  if (l == 0) img.bscale[(size_t)row * img.nbk + kb] = ldexpf(1.f, -esc);
+}
+
+// Stage rows [0, n_rows) of `src` ([rows, K], row-major) with one half-wave per
+// (row, block); `gid` enumerates (row, block) pairs.
+template <int DT>
+__device__ inline void stage_gid(const void* src, int n_rows, int layout, const XImg& img, int gid,
+                                 int l) {
+  const int row = gid / img.nbk, kb = gid - row * img.nbk;
+  if (row >= n_rows) return;
+  stage_block<DT>(src, (size_t)row * img.K, row, kb, layout, img, l);
 }
 
 }  // namespace sv
