@@ -1,0 +1,266 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration the benchmark times, on outputs the oracle computes one by one.
+
+* one SwiGLU expert (7168 -> 2048 -> 7168, two-bit) on R = 1, 2, 4, 8 bf16
+  rows: every output against the oracle;
+* the full MoE layer (256 routed + 1 shared experts, top-8) on R = 5 rows:
+  routing indices bit-exact for every row, routing weights and two sampled rows
+  of y against the oracle;
+* the vocabulary head (129,280 x 7,168, eight-bit) on R = 5 rows: a sample of
+  vocabulary rows (head, tail and random) against the oracle, then spec_accept
+  at V = 129,280 and T = 0.8 on the GPU's logits (T_q = 0.8 and the T_q = 1
+  variant), decisions compared with the oracle's on identical inputs;
+* the cohort: 3 sequences x 5 rows = 15 rows through the same layer and head,
+  per-sequence spec_accept;
+* the R = 1..16 stress sweep: every R against the oracle on sampled vocabulary
+  rows, and the MoE layer's rows checked for batch invariance (row r of an
+  R-row call equals row r of the 16-row call) plus sampled rows against the
+  oracle;
+* a full-vocabulary rejection workload given as probabilities, where decisions
+  and tokens must match the oracle exactly (identical fp32 p, q and u).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle.accept import LOGITS, PROBS
+from tests.gpu_util import dev, empty, host, say
+from tests.parity import accept_flags, assert_close, sample_flag
+
+pytestmark = pytest.mark.gpu
+
+H, I, V, E, TOPK = synth.HIDDEN, synth.INTER, synth.VOCAB, synth.N_ROUTED, synth.TOP_K
+BG = oracle.q2_matrix_bytes(I, H)
+BD = oracle.q2_matrix_bytes(H, I)
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import bit_moe_tiny_amd as m
+    m.load()
+    return m
+
+
+@pytest.fixture(scope="module")
+def layer(sv):
+    """The MoE layer of the moe_layer workload, resident on the GPU, plus the
+    host buffers the oracle reads."""
+    say("generating the MoE layer (257 experts)")
+    w = synth.moe_weights(synth.CFG_MOE)
+    t = [dev(a) for a in (w.gate, w.up, w.down, w.s_gate, w.s_up, w.s_down)]
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, H, I, E, TOPK, *t)
+    return w, desc
+
+
+@pytest.fixture(scope="module")
+def head(sv):
+    say("generating the vocabulary head")
+    buf = synth.lm_head_weights().packed()
+    return buf, dev(buf)
+
+
+def _vocab_sample(seed: int, n: int = 2048) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(V, size=n, replace=False)
+    return np.unique(np.concatenate([np.arange(64), np.arange(V - 64, V), pick]))
+
+
+def _oracle_moe_rows(w, x_bf16, logits, rows):
+    """Oracle y for the given rows only (each row's output depends on that row alone)."""
+    sub_x = x_bf16[rows]
+    sub_l = logits[rows]
+    y, idx, wts = oracle.moe_layer(w.gate, w.up, w.down, w.s_gate, w.s_up, w.s_down, E, TOPK, H,
+                                   I, sub_x, "bf16", sub_l)
+    return y
+
+
+def _run_moe(sv, desc, x, logits):
+    R = x.shape[0]
+    y = empty((R, H), "f32")
+    ti = empty((R, TOPK), "i32")
+    tw = empty((R, TOPK), "f32")
+    sv.vq2_moe_gemm(desc, dev(x), dev(logits), y, ti, tw)
+    return host(y), host(ti), host(tw)
+
+
+def _run_head(sv, wdev, h):
+    R = h.shape[0]
+    z = empty((R, V), "f32")
+    sv.vq8_lmhead_gemm(wdev, V, H, dev(h), z)
+    return host(z)
+
+
+def _check_accept(sv, z, S, K, Tp, Tq, acc):
+    """spec_accept on the GPU vs the oracle on the same fp32 logits."""
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    say("spec_accept", S, K, V, Tp, Tq)
+    sv.spec_accept(S, K, V, dev(z), sv.SV_LOGITS, Tp, dev(acc.draft_logits), sv.SV_LOGITS, Tq,
+                   dev(acc.drafts), dev(acc.uniforms), toks, nacc)
+    gt, gn = host(toks), host(nacc)
+    wt, wn = oracle.spec_accept(S, K, V, z, LOGITS, Tp, acc.draft_logits, LOGITS, Tq, acc.drafts,
+                                acc.uniforms)
+    zz = z.reshape(S, K + 1, V)
+    dd = acc.draft_logits.reshape(S, K, V)
+    for s in range(S):
+        p_rows = [oracle.softmax_t(zz[s, i], Tp) for i in range(K + 1)]
+        q_rows = [oracle.softmax_t(dd[s, i], Tq) for i in range(K)]
+        if accept_flags(p_rows, q_rows, acc.drafts[s], acc.uniforms[s], int(wn[s])):
+            continue   # an accept test within 1e-6 of its boundary: flagged, not failed
+        assert gn[s] == wn[s], f"sequence {s}: n_accepted {gn[s]} vs oracle {wn[s]}"
+        n = int(wn[s])
+        if not np.array_equal(gt[s], wt[s]):
+            wgt = (np.maximum(p_rows[n] - q_rows[n], 0.0) if n < K else p_rows[K])
+            assert sample_flag(wgt, acc.uniforms[s, K]), (
+                f"sequence {s}: tokens {gt[s]} vs oracle {wt[s]}")
+    return wn
+
+
+# ---------------------------------------------------------------- expert
+@pytest.mark.parametrize("R", [1, 2, 4, 8])
+def test_expert_workload(sv, R):
+    ex = synth.expert(R)
+    g, u, d = (ex.mats[m].packed() for m in (synth.M_GATE, synth.M_UP, synth.M_DOWN))
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, H, I, 1, 1, dev(g), dev(u), dev(d))
+    y = empty((R, H), "f32")
+    say("vq2_moe_gemm one expert", R)
+    sv.vq2_moe_gemm(desc, dev(ex.x_bf16), None, y)
+    x64 = oracle.linalg._exact_rows(ex.x_bf16, "bf16")
+    want = oracle.swiglu_expert(g, u, d, H, I, x64)
+    assert_close(host(y), want, what=f"expert R={R}")
+
+
+# ------------------------------------------------------------- MoE layer
+def test_moe_layer_workload(sv, layer):
+    w, desc = layer
+    rows = synth.moe_rows(5, synth.CFG_MOE)
+    say("vq2_moe_gemm full layer R=5")
+    y, ti, tw = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
+    widx, ww = oracle.route_topk(rows.router_logits, TOPK)
+    assert np.array_equal(ti, widx)
+    assert_close(tw, ww, what="topk_w")
+    check = [0, 4]
+    want = _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check)
+    assert_close(y[check], want, what="moe layer y")
+
+
+# ------------------------------------------------------------ vocab head
+@pytest.mark.parametrize("Tq", [0.8, 1.0])
+def test_lm_head_workload_and_accept(sv, head, Tq):
+    buf, wdev = head
+    R, S, K, T = 5, 1, 4, 0.8
+    h = synth.lm_head_hidden(R)
+    say("vq8_lmhead_gemm full head R=5")
+    z = _run_head(sv, wdev, h)
+    cols = _vocab_sample(31)
+    want = oracle.lm_head_logits(buf, V, H, h, "bf16", rows=cols)
+    assert_close(z[:, cols], want, what="lm head")
+    acc = synth.accept_inputs(z, S, K, 1.5, Tq, synth.CFG_LMHEAD)
+    _check_accept(sv, z, S, K, T, Tq, acc)
+
+
+# ---------------------------------------------------------------- cohort
+def test_cohort_workload(sv, layer, head):
+    w, desc = layer
+    buf, wdev = head
+    R, S, K, T = 15, 3, 4, 0.8
+    rows = synth.moe_rows(R, synth.CFG_COHORT)
+    say("vq2_moe_gemm cohort R=15")
+    y, ti, tw = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
+    widx, ww = oracle.route_topk(rows.router_logits, TOPK)
+    assert np.array_equal(ti, widx)
+    assert_close(tw, ww, what="topk_w")
+    check = [7, 14]
+    assert_close(y[check], _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check),
+                 what="cohort moe y")
+    h = synth.lm_head_hidden(R, synth.CFG_COHORT)
+    say("vq8_lmhead_gemm cohort R=15")
+    z = _run_head(sv, wdev, h)
+    cols = _vocab_sample(32, 1024)
+    assert_close(z[:, cols], oracle.lm_head_logits(buf, V, H, h, "bf16", rows=cols),
+                 what="cohort head")
+    acc = synth.accept_inputs(z, S, K, 1.5, T, synth.CFG_COHORT)
+    _check_accept(sv, z, S, K, T, T, acc)
+
+
+# ----------------------------------------------------------------- sweep
+@pytest.fixture(scope="module")
+def sweep16(sv, layer, head):
+    """16-row inputs of the sweep and the GPU results of the 16-row calls."""
+    w, desc = layer
+    buf, wdev = head
+    rows = synth.moe_rows(16, synth.CFG_COHORT, sub=16)
+    h = synth.lm_head_hidden(16, synth.CFG_COHORT, sub=16)
+    say("sweep reference calls R=16")
+    y16, ti16, _ = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
+    z16 = _run_head(sv, wdev, h)
+    return rows, h, y16, ti16, z16
+
+
+def test_sweep_moe_r16_against_oracle(sv, layer, sweep16):
+    w, _ = layer
+    rows, _, y16, ti16, _ = sweep16
+    assert np.array_equal(ti16, oracle.route_topk(rows.router_logits, TOPK)[0])
+    check = [3, 15]
+    assert_close(y16[check], _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check),
+                 what="sweep R=16 moe y")
+
+
+@pytest.mark.parametrize("R", list(range(1, 16)))
+def test_sweep_moe_batch_invariance(sv, layer, sweep16, R):
+    """Row r of an R-row call equals row r of the 16-row call: each row's
+    output depends on that row alone, so the oracle check of the 16-row call
+    carries over (tolerance far below the parity bar)."""
+    _, desc = layer
+    rows, _, y16, ti16, _ = sweep16
+    say("vq2_moe_gemm sweep", R)
+    y, ti, _ = _run_moe(sv, desc, rows.x_bf16[:R].copy(), rows.router_logits[:R].copy())
+    assert np.array_equal(ti, ti16[:R])
+    assert_close(y, y16[:R], tol=1e-5, what=f"moe R={R} vs R=16")
+
+
+@pytest.mark.parametrize("R", list(range(1, 17)))
+def test_sweep_lm_head(sv, head, sweep16, R):
+    buf, wdev = head
+    _, h, _, _, z16 = sweep16
+    say("vq8_lmhead_gemm sweep", R)
+    z = _run_head(sv, wdev, h[:R].copy())
+    cols = _vocab_sample(100 + R, 512)
+    assert_close(z[:, cols], oracle.lm_head_logits(buf, V, H, h[:R], "bf16", rows=cols),
+                 what=f"head R={R}")
+    assert_close(z, z16[:R], tol=1e-5, what=f"head R={R} vs R=16")
+
+
+# ----------------------------------------------- full-vocabulary rejection
+@pytest.mark.parametrize("S,K", [(4, 4), (2, 0), (1, 15)])
+def test_full_vocab_probs_exact(sv, S, K):
+    """p and q over V = 129,280 given as fp32 probabilities (q a perturbed p,
+    so rejections happen): decisions bit-exact, tokens exact unless the
+    sampling target sits on a CDF boundary."""
+    g = synth.generator(120, S, K)
+    zt = synth.normal(g, S * (K + 1) * V, 2.0).reshape(S * (K + 1), V)
+    p = np.stack([oracle.softmax_t(r.astype(np.float32), 1.0) for r in zt]).astype(np.float32)
+    q = np.zeros((0, V), np.float32)
+    drafts = np.zeros((S, K), np.int32)
+    if K:
+        zq = (zt.reshape(S, K + 1, V)[:, :K].reshape(S * K, V)
+              + synth.normal(g, S * K * V, 1.5).reshape(S * K, V))
+        q = np.stack([oracle.softmax_t(r.astype(np.float32), 1.0) for r in zq]).astype(np.float32)
+        drafts = synth.gumbel_drafts(zq.astype(np.float32), 1.0, g).reshape(S, K)
+    u = synth.uniform24(g, S * (K + 1)).reshape(S, K + 1)
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    say("spec_accept probs full vocab", S, K)
+    sv.spec_accept(S, K, V, dev(p), sv.SV_PROBS, 1.0, dev(q) if K else None, sv.SV_PROBS, 1.0,
+                   dev(drafts) if K else None, dev(u), toks, nacc)
+    gt, gn = host(toks), host(nacc)
+    wt, wn = oracle.spec_accept(S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    assert np.array_equal(gn, wn)
+    for s in range(S):
+        if np.array_equal(gt[s], wt[s]):
+            continue
+        n = int(wn[s])
+        pr = p[s * (K + 1) + n].astype(np.float64)
+        wgt = np.maximum(pr - q[s * K + n], 0.0) if n < K else pr
+        assert sample_flag(wgt, u[s, K]), f"sequence {s}: {gt[s]} vs {wt[s]}"
