@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=3, help="routed experts in the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=16384, help="vocab rows in the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the bench, one plain device copy of this many MiB (fp32 x 1.0): "
+                         "the known-size kernel that calibrates profiler byte counters")
     return ap.parse_args()
 
 
@@ -287,6 +290,14 @@ def main():
             cpu = cpu_baseline(float((m["moe_bytes"] + Q8_HEAD_BYTES).mean()), R, args.cpu_experts,
                                args.cpu_vocab)
         print(json.dumps(result_line(args, R, S, m, cpu)), flush=True)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
 
 
 if __name__ == "__main__":

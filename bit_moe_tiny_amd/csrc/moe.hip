@@ -2,17 +2,20 @@
 // projection with a fixed-order weighted combine, and the one-matrix form.
 //
 // Launch sequence of one layer (all on the caller's stream, no host sync):
-//   k_moe_prep    block 0 routes all rows (top-k on logits, softmax weights)
+//   k_moe_prep    block 0 routes all rows (top-k on logits, softmax weights;
+//                 one wave per row, wave-wide reductions on the DPP network)
 //                 and groups (row, slot) pairs by expert so each touched
 //                 expert's weights are read once ("MoE gate_up expert dedup",
-//                 ds4-on-spark README, introduction); the other blocks stage x.
-//   k_q2_gateup   grid (n-tile of inter, unit, column group): 4 waves split K,
-//                 one pass computes gate and up and applies SwiGLU ("fused
-//                 gate+up+swiglu MoE decode", 1x Spark tuned DSpark thread,
-//                 Q&A answer 3).  h is kept in fp32.
-//   k_stage       stages h per (row, slot) assignment.
-//   k_q2_down     grid (64-row group of hidden, unit, column group); each wave
-//                 one 16-row tile over all of inter; per-assignment outputs go
+//                 ds4-on-spark README, introduction); the other blocks stage x
+//                 into the fp16 image the two-bit kernels read.
+//   k_q2_gateup   grid (16-row tile of inter, unit, column group), 8 waves:
+//                 gate and up x 4 K-quarters; the unit's rows are copied into
+//                 LDS once per block; the partial sums meet in LDS and one wave
+//                 applies SwiGLU ("fused gate+up+swiglu MoE decode", 1x Spark
+//                 tuned DSpark thread, Q&A answer 3).  h is kept in fp32.
+//   k_q2_down     grid (128-row group of hidden, unit, column group), 8 waves
+//                 of one 16-row tile over all of inter; the block converts its
+//                 h rows into the LDS image itself; per-assignment outputs go
 //                 to the workspace.
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
@@ -24,6 +27,8 @@
 #include "sv_stage.h"
 
 namespace sv {
+
+constexpr int LDS_BUDGET = 80 * 1024 - 256;   // two 512-thread blocks per CU (160 KB LDS)
 
 // ------------------------------------------------------------ workspace
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
@@ -51,47 +56,124 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
   void* xb = take(ximg_bytes(R, d->hidden, XL_PERM));
-  void* hb = take(plain ? 0 : ximg_bytes(max_assign, d->inter, XL_PERM));
-  if (p) {
-    w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
-    if (!plain) w.h_img = ximg_carve(hb, max_assign, d->inter, XL_PERM);
-  }
+  if (p) w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
   w.max_units = max_units;
   w.max_assign = max_assign;
   if (out) *out = w;
   return off;
 }
 
-// ---------------------------------------------------------------- routing
-__device__ inline bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// ---------------------------------------------------- wave reductions (DPP)
+// Reductions to lane 63 on the row-shift / row-broadcast network, then one
+// readlane: a few cycles per step instead of an LDS round trip per shuffle.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-__device__ inline void wave_argmax(float& bv, int& bi) {
+__device__ inline uint32_t wave_umax(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xF>(v));   // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xF>(v));   // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xF>(v));   // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xF>(v));   // row_shr:8   lane 15 of each row: the row's max
+  v = max(v, dpp_u32<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u32<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ inline uint32_t wave_umin(uint32_t v) {
+  v = min(v, dpp_u32<0x111, 0xF>(v));
+  v = min(v, dpp_u32<0x112, 0xF>(v));
+  v = min(v, dpp_u32<0x114, 0xF>(v));
+  v = min(v, dpp_u32<0x118, 0xF>(v));
+  v = min(v, dpp_u32<0x142, 0xA>(v));
+  v = min(v, dpp_u32<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum in a fixed order (run-to-run identical): zeros are shifted in at row
+// edges and into the rows a broadcast step leaves alone.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, (int)__float_as_uint(x), CTRL, ROWS, 0xF, false);
+  return x + __uint_as_float((uint32_t)y);
+}
+
+__device__ inline float wave_sum(float x) {
+  x = dpp_add<0x111, 0xF>(x);
+  x = dpp_add<0x112, 0xF>(x);
+  x = dpp_add<0x114, 0xF>(x);
+  x = dpp_add<0x118, 0xF>(x);
+  x = dpp_add<0x142, 0xA>(x);
+  x = dpp_add<0x143, 0xC>(x);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
+}
+
+// Order-preserving key of a logit: larger logit -> larger key; NaN -> 0, the
+// smallest (NaN ranks after every number, as in an ascending sort of -logit).
+__device__ inline uint32_t logit_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ---------------------------------------------------------------- routing
+constexpr int PREP_THREADS = 1024;
+
+// One wave: top-k of one row of E logits (E <= 64 * PER), by logit, ties to
+// the lower index; weights = softmax probability over all E.
+template <int PER>
+__device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, int32_t* idx_out,
+                          float* w_out, MoeWs ws) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[PER];
+  float v[PER];
+  unsigned taken = 0;
+  uint32_t lk0 = 0;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(bv, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[(size_t)r * E + e] : -INFINITY;
+    key[i] = logit_key(v[i]);
+    if (e >= E) taken |= 1u << i;
+    else lk0 = max(lk0, key[i]);
+  }
+  const float mx = key_logit(wave_umax(lk0));   // the largest logit
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (!(taken >> i & 1)) sum += expf(v[i] - mx);
+  sum = wave_sum(sum);
+  for (int s = 0; s < k; ++s) {
+    uint32_t lk = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (!(taken >> i & 1)) lk = max(lk, key[i]);
+    const uint32_t gk = wave_umax(lk);
+    uint32_t li = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (!(taken >> i & 1) && key[i] == gk) li = min(li, (uint32_t)(lane + 64 * i));
+    const int bi = (int)wave_umin(li);
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + 64 * i == bi) taken |= 1u << i;
+    if (lane == 0) {
+      const float w = expf(key_logit(gk) - mx) / sum;
+      s_idx[r * k + s] = bi;
+      ws.topk_idx[r * k + s] = bi;
+      ws.topk_w[r * k + s] = w;
+      if (idx_out) idx_out[r * k + s] = bi;
+      if (w_out) w_out[r * k + s] = w;
     }
   }
 }
 
-__device__ inline float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-__device__ inline float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Block 0: top-k + grouping.  256 threads.
+// Block 0 of the prep kernel: top-k of every row, then grouping.
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
                                 int32_t* idx_out, float* w_out, MoeWs ws) {
   __shared__ int s_idx[SV_MAX_ROWS * SV_MAX_TOPK];
@@ -99,9 +181,10 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   __shared__ int eoff[SV_MAX_EXPERTS];
   __shared__ int s_nu;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  constexpr int NW = PREP_THREADS / 64;
+  for (int e = tid; e < E; e += PREP_THREADS) cnt[e] = 0;
   if (logits == nullptr) {  // one expert, no router: weight 1
-    for (int i = tid; i < R * k; i += 256) {
+    for (int i = tid; i < R * k; i += PREP_THREADS) {
       s_idx[i] = 0;
       ws.topk_idx[i] = 0;
       ws.topk_w[i] = 1.f;
@@ -109,61 +192,16 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
       if (w_out) w_out[i] = 1.f;
     }
   } else {
-    constexpr int PER = SV_MAX_EXPERTS / 64;
-    for (int r = wv; r < R; r += 4) {
-      float v[PER];
-      unsigned taken = 0;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? logits[(size_t)r * E + e] : -INFINITY;
-        if (e >= E) taken |= 1u << i;
-        mx = fmaxf(mx, v[i]);
-      }
-      mx = wave_max_f(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (!(taken >> i & 1)) sum += expf(v[i] - mx);
-      sum = wave_sum_f(sum);
-      for (int s = 0; s < k; ++s) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int e = lane + 64 * i;
-          if (!(taken >> i & 1) && better(v[i], e, bv, bi)) {
-            bv = v[i];
-            bi = e;
-          }
-        }
-        wave_argmax(bv, bi);
-        if (bi == 0x7fffffff) {  // only unordered (NaN) values left: lowest free index
-          int fi = 0x7fffffff;
-#pragma unroll
-          for (int i = 0; i < PER; ++i)
-            if (!(taken >> i & 1)) fi = min(fi, lane + 64 * i);
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) fi = min(fi, __shfl_xor(fi, o, 64));
-          bi = fi;
-        }
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (lane + 64 * i == bi) taken |= 1u << i;
-        if (lane == 0) {
-          const float w = expf(bv - mx) / sum;
-          s_idx[r * k + s] = bi;
-          ws.topk_idx[r * k + s] = bi;
-          ws.topk_w[r * k + s] = w;
-          if (idx_out) idx_out[r * k + s] = bi;
-          if (w_out) w_out[r * k + s] = w;
-        }
-      }
+    for (int r = wv; r < R; r += NW) {
+      if (E <= 64) route_row<1>(logits, r, E, k, s_idx, idx_out, w_out, ws);
+      else if (E <= 128) route_row<2>(logits, r, E, k, s_idx, idx_out, w_out, ws);
+      else if (E <= 256) route_row<4>(logits, r, E, k, s_idx, idx_out, w_out, ws);
+      else if (E <= 512) route_row<8>(logits, r, E, k, s_idx, idx_out, w_out, ws);
+      else route_row<16>(logits, r, E, k, s_idx, idx_out, w_out, ws);
     }
   }
   __syncthreads();
-  for (int i = tid; i < R * k; i += 256) atomicAdd(&cnt[s_idx[i]], 1);
+  for (int i = tid; i < R * k; i += PREP_THREADS) atomicAdd(&cnt[s_idx[i]], 1);
   __syncthreads();
   if (wv == 0) {  // touched experts in ascending order -> units, assignment offsets
     int base_u = 0, base_a = 0;
@@ -194,7 +232,7 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   }
   __syncthreads();
   const int nu = s_nu;
-  for (int i = tid; i < R * k; i += 256) {
+  for (int i = tid; i < R * k; i += PREP_THREADS) {
     const int r = i / k, s = i - r * k, e = s_idx[i];
     int rank = 0;  // rows before r that chose e (each row picks an expert at most once)
     for (int j = 0; j < r * k; ++j) rank += s_idx[j] == e;
@@ -203,7 +241,7 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
     ws.amap[r * (k + 1) + s] = a;
   }
   if (has_shared) {
-    for (int r = tid; r < R; r += 256) {
+    for (int r = tid; r < R; r += PREP_THREADS) {
       ws.arow[R * k + r] = r;
       ws.amap[r * (k + 1) + k] = R * k + r;
     }
@@ -220,13 +258,13 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
 }
 
 template <int DT>
-__global__ __launch_bounds__(256) void k_moe_prep(const float* logits, int R, int E, int k,
-                                                  int has_shared, int32_t* idx_out, float* w_out,
-                                                  const void* x, MoeWs ws) {
+__global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, int R, int E, int k,
+                                                           int has_shared, int32_t* idx_out,
+                                                           float* w_out, const void* x, MoeWs ws) {
   if (blockIdx.x == 0) {
     route_and_group(logits, R, E, k, has_shared, idx_out, w_out, ws);
   } else {
-    stage_gid<DT>(x, R, XL_PERM, ws.x_img, (blockIdx.x - 1) * 8 + (threadIdx.x >> 5),
+    stage_gid<DT>(x, R, XL_PERM, ws.x_img, (blockIdx.x - 1) * (PREP_THREADS / 32) + (threadIdx.x >> 5),
                   threadIdx.x & 31);
   }
 }
@@ -236,14 +274,138 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
   const int has_shared = d->s_gate ? 1 : 0;
   const int groups = R * (d->hidden / 256);
-  const dim3 grid(1 + (groups + 7) / 8);
+  constexpr int per_block = PREP_THREADS / 32;
+  const dim3 grid(1 + (groups + per_block - 1) / per_block);
   if (x_dtype == SV_BF16)
-    hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(256), 0, s, router_logits, R, d->n_experts,
-                       d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
+    hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
+                       d->n_experts, d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
   else
-    hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(256), 0, s, router_logits, R, d->n_experts,
-                       d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
+    hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
+                       d->n_experts, d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ LDS staging
+struct XLw {   // writable view of the LDS rows
+  _Float16 *hi, *lo, *sx;
+  float* bst;
+  int K, nbk;
+};
+
+__device__ inline XLw xl_make(uint8_t* lds, int ncols, int K, bool use_lo) {
+  XLw w;
+  xl_carve<_Float16>((_Float16*)lds, ncols, K, use_lo, w.hi, w.lo, w.sx, w.bst);
+  w.K = K;
+  w.nbk = K / 256;
+  return w;
+}
+
+__device__ inline XL xl_view(const XLw& w) {
+  XL x;
+  x.hi = w.hi;
+  x.lo = w.lo;
+  x.sx = w.sx;
+  x.bst = w.bst;
+  x.K = w.K;
+  return x;
+}
+
+// Copy rows rows[0..ncols) of a prepared global image into LDS (whole block).
+__device__ inline void xl_copy_image(const XImg& img, const int* rows, int ncols, bool use_lo,
+                                     const XLw& L) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int K = L.K, per = K / 8;   // 16-byte pieces per row
+  for (int i = tid; i < ncols * per; i += nt) {
+    const int c = i / per, j = i - c * per;
+    const size_t r = (size_t)rows[c];
+    const int o = (8 * j) ^ xl_swz(c);
+    *(uint4*)(L.hi + (size_t)c * K + o) = *(const uint4*)(img.hi + r * K + 8 * j);
+    if (use_lo) *(uint4*)(L.lo + (size_t)c * K + o) = *(const uint4*)(img.lo + r * K + 8 * j);
+  }
+  const int ng = K / 64;   // groups of 4 sub-block sums per row
+  for (int i = tid; i < ncols * ng; i += nt) {
+    const int c = i / ng, j = i - c * ng;
+    const size_t r = (size_t)rows[c];
+    const uint2 h = *(const uint2*)(img.sxh + r * (K / 16) + 4 * j);
+    const uint2 l = *(const uint2*)(img.sxl + r * (K / 16) + 4 * j);
+    *(uint4*)(L.sx + (size_t)c * (K / 8) + 8 * j) = make_uint4(h.x, h.y, l.x, l.y);
+  }
+  for (int i = tid; i < (L.nbk + 1) * XL_MAX_COLS; i += nt) {
+    const int kb = i / XL_MAX_COLS, c = i % XL_MAX_COLS;
+    L.bst[i] = (c < ncols && kb < L.nbk) ? img.bscale[(size_t)rows[c] * img.nbk + kb] : 0.f;
+  }
+}
+
+// Convert fp32 rows src[rows[c]] (length K) into the LDS image: one half-wave
+// per (row, 256-block) pair, same scaling and order as the global stager.
+__device__ inline void xl_stage_f32(const float* src, const int* rows, int ncols, const XLw& L) {
+  const int l = threadIdx.x & 31, hw = threadIdx.x >> 5, nhw = blockDim.x >> 5;
+  for (int p = hw; p < ncols * L.nbk; p += nhw) {
+    const int c = p / L.nbk, kb = p - c * L.nbk;
+    const float* row = src + (size_t)rows[c] * L.K;
+    const int k0 = kb * 256;
+    // lane = chunk (t, g) of the block: element e = 2j + hb <-> k = 16 s + 4 hs + j + 8 hb
+    const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
+    const float4 a = *(const float4*)(row + k0 + 16 * s + 4 * hs);
+    const float4 b = *(const float4*)(row + k0 + 16 * s + 4 * hs + 8);
+    const float v[8] = {a.x, b.x, a.y, b.y, a.z, b.z, a.w, b.w};
+    float mx = 0.f;
+    int bad = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float m = fabsf(v[e]);
+      bad |= !(m <= 3.402823466e38f);
+      mx = fmaxf(mx, m);
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+      bad |= __shfl_xor(bad, o, 32);
+    }
+    int esc = 0;
+    if (!bad && mx > 0.f) {
+      int E;
+      frexpf(mx, &E);
+      esc = 11 - E;
+      esc = esc < -120 ? -120 : (esc > 120 ? 120 : esc);
+    }
+    h8_t hv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float sv = ldexpf(v[e], esc - 2 * (e >> 1));   // 4^-j folded in
+      const _Float16 h = (_Float16)sv;
+      hv[e] = h;
+      lv[e] = (_Float16)(sv - (float)h);
+    }
+    const size_t dst = (size_t)c * L.K + (((kb * 32 + l) * 8) ^ xl_swz(c));
+    *(h8_t*)(L.hi + dst) = hv;
+    *(h8_t*)(L.lo + dst) = lv;
+    if (l < 16) {   // sum of sub-block l (the min term)
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x4 = *(const float4*)(row + k0 + 16 * l + 4 * q);
+        acc += ldexpf(x4.x, esc);
+        acc += ldexpf(x4.y, esc);
+        acc += ldexpf(x4.z, esc);
+        acc += ldexpf(x4.w, esc);
+      }
+      const _Float16 h = (_Float16)acc;
+      _Float16* sp = L.sx + (size_t)c * (L.K / 8) + (kb * 4 + (l >> 2)) * 8 + (l & 3);
+      sp[0] = h;
+      sp[4] = (_Float16)(acc - (float)h);
+    }
+    if (l == 0) L.bst[kb * XL_MAX_COLS + c] = ldexpf(1.f, -esc);
+  }
+  for (int i = threadIdx.x; i < (L.nbk + 1) * XL_MAX_COLS; i += blockDim.x)
+    if (i % XL_MAX_COLS >= ncols || i >= L.nbk * XL_MAX_COLS) L.bst[i] = 0.f;
+}
+
+// Largest column group (rows per block) whose LDS copy fits the budget.
+static int col_group(int K, bool use_lo, int R) {
+  int cg = XL_MAX_COLS;
+  while (cg > 1 && xl_bytes(cg, K, use_lo) > (size_t)LDS_BUDGET) --cg;
+  return cg < R ? cg : R;
 }
 
 // ------------------------------------------------------------- gate / up
@@ -252,44 +414,6 @@ struct ExpertPtrs {
   const uint8_t *sg, *su, *sd;   // shared
   size_t bytes_gu, bytes_d;
 };
-
-template <bool USE_LO>
-__global__ __launch_bounds__(256) void k_q2_gateup(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
-  const int nt = blockIdx.x, u = blockIdx.y, cg = blockIdx.z;
-  if (u >= ws.meta->n_units) return;
-  const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
-  const int c0 = cg * 16;
-  if (c0 >= cnt) return;
-  Q2View W[2];
-  W[0] = q2_view(e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg, inter, hidden);
-  W[1] = q2_view(e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su, inter, hidden);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const int n = nt * 16 + nl;
-  const XRow x = xrow(ws.x_img, (c0 + nl < cnt) ? ws.arow[off + c0 + nl] : -1, ws.arow[off]);
-  const int nb = hidden / 256;
-  const int kb0 = nb * wv / 4;
-  f4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  q2_run<2, USE_LO>(W, n, kb0, nb * (wv + 1) / 4 - kb0, x, lane, acc);
-  __shared__ f4_t red[2][4][64];
-  red[0][wv][lane] = acc[0];
-  red[1][wv][lane] = acc[1];
-  __syncthreads();
-  if (wv != 0) return;
-  f4_t sg = red[0][0][lane], su = red[1][0][lane];
-#pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    sg += red[0][w][lane];
-    su += red[1][w][lane];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = c0 + 4 * g + i;
-    if (c >= cnt) continue;
-    const float gv = sg[i], uv = su[i];
-    ws.h[(size_t)(off + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
-  }
-}
 
 static ExpertPtrs expert_ptrs(const sv_moe_desc* d) {
   ExpertPtrs P;
@@ -304,78 +428,104 @@ static ExpertPtrs expert_ptrs(const sv_moe_desc* d) {
   return P;
 }
 
-hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws,
-                            hipStream_t s) {
-  const dim3 grid(d->inter / 16, ws.max_units, (R + 15) / 16);
-  if (use_lo)
-    hipLaunchKernelGGL(k_q2_gateup<true>, grid, dim3(256), 0, s, expert_ptrs(d), d->hidden,
-                       d->inter, ws);
-  else
-    hipLaunchKernelGGL(k_q2_gateup<false>, grid, dim3(256), 0, s, expert_ptrs(d), d->hidden,
-                       d->inter, ws);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // h -> image, one block per assignment actually present
-  return launch_stage(ws.h, SV_F32, ws.max_assign, d->inter, XL_PERM, &ws.meta->n_assign,
-                      ws.h_img, s);
+constexpr int GU_THREADS = 512;   // 8 waves: (gate, up) x 4 K-quarters of one 16-row tile
+
+template <bool USE_LO, bool WIDE_D>
+__global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int hidden, int inter,
+                                                             int CG, MoeWs ws) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_rows[XL_MAX_COLS];
+  const int tile = blockIdx.x, u = blockIdx.y;
+  if (u >= ws.meta->n_units) return;
+  const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
+  const int c0 = blockIdx.z * CG;
+  if (c0 >= cnt) return;
+  const int ncols = min(CG, cnt - c0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m = wv >> 2, q = wv & 3;
+  const int nl = lane & 15, g = lane >> 4;
+  const int n = tile * 16 + nl;
+  const int nb = hidden / 256;
+  const uint8_t* base = m == 0 ? (e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg)
+                               : (e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su);
+  const Q2View W = q2_view(base, inter, hidden);
+  const XLw L = xl_make(lds, ncols, hidden, USE_LO);
+  f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto stage = [&]() {
+    if (tid < ncols) s_rows[tid] = ws.arow[off + c0 + tid];
+    __syncthreads();
+    xl_copy_image(ws.x_img, s_rows, ncols, USE_LO, L);
+    __syncthreads();
+  };
+  q2_range_staged<WIDE_D, USE_LO>(W, n, nb * q / 4, nb * (q + 1) / 4, xl_view(L), min(nl, ncols - 1),
+                                  lane, acc, stage);
+  __syncthreads();   // every wave is done with the rows: reuse LDS for the partial sums
+  f4_t* red = (f4_t*)lds;
+  red[wv * 64 + lane] = acc;
+  __syncthreads();
+  if (wv != 0) return;
+  const f4_t gs = ((red[lane] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
+  const f4_t us = ((red[256 + lane] + red[320 + lane]) + red[384 + lane]) + red[448 + lane];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 4 * g + i;
+    if (c >= ncols) continue;
+    const float gv = gs[i], uv = us[i];
+    ws.h[(size_t)(off + c0 + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
+  }
+}
+
+static size_t gu_lds(int hidden, bool use_lo, int CG) {
+  const size_t x = xl_bytes(CG, hidden, use_lo), red = (size_t)GU_THREADS * 16;
+  return x > red ? x : red;
+}
+
+hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, hipStream_t s) {
+  const int CG = col_group(d->hidden, use_lo, R);
+  const dim3 grid(d->inter / 16, ws.max_units, (R + CG - 1) / CG);
+  const size_t lb = gu_lds(d->hidden, use_lo, CG);
+  const bool wide = q2_wide_d(d->hidden / 256);
+  const ExpertPtrs P = expert_ptrs(d);
+#define SV_GU(LO, WD)                                                                              \
+  hipLaunchKernelGGL((k_q2_gateup<LO, WD>), grid, dim3(GU_THREADS), lb, s, P, d->hidden, d->inter, \
+                     CG, ws)
+  if (use_lo) {
+    if (wide) SV_GU(true, true); else SV_GU(true, false);
+  } else {
+    if (wide) SV_GU(false, true); else SV_GU(false, false);
+  }
+#undef SV_GU
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ down
-// Grid (64-row group of hidden, unit, group of 4 columns).  The block's (up
-// to 4) h rows are staged in LDS once -- all 4 waves use the same rows over
-// all of inter -- then each wave streams one 16-row tile of the down matrix.
-constexpr int DOWN_COLS = 4;
+constexpr int DN_THREADS = 512;   // 8 waves, one 16-row tile each, all of inter
 
-__host__ __device__ inline size_t down_lds_bytes(int inter) {
-  return (size_t)DOWN_COLS * inter * 2 * 2 + (size_t)DOWN_COLS * (inter / 16) * 2 * 2 +
-         (size_t)DOWN_COLS * (inter / 256) * 4;
-}
-
-__global__ __launch_bounds__(256) void k_q2_down(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
+template <bool WIDE_D>
+__global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter,
+                                                           int CG, MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int grp = blockIdx.x, u = blockIdx.y, cg = blockIdx.z;
+  __shared__ int s_rows[XL_MAX_COLS];
+  const int u = blockIdx.y;
   if (u >= ws.meta->n_units) return;
   const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
-  const int c0 = cg * DOWN_COLS;
+  const int c0 = blockIdx.z * CG;
   if (c0 >= cnt) return;
-  const int ncols = min(DOWN_COLS, cnt - c0);
+  const int ncols = min(CG, cnt - c0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nl = lane & 15;
-  const int n = grp * 64 + wv * 16 + nl;
-  const int nbk = inter / 256;
-  XLds X;
-  X.K = inter;
-  X.nbk = nbk;
-  _Float16* hi = (_Float16*)lds;
-  _Float16* lo = hi + DOWN_COLS * inter;
-  _Float16* sxh = lo + DOWN_COLS * inter;
-  _Float16* sxl = sxh + DOWN_COLS * (inter / 16);
-  float* bs = (float*)(sxl + DOWN_COLS * (inter / 16));
-  X.hi = hi;
-  X.lo = lo;
-  X.sxh = sxh;
-  X.sxl = sxl;
-  X.bs = bs;
-  // stage the rows of assignments off+c0 .. off+c0+ncols-1 (16-byte pieces)
-  const XImg& H = ws.h_img;
-  for (int c = 0; c < ncols; ++c) {
-    const size_t a = (size_t)(off + c0 + c);
-    for (int i = tid; i < inter / 8; i += 256) {
-      *(uint4*)(hi + c * inter + 8 * i) = *(const uint4*)(H.hi + a * inter + 8 * i);
-      *(uint4*)(lo + c * inter + 8 * i) = *(const uint4*)(H.lo + a * inter + 8 * i);
-    }
-    for (int i = tid; i < inter / 16; i += 256) {
-      sxh[c * (inter / 16) + i] = H.sxh[a * (inter / 16) + i];
-      sxl[c * (inter / 16) + i] = H.sxl[a * (inter / 16) + i];
-    }
-    for (int i = tid; i < nbk; i += 256) bs[c * nbk + i] = H.bscale[a * nbk + i];
-  }
-  __syncthreads();
+  const int nl = lane & 15, g = lane >> 4;
+  const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
+  const XLw L = xl_make(lds, ncols, inter, true);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // lane column c = nl reads LDS row nl & 3; columns >= ncols are padding (not stored)
-  q2_run_lds(D, n, nbk, X, nl & 3, lane, acc);
-  const int g = lane >> 4;
+  auto stage = [&]() {
+    if (tid < ncols) s_rows[tid] = off + c0 + tid;   // assignments: rows of h
+    __syncthreads();
+    xl_stage_f32(ws.h, s_rows, ncols, L);
+    __syncthreads();
+  };
+  q2_range_staged<WIDE_D, true>(D, n, 0, inter / 256, xl_view(L), min(nl, ncols - 1), lane, acc,
+                                stage);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;   // tile column; only 0..ncols-1 are real
@@ -384,9 +534,16 @@ __global__ __launch_bounds__(256) void k_q2_down(ExpertPtrs P, int hidden, int i
 }
 
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const dim3 grid(d->hidden / 64, ws.max_units, (R + DOWN_COLS - 1) / DOWN_COLS);
-  hipLaunchKernelGGL(k_q2_down, grid, dim3(256), down_lds_bytes(d->inter), s, expert_ptrs(d),
-                     d->hidden, d->inter, ws);
+  const int CG = col_group(d->inter, true, R);
+  const dim3 grid(d->hidden / 128, ws.max_units, (R + CG - 1) / CG);
+  const size_t lb = xl_bytes(CG, d->inter, true);
+  const ExpertPtrs P = expert_ptrs(d);
+  if (q2_wide_d(d->inter / 256))
+    hipLaunchKernelGGL(k_q2_down<true>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, CG,
+                       ws);
+  else
+    hipLaunchKernelGGL(k_q2_down<false>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, CG,
+                       ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_moe_combine(d, R, ws, y, s);
@@ -394,8 +551,6 @@ hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipSt
 
 // --------------------------------------------------------------- combine
 // y[r, n] = sum_{s<k} w[r, s] * part[a(r, s), n] (+ part[a(r, shared), n]), in slot order.
-// Grid (hidden/256, R): the row's slot map goes to LDS first, then all of its
-// partial loads are issued together.
 __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_shared, MoeWs ws,
                                                      float* y) {
   __shared__ int s_a[SV_MAX_TOPK + 1];
@@ -404,61 +559,87 @@ __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_
   if (tid <= k) s_a[tid] = ws.amap[r * (k + 1) + tid];
   if (tid < k) s_w[tid] = ws.topk_w[r * k + tid];
   __syncthreads();
-  const int n = blockIdx.x * 256 + tid;
-  if (n >= hidden) return;
+  const int n4 = blockIdx.x * 256 + tid;   // 4 outputs per thread
+  if (4 * n4 >= hidden) return;
   const int ns = k + has_shared;
-  float v[SV_MAX_TOPK + 1];
+  float4 v[SV_MAX_TOPK + 1];
 #pragma unroll
   for (int s = 0; s <= SV_MAX_TOPK; ++s)
-    if (s < ns) v[s] = ws.part[(size_t)s_a[s] * hidden + n];
-  float acc = 0.f;
+    if (s < ns) v[s] = *(const float4*)(ws.part + (size_t)s_a[s] * hidden + 4 * n4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int s = 0; s < SV_MAX_TOPK; ++s)
-    if (s < k) acc = fmaf(s_w[s], v[s], acc);
-  if (has_shared) acc += v[k];
-  y[(size_t)r * hidden + n] = acc;
+  for (int s = 0; s <= SV_MAX_TOPK; ++s) {
+    if (s < k) {
+      acc.x = fmaf(s_w[s], v[s].x, acc.x);
+      acc.y = fmaf(s_w[s], v[s].y, acc.y);
+      acc.z = fmaf(s_w[s], v[s].z, acc.z);
+      acc.w = fmaf(s_w[s], v[s].w, acc.w);
+    } else if (s == k && has_shared) {   // the shared expert last, weight 1
+      acc.x += v[s].x;
+      acc.y += v[s].y;
+      acc.z += v[s].z;
+      acc.w += v[s].w;
+    }
+  }
+  *(float4*)(y + (size_t)r * hidden + 4 * n4) = acc;
 }
 
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden + 255) / 256, R), dim3(256), 0, s, d->hidden,
-                     d->top_k, d->s_gate ? 1 : 0, ws, y);
+  hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden / 4 + 255) / 256, R), dim3(256), 0, s,
+                     d->hidden, d->top_k, d->s_gate ? 1 : 0, ws, y);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- plain
-// y[R, n_out] = W x for one two-bit matrix; each wave one 16-row tile over all K.
-template <bool USE_LO>
-__global__ __launch_bounds__(256) void k_q2_plain(const uint8_t* w, int n_out, int k_in, int R,
-                                                  XImg img, float* y) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nt = blockIdx.x * 4 + wv, cg = blockIdx.z;
-  if (nt * 16 >= n_out) return;
+// y[R, n_out] = W x for one two-bit matrix: 8 waves of one 16-row tile each
+// over all of K, the block's rows (a group of up to CG of the R rows) in LDS.
+template <bool USE_LO, bool WIDE_D>
+__global__ __launch_bounds__(DN_THREADS, 4) void k_q2_plain(const uint8_t* w, int n_out, int k_in,
+                                                            int R, int CG, XImg img, float* y) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ int s_rows[XL_MAX_COLS];
+  const int c0 = blockIdx.z * CG;
+  const int ncols = min(CG, R - c0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int n = nt * 16 + nl;
+  const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const int nld = n < n_out ? n : n_out - 1;   // ragged tail: load a valid row, drop the result
   const Q2View W = q2_view(w, n_out, k_in);
-  const int c = cg * 16 + nl;
-  const XRow x = xrow(img, c < R ? c : -1, 0);
+  const XLw L = xl_make(lds, ncols, k_in, USE_LO);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  q2_run<1, USE_LO>(&W, nld, 0, W.nb, x, lane, &acc);
+  auto stage = [&]() {
+    if (tid < ncols) s_rows[tid] = c0 + tid;
+    __syncthreads();
+    xl_copy_image(img, s_rows, ncols, USE_LO, L);
+    __syncthreads();
+  };
+  q2_range_staged<WIDE_D, USE_LO>(W, nld, 0, k_in / 256, xl_view(L), min(nl, ncols - 1), lane, acc,
+                                  stage);
   if (n >= n_out) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int cc = cg * 16 + 4 * g + i;
-    if (cc < R) y[(size_t)cc * n_out + n] = acc[i];
+    const int c = 4 * g + i;
+    if (c < ncols) y[(size_t)(c0 + c) * n_out + n] = acc[i];
   }
 }
 
 hipError_t launch_q2_plain(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, float* y,
                            hipStream_t s) {
+  const int CG = col_group(d->hidden, use_lo, R);
   const int tiles = (d->inter + 15) / 16;
-  const dim3 grid((tiles + 3) / 4, 1, (R + 15) / 16);
-  if (use_lo)
-    hipLaunchKernelGGL(k_q2_plain<true>, grid, dim3(256), 0, s, (const uint8_t*)d->w_gate,
-                       d->inter, d->hidden, R, ws.x_img, y);
-  else
-    hipLaunchKernelGGL(k_q2_plain<false>, grid, dim3(256), 0, s, (const uint8_t*)d->w_gate,
-                       d->inter, d->hidden, R, ws.x_img, y);
+  const dim3 grid((tiles + 7) / 8, 1, (R + CG - 1) / CG);
+  const size_t lb = xl_bytes(CG, d->hidden, use_lo);
+  const bool wide = q2_wide_d(d->hidden / 256);
+  const uint8_t* w = (const uint8_t*)d->w_gate;
+#define SV_PL(LO, WD)                                                                          \
+  hipLaunchKernelGGL((k_q2_plain<LO, WD>), grid, dim3(DN_THREADS), lb, s, w, d->inter, d->hidden, \
+                     R, CG, ws.x_img, y)
+  if (use_lo) {
+    if (wide) SV_PL(true, true); else SV_PL(true, false);
+  } else {
+    if (wide) SV_PL(false, true); else SV_PL(false, false);
+  }
+#undef SV_PL
   return hipGetLastError();
 }
 

@@ -1,74 +1,48 @@
-// Two-bit block x activation-image contraction on the fp16 matrix cores.
+// Two-bit block x activation contraction on the fp16 matrix cores, with the
+// activation rows held in LDS.
 //
 // One wave computes a 16 (weight rows n) x 16 (activation columns c) tile over
-// a range of 256-element blocks with v_mfma_f32_16x16x32_f16:
-//   A operand = activation image (lane: column c = lane&15, k-group g = lane>>4)
-//   B operand = weights          (lane: row n = lane&15,    k-group g = lane>>4)
+// a range of 256-element blocks of one matrix with v_mfma_f32_16x16x32_f16:
+//   A operand = activations (lane: column c = lane&15, k-group g = lane>>4),
+//               read from the block's LDS copy of the rows;
+//   B operand = weights (lane: row n = lane&15, k-group g = lane>>4);
 //   result    = D[c][n]: lane holds n = lane&15 and c = 4*(lane>>4) + 0..3.
-// Each lane loads, per block, the 16 code bytes of sub-blocks 4g..4g+3 of its
-// row (one dwordx4), their 4 nibble bytes (one dword) and the row's d / dmin;
-// a wave issues these loads for up to 8 blocks before computing any of them.
-// Per step t (0..7) a lane turns one half of one sub-block into 8 fp16 weights
-// sc * q * 4^j -- exact integers: the code is OR-ed into the mantissa of
-// 1024.0 at bit position 2j (value 1024 + 4^j q) and one packed fma with
-// (sc, -1024 sc) removes the offset and applies the sub-block scale.  The
-// image carries the matching 4^-j.  The block's min term dmin * m * sum(x)
-// is one 16x16x16 product of the per-sub-block sums with the m nibbles, and
-// the block scales are applied in fp32:
-//   acc += s_x * (d * D_codes - dmin * D_min),  s_x = the image's block scale.
+//
+// Weight loads are all 16 bytes per lane (the vector-memory address path, not
+// HBM, limits narrower loads):
+//   codes  one load per block: lane (n, g) gets the 16 code bytes of sub-blocks
+//          4g..4g+3 of row n (the 4 lanes of a row cover its 64 bytes);
+//   scales one load per 4 blocks: lane-row g gets all 16 nibble bytes of block
+//          kb+g; two permlane16 and two permlane32 swaps transpose the 4x4
+//          dwords so that every lane holds its own 4 sub-blocks of each block;
+//   d/dmin one load per 8 blocks (when the row's block count is even and at
+//          least 8): even lane-rows read 8 block scales d, odd lane-rows the 8
+//          min-scales; one permlane16 swap per dword gives every lane both.
+// All loads of a chunk of up to 8 blocks are issued before any is used, in the
+// order they are consumed, so the whole chunk is in flight at once.
+//
+// Per block, a lane turns one half of one sub-block into 8 fp16 weights
+// sc * q * 4^j per step (t = 0..7) -- exact integers: the code is OR-ed into
+// the mantissa of 1024.0 at bit position 2j (value 1024 + 4^j q) and one
+// packed fma with (sc, -1024 sc) removes the offset and applies the sub-block
+// scale; the activation rows carry the matching 4^-j.  The min term
+// dmin * m * sum(x) is one 16x16x16 product of the per-sub-block sums with the
+// m nibbles.  Block scales are applied in fp32:
+//   acc += s_x * (d * D_codes - dmin * D_min),  s_x = the rows' block scale.
 #pragma once
 
 #include "sv_internal.h"
 
 namespace sv {
 
-__device__ inline float f16bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ float f16bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
-__device__ inline h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
-
-struct XRow {
-  const _Float16* hi;   // image row of this lane's column
-  const _Float16* lo;
-  const _Float16* sxh;
-  const _Float16* sxl;
-  const float* bs;      // block scales of the row
-};
-
-// `row` is this lane's column; padding columns (beyond the rows in use) read
-// row `fallback` instead: an output column depends only on its own operand
-// row, and padding columns are never stored, so their values do not matter --
-// this keeps every load unconditional (no branches, no serialising waits).
-__device__ inline XRow xrow(const XImg& img, int row, int fallback) {
-  const size_t r = (size_t)(row >= 0 ? row : fallback);
-  XRow x;
-  x.hi = img.hi + r * img.K;
-  x.lo = img.lo + r * img.K;
-  x.sxh = img.sxh + r * (img.K / 16);
-  x.sxl = img.sxl + r * (img.K / 16);
-  x.bs = img.bscale + r * img.nbk;
-  return x;
-}
-
-struct Q2Blk {
-  uint4 qs;
-  uint32_t sc;
-  uint16_t d, dm;
-};
-
-__device__ inline Q2Blk q2_load(const Q2View& W, int n, int kb, int g) {
-  const size_t b = (size_t)n * W.nb + kb;
-  Q2Blk k;
-  k.qs = *(const uint4*)(W.qs + b * 64 + 16 * g);
-  k.sc = *(const uint32_t*)(W.sc + b * 16 + 4 * g);
-  k.d = W.d[b];
-  k.dm = W.dm[b];
-  return k;
-}
+__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
 // (x & m) | o in one instruction.  gfx9 VOP3 encodings take no 32-bit
 // literals, so the compiler splits this into v_and_b32 + v_or_b32 with
 // literals; here the mask comes in an SGPR and the OR constant in a VGPR.
-__device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
   return r;
@@ -76,10 +50,10 @@ __device__ inline uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
 
 // fp16 (1024 + byte) pairs from bytes (0,1) / (2,3) of u: v_perm_b32 picks
 // bytes 0-3 from its second operand and 4-7 from its first.
-__device__ inline h2_t q2_bytes01(uint32_t u) {
+__device__ __forceinline__ h2_t q2_bytes01(uint32_t u) {
   return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
 }
-__device__ inline h2_t q2_bytes23(uint32_t u) {
+__device__ __forceinline__ h2_t q2_bytes23(uint32_t u) {
   return __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
 }
 
@@ -91,7 +65,7 @@ struct Q2Sc {
   h4_t m;
 };
 
-__device__ inline Q2Sc q2_scales(uint32_t scw) {
+__device__ __forceinline__ Q2Sc q2_scales(uint32_t scw) {
   const h2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
   const h2_t kneg = {(_Float16)-1024.f, (_Float16)-1024.f};
   const uint32_t lo = scw & 0x0F0F0F0Fu, hi = (scw >> 4) & 0x0F0F0F0Fu;
@@ -107,7 +81,7 @@ __device__ inline Q2Sc q2_scales(uint32_t scw) {
 
 // Weights of step t as the B operand (8 fp16): 4^j * sc * q for the 8 codes.
 // `magic` holds 0x64006400 (fp16 pair 1024.0) in a register.
-__device__ inline h8_t q2_bop(const uint4& qs, const Q2Sc& S, int t, uint32_t magic) {
+__device__ __forceinline__ h8_t q2_bop(const uint4& qs, const Q2Sc& S, int t, uint32_t magic) {
   const int i = t >> 1, hs = t & 1;
   const uint32_t dw = (i == 0 ? qs.x : i == 1 ? qs.y : i == 2 ? qs.z : qs.w) >> (8 * hs);
   const h2_t scp = (i == 0) ? (h2_t){S.sc01.x, S.sc01.x} : (i == 1) ? (h2_t){S.sc01.y, S.sc01.y}
@@ -126,204 +100,257 @@ __device__ inline h8_t q2_bop(const uint4& qs, const Q2Sc& S, int t, uint32_t ma
 }
 
 // The OR constant as an opaque register value (kept in one VGPR).
-__device__ inline uint32_t q2_magic() {
+__device__ __forceinline__ uint32_t q2_magic() {
   uint32_t m = 0x64006400u;
   asm volatile("" : "+v"(m));
   return m;
 }
 
-// Activation operands of one block for this lane's column.
-template <bool USE_LO>
-struct XBlk {
-  h8_t hi[8];
-  h8_t lo[USE_LO ? 8 : 1];
-  h4_t sxh, sxl;
-  f4_t xs;   // block scales of the lane's 4 output columns
-};
+// ------------------------------------------------------------ LDS rows
+// Activation rows of one block in LDS (layout written by the stagers):
+//   hi, lo  [ncols][K] fp16 in the PERM order of sv_internal.h (element
+//           ((kb*8 + t)*4 + g)*8 + i of a row is the A-operand value i of
+//           lane-group g at step t of block kb), with the 64-byte pieces of
+//           row c XOR-swizzled by (c & 7) so that different rows at the same
+//           offset fall in different banks (the swizzle stays inside each
+//           256-element block);
+//   sx      [ncols][K/8] fp16: per 4-sub-block group (kb*4 + g), the 4
+//           sub-block sums' high parts then their 4 remainders;
+//   bst     [nbk + 1][8] fp32: block scale of column c (< 8) of block kb (the
+//           extra row keeps the lanes of padding columns 8..15 in bounds).
+constexpr int XL_MAX_COLS = 8;
 
-template <bool USE_LO>
-__device__ inline void x_load(const XRow& x, int kb, int lane, XBlk<USE_LO>& X) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const size_t off = (size_t)((kb * 8 + t) * 4 + g) * 8;
-    X.hi[t] = *(const h8_t*)(x.hi + off);
-    if (USE_LO) X.lo[t] = *(const h8_t*)(x.lo + off);
-  }
-  const size_t so = (size_t)kb * 16 + 4 * g;
-  X.sxh = *(const h4_t*)(x.sxh + so);
-  X.sxl = *(const h4_t*)(x.sxl + so);
-  // lane c (< 16) holds column c's A operand: fetch the 4 output columns' scales from there
-  const float s_own = x.bs[kb];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) X.xs[e] = __shfl(s_own, 4 * g + e, 64);
-}
-
-// acc (the lane's 4 outputs D[4g+e][n]) += block contribution.
-template <bool USE_LO>
-__device__ inline void q2_block(const Q2Blk& k, const XBlk<USE_LO>& X, f4_t& acc) {
-  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t magic = q2_magic();
-  const Q2Sc S = q2_scales(k.sc);
-  f4_t dt = zero;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const h8_t b = q2_bop(k.qs, S, t, magic);
-    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(X.hi[t], b, dt, 0, 0, 0);
-    if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(X.lo[USE_LO ? t : 0], b, dt, 0, 0, 0);
-  }
-  // the 16-element sums are never fp16-exact: their remainder is always used
-  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(X.sxh, S.m, zero, 0, 0, 0);
-  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(X.sxl, S.m, dm, 0, 0, 0);
-  const float d = f16bits_to_f32(k.d), dmin = f16bits_to_f32(k.dm);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = fmaf(X.xs[e], fmaf(d, dt[e], -dmin * dm[e]), acc[e]);
-}
-
-// One pipeline slot: a block's weights for NM matrices and its activation operands.
-template <int NM, bool USE_LO>
-struct Q2Slot {
-  Q2Blk w[NM];
-  XBlk<USE_LO> x;
-};
-
-template <int NM, bool USE_LO>
-__device__ inline void q2_slot_load(const Q2View* W, int n, int kb, const XRow& x, int lane,
-                                    Q2Slot<NM, USE_LO>& S) {
-  x_load<USE_LO>(x, kb, lane, S.x);
-#pragma unroll
-  for (int m = 0; m < NM; ++m) S.w[m] = q2_load(W[m], n, kb, lane >> 4);
-}
-
-// NM matrices (sharing one activation row per lane) over NB blocks from kb0
-// of weight row n, software-pipelined over three register slots: the weights
-// and activation operands of block i+2 are requested before block i is
-// computed (i+1 with the remainder operand, whose registers allow only two
-// slots).  Vector-memory loads retire in issue order, so they are issued in
-// the order they are used and without branches; the wait for block i then
-// leaves the later blocks in flight.  The slots are distinct variables (not an
-// array) so each keeps its own registers, and a scheduling barrier keeps every
-// block's loads in its stage.
-template <int NM, bool USE_LO, int NB>
-__device__ inline void q2_pipe(const Q2View* W, int n, int kb0, const XRow& x, int lane,
-                               f4_t* acc) {
-  constexpr int PD = USE_LO ? 1 : 2;
-  Q2Slot<NM, USE_LO> s0, s1, s2;
-  q2_slot_load<NM, USE_LO>(W, n, kb0, x, lane, s0);
-  if (PD > 1 && NB > 1) q2_slot_load<NM, USE_LO>(W, n, kb0 + 1, x, lane, s1);
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int ld = i + PD;   // block requested in this stage
-    if (ld < NB) {
-      const int sl = ld % (PD + 1);
-      q2_slot_load<NM, USE_LO>(W, n, kb0 + ld, x, lane, sl == 0 ? s0 : sl == 1 ? s1 : s2);
-    }
-    const int sc = i % (PD + 1);
-    const Q2Slot<NM, USE_LO>& cur = sc == 0 ? s0 : sc == 1 ? s1 : s2;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) q2_block<USE_LO>(cur.w[m], cur.x, acc[m]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Any block count: pipelined chunks of 8, then the remainder.
-template <int NM, bool USE_LO>
-__device__ inline void q2_run(const Q2View* W, int n, int kb0, int nblk, const XRow& x, int lane,
-                              f4_t* acc) {
-  int kb = kb0;
-  for (; kb + 8 <= kb0 + nblk; kb += 8) q2_pipe<NM, USE_LO, 8>(W, n, kb, x, lane, acc);
-  switch (kb0 + nblk - kb) {
-    case 1: q2_pipe<NM, USE_LO, 1>(W, n, kb, x, lane, acc); break;
-    case 2: q2_pipe<NM, USE_LO, 2>(W, n, kb, x, lane, acc); break;
-    case 3: q2_pipe<NM, USE_LO, 3>(W, n, kb, x, lane, acc); break;
-    case 4: q2_pipe<NM, USE_LO, 4>(W, n, kb, x, lane, acc); break;
-    case 5: q2_pipe<NM, USE_LO, 5>(W, n, kb, x, lane, acc); break;
-    case 6: q2_pipe<NM, USE_LO, 6>(W, n, kb, x, lane, acc); break;
-    case 7: q2_pipe<NM, USE_LO, 7>(W, n, kb, x, lane, acc); break;
-    default: break;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Variant with the activation operands in LDS.  Used where the waves of a
-// block share their activation rows: the rows are staged once per block, the
-// per-step operand reads go to LDS (their waits are counted apart from the
-// weight loads, which stay in flight), and the registers hold only weights.
-struct XLds {
-  const _Float16* hi;    // [4][K] PERM layout
+struct XL {
+  const _Float16* hi;
   const _Float16* lo;
-  const _Float16* sxh;   // [4][K/16]
-  const _Float16* sxl;
-  const float* bs;       // [4][nbk]
-  int K, nbk;
+  const _Float16* sx;
+  const float* bst;
+  int K;
 };
 
-// acc += block kb of weight row n against LDS column `col` (0..3) of this lane.
-__device__ inline void q2_block_lds(const Q2Blk& k, const XLds& X, int col, int kb, int lane,
-                                    f4_t& acc) {
-  const int g = lane >> 4;
-  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* xh = X.hi + (size_t)col * X.K;
-  const _Float16* xl = X.lo + (size_t)col * X.K;
-  const uint32_t magic = q2_magic();
-  const Q2Sc S = q2_scales(k.sc);
-  f4_t dt = zero;
+__host__ __device__ inline int xl_swz(int c) { return (c & 7) << 5; }
+
+__host__ __device__ inline size_t xl_bytes(int ncols, int K, bool use_lo) {
+  const size_t rows = (size_t)ncols * K * 2 * (use_lo ? 2 : 1);
+  const size_t sx = (size_t)ncols * (K / 8) * 2;
+  const size_t bst = (size_t)(K / 256 + 1) * XL_MAX_COLS * 4;
+  return up256(rows) + up256(sx) + up256(bst);
+}
+
+template <typename P>
+__device__ __forceinline__ void xl_carve(P* base, int ncols, int K, bool use_lo, P*& hi, P*& lo, P*& sx,
+                                float*& bst) {
+  uint8_t* p = (uint8_t*)base;
+  const size_t row = (size_t)K * 2;
+  hi = (P*)p;
+  lo = (P*)(p + (size_t)ncols * row);
+  p += up256((size_t)ncols * row * (use_lo ? 2 : 1));
+  sx = (P*)p;
+  p += up256((size_t)ncols * (K / 8) * 2);
+  bst = (float*)p;
+}
+
+// ------------------------------------------------------------ wide loads
+constexpr int WB = 8;   // blocks per load chunk
+
+template <int NBW, bool WIDE_D>
+struct Q2Chunk {
+  uint4 qs[NBW];
+  uint4 sc[(NBW + 3) / 4];
+  uint4 dd;                          // WIDE_D
+  uint16_t d[WIDE_D ? 1 : NBW], dm[WIDE_D ? 1 : NBW];
+};
+
+// First block of the 8-block d/dmin window of a chunk starting at kb0: even
+// (so the 16-byte load is dword aligned) and inside the row; it covers 8
+// blocks from an even kb0 and 7 from an odd one (chunks are cut to fit).
+__device__ __forceinline__ int q2_dwin(int kb0, int nb) { return min(kb0 & ~1, nb - 8); }
+
+// Issue every load of blocks kb0..kb0+NBW-1 of weight row n, in the order the
+// blocks consume them.
+template <int NBW, bool WIDE_D>
+__device__ __forceinline__ void q2_chunk_load(const Q2View& W, int n, int kb0, int g,
+                                     Q2Chunk<NBW, WIDE_D>& c) {
+  const size_t rb = (size_t)n * W.nb;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const h8_t b = q2_bop(k.qs, S, t, magic);
-    const int off = ((kb * 8 + t) * 4 + g) * 8;
-    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + off), b, dt, 0, 0, 0);
-    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + off), b, dt, 0, 0, 0);
-  }
-  const int so = col * (X.K / 16) + kb * 16 + 4 * g;
-  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(*(const h4_t*)(X.sxh + so), S.m, zero, 0, 0, 0);
-  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(*(const h4_t*)(X.sxl + so), S.m, dm, 0, 0, 0);
-  const float d = f16bits_to_f32(k.d), dmin = f16bits_to_f32(k.dm);
-  // block scales of the lane's 4 output columns (column c of the tile = LDS row c & 3)
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float xs = X.bs[((4 * g + e) & 3) * X.nbk + kb];
-    acc[e] = fmaf(xs, fmaf(d, dt[e], -dmin * dm[e]), acc[e]);
+  for (int i = 0; i < NBW; ++i) {
+    if (i % 4 == 0) {
+      const int kb = min(kb0 + i + g, W.nb - 1);   // lane-row g: all nibbles of block kb0+i+g
+      c.sc[i / 4] = *(const uint4*)(W.sc + (rb + kb) * 16);
+    }
+    if (i == 0) {
+      if (WIDE_D) {
+        const uint16_t* pl = (g & 1) ? W.dm : W.d;
+        c.dd = *(const uint4*)(pl + rb + q2_dwin(kb0, W.nb));
+      }
+    }
+    c.qs[i] = *(const uint4*)(W.qs + (rb + kb0 + i) * 64 + 16 * g);
+    if (!WIDE_D) {
+      c.d[WIDE_D ? 0 : i] = W.d[rb + kb0 + i];
+      c.dm[WIDE_D ? 0 : i] = W.dm[rb + kb0 + i];
+    }
   }
 }
 
-// NB blocks from kb0, weights pipelined PD = 3 blocks ahead in registers.
-template <int NB>
-__device__ inline void q2_pipe_lds(const Q2View& W, int n, int kb0, const XLds& X, int col,
-                                   int lane, f4_t& acc) {
-  constexpr int PD = 3;
+// 4x4 dword transpose across the four 16-lane rows: on entry lane-row g holds
+// r[j] = dword j of block g; on exit lane-row g holds in r[j] dword g of block j.
+__device__ __forceinline__ void xpose4(const uint4& v, uint32_t* r) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v.x, v.y, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(v.z, v.w, false, false);
+  const auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+  r[0] = c[0];
+  r[1] = d[0];
+  r[2] = c[1];
+  r[3] = d[1];
+}
+
+// acc += block kb of the chunk (index i) for this lane's column row.
+__device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d, float dmin, const XL& X,
+                                int cr, int kb, int lane, f4_t& acc, bool use_lo) {
   const int g = lane >> 4;
-  Q2Blk s0, s1, s2, s3;
-  s0 = q2_load(W, n, kb0, g);
-  if (NB > 1) s1 = q2_load(W, n, kb0 + 1, g);
-  if (NB > 2) s2 = q2_load(W, n, kb0 + 2, g);
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const _Float16* xh = X.hi + (size_t)cr * X.K;
+  const _Float16* xl = X.lo + (size_t)cr * X.K;
+  const int swz = xl_swz(cr);
+  const uint32_t magic = q2_magic();
+  const Q2Sc S = q2_scales(scw);
+  f4_t dt = zero;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int ld = i + PD;
-    if (ld < NB) {
-      const int sl = ld & 3;
-      (sl == 0 ? s0 : sl == 1 ? s1 : sl == 2 ? s2 : s3) = q2_load(W, n, kb0 + ld, g);
+  for (int t = 0; t < 8; ++t) {
+    const h8_t b = q2_bop(qs, S, t, magic);
+    const int off = (((kb * 8 + t) * 4 + g) * 8) ^ swz;
+    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + off), b, dt, 0, 0, 0);
+    if (use_lo) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + off), b, dt, 0, 0, 0);
+  }
+  const h8_t sx = *(const h8_t*)(X.sx + (size_t)cr * (X.K / 8) + (kb * 4 + g) * 8);
+  const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
+  // the 16-element sums are never fp16-exact: their remainder is always used
+  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, S.m, zero, 0, 0, 0);
+  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, S.m, dm, 0, 0, 0);
+  const f4_t xs = *(const f4_t*)(X.bst + kb * XL_MAX_COLS + 4 * g);   // the lane's 4 columns
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] = fmaf(xs[e], fmaf(d, dt[e], -dmin * dm[e]), acc[e]);
+}
+
+// fp16 value at position p (0..7) of an 8-value window held as 4 dwords.
+__device__ __forceinline__ float win_val(const uint32_t* w, int p) {
+  return f16bits_to_f32((uint16_t)(w[p >> 1] >> (16 * (p & 1))));
+}
+
+// Blocks kb0..kb0+NBW-1 given their issued loads.
+template <int NBW, bool WIDE_D, bool USE_LO>
+__device__ __forceinline__ void q2_chunk_compute(const Q2View& W, const Q2Chunk<NBW, WIDE_D>& c, int kb0,
+                                        int n, const XL& X, int cr, int lane, f4_t& acc) {
+  float dF[NBW], mF[NBW];
+  if (WIDE_D) {
+    uint32_t dv[4], mv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = j == 0 ? c.dd.x : j == 1 ? c.dd.y : j == 2 ? c.dd.z : c.dd.w;
+      const auto s = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+      dv[j] = s[0];   // d of window blocks 2j, 2j + 1
+      mv[j] = s[1];   // dmin of the same blocks
     }
-    const int sc = i & 3;
-    q2_block_lds(sc == 0 ? s0 : sc == 1 ? s1 : sc == 2 ? s2 : s3, X, col, kb0 + i, lane, acc);
+    const int o = kb0 - q2_dwin(kb0, W.nb);   // wave-uniform offset of block kb0 in the window
+    if (o <= 1) {
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int p1 = i + 1 < 8 ? i + 1 : 7;
+        dF[i] = o ? win_val(dv, p1) : win_val(dv, i);
+        mF[i] = o ? win_val(mv, p1) : win_val(mv, i);
+      }
+    } else {   // window clamped at the row end (shapes where a chunk starts late)
+      const size_t rb = (size_t)n * W.nb + kb0;
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        dF[i] = f16bits_to_f32(W.d[rb + i]);
+        mF[i] = f16bits_to_f32(W.dm[rb + i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      dF[i] = f16bits_to_f32(c.d[WIDE_D ? 0 : i]);
+      mF[i] = f16bits_to_f32(c.dm[WIDE_D ? 0 : i]);
+    }
+  }
+  uint32_t sct[4];
+#pragma unroll
+  for (int i = 0; i < NBW; ++i) {
+    if (i % 4 == 0) xpose4(c.sc[i / 4], sct);
+    q2_block(c.qs[i], sct[i % 4], dF[i], mF[i], X, cr, kb0 + i, lane, acc, USE_LO);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__device__ inline void q2_run_lds(const Q2View& W, int n, int nblk, const XLds& X, int col,
-                                  int lane, f4_t& acc) {
-  int kb = 0;
-  for (; kb + 8 <= nblk; kb += 8) q2_pipe_lds<8>(W, n, kb, X, col, lane, acc);
-  switch (nblk - kb) {
-    case 1: q2_pipe_lds<1>(W, n, kb, X, col, lane, acc); break;
-    case 2: q2_pipe_lds<2>(W, n, kb, X, col, lane, acc); break;
-    case 3: q2_pipe_lds<3>(W, n, kb, X, col, lane, acc); break;
-    case 4: q2_pipe_lds<4>(W, n, kb, X, col, lane, acc); break;
-    case 5: q2_pipe_lds<5>(W, n, kb, X, col, lane, acc); break;
-    case 6: q2_pipe_lds<6>(W, n, kb, X, col, lane, acc); break;
-    case 7: q2_pipe_lds<7>(W, n, kb, X, col, lane, acc); break;
-    default: break;
+template <int NBW, bool WIDE_D, bool USE_LO>
+__device__ __forceinline__ void q2_chunk(const Q2View& W, int n, int kb0, const XL& X, int cr, int lane,
+                                f4_t& acc) {
+  Q2Chunk<NBW, WIDE_D> c;
+  q2_chunk_load<NBW, WIDE_D>(W, n, kb0, lane >> 4, c);
+  q2_chunk_compute<NBW, WIDE_D, USE_LO>(W, c, kb0, n, X, cr, lane, acc);
+}
+
+// Length of the chunk starting at kb with `left` blocks to go: at most WB,
+// and 7 from an odd block so that its d/dmin window (even start) covers it.
+template <bool WIDE_D>
+__device__ __forceinline__ int q2_chunk_len(int kb, int left) {
+  return min(left, (WIDE_D && (kb & 1)) ? WB - 1 : WB);
+}
+
+// Blocks [kb0, kb1) of row n, chunk by chunk.
+template <bool WIDE_D, bool USE_LO>
+__device__ __forceinline__ void q2_range(const Q2View& W, int n, int kb0, int kb1, const XL& X, int cr,
+                                int lane, f4_t& acc) {
+  for (int kb = kb0; kb < kb1;) {
+    const int len = q2_chunk_len<WIDE_D>(kb, kb1 - kb);
+    switch (len) {
+      case 1: q2_chunk<1, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 2: q2_chunk<2, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 3: q2_chunk<3, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 4: q2_chunk<4, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 5: q2_chunk<5, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 6: q2_chunk<6, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 7: q2_chunk<7, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      default: q2_chunk<8, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+    }
+    kb += len;
   }
 }
+
+// Same, with the first chunk's loads issued before `stage()` (which fills the
+// LDS rows and ends in a block barrier) so they are in flight meanwhile.
+// Every wave calls stage() exactly once.
+template <bool WIDE_D, bool USE_LO, typename F>
+__device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0, int kb1, const XL& X,
+                                       int cr, int lane, f4_t& acc, F&& stage) {
+  const int len = q2_chunk_len<WIDE_D>(kb0, kb1 - kb0);
+  const int g = lane >> 4;
+#define SV_STAGED_CASE(L)                                               \
+  case L: {                                                             \
+    Q2Chunk<L, WIDE_D> c;                                               \
+    q2_chunk_load<L, WIDE_D>(W, n, kb0, g, c);                          \
+    stage();                                                            \
+    q2_chunk_compute<L, WIDE_D, USE_LO>(W, c, kb0, n, X, cr, lane, acc); \
+    break;                                                              \
+  }
+  switch (len) {
+    SV_STAGED_CASE(1)
+    SV_STAGED_CASE(2)
+    SV_STAGED_CASE(3)
+    SV_STAGED_CASE(4)
+    SV_STAGED_CASE(5)
+    SV_STAGED_CASE(6)
+    SV_STAGED_CASE(7)
+    SV_STAGED_CASE(8)
+    default: stage(); return;   // empty range
+  }
+#undef SV_STAGED_CASE
+  q2_range<WIDE_D, USE_LO>(W, n, kb0 + len, kb1, X, cr, lane, acc);
+}
+
+// Whether the 8-block d/dmin window loads apply to rows of nb blocks.
+__host__ __device__ inline bool q2_wide_d(int nb) { return nb >= 8 && nb % 2 == 0; }
 
 }  // namespace sv
