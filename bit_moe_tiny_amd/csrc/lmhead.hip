@@ -94,7 +94,6 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
   const int c = min(cg * 16 + nl, R - 1);
   const _Float16* xh = img.hi + (size_t)c * K + kofs;
   const _Float16* xl = img.lo + (size_t)c * K + kofs;
-  const float* bs = img.bscale + (size_t)c * img.nbk;
   size_t rowb[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -120,13 +119,6 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
       }
     }
     if (kg + 8 < nb) q8_grp_load<T, DVEC>(W, rowb, kg + 8, min(8, nb - kg - 8), g, nxt);
-    const float s_own = bs[kg >> 3];
-    f4_t xs;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) xs[e] = __shfl(s_own, 4 * g + e, 64);
-    f4_t gacc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) gacc[t] = zero;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if (DVEC || 2 * p < nblk) {
@@ -150,18 +142,17 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
               }
               const float d = f16b_to_f32(db);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) gacc[t][e] = fmaf(d, dt[e], gacc[t][e]);
+              for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(d, dt[e], acc[t][e]);
             }
           }
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(xs[e], gacc[t][e], acc[t][e]);
     cur = nxt;
   }
+  f4_t xs;   // row scales of the lane's 4 output columns
+#pragma unroll
+  for (int e = 0; e < 4; ++e) xs[e] = img.rscale[min(cg * 16 + 4 * g + e, R - 1)];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const int n = (tile0 + t) * 16 + nl;
@@ -169,7 +160,7 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int cc = cg * 16 + 4 * g + e;
-      if (cc < R) logits[(size_t)cc * vocab + n] = acc[t][e];
+      if (cc < R) logits[(size_t)cc * vocab + n] = acc[t][e] * xs[e];
     }
   }
 }

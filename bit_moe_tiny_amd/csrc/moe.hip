@@ -261,11 +261,11 @@ template <int DT>
 __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, int R, int E, int k,
                                                            int has_shared, int32_t* idx_out,
                                                            float* w_out, const void* x, MoeWs ws) {
+  __shared__ int sh[2 * PREP_THREADS / 64];
   if (blockIdx.x == 0) {
     route_and_group(logits, R, E, k, has_shared, idx_out, w_out, ws);
   } else {
-    stage_gid<DT>(x, R, XL_PERM, ws.x_img, (blockIdx.x - 1) * (PREP_THREADS / 32) + (threadIdx.x >> 5),
-                  threadIdx.x & 31);
+    stage_row<DT>(x, blockIdx.x - 1, XL_PERM, ws.x_img, sh);   // one block per row
   }
 }
 
@@ -273,9 +273,7 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            const void* x, int x_dtype, int32_t* topk_idx_out,
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
   const int has_shared = d->s_gate ? 1 : 0;
-  const int groups = R * (d->hidden / 256);
-  constexpr int per_block = PREP_THREADS / 32;
-  const dim3 grid(1 + (groups + per_block - 1) / per_block);
+  const dim3 grid(1 + R);
   if (x_dtype == SV_BF16)
     hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
                        d->n_experts, d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
@@ -288,15 +286,16 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
 // ------------------------------------------------------------ LDS staging
 struct XLw {   // writable view of the LDS rows
   _Float16 *hi, *lo, *sx;
-  float* bst;
-  int K, nbk;
+  float* rsc;
+  int K, rs, sxs;
 };
 
 __device__ inline XLw xl_make(uint8_t* lds, int ncols, int K, bool use_lo) {
   XLw w;
-  xl_carve<_Float16>((_Float16*)lds, ncols, K, use_lo, w.hi, w.lo, w.sx, w.bst);
+  xl_carve<_Float16>((_Float16*)lds, ncols, K, use_lo, w.hi, w.lo, w.sx, w.rsc);
   w.K = K;
-  w.nbk = K / 256;
+  w.rs = xl_rs(K);
+  w.sxs = K / 8;
   return w;
 }
 
@@ -305,100 +304,47 @@ __device__ inline XL xl_view(const XLw& w) {
   x.hi = w.hi;
   x.lo = w.lo;
   x.sx = w.sx;
-  x.bst = w.bst;
-  x.K = w.K;
+  x.rsc = w.rsc;
+  x.rs = w.rs;
+  x.sxs = w.sxs;
   return x;
 }
 
-// Copy rows rows[0..ncols) of a prepared global image into LDS (whole block).
-__device__ inline void xl_copy_image(const XImg& img, const int* rows, int ncols, bool use_lo,
-                                     const XLw& L) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int K = L.K, per = K / 8;   // 16-byte pieces per row
-  for (int i = tid; i < ncols * per; i += nt) {
-    const int c = i / per, j = i - c * per;
-    const size_t r = (size_t)rows[c];
-    const int o = (8 * j) ^ xl_swz(c);
-    *(uint4*)(L.hi + (size_t)c * K + o) = *(const uint4*)(img.hi + r * K + 8 * j);
-    if (use_lo) *(uint4*)(L.lo + (size_t)c * K + o) = *(const uint4*)(img.lo + r * K + 8 * j);
-  }
-  const int ng = K / 64;   // groups of 4 sub-block sums per row
-  for (int i = tid; i < ncols * ng; i += nt) {
-    const int c = i / ng, j = i - c * ng;
-    const size_t r = (size_t)rows[c];
-    const uint2 h = *(const uint2*)(img.sxh + r * (K / 16) + 4 * j);
-    const uint2 l = *(const uint2*)(img.sxl + r * (K / 16) + 4 * j);
-    *(uint4*)(L.sx + (size_t)c * (K / 8) + 8 * j) = make_uint4(h.x, h.y, l.x, l.y);
-  }
-  for (int i = tid; i < (L.nbk + 1) * XL_MAX_COLS; i += nt) {
-    const int kb = i / XL_MAX_COLS, c = i % XL_MAX_COLS;
-    L.bst[i] = (c < ncols && kb < L.nbk) ? img.bscale[(size_t)rows[c] * img.nbk + kb] : 0.f;
-  }
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+// One 1 KB piece of a contiguous run, global -> LDS without registers: lane i
+// copies bytes [16 i, 16 i + 16) of the piece (lanes past `bytes` skip).
+__device__ __forceinline__ void dma_piece(const uint8_t* src, uint8_t* dst, int bytes, int lane) {
+  if (16 * lane < bytes)
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * lane), (lds_vptr)dst, 16, 0, 0);
 }
 
-// Convert fp32 rows src[rows[c]] (length K) into the LDS image: one half-wave
-// per (row, 256-block) pair, same scaling and order as the global stager.
-__device__ inline void xl_stage_f32(const float* src, const int* rows, int ncols, const XLw& L) {
-  const int l = threadIdx.x & 31, hw = threadIdx.x >> 5, nhw = blockDim.x >> 5;
-  for (int p = hw; p < ncols * L.nbk; p += nhw) {
-    const int c = p / L.nbk, kb = p - c * L.nbk;
-    const float* row = src + (size_t)rows[c] * L.K;
-    const int k0 = kb * 256;
-    // lane = chunk (t, g) of the block: element e = 2j + hb <-> k = 16 s + 4 hs + j + 8 hb
-    const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
-    const float4 a = *(const float4*)(row + k0 + 16 * s + 4 * hs);
-    const float4 b = *(const float4*)(row + k0 + 16 * s + 4 * hs + 8);
-    const float v[8] = {a.x, b.x, a.y, b.y, a.z, b.z, a.w, b.w};
-    float mx = 0.f;
-    int bad = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float m = fabsf(v[e]);
-      bad |= !(m <= 3.402823466e38f);
-      mx = fmaxf(mx, m);
+// Start copying rows rows[0..ncols) of a prepared global image into LDS: the
+// waves of the block share the 1 KB pieces (hi rows, lo rows, the sub-block
+// sums).  Completion: vmcnt of the issuing wave, then a block barrier.
+__device__ inline void xl_dma_image(const XImg& img, const int* rows, int ncols, bool use_lo,
+                                    const XLw& L) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int K = L.K;
+  const int prow = (2 * K + 1023) / 1024;       // pieces per hi / lo row
+  const int psx = (K / 4 + 1023) / 1024;        // pieces per sum row (K/8 fp16)
+  const int per_c = prow * (use_lo ? 2 : 1) + psx;
+  for (int q = wv; q < ncols * per_c; q += nw) {
+    const int c = q / per_c, j = q - c * per_c;
+    const size_t r = (size_t)rows[c];
+    if (j < prow) {
+      dma_piece((const uint8_t*)(img.hi + r * K) + 1024 * j, (uint8_t*)(L.hi + (size_t)c * L.rs) + 1024 * j,
+                2 * K - 1024 * j, lane);
+    } else if (use_lo && j < 2 * prow) {
+      const int jj = j - prow;
+      dma_piece((const uint8_t*)(img.lo + r * K) + 1024 * jj, (uint8_t*)(L.lo + (size_t)c * L.rs) + 1024 * jj,
+                2 * K - 1024 * jj, lane);
+    } else {
+      const int jj = j - prow * (use_lo ? 2 : 1);
+      dma_piece((const uint8_t*)(img.sx + r * (K / 8)) + 1024 * jj,
+                (uint8_t*)(L.sx + (size_t)c * L.sxs) + 1024 * jj, K / 4 - 1024 * jj, lane);
     }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-      bad |= __shfl_xor(bad, o, 32);
-    }
-    int esc = 0;
-    if (!bad && mx > 0.f) {
-      int E;
-      frexpf(mx, &E);
-      esc = 11 - E;
-      esc = esc < -120 ? -120 : (esc > 120 ? 120 : esc);
-    }
-    h8_t hv, lv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float sv = ldexpf(v[e], esc - 2 * (e >> 1));   // 4^-j folded in
-      const _Float16 h = (_Float16)sv;
-      hv[e] = h;
-      lv[e] = (_Float16)(sv - (float)h);
-    }
-    const size_t dst = (size_t)c * L.K + (((kb * 32 + l) * 8) ^ xl_swz(c));
-    *(h8_t*)(L.hi + dst) = hv;
-    *(h8_t*)(L.lo + dst) = lv;
-    if (l < 16) {   // sum of sub-block l (the min term)
-      float acc = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 x4 = *(const float4*)(row + k0 + 16 * l + 4 * q);
-        acc += ldexpf(x4.x, esc);
-        acc += ldexpf(x4.y, esc);
-        acc += ldexpf(x4.z, esc);
-        acc += ldexpf(x4.w, esc);
-      }
-      const _Float16 h = (_Float16)acc;
-      _Float16* sp = L.sx + (size_t)c * (L.K / 8) + (kb * 4 + (l >> 2)) * 8 + (l & 3);
-      sp[0] = h;
-      sp[4] = (_Float16)(acc - (float)h);
-    }
-    if (l == 0) L.bst[kb * XL_MAX_COLS + c] = ldexpf(1.f, -esc);
   }
-  for (int i = threadIdx.x; i < (L.nbk + 1) * XL_MAX_COLS; i += blockDim.x)
-    if (i % XL_MAX_COLS >= ncols || i >= L.nbk * XL_MAX_COLS) L.bst[i] = 0.f;
 }
 
 // Largest column group (rows per block) whose LDS copy fits the budget.
@@ -434,13 +380,15 @@ template <bool USE_LO, bool WIDE_D>
 __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int hidden, int inter,
                                                              int CG, MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_rows[XL_MAX_COLS];
   const int tile = blockIdx.x, u = blockIdx.y;
   if (u >= ws.meta->n_units) return;
   const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
   const int c0 = blockIdx.z * CG;
   if (c0 >= cnt) return;
   const int ncols = min(CG, cnt - c0);
+  int rows[XL_MAX_COLS];   // activation rows of the block's columns (wave-uniform)
+#pragma unroll
+  for (int c = 0; c < XL_MAX_COLS; ++c) rows[c] = c < ncols ? ws.arow[off + c0 + c] : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m = wv >> 2, q = wv & 3;
   const int nl = lane & 15, g = lane >> 4;
@@ -451,14 +399,13 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   const Q2View W = q2_view(base, inter, hidden);
   const XLw L = xl_make(lds, ncols, hidden, USE_LO);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto stage = [&]() {
-    if (tid < ncols) s_rows[tid] = ws.arow[off + c0 + tid];
-    __syncthreads();
-    xl_copy_image(ws.x_img, s_rows, ncols, USE_LO, L);
-    __syncthreads();
+  auto issue = [&]() { xl_dma_image(ws.x_img, rows, ncols, USE_LO, L); };
+  auto sync = [&](int nload) {
+    wait_vmcnt_le(nload);   // this wave's DMA pieces have landed (they precede the weight loads)
+    barrier_keep_loads();
   };
   q2_range_staged<WIDE_D, USE_LO>(W, n, nb * q / 4, nb * (q + 1) / 4, xl_view(L), min(nl, ncols - 1),
-                                  lane, acc, stage);
+                                  lane, acc, issue, sync);
   __syncthreads();   // every wave is done with the rows: reuse LDS for the partial sums
   f4_t* red = (f4_t*)lds;
   red[wv * 64 + lane] = acc;
@@ -470,7 +417,8 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;
     if (c >= ncols) continue;
-    const float gv = gs[i], uv = us[i];
+    const float rs = ws.x_img.rscale[ws.arow[off + c0 + c]];
+    const float gv = gs[i] * rs, uv = us[i] * rs;
     ws.h[(size_t)(off + c0 + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
   }
 }
@@ -501,11 +449,17 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, 
 // ------------------------------------------------------------------ down
 constexpr int DN_THREADS = 512;   // 8 waves, one 16-row tile each, all of inter
 
+// The block's h rows are read into registers before the weight loads are
+// issued (so their wait does not include the weights), then converted into
+// the LDS image: each row scaled by its own power of two, one half-wave per
+// (row, 256-block) pair, at most DN_PAIRS pairs per half-wave.
+constexpr int DN_PAIRS = 4;
+
 template <bool WIDE_D>
 __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter,
                                                            int CG, MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_rows[XL_MAX_COLS];
+  __shared__ int s_max[2 * DN_PAIRS * (DN_THREADS / 32)];   // per pair: max bits, bad flag
   const int u = blockIdx.y;
   if (u >= ws.meta->n_units) return;
   const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
@@ -517,24 +471,102 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hid
   const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
   const XLw L = xl_make(lds, ncols, inter, true);
+  const int nbk = inter / 256, npairs = ncols * nbk;
+  const int l = tid & 31, hw = tid >> 5;
+  const int t = l >> 2, gg = l & 3, sb = 4 * gg + (t >> 1), hs = t & 1;
+  float4 pa[DN_PAIRS], pb[DN_PAIRS];
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto stage = [&]() {
-    if (tid < ncols) s_rows[tid] = off + c0 + tid;   // assignments: rows of h
+  auto issue = [&]() {
+#pragma unroll
+    for (int i = 0; i < DN_PAIRS; ++i) {
+      const int p = hw + (DN_THREADS / 32) * i;
+      if (p < npairs) {
+        const int c = p / nbk, kb = p - c * nbk;
+        const float* src = ws.h + (size_t)(off + c0 + c) * inter + kb * 256 + 16 * sb + 4 * hs;
+        pa[i] = *(const float4*)src;
+        pb[i] = *(const float4*)(src + 8);
+      }
+    }
+  };
+  auto sync = [&](int) {
+#pragma unroll
+    for (int i = 0; i < DN_PAIRS; ++i) {   // per-pair maxima
+      const int p = hw + (DN_THREADS / 32) * i;
+      if (p < npairs) {
+        const float a8[8] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w, pb[i].x, pb[i].y, pb[i].z, pb[i].w};
+        float mx = 0.f;
+        int bad = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float av = fabsf(a8[k]);
+          bad |= !(av <= 3.402823466e38f);
+          mx = fmaxf(mx, av);
+        }
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) {
+          mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+          bad |= __shfl_xor(bad, o, 32);
+        }
+        if (l == 0) {
+          s_max[2 * p] = __float_as_int(mx);
+          s_max[2 * p + 1] = bad;
+        }
+      }
+    }
     __syncthreads();
-    xl_stage_f32(ws.h, s_rows, ncols, L);
+#pragma unroll
+    for (int i = 0; i < DN_PAIRS; ++i) {   // convert
+      const int p = hw + (DN_THREADS / 32) * i;
+      if (p < npairs) {
+        const int c = p / nbk, kb = p - c * nbk;
+        float mx = 0.f;
+        int bad = 0;
+        for (int j = 0; j < nbk; ++j) {
+          mx = fmaxf(mx, __int_as_float(s_max[2 * (c * nbk + j)]));
+          bad |= s_max[2 * (c * nbk + j) + 1];
+        }
+        const int esc = row_exponent(mx, bad);
+        const float v[8] = {pa[i].x, pb[i].x, pa[i].y, pb[i].y, pa[i].z, pb[i].z, pa[i].w, pb[i].w};
+        h8_t hv, lv;
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float sv = ldexpf(v[k], esc - 2 * (k >> 1));   // 4^-j folded in
+          const _Float16 h = (_Float16)sv;
+          hv[k] = h;
+          lv[k] = (_Float16)(sv - (float)h);
+          part += ldexpf(v[k], esc);
+        }
+        const size_t dst = (size_t)c * L.rs + (size_t)(kb * 32 + l) * 8;
+        *(h8_t*)(L.hi + dst) = hv;
+        *(h8_t*)(L.lo + dst) = lv;
+        const float sum = part + __shfl_xor(part, 4, 32);   // the other half of sub-block sb
+        if (hs == 0) {
+          const _Float16 h = (_Float16)sum;
+          _Float16* sp = L.sx + (size_t)c * L.sxs + (kb * 4 + gg) * 8 + (t >> 1);
+          sp[0] = h;
+          sp[4] = (_Float16)(sum - (float)h);
+        }
+        if (kb == 0 && l == 0) L.rsc[c] = ldexpf(1.f, -esc);
+      }
+    }
+    if (tid >= ncols && tid < 16) L.rsc[tid] = 0.f;
     __syncthreads();
   };
-  q2_range_staged<WIDE_D, true>(D, n, 0, inter / 256, xl_view(L), min(nl, ncols - 1), lane, acc,
-                                stage);
+  q2_range_staged<WIDE_D, true>(D, n, 0, nbk, xl_view(L), min(nl, ncols - 1), lane, acc, issue,
+                                sync);
+  const f4_t rsc_c = *(const f4_t*)(L.rsc + 4 * g);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;   // tile column; only 0..ncols-1 are real
-    if (c < ncols) ws.part[(size_t)(off + c0 + c) * hidden + n] = acc[i];
+    if (c < ncols) ws.part[(size_t)(off + c0 + c) * hidden + n] = acc[i] * rsc_c[i];
   }
 }
 
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const int CG = col_group(d->inter, true, R);
+  int CG = col_group(d->inter, true, R);
+  const int pair_cap = DN_PAIRS * (DN_THREADS / 32) / (d->inter / 256);   // staged (row, block) pairs
+  if (CG > pair_cap) CG = pair_cap > 0 ? pair_cap : 1;
   const dim3 grid(d->hidden / 128, ws.max_units, (R + CG - 1) / CG);
   const size_t lb = xl_bytes(CG, d->inter, true);
   const ExpertPtrs P = expert_ptrs(d);
@@ -597,9 +629,11 @@ template <bool USE_LO, bool WIDE_D>
 __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_plain(const uint8_t* w, int n_out, int k_in,
                                                             int R, int CG, XImg img, float* y) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_rows[XL_MAX_COLS];
   const int c0 = blockIdx.z * CG;
   const int ncols = min(CG, R - c0);
+  int rows[XL_MAX_COLS];
+#pragma unroll
+  for (int c = 0; c < XL_MAX_COLS; ++c) rows[c] = c0 + (c < ncols ? c : 0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int n = (blockIdx.x * 8 + wv) * 16 + nl;
@@ -607,19 +641,18 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_plain(const uint8_t* w, in
   const Q2View W = q2_view(w, n_out, k_in);
   const XLw L = xl_make(lds, ncols, k_in, USE_LO);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto stage = [&]() {
-    if (tid < ncols) s_rows[tid] = c0 + tid;
-    __syncthreads();
-    xl_copy_image(img, s_rows, ncols, USE_LO, L);
-    __syncthreads();
+  auto issue = [&]() { xl_dma_image(img, rows, ncols, USE_LO, L); };
+  auto sync = [&](int nload) {
+    wait_vmcnt_le(nload);   // this wave's DMA pieces have landed (they precede the weight loads)
+    barrier_keep_loads();
   };
   q2_range_staged<WIDE_D, USE_LO>(W, nld, 0, k_in / 256, xl_view(L), min(nl, ncols - 1), lane, acc,
-                                  stage);
+                                  issue, sync);
   if (n >= n_out) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;
-    if (c < ncols) y[(size_t)(c0 + c) * n_out + n] = acc[i];
+    if (c < ncols) y[(size_t)(c0 + c) * n_out + n] = acc[i] * img.rscale[c0 + c];
   }
 }
 

@@ -71,32 +71,32 @@ __host__ __device__ inline Q8View q8_view(const void* base, int n_out, int k_in)
 }
 
 // ------------------------------------------------------- activation images
-// Rows of activations prepared for the fp16 matrix cores.  Every 256-element
-// block of a row is scaled by its own power of two 2^e (its largest magnitude
-// lands in [2^10, 2^11), far from fp16 overflow even after 16-element sums)
-// and split into an fp16 high part and an fp16 remainder (~22 significant
-// bits together).  bscale holds 2^-e per (row, block); consumers multiply
-// each block's partial result by it, so the scaling is exact end to end.
+// Rows of activations prepared for the fp16 matrix cores.  Every row is
+// scaled by its own power of two 2^e (its largest magnitude lands in
+// [2^10, 2^11), far from fp16 overflow even after 16-element sums) and split
+// into an fp16 high part and an fp16 remainder (~22 significant bits
+// together; a bf16 row is exact in the high part alone).  rscale holds 2^-e
+// per row; consumers multiply their finished sums by it, so the scaling is
+// exact end to end.
 //  layout PERM (two-bit kernels): element order matches the register order in
 //    which the two-bit kernel unpacks codes, with the 4^-j factor of each
-//    position folded in; plus per-16-element sums (for the min term).
+//    position folded in; plus per-16-element sums (for the min term), stored
+//    per group of 4 sub-blocks as their 4 high parts then their 4 remainders
+//    (the order the kernel reads them in).
 //  layout PLAIN (eight-bit kernel): natural order.
 struct XImg {
   _Float16* hi;      // [rows, K]
   _Float16* lo;      // [rows, K]
-  _Float16* sxh;     // [rows, K/16]  (PERM only)
-  _Float16* sxl;     // [rows, K/16]
-  float* bscale;     // [rows, nbk]  2^-e per 256-element block
+  _Float16* sx;      // [rows, K/8]  (PERM only)
+  float* rscale;     // [rows]  2^-e
   int K;
-  int nbk;           // ceil(K / 256)
 };
 
 enum { XL_PERM = 0, XL_PLAIN = 1 };
 
 __host__ __device__ inline size_t ximg_bytes(size_t rows, size_t K, int layout) {
-  size_t nbk = (K + 255) / 256;
-  size_t b = 2 * up256(rows * K * 2) + up256(rows * nbk * 4);
-  if (layout == XL_PERM) b += 2 * up256(rows * (K / 16) * 2);
+  size_t b = 2 * up256(rows * K * 2) + up256(rows * 4);
+  if (layout == XL_PERM) b += up256(rows * (K / 8) * 2);
   return b;
 }
 
@@ -104,20 +104,17 @@ inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
   uint8_t* p = (uint8_t*)base;
   XImg x;
   x.K = K;
-  x.nbk = (K + 255) / 256;
   x.hi = (_Float16*)p;
   p += up256(rows * K * 2);
   x.lo = (_Float16*)p;
   p += up256(rows * K * 2);
   if (layout == XL_PERM) {
-    x.sxh = (_Float16*)p;
-    p += up256(rows * (K / 16) * 2);
-    x.sxl = (_Float16*)p;
-    p += up256(rows * (K / 16) * 2);
+    x.sx = (_Float16*)p;
+    p += up256(rows * (K / 8) * 2);
   } else {
-    x.sxh = x.sxl = nullptr;
+    x.sx = nullptr;
   }
-  x.bscale = (float*)p;
+  x.rscale = (float*)p;
   return x;
 }
 
@@ -140,7 +137,6 @@ struct MoeWs {
   float* h;           // [max_assign, inter]  SwiGLU output
   float* part;        // [max_assign, hidden] per-assignment down outputs
   XImg x_img;         // staged x  [R, hidden]
-  XImg h_img;         // staged h  [max_assign, inter]
   int max_units, max_assign;
 };
 

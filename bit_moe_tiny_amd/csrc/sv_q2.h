@@ -108,46 +108,46 @@ __device__ __forceinline__ uint32_t q2_magic() {
 
 // ------------------------------------------------------------ LDS rows
 // Activation rows of one block in LDS (layout written by the stagers):
-//   hi, lo  [ncols][K] fp16 in the PERM order of sv_internal.h (element
+//   hi, lo  [ncols][rs] fp16 in the PERM order of sv_internal.h (element
 //           ((kb*8 + t)*4 + g)*8 + i of a row is the A-operand value i of
-//           lane-group g at step t of block kb), with the 64-byte pieces of
-//           row c XOR-swizzled by (c & 7) so that different rows at the same
-//           offset fall in different banks (the swizzle stays inside each
-//           256-element block);
+//           lane-group g at step t of block kb); rs = K + 8 (16 bytes of
+//           padding move each row to other banks)
 //   sx      [ncols][K/8] fp16: per 4-sub-block group (kb*4 + g), the 4
-//           sub-block sums' high parts then their 4 remainders;
-//   bst     [nbk + 1][8] fp32: block scale of column c (< 8) of block kb (the
-//           extra row keeps the lanes of padding columns 8..15 in bounds).
+//           sub-block sums' high parts then their 4 remainders
+//   rsc     [16] fp32: the row scale 2^-e of column c (0 beyond ncols)
+// A lane reads its column's row from a base address fixed for the chunk, so
+// every read of a block is base + an immediate offset.
 constexpr int XL_MAX_COLS = 8;
 
 struct XL {
   const _Float16* hi;
   const _Float16* lo;
   const _Float16* sx;
-  const float* bst;
-  int K;
+  const float* rsc;
+  int rs, sxs;
 };
 
-__host__ __device__ inline int xl_swz(int c) { return (c & 7) << 5; }
+__host__ __device__ inline int xl_rs(int K) { return K + 8; }
+
+__host__ __device__ inline size_t up16(size_t n) { return (n + 15) & ~size_t(15); }
 
 __host__ __device__ inline size_t xl_bytes(int ncols, int K, bool use_lo) {
-  const size_t rows = (size_t)ncols * K * 2 * (use_lo ? 2 : 1);
+  const size_t rows = (size_t)ncols * xl_rs(K) * 2 * (use_lo ? 2 : 1);
   const size_t sx = (size_t)ncols * (K / 8) * 2;
-  const size_t bst = (size_t)(K / 256 + 1) * XL_MAX_COLS * 4;
-  return up256(rows) + up256(sx) + up256(bst);
+  return up16(rows) + up16(sx) + 16 * 4;
 }
 
 template <typename P>
-__device__ __forceinline__ void xl_carve(P* base, int ncols, int K, bool use_lo, P*& hi, P*& lo, P*& sx,
-                                float*& bst) {
+__device__ __forceinline__ void xl_carve(P* base, int ncols, int K, bool use_lo, P*& hi, P*& lo,
+                                         P*& sx, float*& rsc) {
   uint8_t* p = (uint8_t*)base;
-  const size_t row = (size_t)K * 2;
+  const size_t row = (size_t)xl_rs(K) * 2;
   hi = (P*)p;
   lo = (P*)(p + (size_t)ncols * row);
-  p += up256((size_t)ncols * row * (use_lo ? 2 : 1));
+  p += up16((size_t)ncols * row * (use_lo ? 2 : 1));
   sx = (P*)p;
-  p += up256((size_t)ncols * (K / 8) * 2);
-  bst = (float*)p;
+  p += up16((size_t)ncols * (K / 8) * 2);
+  rsc = (float*)p;
 }
 
 // ------------------------------------------------------------ wide loads
@@ -205,32 +205,31 @@ __device__ __forceinline__ void xpose4(const uint4& v, uint32_t* r) {
   r[3] = d[1];
 }
 
-// acc += block kb of the chunk (index i) for this lane's column row.
-__device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d, float dmin, const XL& X,
-                                int cr, int kb, int lane, f4_t& acc, bool use_lo) {
-  const int g = lane >> 4;
+// acc += one block for this lane's column: xh/xl point at the block's
+// A operands of this lane (step t at +32 t elements), xs at its 4-sub-block
+// sum group.  The row scale is applied by the caller.
+template <bool USE_LO>
+__device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d, float dmin,
+                                         const _Float16* xh, const _Float16* xl,
+                                         const _Float16* xs, f4_t& acc) {
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  const _Float16* xh = X.hi + (size_t)cr * X.K;
-  const _Float16* xl = X.lo + (size_t)cr * X.K;
-  const int swz = xl_swz(cr);
   const uint32_t magic = q2_magic();
   const Q2Sc S = q2_scales(scw);
   f4_t dt = zero;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const h8_t b = q2_bop(qs, S, t, magic);
-    const int off = (((kb * 8 + t) * 4 + g) * 8) ^ swz;
-    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + off), b, dt, 0, 0, 0);
-    if (use_lo) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + off), b, dt, 0, 0, 0);
+    dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + 32 * t), b, dt, 0, 0, 0);
+    if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + 32 * t), b, dt, 0, 0, 0);
   }
-  const h8_t sx = *(const h8_t*)(X.sx + (size_t)cr * (X.K / 8) + (kb * 4 + g) * 8);
+  const h8_t sx = *(const h8_t*)xs;
   const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
   // the 16-element sums are never fp16-exact: their remainder is always used
   f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, S.m, zero, 0, 0, 0);
   dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, S.m, dm, 0, 0, 0);
-  const f4_t xs = *(const f4_t*)(X.bst + kb * XL_MAX_COLS + 4 * g);   // the lane's 4 columns
+  const float nd = -dmin;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = fmaf(xs[e], fmaf(d, dt[e], -dmin * dm[e]), acc[e]);
+  for (int e = 0; e < 4; ++e) acc[e] = fmaf(nd, dm[e], fmaf(d, dt[e], acc[e]));
 }
 
 // fp16 value at position p (0..7) of an 8-value window held as 4 dwords.
@@ -275,11 +274,16 @@ __device__ __forceinline__ void q2_chunk_compute(const Q2View& W, const Q2Chunk<
       mF[i] = f16bits_to_f32(c.dm[WIDE_D ? 0 : i]);
     }
   }
+  const int g = lane >> 4;
+  const _Float16* xh = X.hi + (size_t)cr * X.rs + kb0 * 256 + g * 8;
+  const _Float16* xl = X.lo + (size_t)cr * X.rs + kb0 * 256 + g * 8;
+  const _Float16* xs = X.sx + (size_t)cr * X.sxs + kb0 * 32 + g * 8;
   uint32_t sct[4];
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     if (i % 4 == 0) xpose4(c.sc[i / 4], sct);
-    q2_block(c.qs[i], sct[i % 4], dF[i], mF[i], X, cr, kb0 + i, lane, acc, USE_LO);
+    q2_block<USE_LO>(c.qs[i], sct[i % 4], dF[i], mF[i], xh + 256 * i, xl + 256 * i, xs + 32 * i,
+                     acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -319,19 +323,33 @@ __device__ __forceinline__ void q2_range(const Q2View& W, int n, int kb0, int kb
   }
 }
 
-// Same, with the first chunk's loads issued before `stage()` (which fills the
-// LDS rows and ends in a block barrier) so they are in flight meanwhile.
-// Every wave calls stage() exactly once.
-template <bool WIDE_D, bool USE_LO, typename F>
-__device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0, int kb1, const XL& X,
-                                       int cr, int lane, f4_t& acc, F&& stage) {
+// Number of vector loads q2_chunk_load issues for a chunk of NBW blocks when
+// every load is 16 bytes wide (the compiler cannot merge those).  The narrow
+// d/dmin loads may be merged into wider ones, so their count is unknown: 0
+// then, and a wait for it waits for everything.
+template <int NBW, bool WIDE_D>
+constexpr int q2_chunk_nloads() {
+  return WIDE_D ? NBW + (NBW + 3) / 4 + 1 : 0;
+}
+
+// Same as q2_range, for the start of a kernel: `issue()` runs first (it
+// starts the loads that fill the LDS rows), then the first chunk's weight
+// loads are issued, then `sync(n)` (n = the number of weight loads issued
+// after issue()'s, so it can wait for exactly its own; it ends in a block
+// barrier), then the blocks are computed.  Every wave calls both exactly once.
+template <bool WIDE_D, bool USE_LO, typename F, typename G>
+__device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0, int kb1,
+                                                const XL& X, int cr, int lane, f4_t& acc,
+                                                F&& issue, G&& sync) {
   const int len = q2_chunk_len<WIDE_D>(kb0, kb1 - kb0);
   const int g = lane >> 4;
+  issue();
+  asm volatile("" ::: "memory");   // the weight loads stay after issue()'s loads
 #define SV_STAGED_CASE(L)                                               \
   case L: {                                                             \
     Q2Chunk<L, WIDE_D> c;                                               \
     q2_chunk_load<L, WIDE_D>(W, n, kb0, g, c);                          \
-    stage();                                                            \
+    sync(q2_chunk_nloads<L, WIDE_D>());                                 \
     q2_chunk_compute<L, WIDE_D, USE_LO>(W, c, kb0, n, X, cr, lane, acc); \
     break;                                                              \
   }
@@ -344,10 +362,30 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
     SV_STAGED_CASE(6)
     SV_STAGED_CASE(7)
     SV_STAGED_CASE(8)
-    default: stage(); return;   // empty range
+    default: sync(0); return;   // empty range
   }
 #undef SV_STAGED_CASE
   q2_range<WIDE_D, USE_LO>(W, n, kb0 + len, kb1, X, cr, lane, acc);
+}
+
+// Block barrier that does not wait for outstanding vector-memory loads (the
+// compiler's __syncthreads() waits for all of them); a compiler-only memory
+// fence keeps LDS accesses on their side of it.  Callers make their own LDS
+// writes complete first.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+
+// s_waitcnt that waits until at most n vector-memory loads are outstanding
+// (n a compile-time constant after inlining), leaving the other counters alone.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+#define SV_W(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | ((((N) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8)); break;
+  switch (n) {
+    SV_W(0) SV_W(1) SV_W(2) SV_W(3) SV_W(4) SV_W(5) SV_W(6) SV_W(7) SV_W(8) SV_W(9)
+    SV_W(10) SV_W(11) SV_W(12) SV_W(13) SV_W(14) SV_W(15) SV_W(16) SV_W(17) SV_W(18)
+    SV_W(19) SV_W(20) SV_W(21) SV_W(22) SV_W(23) SV_W(24) SV_W(25) SV_W(26) SV_W(27)
+    SV_W(28) SV_W(29) SV_W(30) SV_W(31)
+    default: __builtin_amdgcn_s_waitcnt(0); break;   // (more loads than encodable: wait for all)
+  }
+#undef SV_W
 }
 
 // Whether the 8-block d/dmin window loads apply to rows of nb blocks.
