@@ -82,7 +82,7 @@ __device__ inline void q8_regroup(uint4 v, uint2& a, uint2& b) {
 // guards at all, and a group's 8 block scales come in one 16-byte load.
 template <bool USE_LO, int T, bool DVEC>
 __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, float* logits) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = wave_id();
   const int tile0 = (blockIdx.x * 4 + wv) * T;
   const int vocab = W.n_out, K = W.nb * 32, nb = W.nb;
   if (tile0 * 16 >= vocab) return;

@@ -55,12 +55,45 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.topk_w = (float*)take(sizeof(float) * R * k);
   w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
+  // column groups of at least one column: at most one item per unit plus one
+  // per further column
+  const int max_work = max_units + max_assign;
+  w.work_gu = (MoeWork*)take(sizeof(MoeWork) * max_work);
+  w.work_dn = (MoeWork*)take(sizeof(MoeWork) * max_work);
   void* xb = take(ximg_bytes(R, d->hidden, XL_PERM));
   if (p) w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
   w.max_units = max_units;
   w.max_assign = max_assign;
+  w.max_work = max_work;
   if (out) *out = w;
   return off;
+}
+
+// Activation rows are copied into LDS in 1 KB pieces.
+
+__host__ __device__ inline int xl_pieces_per_row(int K, bool use_lo) {
+  return ((2 * K + 1023) / 1024) * (use_lo ? 2 : 1) + (K / 4 + 1023) / 1024;
+}
+
+// Largest column group (rows per block) whose LDS copy fits the budget.
+static int col_group(int K, bool use_lo, int R) {
+  int cg = XL_MAX_COLS;
+  while (cg > 1 && xl_bytes(cg, K, use_lo) > (size_t)LDS_BUDGET) --cg;
+  return cg < R ? cg : R;
+}
+
+constexpr int DN_THREADS = 512;   // down: 8 waves, one 16-row tile each, all of inter
+constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave
+
+static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo) {
+  return col_group(d->hidden, use_lo, R);
+}
+
+static int down_cols(const sv_moe_desc* d, int R) {
+  int cg = col_group(d->inter, true, R);
+  const int pair_cap = DN_PAIRS * (DN_THREADS / 32) / (d->inter / 256);
+  if (cg > pair_cap) cg = pair_cap > 0 ? pair_cap : 1;
+  return cg;
 }
 
 // ---------------------------------------------------- wave reductions (DPP)
@@ -174,13 +207,45 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 }
 
 // Block 0 of the prep kernel: top-k of every row, then grouping.
+// Work items of one expert kernel: each unit's assignments cut into groups
+// of at most cg columns (wave 0).
+__device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucnt, int nu,
+                          const int* s_arow, int cg, MoeWork* work, int* n_work) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int u0 = 0; u0 < nu; u0 += 64) {
+    const int u = u0 + lane;
+    const int ng = u < nu ? (s_ucnt[u] + cg - 1) / cg : 0;
+    int incl = ng;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    for (int j = 0; j < ng; ++j) {
+      MoeWork w;
+      w.expert = s_uexp[u];
+      w.a0 = s_uoff[u] + j * cg;
+      w.ncols = min(cg, s_ucnt[u] - j * cg);
+      w.pad = 0;
+#pragma unroll
+      for (int c = 0; c < MOE_WORK_COLS; ++c) w.rows[c] = c < w.ncols ? s_arow[w.a0 + c] : 0;
+      work[base + incl - ng + j] = w;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) *n_work = base;
+}
+
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
-                                int32_t* idx_out, float* w_out, MoeWs ws) {
+                                int cg_gu, int cg_dn, int32_t* idx_out, float* w_out, MoeWs ws) {
   __shared__ int s_idx[SV_MAX_ROWS * SV_MAX_TOPK];
   __shared__ int cnt[SV_MAX_EXPERTS];
   __shared__ int eoff[SV_MAX_EXPERTS];
+  __shared__ int s_uexp[SV_MAX_EXPERTS + 1], s_uoff[SV_MAX_EXPERTS + 1], s_ucnt[SV_MAX_EXPERTS + 1];
+  __shared__ int s_arow[SV_MAX_ROWS * (SV_MAX_TOPK + 1)];
   __shared__ int s_nu;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   constexpr int NW = PREP_THREADS / 64;
   for (int e = tid; e < E; e += PREP_THREADS) cnt[e] = 0;
   if (logits == nullptr) {  // one expert, no router: weight 1
@@ -224,6 +289,9 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
         ws.unit_expert[u] = e;
         ws.unit_off[u] = a;
         ws.unit_cnt[u] = ce;
+        s_uexp[u] = e;
+        s_uoff[u] = a;
+        s_ucnt[u] = ce;
       }
       base_u += __shfl(fu, 63, 64);
       base_a += __shfl(fa, 63, 64);
@@ -238,32 +306,43 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
     for (int j = 0; j < r * k; ++j) rank += s_idx[j] == e;
     const int a = eoff[e] + rank;
     ws.arow[a] = r;
+    s_arow[a] = r;
     ws.amap[r * (k + 1) + s] = a;
   }
   if (has_shared) {
     for (int r = tid; r < R; r += PREP_THREADS) {
       ws.arow[R * k + r] = r;
+      s_arow[R * k + r] = r;
       ws.amap[r * (k + 1) + k] = R * k + r;
     }
     if (tid == 0) {
       ws.unit_expert[nu] = -1;
       ws.unit_off[nu] = R * k;
       ws.unit_cnt[nu] = R;
+      s_uexp[nu] = -1;
+      s_uoff[nu] = R * k;
+      s_ucnt[nu] = R;
     }
   }
   if (tid == 0) {
     ws.meta->n_units = nu + has_shared;
     ws.meta->n_assign = R * k + has_shared * R;
   }
+  __syncthreads();
+  if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, cg_gu, ws.work_gu,
+                         &ws.meta->n_work_gu);
+  if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, cg_dn, ws.work_dn,
+                         &ws.meta->n_work_dn);
 }
 
 template <int DT>
 __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, int R, int E, int k,
-                                                           int has_shared, int32_t* idx_out,
-                                                           float* w_out, const void* x, MoeWs ws) {
+                                                           int has_shared, int cg_gu, int cg_dn,
+                                                           int32_t* idx_out, float* w_out,
+                                                           const void* x, MoeWs ws) {
   __shared__ int sh[2 * PREP_THREADS / 64];
   if (blockIdx.x == 0) {
-    route_and_group(logits, R, E, k, has_shared, idx_out, w_out, ws);
+    route_and_group(logits, R, E, k, has_shared, cg_gu, cg_dn, idx_out, w_out, ws);
   } else {
     stage_row<DT>(x, blockIdx.x - 1, XL_PERM, ws.x_img, sh);   // one block per row
   }
@@ -274,12 +353,15 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
   const int has_shared = d->s_gate ? 1 : 0;
   const dim3 grid(1 + R);
+  const int cg_gu = gateup_cols(d, R, x_dtype == SV_F32), cg_dn = down_cols(d, R);
   if (x_dtype == SV_BF16)
     hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
-                       d->n_experts, d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
+                       d->n_experts, d->top_k, has_shared, cg_gu, cg_dn, topk_idx_out, topk_w_out,
+                       x, ws);
   else
     hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
-                       d->n_experts, d->top_k, has_shared, topk_idx_out, topk_w_out, x, ws);
+                       d->n_experts, d->top_k, has_shared, cg_gu, cg_dn, topk_idx_out, topk_w_out,
+                       x, ws);
   return hipGetLastError();
 }
 
@@ -310,48 +392,70 @@ __device__ inline XL xl_view(const XLw& w) {
   return x;
 }
 
-typedef __attribute__((address_space(3))) void* lds_vptr;
+// Prepared image rows are copied into LDS with global-to-LDS loads (no
+// registers), issued before the weight loads; each wave then waits for its own
+// copies with an explicit vmcnt (they are older than every weight load) and
+// the block meets at a barrier.  The copy is written as inline assembly: when
+// the compiler sees an outstanding global-to-LDS load it waits for every
+// vector load before the next use, which would serialise the weight stream.
+// Source, destination and length of piece j of column c (image row r).
+struct XLPiece {
+  const uint8_t* src;
+  uint8_t* dst;
+  int bytes;
+};
 
-// One 1 KB piece of a contiguous run, global -> LDS without registers: lane i
-// copies bytes [16 i, 16 i + 16) of the piece (lanes past `bytes` skip).
-__device__ __forceinline__ void dma_piece(const uint8_t* src, uint8_t* dst, int bytes, int lane) {
-  if (16 * lane < bytes)
-    __builtin_amdgcn_global_load_lds((const void*)(src + 16 * lane), (lds_vptr)dst, 16, 0, 0);
-}
-
-// Start copying rows rows[0..ncols) of a prepared global image into LDS: the
-// waves of the block share the 1 KB pieces (hi rows, lo rows, the sub-block
-// sums).  Completion: vmcnt of the issuing wave, then a block barrier.
-__device__ inline void xl_dma_image(const XImg& img, const int* rows, int ncols, bool use_lo,
-                                    const XLw& L) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int K = L.K;
-  const int prow = (2 * K + 1023) / 1024;       // pieces per hi / lo row
-  const int psx = (K / 4 + 1023) / 1024;        // pieces per sum row (K/8 fp16)
-  const int per_c = prow * (use_lo ? 2 : 1) + psx;
-  for (int q = wv; q < ncols * per_c; q += nw) {
-    const int c = q / per_c, j = q - c * per_c;
-    const size_t r = (size_t)rows[c];
-    if (j < prow) {
-      dma_piece((const uint8_t*)(img.hi + r * K) + 1024 * j, (uint8_t*)(L.hi + (size_t)c * L.rs) + 1024 * j,
-                2 * K - 1024 * j, lane);
-    } else if (use_lo && j < 2 * prow) {
-      const int jj = j - prow;
-      dma_piece((const uint8_t*)(img.lo + r * K) + 1024 * jj, (uint8_t*)(L.lo + (size_t)c * L.rs) + 1024 * jj,
-                2 * K - 1024 * jj, lane);
-    } else {
-      const int jj = j - prow * (use_lo ? 2 : 1);
-      dma_piece((const uint8_t*)(img.sx + r * (K / 8)) + 1024 * jj,
-                (uint8_t*)(L.sx + (size_t)c * L.sxs) + 1024 * jj, K / 4 - 1024 * jj, lane);
-    }
+__device__ __forceinline__ XLPiece xl_piece(const XImg& img, const XLw& L, int r, int c, int j,
+                                            bool use_lo) {
+  const int K = L.K, prow = (2 * K + 1023) / 1024;
+  XLPiece p;
+  if (j < prow) {
+    p.src = (const uint8_t*)(img.hi + (size_t)r * K) + 1024 * j;
+    p.dst = (uint8_t*)(L.hi + (size_t)c * L.rs) + 1024 * j;
+    p.bytes = 2 * K - 1024 * j;
+  } else if (use_lo && j < 2 * prow) {
+    const int jj = j - prow;
+    p.src = (const uint8_t*)(img.lo + (size_t)r * K) + 1024 * jj;
+    p.dst = (uint8_t*)(L.lo + (size_t)c * L.rs) + 1024 * jj;
+    p.bytes = 2 * K - 1024 * jj;
+  } else {
+    const int jj = j - prow * (use_lo ? 2 : 1);
+    p.src = (const uint8_t*)(img.sx + (size_t)r * (K / 8)) + 1024 * jj;
+    p.dst = (uint8_t*)(L.sx + (size_t)c * L.sxs) + 1024 * jj;
+    p.bytes = K / 4 - 1024 * jj;
   }
+  return p;
 }
 
-// Largest column group (rows per block) whose LDS copy fits the budget.
-static int col_group(int K, bool use_lo, int R) {
-  int cg = XL_MAX_COLS;
-  while (cg > 1 && xl_bytes(cg, K, use_lo) > (size_t)LDS_BUDGET) --cg;
-  return cg < R ? cg : R;
+// Row c of the block is image row rows[c] (rows in global memory, read with
+// wave-uniform scalar loads), or row0 + c when rows is null.
+__device__ __forceinline__ int xl_row(const int* rows, int row0, int c) {
+  return rows ? rows[c] : row0 + c;
+}
+
+// Lane i copies bytes [16 i, 16 i + 16) of a 1 KB piece from global memory to
+// LDS (lanes past `bytes` skip); dst is wave-uniform.
+__device__ __forceinline__ void dma_piece(const uint8_t* src, uint8_t* dst, int bytes) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)dst;
+  if (16 * lane < bytes)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src + 16 * lane), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory", "m0");
+}
+
+// Start copying the block's rows (columns 0..ncols-1) into LDS: pieces
+// w, w + nw, ... go to wave w.  Completion: wait_vmcnt_le(#later loads), then
+// a block barrier.
+__device__ __forceinline__ void xl_img_dma(const XImg& img, const int* rows, int row0, int ncols,
+                                           bool use_lo, const XLw& L) {
+  const int wv = wave_id(), nw = blockDim.x >> 6;
+  const int per_c = xl_pieces_per_row(L.K, use_lo), total = ncols * per_c;
+  for (int q = wv; q < total; q += nw) {
+    const int c = q / per_c;
+    const XLPiece p = xl_piece(img, L, xl_row(rows, row0, c), c, q - c * per_c, use_lo);
+    dma_piece(p.src, p.dst, p.bytes);
+  }
 }
 
 // ------------------------------------------------------------- gate / up
@@ -378,18 +482,15 @@ constexpr int GU_THREADS = 512;   // 8 waves: (gate, up) x 4 K-quarters of one 1
 
 template <bool USE_LO, bool WIDE_D>
 __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int hidden, int inter,
-                                                             int CG, MoeWs ws) {
+                                                             MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int tile = blockIdx.x, u = blockIdx.y;
-  if (u >= ws.meta->n_units) return;
-  const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
-  const int c0 = blockIdx.z * CG;
-  if (c0 >= cnt) return;
-  const int ncols = min(CG, cnt - c0);
-  int rows[XL_MAX_COLS];   // activation rows of the block's columns (wave-uniform)
-#pragma unroll
-  for (int c = 0; c < XL_MAX_COLS; ++c) rows[c] = c < ncols ? ws.arow[off + c0 + c] : 0;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tile = blockIdx.x;
+  const int nwork = ws.meta->n_work_gu;
+  const MoeWork wk = ws.work_gu[blockIdx.y];   // in bounds for every launched block
+  if ((int)blockIdx.y >= nwork) return;
+  const int e = wk.expert, a0 = wk.a0, ncols = wk.ncols;
+  const int* rows = ws.work_gu[blockIdx.y].rows;   // activation rows of the block's columns
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int m = wv >> 2, q = wv & 3;
   const int nl = lane & 15, g = lane >> 4;
   const int n = tile * 16 + nl;
@@ -399,9 +500,9 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   const Q2View W = q2_view(base, inter, hidden);
   const XLw L = xl_make(lds, ncols, hidden, USE_LO);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto issue = [&]() { xl_dma_image(ws.x_img, rows, ncols, USE_LO, L); };
+  auto issue = [&]() { xl_img_dma(ws.x_img, rows, 0, ncols, USE_LO, L); };
   auto sync = [&](int nload) {
-    wait_vmcnt_le(nload);   // this wave's DMA pieces have landed (they precede the weight loads)
+    wait_vmcnt_le(nload);   // this wave's copies (older than its nload weight loads) have landed
     barrier_keep_loads();
   };
   q2_range_staged<WIDE_D, USE_LO>(W, n, nb * q / 4, nb * (q + 1) / 4, xl_view(L), min(nl, ncols - 1),
@@ -417,9 +518,9 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;
     if (c >= ncols) continue;
-    const float rs = ws.x_img.rscale[ws.arow[off + c0 + c]];
+    const float rs = ws.x_img.rscale[rows[c]];
     const float gv = gs[i] * rs, uv = us[i] * rs;
-    ws.h[(size_t)(off + c0 + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
+    ws.h[(size_t)(a0 + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
   }
 }
 
@@ -429,14 +530,14 @@ static size_t gu_lds(int hidden, bool use_lo, int CG) {
 }
 
 hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, hipStream_t s) {
-  const int CG = col_group(d->hidden, use_lo, R);
-  const dim3 grid(d->inter / 16, ws.max_units, (R + CG - 1) / CG);
+  const int CG = gateup_cols(d, R, use_lo);
+  const dim3 grid(d->inter / 16, ws.max_work, 1);
   const size_t lb = gu_lds(d->hidden, use_lo, CG);
   const bool wide = q2_wide_d(d->hidden / 256);
   const ExpertPtrs P = expert_ptrs(d);
 #define SV_GU(LO, WD)                                                                              \
   hipLaunchKernelGGL((k_q2_gateup<LO, WD>), grid, dim3(GU_THREADS), lb, s, P, d->hidden, d->inter, \
-                     CG, ws)
+                     ws)
   if (use_lo) {
     if (wide) SV_GU(true, true); else SV_GU(true, false);
   } else {
@@ -447,26 +548,21 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, 
 }
 
 // ------------------------------------------------------------------ down
-constexpr int DN_THREADS = 512;   // 8 waves, one 16-row tile each, all of inter
 
 // The block's h rows are read into registers before the weight loads are
 // issued (so their wait does not include the weights), then converted into
 // the LDS image: each row scaled by its own power of two, one half-wave per
 // (row, 256-block) pair, at most DN_PAIRS pairs per half-wave.
-constexpr int DN_PAIRS = 4;
-
 template <bool WIDE_D>
 __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter,
-                                                           int CG, MoeWs ws) {
+                                                           MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_max[2 * DN_PAIRS * (DN_THREADS / 32)];   // per pair: max bits, bad flag
-  const int u = blockIdx.y;
-  if (u >= ws.meta->n_units) return;
-  const int e = ws.unit_expert[u], off = ws.unit_off[u], cnt = ws.unit_cnt[u];
-  const int c0 = blockIdx.z * CG;
-  if (c0 >= cnt) return;
-  const int ncols = min(CG, cnt - c0);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nwork = ws.meta->n_work_dn;
+  const MoeWork wk = ws.work_dn[blockIdx.y];   // in bounds for every launched block
+  if ((int)blockIdx.y >= nwork) return;
+  const int e = wk.expert, a0 = wk.a0, ncols = wk.ncols;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int nl = lane & 15, g = lane >> 4;
   const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
@@ -482,7 +578,7 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hid
       const int p = hw + (DN_THREADS / 32) * i;
       if (p < npairs) {
         const int c = p / nbk, kb = p - c * nbk;
-        const float* src = ws.h + (size_t)(off + c0 + c) * inter + kb * 256 + 16 * sb + 4 * hs;
+        const float* src = ws.h + (size_t)(a0 + c) * inter + kb * 256 + 16 * sb + 4 * hs;
         pa[i] = *(const float4*)src;
         pb[i] = *(const float4*)(src + 8);
       }
@@ -559,23 +655,19 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hid
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = 4 * g + i;   // tile column; only 0..ncols-1 are real
-    if (c < ncols) ws.part[(size_t)(off + c0 + c) * hidden + n] = acc[i] * rsc_c[i];
+    if (c < ncols) ws.part[(size_t)(a0 + c) * hidden + n] = acc[i] * rsc_c[i];
   }
 }
 
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  int CG = col_group(d->inter, true, R);
-  const int pair_cap = DN_PAIRS * (DN_THREADS / 32) / (d->inter / 256);   // staged (row, block) pairs
-  if (CG > pair_cap) CG = pair_cap > 0 ? pair_cap : 1;
-  const dim3 grid(d->hidden / 128, ws.max_units, (R + CG - 1) / CG);
+  const int CG = down_cols(d, R);
+  const dim3 grid(d->hidden / 128, ws.max_work, 1);
   const size_t lb = xl_bytes(CG, d->inter, true);
   const ExpertPtrs P = expert_ptrs(d);
   if (q2_wide_d(d->inter / 256))
-    hipLaunchKernelGGL(k_q2_down<true>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, CG,
-                       ws);
+    hipLaunchKernelGGL(k_q2_down<true>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws);
   else
-    hipLaunchKernelGGL(k_q2_down<false>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, CG,
-                       ws);
+    hipLaunchKernelGGL(k_q2_down<false>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_moe_combine(d, R, ws, y, s);
@@ -631,19 +723,16 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_plain(const uint8_t* w, in
   extern __shared__ __align__(16) uint8_t lds[];
   const int c0 = blockIdx.z * CG;
   const int ncols = min(CG, R - c0);
-  int rows[XL_MAX_COLS];
-#pragma unroll
-  for (int c = 0; c < XL_MAX_COLS; ++c) rows[c] = c0 + (c < ncols ? c : 0);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   const int nl = lane & 15, g = lane >> 4;
   const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const int nld = n < n_out ? n : n_out - 1;   // ragged tail: load a valid row, drop the result
   const Q2View W = q2_view(w, n_out, k_in);
   const XLw L = xl_make(lds, ncols, k_in, USE_LO);
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto issue = [&]() { xl_dma_image(img, rows, ncols, USE_LO, L); };
+  auto issue = [&]() { xl_img_dma(img, nullptr, c0, ncols, USE_LO, L); };
   auto sync = [&](int nload) {
-    wait_vmcnt_le(nload);   // this wave's DMA pieces have landed (they precede the weight loads)
+    wait_vmcnt_le(nload);
     barrier_keep_loads();
   };
   q2_range_staged<WIDE_D, USE_LO>(W, nld, 0, k_in / 256, xl_view(L), min(nl, ncols - 1), lane, acc,

@@ -16,6 +16,11 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 
 __host__ __device__ inline size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// Index of the calling wave in its block, as a wave-uniform (scalar) value:
+// the compiler cannot tell that threadIdx.x / 64 is uniform, and everything
+// derived from it would otherwise be computed per lane.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // ---------------------------------------------------------------- formats
 // Two-bit matrix [n_out x k_in]: planes codes / nibbles / d / dmin, each at a
 // 256-byte aligned offset (layout documented in specverify.h).
@@ -123,6 +128,17 @@ inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
 struct MoeMeta {
   int n_units;    // touched routed experts + shared
   int n_assign;   // (row, slot) assignments incl. shared rows
+  int n_work_gu;  // work items of the gate/up kernel
+  int n_work_dn;  // work items of the down kernel
+};
+
+// One block's work in the expert kernels: an expert (-1 = shared), the first
+// of its assignments the block covers, how many (its columns), and the
+// activation row of each -- everything a block needs in one 48-byte load.
+constexpr int MOE_WORK_COLS = 8;
+struct MoeWork {
+  int expert, a0, ncols, pad;
+  int rows[MOE_WORK_COLS];
 };
 
 struct MoeWs {
@@ -136,8 +152,10 @@ struct MoeWs {
   float* topk_w;      // [R, top_k]
   float* h;           // [max_assign, inter]  SwiGLU output
   float* part;        // [max_assign, hidden] per-assignment down outputs
+  MoeWork* work_gu;    // [max_work]
+  MoeWork* work_dn;    // [max_work]
   XImg x_img;         // staged x  [R, hidden]
-  int max_units, max_assign;
+  int max_units, max_assign, max_work;
 };
 
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out);

@@ -344,7 +344,7 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
   const int len = q2_chunk_len<WIDE_D>(kb0, kb1 - kb0);
   const int g = lane >> 4;
   issue();
-  asm volatile("" ::: "memory");   // the weight loads stay after issue()'s loads
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the weight loads stay after issue()'s loads
 #define SV_STAGED_CASE(L)                                               \
   case L: {                                                             \
     Q2Chunk<L, WIDE_D> c;                                               \
@@ -369,14 +369,21 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
 }
 
 // Block barrier that does not wait for outstanding vector-memory loads (the
-// compiler's __syncthreads() waits for all of them); a compiler-only memory
-// fence keeps LDS accesses on their side of it.  Callers make their own LDS
-// writes complete first.
-__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_barrier" ::: "memory"); }
+// compiler's __syncthreads() waits for all of them once LDS DMA is pending);
+// compiler-only fences keep memory accesses on their side of it.  Callers make
+// their own LDS writes complete first.  (Not inline asm: after an asm
+// statement the compiler no longer knows which loads are outstanding and waits
+// for all of them at the next use.)
+__device__ __forceinline__ void barrier_keep_loads() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // s_waitcnt that waits until at most n vector-memory loads are outstanding
 // (n a compile-time constant after inlining), leaving the other counters alone.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
+  asm volatile("" ::: "memory");   // no later load may be hoisted above the wait
 #define SV_W(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | ((((N) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8)); break;
   switch (n) {
     SV_W(0) SV_W(1) SV_W(2) SV_W(3) SV_W(4) SV_W(5) SV_W(6) SV_W(7) SV_W(8) SV_W(9)
