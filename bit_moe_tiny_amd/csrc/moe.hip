@@ -85,9 +85,10 @@ static int col_group(int K, bool use_lo, int R) {
 constexpr int DN_THREADS = 512;   // down: 8 waves, one 16-row tile each, all of inter
 constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave
 
-static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo) {
-  return col_group(d->hidden, use_lo, R);
-}
+struct GpCfg;
+static GpCfg gp_config(int hidden, bool use_lo, int R);
+
+static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo);
 
 static int down_cols(const sv_moe_desc* d, int R) {
   int cg = col_group(d->inter, true, R);
@@ -401,9 +402,16 @@ __device__ inline XL xl_view(const XLw& w) {
 // Source, destination and length of piece j of column c (image row r).
 struct XLPiece {
   const uint8_t* src;
-  uint8_t* dst;
+  uint32_t la;      // LDS byte address of the destination
   int bytes;
 };
+
+// LDS byte address of a generic pointer into the LDS aperture.  Each branch of
+// xl_piece converts its own pointer, so that no select of generic LDS
+// pointers reaches the conversion (the backend fails on that form).
+__device__ __forceinline__ uint32_t lds_la(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
 
 __device__ __forceinline__ XLPiece xl_piece(const XImg& img, const XLw& L, int r, int c, int j,
                                             bool use_lo) {
@@ -411,50 +419,46 @@ __device__ __forceinline__ XLPiece xl_piece(const XImg& img, const XLw& L, int r
   XLPiece p;
   if (j < prow) {
     p.src = (const uint8_t*)(img.hi + (size_t)r * K) + 1024 * j;
-    p.dst = (uint8_t*)(L.hi + (size_t)c * L.rs) + 1024 * j;
+    p.la = lds_la(L.hi + (size_t)c * L.rs) + 1024 * j;
     p.bytes = 2 * K - 1024 * j;
   } else if (use_lo && j < 2 * prow) {
     const int jj = j - prow;
     p.src = (const uint8_t*)(img.lo + (size_t)r * K) + 1024 * jj;
-    p.dst = (uint8_t*)(L.lo + (size_t)c * L.rs) + 1024 * jj;
+    p.la = lds_la(L.lo + (size_t)c * L.rs) + 1024 * jj;
     p.bytes = 2 * K - 1024 * jj;
   } else {
     const int jj = j - prow * (use_lo ? 2 : 1);
     p.src = (const uint8_t*)(img.sx + (size_t)r * (K / 8)) + 1024 * jj;
-    p.dst = (uint8_t*)(L.sx + (size_t)c * L.sxs) + 1024 * jj;
+    p.la = lds_la(L.sx + (size_t)c * L.sxs) + 1024 * jj;
     p.bytes = K / 4 - 1024 * jj;
   }
+  p.la = __builtin_amdgcn_readfirstlane(p.la);
   return p;
 }
 
 // Row c of the block is image row rows[c] (rows in global memory, read with
 // wave-uniform scalar loads), or row0 + c when rows is null.
 __device__ __forceinline__ int xl_row(const int* rows, int row0, int c) {
-  return rows ? rows[c] : row0 + c;
+  return rows ? const_ptr(rows)[c] : row0 + c;
 }
 
 // Lane i copies bytes [16 i, 16 i + 16) of a 1 KB piece from global memory to
-// LDS (lanes past `bytes` skip); dst is wave-uniform.
-__device__ __forceinline__ void dma_piece(const uint8_t* src, uint8_t* dst, int bytes) {
+// LDS (lanes past `bytes` skip); la is the wave-uniform LDS byte address.
+__device__ __forceinline__ void dma_piece(const uint8_t* src, uint32_t la, int bytes) {
   const int lane = threadIdx.x & 63;
-  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)dst;
   if (16 * lane < bytes)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src + 16 * lane), "s"(__builtin_amdgcn_readfirstlane(la))
-                 : "memory", "m0");
+                 :: "v"(src + 16 * lane), "s"(la) : "memory", "m0");
 }
 
-// Start copying the block's rows (columns 0..ncols-1) into LDS: pieces
-// w, w + nw, ... go to wave w.  Completion: wait_vmcnt_le(#later loads), then
-// a block barrier.
 __device__ __forceinline__ void xl_img_dma(const XImg& img, const int* rows, int row0, int ncols,
                                            bool use_lo, const XLw& L) {
   const int wv = wave_id(), nw = blockDim.x >> 6;
   const int per_c = xl_pieces_per_row(L.K, use_lo), total = ncols * per_c;
   for (int q = wv; q < total; q += nw) {
-    const int c = q / per_c;
+    const int c = __builtin_amdgcn_readfirstlane(q / per_c);   // wave-uniform: scalar row reads
     const XLPiece p = xl_piece(img, L, xl_row(rows, row0, c), c, q - c * per_c, use_lo);
-    dma_piece(p.src, p.dst, p.bytes);
+    dma_piece(p.src, p.la, p.bytes);
   }
 }
 
@@ -524,17 +528,296 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   }
 }
 
+// ------------------------------------------------ gate / up, persistent
+// Blocks of 8 waves: wave (m, q) = (matrix gate/up, K part q of 4), each part
+// NQ = nb / 4 consecutive 256-element blocks.  Block b owns the contiguous
+// item range [b I / G, (b + 1) I / G) of the I = n_work * (inter/16) items
+// (work descriptor, 16-row tile), which are ordered by descriptor, and every
+// wave works on its (m, q) share of each item in turn.  A wave issues the
+// next item's loads while it computes the current item -- the loads of the
+// first half of its part once that half is computed, the rest after the
+// second half -- so its loads stay in flight across items and across the
+// per-item barrier.  The activation rows are copied into LDS only when the
+// descriptor changes.  Partial sums meet in a double-buffered LDS area;
+// wave (item mod 8) adds them up and applies SwiGLU.  Two blocks share a CU
+// (four waves per SIMD, two of each block).
+constexpr int GP_WAVES = 8, GP_PARTS = 4;
+
+struct GpCfg {
+  bool ok;
+  int nq, cols;
+  size_t lds;
+};
+
+// d/dmin window of a part starting at block kb0: 2 DW values from the even
+// block w0 = kb0 & ~1 (even lane-rows d, odd lane-rows dmin, one dword per 2
+// blocks); the part's values start at half (kb0 & 1) of it.
+__host__ __device__ constexpr int gp_dw(int nq) { return (nq + (nq & 1) + 1) / 2; }
+
+static GpCfg gp_config(int hidden, bool use_lo, int R) {
+  GpCfg c{};
+  const int nb = hidden / 256;
+  if (hidden % 256 != 0 || nb % GP_PARTS != 0) return c;
+  c.nq = nb / GP_PARTS;
+  if (c.nq < 1 || c.nq > 8) return c;
+  const int dw = gp_dw(c.nq);
+  if (dw > 4) return c;
+  for (int q = 0; q < GP_PARTS; ++q)   // every window inside the row
+    if ((c.nq * q & ~1) + 2 * dw > nb) return c;
+  const size_t budget = (size_t)80 * 1024 - 512;   // two blocks per CU
+  const size_t red = (size_t)2 * GP_WAVES * 64 * 16 + 2 * XL_MAX_COLS * 4;
+  int cg = XL_MAX_COLS;
+  while (cg > 1 && xl_bytes(cg, hidden, use_lo) + red > budget) --cg;
+  if (xl_bytes(cg, hidden, use_lo) + red > budget) return c;
+  c.cols = cg < R ? cg : R;
+  c.lds = xl_bytes(c.cols, hidden, use_lo) + red;
+  c.ok = true;
+  return c;
+}
+
+// The loads of one half of a part: N code blocks, plus (first half) the
+// block scales and the scale nibbles of the first 4 blocks, or (second half
+// of a part of more than 4 blocks) the nibbles of blocks 4..7.  Nibble loads:
+// lane-row g gets block base + g (clamped to the row).
+template <int NQ, bool FIRST>
+struct GpHalf {
+  static constexpr int N0 = NQ > 4 ? 4 : (NQ + 1) / 2;
+  static constexpr int N = FIRST ? N0 : NQ - N0;
+  static constexpr bool SC = FIRST || NQ > 4;
+  static constexpr int DW = FIRST ? gp_dw(NQ) : 0;
+  static constexpr int LOADS = N + (SC ? 1 : 0) + (DW > 0 ? 1 : 0);
+  uint4 qs[N > 0 ? N : 1];
+  uint4 sc;
+  uint32_t dd[DW > 0 ? DW : 1];
+};
+
+template <int NQ, bool FIRST>
+__device__ __forceinline__ void gp_load(const Q2View& W, size_t rb, int kb0, int g,
+                                        GpHalf<NQ, FIRST>& h) {
+  using H = GpHalf<NQ, FIRST>;
+  const int b0 = kb0 + (FIRST ? 0 : H::N0);
+  if (H::SC) h.sc = *(const uint4*)(W.sc + (rb + min(b0 + g, W.nb - 1)) * 16);
+  if (H::DW > 0) {
+    const uint16_t* dp = ((g & 1) ? W.dm : W.d) + rb + (kb0 & ~1);
+    if (H::DW == 1) {
+      h.dd[0] = *(const uint32_t*)dp;
+    } else if (H::DW == 2) {
+      const uint2 v = *(const uint2*)dp;
+      h.dd[0] = v.x;
+      h.dd[1] = v.y;
+    } else if (H::DW == 3) {
+      const uint3 v = *(const uint3*)dp;
+      h.dd[0] = v.x;
+      h.dd[1] = v.y;
+      h.dd[2] = v.z;
+    } else {
+      const uint4 v = *(const uint4*)dp;
+      h.dd[0] = v.x;
+      h.dd[1] = v.y;
+      h.dd[2] = v.z;
+      h.dd[3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < H::N; ++i) h.qs[i] = *(const uint4*)(W.qs + (rb + b0 + i) * 64 + 16 * g);
+}
+
+template <bool USE_LO, int NQ>
+__global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, int hidden, int inter,
+                                                                  int CG, MoeWs ws) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  using H0 = GpHalf<NQ, true>;
+  using H1 = GpHalf<NQ, false>;
+  constexpr int N0 = H0::N0, DW = H0::DW;
+  const int T = inter / 16;
+  const long total = (long)ws.meta->n_work_gu * T;
+  // (the 64-bit divisions run on the vector unit: make the results uniform so
+  // that descriptor reads are scalar loads)
+  const int i0 = __builtin_amdgcn_readfirstlane((int)(total * blockIdx.x / gridDim.x));
+  const int i1 = __builtin_amdgcn_readfirstlane((int)(total * (blockIdx.x + 1) / gridDim.x));
+  if (i0 >= i1) return;
+  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int m = wv >= GP_PARTS, q = wv & (GP_PARTS - 1);
+  const int nl = lane & 15, g = lane >> 4;
+  const int nb = hidden / 256, kb0 = NQ * q;
+  const uint32_t dshift = 16 * (kb0 & 1);   // the part's first value: half (kb0 & 1) of the window
+  const auto work = const_ptr(ws.work_gu);   // descriptor reads as scalar loads
+  f4_t* red = (f4_t*)(lds + xl_bytes(CG, hidden, USE_LO));
+  // row scales of a descriptor's columns, in LDS slot (descriptor index & 1):
+  // the epilogue of the old descriptor's last item may still read its slot
+  // while the next descriptor's scales are written
+  float* rsc_slots = (float*)(lds + xl_bytes(CG, hidden, USE_LO) + (size_t)2 * GP_WAVES * 64 * 16);
+  auto wview = [&](int e) {
+    const uint8_t* base = m == 0 ? (e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg)
+                                 : (e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su);
+    return q2_view(base, inter, hidden);
+  };
+
+  // load cursor: the item whose weights are issued next (stays on the last
+  // item of the range once there: those loads re-read cached lines and keep
+  // the compiler's load counting identical on every path)
+  int lw = __builtin_amdgcn_readfirstlane(i0 / T), lt = i0 - lw * T, li = i0;
+  Q2View LW = wview(work[lw].expert);
+  auto issue0 = [&](H0& h) { gp_load<NQ, true>(LW, (size_t)(lt * 16 + nl) * nb, kb0, g, h); };
+  auto issue1 = [&](H1& h) {
+    gp_load<NQ, false>(LW, (size_t)(lt * 16 + nl) * nb, kb0, g, h);
+    if (li + 1 < i1) {
+      ++li;
+      if (++lt == T) {
+        lt = 0;
+        ++lw;
+        LW = wview(work[lw].expert);
+      }
+    }
+  };
+
+  // compute cursor
+  int w = lw, t = lt;
+  int a0_cur = work[w].a0, nc_cur = work[w].ncols;
+  auto row_scales = [&]() {
+    if (wv == 0 && lane < XL_MAX_COLS)
+      rsc_slots[(w & 1) * XL_MAX_COLS + lane] = lane < nc_cur ? ws.x_img.rscale[work[w].rows[lane]] : 0.f;
+  };
+  row_scales();
+  // the first descriptor's activation copies, then the first item's weights
+  xl_img_dma(ws.x_img, (const int*)work[w].rows, 0, nc_cur, USE_LO, xl_make(lds, nc_cur, hidden, USE_LO));
+  H0 h0;
+  H1 h1;
+  issue0(h0);
+  issue1(h1);
+  wait_vmcnt_le(H0::LOADS + H1::LOADS);   // this wave's activation copies are done
+  barrier_lds();
+
+  for (int i = i0; i < i1; ++i) {
+    const XLw L = xl_make(lds, nc_cur, hidden, USE_LO);   // rebuilt, not carried
+    const int cr = min(nl, nc_cur - 1);
+    const _Float16* xh = L.hi + (size_t)cr * L.rs + kb0 * 256 + g * 8;
+    const _Float16* xl = L.lo + (size_t)cr * L.rs + kb0 * 256 + g * 8;
+    const _Float16* xs = L.sx + (size_t)cr * L.sxs + kb0 * 32 + g * 8;
+    f4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // block scales: both halves of the window to every lane, aligned so that
+    // value b belongs to block kb0 + b
+    uint32_t dv[DW], mv[DW];
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(h0.dd[j], h0.dd[j], false, false);
+      dv[j] = sw[0];
+      mv[j] = sw[1];
+    }
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      dv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? dv[j + 1] : 0u, dv[j], dshift);
+      mv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? mv[j + 1] : 0u, mv[j], dshift);
+    }
+    {
+      uint32_t sct[4];
+      xpose4(h0.sc, sct);
+#pragma unroll
+      for (int b = 0; b < N0; ++b) {
+        q2_block<USE_LO>(h0.qs[b], sct[b], win_val(dv, b), win_val(mv, b), xh + 256 * b, xl + 256 * b,
+                         xs + 32 * b, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (NQ <= 4) {
+#pragma unroll
+        for (int b = N0; b < NQ; ++b) {
+          // (second-half blocks of a part of at most 4 use the first nibble load)
+          q2_block<USE_LO>(h1.qs[b - N0], sct[b], win_val(dv, b), win_val(mv, b), xh + 256 * b,
+                           xl + 256 * b, xs + 32 * b, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    issue0(h0);
+    if (NQ > 4) {
+      uint32_t sct[4];
+      xpose4(h1.sc, sct);
+#pragma unroll
+      for (int b = N0; b < NQ; ++b) {
+        q2_block<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), xh + 256 * b,
+                         xl + 256 * b, xs + 32 * b, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    issue1(h1);
+
+    // partial sums of item i meet in buffer i & 1
+    f4_t* rbuf = red + (size_t)(i & 1) * GP_WAVES * 64;
+    rbuf[wv * 64 + lane] = acc;
+    barrier_lds();
+    if (wv == (i & (GP_WAVES - 1))) {
+      // (addressed from the lane id, which the compiler recomputes instead of
+      // keeping a register live across the item)
+      const f4_t* rl = red + (size_t)(i & 1) * GP_WAVES * 64 + __lane_id();
+      const f4_t gs = ((rl[0] + rl[64]) + rl[128]) + rl[192];
+      const f4_t us = ((rl[256] + rl[320]) + rl[384]) + rl[448];
+      const int n = t * 16 + nl;
+      // (lane groups g >= 2 hold columns 8..15, never present: kept in bounds)
+      const float* rsv = rsc_slots + (w & 1) * XL_MAX_COLS + min(4 * g, XL_MAX_COLS - 4);
+      const int ne = min(4, nc_cur - 4 * g);
+      for (int e = 0; e < ne; ++e) {
+        const float gv = gs[e] * rsv[e], uv = us[e] * rsv[e];
+        ws.h[(size_t)(a0_cur + 4 * g + e) * inter + n] = gv / (1.f + __expf(-gv)) * uv;
+      }
+    }
+    // next compute item; a new descriptor's rows replace the old ones once
+    // every wave is past item i
+    if (++t == T && i + 1 < i1) {
+      t = 0;
+      ++w;
+      a0_cur = work[w].a0;
+      nc_cur = work[w].ncols;
+      xl_img_dma(ws.x_img, (const int*)work[w].rows, 0, nc_cur, USE_LO, xl_make(lds, nc_cur, hidden, USE_LO));
+      row_scales();
+      wait_vmcnt_le(0);
+      barrier_lds();
+    }
+  }
+}
+
+static int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 static size_t gu_lds(int hidden, bool use_lo, int CG) {
   const size_t x = xl_bytes(CG, hidden, use_lo), red = (size_t)GU_THREADS * 16;
   return x > red ? x : red;
 }
 
+static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo) {
+  const GpCfg c = gp_config(d->hidden, use_lo, R);
+  return c.ok ? c.cols : col_group(d->hidden, use_lo, R);
+}
+
 hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, hipStream_t s) {
+  const ExpertPtrs P = expert_ptrs(d);
+  const GpCfg c = gp_config(d->hidden, use_lo, R);
+  if (c.ok) {
+    const dim3 grid(2 * num_cus()), block(64 * GP_WAVES);
+#define SV_GP(Q)                                                                                   \
+  case Q:                                                                                          \
+    if (use_lo)                                                                                    \
+      hipLaunchKernelGGL((k_q2_gateup_p<true, Q>), grid, block, c.lds, s, P, d->hidden, d->inter,  \
+                         c.cols, ws);                                                              \
+    else                                                                                           \
+      hipLaunchKernelGGL((k_q2_gateup_p<false, Q>), grid, block, c.lds, s, P, d->hidden, d->inter, \
+                         c.cols, ws);                                                              \
+    break;
+    switch (c.nq) { SV_GP(1) SV_GP(2) SV_GP(3) SV_GP(4) SV_GP(5) SV_GP(6) SV_GP(7) SV_GP(8) default: break; }
+#undef SV_GP
+    return hipGetLastError();
+  }
   const int CG = gateup_cols(d, R, use_lo);
   const dim3 grid(d->inter / 16, ws.max_work, 1);
   const size_t lb = gu_lds(d->hidden, use_lo, CG);
   const bool wide = q2_wide_d(d->hidden / 256);
-  const ExpertPtrs P = expert_ptrs(d);
 #define SV_GU(LO, WD)                                                                              \
   hipLaunchKernelGGL((k_q2_gateup<LO, WD>), grid, dim3(GU_THREADS), lb, s, P, d->hidden, d->inter, \
                      ws)

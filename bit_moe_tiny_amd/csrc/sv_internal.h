@@ -21,6 +21,15 @@ __host__ __device__ inline size_t up256(size_t n) { return (n + 255) & ~size_t(2
 // derived from it would otherwise be computed per lane.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// A global pointer to data that no kernel of this launch writes, in the
+// constant address space: uniform reads through it become scalar loads even
+// in kernels that store to global memory (the compiler cannot otherwise rule
+// out that the stores change the data).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* const_ptr(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
+
 // ---------------------------------------------------------------- formats
 // Two-bit matrix [n_out x k_in]: planes codes / nibbles / d / dmin, each at a
 // 256-byte aligned offset (layout documented in specverify.h).

@@ -39,13 +39,18 @@ __device__ __forceinline__ float f16bits_to_f32(uint16_t b) { return (float)__bu
 
 __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
 
-// (x & m) | o in one instruction.  gfx9 VOP3 encodings take no 32-bit
-// literals, so the compiler splits this into v_and_b32 + v_or_b32 with
-// literals; here the mask comes in an SGPR and the OR constant in a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(o));
-  return r;
+// (x & m) | o in one instruction (v_and_or_b32).  gfx9 VOP3 encodings take
+// no 32-bit literals, so with constant m and o the compiler would split this
+// into v_and_b32 + v_or_b32; given m in an SGPR and o in a VGPR it selects the
+// single instruction by itself (and, unlike inline asm, still knows which
+// registers it writes, so it adds no defensive wait states).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
+
+// Constant c held in a scalar register (opaque to constant folding; not
+// volatile, so that the copies are shared and hoisted out of loops).
+__device__ __forceinline__ uint32_t sreg(uint32_t c) {
+  asm("" : "+s"(c));
+  return c;
 }
 
 // fp16 (1024 + byte) pairs from bytes (0,1) / (2,3) of u: v_perm_b32 picks
@@ -91,7 +96,7 @@ __device__ __forceinline__ h8_t q2_bop(const uint4& qs, const Q2Sc& S, int t, ui
   h8_t b;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const h2_t p = as_h2(and_or(dw, 0x00030003u << (2 * j), magic));
+    const h2_t p = as_h2(and_or(dw, sreg(0x00030003u << (2 * j)), magic));
     const h2_t a = __builtin_elementwise_fma(p, scp, neg);
     b[2 * j] = a.x;
     b[2 * j + 1] = a.y;
@@ -376,6 +381,15 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
 // for all of them at the next use.)
 __device__ __forceinline__ void barrier_keep_loads() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Block barrier after this wave's LDS writes are done, leaving its vector
+// memory loads in flight (the LDS-scope part of __syncthreads only).
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
