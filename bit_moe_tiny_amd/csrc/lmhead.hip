@@ -165,6 +165,159 @@ __global__ __launch_bounds__(256) void k_q8_lmhead(Q8View W, int R, XImg img, fl
   }
 }
 
+// ---------------------------------------------------------------------------
+// Activation operands from LDS (block counts a multiple of 16).  Blocks of 8
+// waves, 2 tiles per wave.  The block's columns are copied into LDS -- all of
+// K at once when they fit (then there is no synchronisation in the K loop),
+// else one window of `wg` groups at a time, double buffered, with one
+// barrier per window (a window's copies are issued before the previous
+// window is computed).  Every wave reads its activation operands from LDS
+// instead of through the vector-memory path, which the weight stream then has
+// to itself.
+constexpr int LM_WAVES = 8, LM_T = 2;        // waves per block, tiles per wave
+constexpr int LM_WIN_GROUPS = 4;             // window length (groups of 256 k) when K does not fit
+constexpr size_t LM_LDS_CAP = 78 * 1024;     // two blocks per CU
+
+struct LmCfg {
+  int wg, nbuf, ncols, rs;   // window groups, buffers, columns per block, row stride (fp16)
+  size_t lds;
+};
+
+static LmCfg lm_config(int K, int R, bool use_lo) {
+  LmCfg c;
+  c.ncols = R < 16 ? R : 16;
+  const int ngroups = K / 256;
+  const size_t pl = use_lo ? 2 : 1;
+  c.wg = ngroups;
+  c.nbuf = 1;
+  c.rs = K + 8;
+  if ((size_t)c.ncols * c.rs * 2 * pl > LM_LDS_CAP) {
+    c.wg = LM_WIN_GROUPS;
+    c.nbuf = 2;
+    c.rs = LM_WIN_GROUPS * 256 + 8;
+  }
+  c.lds = (size_t)c.nbuf * c.ncols * c.rs * 2 * pl;
+  return c;
+}
+
+// Copy window `wi` (wg groups) of columns c0 .. c0+nc-1 (hi, and lo when
+// USE_LO) into buffer `buf`: 1 KB pieces, pieces w, w+8, ... to wave w.
+template <bool USE_LO>
+__device__ __forceinline__ void lm_window_dma(const XImg& img, int K, int c0, int nc, int wi, int buf,
+                                              int wg, int nbuf, int ncols, int rs, uint32_t lds_base) {
+  const int wv = wave_id(), lane = threadIdx.x & 63;
+  const int ppc = wg * 256 * 2 / 1024;   // pieces per column and plane
+  const int total = nc * ppc * (USE_LO ? 2 : 1);
+  for (int q = wv; q < total; q += LM_WAVES) {
+    const int pl = q / (nc * ppc), r = q - pl * nc * ppc, c = r / ppc, pc = r - c * ppc;
+    const _Float16* src = (pl ? img.lo : img.hi) + (size_t)(c0 + c) * K + (size_t)wi * wg * 256 + pc * 512;
+    const uint32_t la = lds_base + (uint32_t)((((pl * nbuf + buf) * ncols + c) * rs) * 2 + pc * 1024);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"((const uint8_t*)src + 16 * lane), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory", "m0");
+  }
+}
+
+template <bool USE_LO>
+__global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, int R, XImg img, float* logits,
+                                                                    LmCfg cfg) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int vocab = W.n_out, nb = W.nb, K = nb * 32;
+  const int cg = blockIdx.z, c0 = cg * 16, nc = min(16, R - c0);
+  const int wg = cfg.wg, nbuf = cfg.nbuf, ncols = cfg.ncols, rs = cfg.rs;
+  const int tile0 = (blockIdx.x * LM_WAVES + wv) * LM_T;
+  const int nl = lane & 15, g = lane >> 4;
+  const int kofs = 8 * (((g & 1) << 1) | (g >> 1));   // k offset of this lane's 8 values in a block
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  const _Float16* xw = (const _Float16*)lds;
+  const int cr = min(nl, nc - 1);   // padding columns read the last real column; never stored
+  size_t rowb[LM_T];
+#pragma unroll
+  for (int t = 0; t < LM_T; ++t) {
+    const int n = (tile0 + t) * 16 + nl;
+    // rows past the vocabulary (whole tiles past it included) read a valid row; dropped
+    rowb[t] = (size_t)(n < vocab ? n : vocab - 1) * nb;
+  }
+  const int nwin = nb / (8 * wg);
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f4_t acc[LM_T];
+#pragma unroll
+  for (int t = 0; t < LM_T; ++t) acc[t] = zero;
+
+  lm_window_dma<USE_LO>(img, K, c0, nc, 0, 0, wg, nbuf, ncols, rs, lds_base);
+  Q8Grp<LM_T, true> ga, gb;
+  q8_grp_load<LM_T, true>(W, rowb, 0, 8, g, ga);
+  wait_vmcnt_le(5 * LM_T);   // window 0 copied (the group loads came after it)
+  barrier_lds();
+  for (int wi = 0; wi < nwin; ++wi) {
+    const int buf = wi & 1;
+    if (wi + 1 < nwin) lm_window_dma<USE_LO>(img, K, c0, nc, wi + 1, buf ^ 1, wg, nbuf, ncols, rs, lds_base);
+    const _Float16* xh = xw + (size_t)(buf * ncols + cr) * rs + kofs;
+    const _Float16* xl = xw + (size_t)((nbuf + buf) * ncols + cr) * rs + kofs;
+    // one group: the next group's loads go out first, into the other buffer
+    // (the two buffers alternate by name, so no copy waits on loads in flight)
+    auto group = [&](int j, Q8Grp<LM_T, true>& cu, Q8Grp<LM_T, true>& nx) {
+      const int kg = (wi * wg + j) * 8;
+      // the last group's "next" loads re-read it (cache hits) so that every
+      // path issues the same loads
+      q8_grp_load<LM_T, true>(W, rowb, kg + 8 < nb ? kg + 8 : kg, 8, g, nx);
+      __builtin_amdgcn_sched_barrier(0);   // keep them ahead of this group's math
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // activation operands of blocks 2p, 2p+1 (read when needed: keeping a
+        // group's worth live would not fit beside the double-buffered weights)
+        h8_t xa[2], xb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          xa[h] = *(const h8_t*)(xh + (j * 8 + 2 * p + h) * 32);
+          if (USE_LO) xb[h] = *(const h8_t*)(xl + (j * 8 + 2 * p + h) * 32);
+        }
+#pragma unroll
+        for (int t = 0; t < LM_T; ++t) {
+          uint2 qa, qb;
+          q8_regroup(cu.q[t][p], qa, qb);
+          const uint32_t w32 = p == 0 ? cu.dv[t].x : p == 1 ? cu.dv[t].y : p == 2 ? cu.dv[t].z : cu.dv[t].w;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const h8_t bw = q8_bop(h == 0 ? qa : qb);
+            f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[h], bw, zero, 0, 0, 0);
+            if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xb[h], bw, dt, 0, 0, 0);
+            const float d = f16b_to_f32((uint16_t)(w32 >> (16 * h)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][e] = fmaf(d, dt[e], acc[t][e]);
+          }
+        }
+      }
+    };
+    // (wg is even; the buffers are back to (ga, gb) after every pair)
+#pragma unroll 1
+    for (int j = 0; j < wg; j += 2) {
+      group(j, ga, gb);
+      group(j + 1, gb, ga);
+    }
+    if (wi + 1 < nwin) {
+      // this wave's copies of the next window were issued before the last
+      // group's weight loads (5 per tile): wait for them, then for everyone
+      wait_vmcnt_le(5 * LM_T);
+      barrier_lds();
+    }
+  }
+  f4_t xs;   // row scales of the lane's 4 output columns
+#pragma unroll
+  for (int e = 0; e < 4; ++e) xs[e] = img.rscale[min(c0 + 4 * g + e, R - 1)];
+#pragma unroll
+  for (int t = 0; t < LM_T; ++t) {
+    const int n = (tile0 + t) * 16 + nl;
+    if (n >= vocab) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int cc = c0 + 4 * g + e;
+      if (cc < R) logits[(size_t)cc * vocab + n] = acc[t][e] * xs[e];
+    }
+  }
+}
+
 // two tiles per wave: with double-buffered weight groups this keeps two waves
 // per SIMD resident; 129280 rows then run in two full rounds of waves
 template <bool USE_LO, int T>
@@ -181,6 +334,17 @@ static void launch_lm(int R, hipStream_t s, const Q8View& W, const XImg& img, fl
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo, XImg img,
                             float* logits, hipStream_t s) {
   const Q8View W = q8_view(w, vocab, hidden);
+  // (groups in pairs; windows of LM_WIN_GROUPS groups when K does not fit)
+  if (W.nb % (8 * LM_WIN_GROUPS) == 0) {
+    const LmCfg cfg = lm_config(hidden, R, use_lo);
+    const int tiles = (vocab + 15) / 16;
+    const dim3 grid((tiles + LM_WAVES * LM_T - 1) / (LM_WAVES * LM_T), 1, (R + 15) / 16);
+    if (use_lo)
+      hipLaunchKernelGGL((k_q8_lmhead_lds<true>), grid, dim3(LM_WAVES * 64), cfg.lds, s, W, R, img, logits, cfg);
+    else
+      hipLaunchKernelGGL((k_q8_lmhead_lds<false>), grid, dim3(LM_WAVES * 64), cfg.lds, s, W, R, img, logits, cfg);
+    return hipGetLastError();
+  }
   if (use_lo)
     launch_lm<true, 2>(R, s, W, img, logits);
   else

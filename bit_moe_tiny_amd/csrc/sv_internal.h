@@ -21,6 +21,39 @@ __host__ __device__ inline size_t up256(size_t n) { return (n + 255) & ~size_t(2
 // derived from it would otherwise be computed per lane.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Block barrier after this wave's LDS writes are done, leaving its vector
+// memory loads in flight (the LDS-scope part of __syncthreads only).
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt that waits until at most n vector-memory loads are outstanding
+// (n a compile-time constant after inlining), leaving the other counters alone.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  asm volatile("" ::: "memory");   // no later load may be hoisted above the wait
+#define SV_W(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | ((((N) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8)); break;
+  switch (n) {
+    SV_W(0) SV_W(1) SV_W(2) SV_W(3) SV_W(4) SV_W(5) SV_W(6) SV_W(7) SV_W(8) SV_W(9)
+    SV_W(10) SV_W(11) SV_W(12) SV_W(13) SV_W(14) SV_W(15) SV_W(16) SV_W(17) SV_W(18)
+    SV_W(19) SV_W(20) SV_W(21) SV_W(22) SV_W(23) SV_W(24) SV_W(25) SV_W(26) SV_W(27)
+    SV_W(28) SV_W(29) SV_W(30) SV_W(31)
+    default: __builtin_amdgcn_s_waitcnt(0); break;   // (more loads than encodable: wait for all)
+  }
+#undef SV_W
+}
+
+// 16-byte load with the non-temporal hint, for weights that are streamed
+// once: on this part such loads sustain a markedly higher read rate than
+// plain ones (they do not displace reusable lines from the caches).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+  const u4v t = __builtin_nontemporal_load((const u4v*)p);
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // A global pointer to data that no kernel of this launch writes, in the
 // constant address space: uniform reads through it become scalar loads even
 // in kernels that store to global memory (the compiler cannot otherwise rule

@@ -385,29 +385,6 @@ __device__ __forceinline__ void barrier_keep_loads() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Block barrier after this wave's LDS writes are done, leaving its vector
-// memory loads in flight (the LDS-scope part of __syncthreads only).
-__device__ __forceinline__ void barrier_lds() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// s_waitcnt that waits until at most n vector-memory loads are outstanding
-// (n a compile-time constant after inlining), leaving the other counters alone.
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  asm volatile("" ::: "memory");   // no later load may be hoisted above the wait
-#define SV_W(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | ((((N) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8)); break;
-  switch (n) {
-    SV_W(0) SV_W(1) SV_W(2) SV_W(3) SV_W(4) SV_W(5) SV_W(6) SV_W(7) SV_W(8) SV_W(9)
-    SV_W(10) SV_W(11) SV_W(12) SV_W(13) SV_W(14) SV_W(15) SV_W(16) SV_W(17) SV_W(18)
-    SV_W(19) SV_W(20) SV_W(21) SV_W(22) SV_W(23) SV_W(24) SV_W(25) SV_W(26) SV_W(27)
-    SV_W(28) SV_W(29) SV_W(30) SV_W(31)
-    default: __builtin_amdgcn_s_waitcnt(0); break;   // (more loads than encodable: wait for all)
-  }
-#undef SV_W
-}
 
 // Whether the 8-block d/dmin window loads apply to rows of nb blocks.
 __host__ __device__ inline bool q2_wide_d(int nb) { return nb >= 8 && nb % 2 == 0; }
