@@ -318,6 +318,137 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
   }
 }
 
+// ---------------------------------------------------------------------------
+// Weights streamed into LDS (block counts a multiple of 16, up to 8 columns;
+// 4 with fp32 inputs).  One block of 8 waves per CU, persistent over tiles:
+// in round r wave w of block b owns tile (r G + b) 8 + w.  K is swept in
+// stages of 16 blocks (512 k).  For each stage a wave copies its tile's 16
+// rows x 512 code bytes and 16 x 32 scale bytes into its own LDS buffer with
+// global_load_lds (full 128-byte lines, non-temporal: this is the pattern
+// that streams fastest on this part), and the block copies the activation
+// columns of the stage into a shared buffer.  Everything is double buffered:
+// stage s+1 is in flight while stage s is computed; one barrier per stage.
+// Code rows are stored rotated by their row index in 16-byte units so that
+// the 16 rows of an MFMA operand read fall in distinct LDS banks.
+constexpr int LD_WAVES = 8;
+constexpr int LD_SB = 16;                                   // blocks (of 32) per stage
+constexpr int LD_WBUF = 16 * LD_SB * 32;                    // code bytes per wave and stage (8 KB)
+constexpr int LD_DBUF = 16 * LD_SB * 2;                     // scale bytes per wave and stage (512)
+constexpr int LD_XRS = LD_SB * 32 + 8;                      // activation row stride (fp16)
+constexpr int LD_XMAX = 8;                                  // columns (hi only; half with lo planes)
+
+static size_t ld_lds_bytes(int ncols, bool use_lo) {
+  return (size_t)LD_WAVES * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+
+template <bool USE_LO>
+__global__ __launch_bounds__(LD_WAVES * 64, 1) void k_q8_lmhead_dma(Q8View W, int R, XImg img, float* logits,
+                                                                    int ncols) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int vocab = W.n_out, nb = W.nb, K = nb * 32;
+  const int tiles = (vocab + 15) / 16, ns = nb / LD_SB;
+  const int rounds = (tiles + gridDim.x * LD_WAVES - 1) / (gridDim.x * LD_WAVES);
+  const int nl = lane & 15, g = lane >> 4;
+  const int kofs = 8 * (((g & 1) << 1) | (g >> 1));   // k offset of this lane's 8 values in a block
+  const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  const uint32_t wbase = lbase + wv * 2 * LD_WBUF;
+  const uint32_t dbase = lbase + LD_WAVES * 2 * LD_WBUF + wv * 2 * LD_DBUF;
+  const uint32_t xbase = lbase + LD_WAVES * 2 * (LD_WBUF + LD_DBUF);
+  const uint8_t* wl = lds + (wbase - lbase);
+  const uint8_t* dl = lds + (dbase - lbase);
+  const _Float16* xl16 = (const _Float16*)(lds + (xbase - lbase));
+  const int cr = min(nl, ncols - 1);   // padding columns read the last real column; never stored
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+
+  // stage copies of (round r, stage st) into LDS buffer `buf` (the parity of
+  // the running stage count).  Wave-private code and scale rows; activation
+  // columns shared by the block (column c by wave c mod 8).
+  auto issue = [&](int r, int st, int buf) {
+    const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
+    if (tile < tiles) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 2 * i + (lane >> 5), c = lane & 31;
+        const int n = min(tile * 16 + row, vocab - 1);
+        const int8_t* src = W.qs + ((size_t)n * nb + st * LD_SB) * 32 + ((c + row) & 31) * 16;
+        dma16_nt(src, wbase + buf * LD_WBUF + i * 1024);
+      }
+      if (lane < 32) {   // scales: two 16-byte pieces per row, lanes 0..31
+        const int row = lane >> 1;
+        const int n = min(tile * 16 + row, vocab - 1);
+        dma16(W.d + (size_t)n * nb + st * LD_SB + 8 * (lane & 1), dbase + buf * LD_DBUF);
+      }
+    }
+    for (int c = wv; c < ncols * (USE_LO ? 2 : 1); c += LD_WAVES) {
+      const int pl = c >= ncols, cc = c - (pl ? ncols : 0);
+      const _Float16* src = (pl ? img.lo : img.hi) + (size_t)cc * K + st * LD_SB * 32 + 8 * lane;
+      dma16(src, xbase + (uint32_t)(((pl * 2 + buf) * ncols + cc) * LD_XRS * 2));
+    }
+  };
+
+  issue(0, 0, 0);
+  int buf = 0;   // parity of the running stage count
+  for (int r = 0; r < rounds; ++r) {
+    const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
+    f4_t acc = zero;
+    for (int st = 0; st < ns; ++st, buf ^= 1) {
+      // this wave's copies of stage st are done; after the barrier everyone's
+      // are, and every wave is past stage st-1 (whose buffers the next copies reuse)
+      wait_vmcnt_le(0);
+      barrier_lds();
+      if (st + 1 < ns) issue(r, st + 1, buf ^ 1);
+      else if (r + 1 < rounds) issue(r + 1, 0, buf ^ 1);
+      if (tile >= tiles) continue;
+      const uint8_t* wb = wl + buf * LD_WBUF + nl * (LD_SB * 32);
+      const _Float16* xh = xl16 + (size_t)(buf * ncols + cr) * LD_XRS + kofs;
+      const _Float16* xo = xl16 + (size_t)((2 + buf) * ncols + cr) * LD_XRS + kofs;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 dv = *(const uint4*)(dl + buf * LD_DBUF + nl * 32 + 16 * j);   // 8 block scales of row nl
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int k16 = 16 * j + 4 * p + g;   // 16-byte piece of the row's stage bytes
+          const uint4 qv = *(const uint4*)(wb + ((k16 - nl) & 31) * 16);
+          uint2 qa, qb;
+          q8_regroup(qv, qa, qb);
+          const uint32_t w32 = p == 0 ? dv.x : p == 1 ? dv.y : p == 2 ? dv.z : dv.w;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int blk = j * 8 + 2 * p + h;
+            const h8_t bw = q8_bop(h == 0 ? qa : qb);
+            f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + blk * 32), bw, zero, 0, 0, 0);
+            if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xo + blk * 32), bw, dt, 0, 0, 0);
+            const float d = f16b_to_f32((uint16_t)(w32 >> (16 * h)));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(d, dt[e], acc[e]);
+          }
+        }
+      }
+    }
+    if (tile < tiles) {
+      const int n = tile * 16 + nl;
+      if (n < vocab) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cc = 4 * g + e;
+          if (cc < R) logits[(size_t)cc * vocab + n] = acc[e] * img.rscale[cc];
+        }
+      }
+    }
+  }
+  wait_vmcnt_le(0);
+}
+
 // two tiles per wave: with double-buffered weight groups this keeps two waves
 // per SIMD resident; 129280 rows then run in two full rounds of waves
 template <bool USE_LO, int T>
@@ -334,6 +465,21 @@ static void launch_lm(int R, hipStream_t s, const Q8View& W, const XImg& img, fl
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo, XImg img,
                             float* logits, hipStream_t s) {
   const Q8View W = q8_view(w, vocab, hidden);
+  if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX / 2 : LD_XMAX)) {
+    static int ncu = 0;
+    if (ncu == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+        ncu = 256;
+    }
+    const size_t lb = ld_lds_bytes(R, use_lo);
+    if (use_lo)
+      hipLaunchKernelGGL((k_q8_lmhead_dma<true>), dim3(ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
+    else
+      hipLaunchKernelGGL((k_q8_lmhead_dma<false>), dim3(ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
+    return hipGetLastError();
+  }
   // (groups in pairs; windows of LM_WIN_GROUPS groups when K does not fit)
   if (W.nb % (8 * LM_WIN_GROUPS) == 0) {
     const LmCfg cfg = lm_config(hidden, R, use_lo);
