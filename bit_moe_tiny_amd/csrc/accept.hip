@@ -219,59 +219,76 @@ __global__ __launch_bounds__(256) void k_acc_chunk(int S, int K, int V, const fl
   const int c = blockIdx.x, s = blockIdx.y, CH = gridDim.x;
   const int nrows = 2 * K + 1;
   const int tid = threadIdx.x;
-  // 1. recombine the sequence's row statistics (fixed chunk order)
-  if (tid < nrows) {
-    const int r = tid <= K ? s * (K + 1) + tid : S * (K + 1) + s * K + (tid - K - 1);
-    const bool logits = (tid <= K ? tkind : dkind) == SV_LOGITS;
-    double m = -INFINITY, z = 0.0;
-    int bad = 0;
-    for (int cc = 0; cc < CH; ++cc) {
-      m = fmax(m, ws.cmax[(size_t)r * CH + cc]);
-      bad |= ws.cbad[(size_t)r * CH + cc];
+  // 1. recombine the sequence's row statistics: wave w takes rows w, w+4, ...,
+  //    lane l chunks l, l+64, ...; butterfly reductions, so the order (and
+  //    the result) is the same in every block
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int i = wv; i < nrows; i += 4) {
+      const int r = i <= K ? s * (K + 1) + i : S * (K + 1) + s * K + (i - K - 1);
+      const bool logits = (i <= K ? tkind : dkind) == SV_LOGITS;
+      double m = -INFINITY;
+      int bad = 0;
+      for (int cc = lane; cc < CH; cc += 64) {
+        m = fmax(m, ws.cmax[(size_t)r * CH + cc]);
+        bad |= ws.cbad[(size_t)r * CH + cc];
+      }
+      m = logits ? wave_max_d(m) : 0.0;
+      bad = __any(bad) ? 1 : 0;
+      double z = 0.0;
+      for (int cc = lane; cc < CH; cc += 64) {
+        const double cs = ws.csum[(size_t)r * CH + cc];
+        z += logits ? cs * exp(ws.cmax[(size_t)r * CH + cc] - m) : cs;
+      }
+      z = wave_sum_d(z);
+      if (lane == 0) {
+        rm[i] = m;
+        rz[i] = z;
+        rbad[i] = bad | (logits ? 0 : !(z > 0.0));
+      }
     }
-    if (!logits) m = 0.0;
-    for (int cc = 0; cc < CH; ++cc) {
-      const double cs = ws.csum[(size_t)r * CH + cc];
-      z += logits ? cs * exp(ws.cmax[(size_t)r * CH + cc] - m) : cs;
-    }
-    rm[tid] = m;
-    rz[tid] = z;
-    rbad[tid] = bad | (logits ? 0 : !(z > 0.0));
   }
   __syncthreads();
-  // 2. validity and 3. the accept chain (thread 0)
-  if (tid == 0) {
+  // 2. validity and 3. the accept chain: wave 0 tests every draft at once
+  //    (lane i: draft i), the chain stops at the first rejection
+  if (tid < 64) {
     int inv = 0;
-    for (int i = 0; i < nrows; ++i) inv |= rbad[i];
-    for (int i = 0; i < K; ++i) {
+    for (int i = tid; i < nrows; i += 64) inv |= rbad[i];
+    for (int i = tid; i < K; i += 64) {
       const int d = drafts[s * K + i];
       inv |= !(d >= 0 && d < V);
     }
-    for (int i = 0; i <= K; ++i) {
+    for (int i = tid; i <= K; i += 64) {
       const float u = uni[s * (K + 1) + i];
       inv |= !(u >= 0.f && u < 1.f);
     }
-    int n = 0;
+    inv = __any(inv) ? 1 : 0;
+    int rej = 0;   // this lane's draft is rejected (lanes past K: rejected)
     if (!inv) {
-      for (; n < K; ++n) {
-        const int d = drafts[s * K + n];
+      rej = 1;
+      if (tid < K) {
+        const int d = drafts[s * K + tid];
         RowSrc P, Q;
-        sample_rows(s, n, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
-        const double p = dist_val(P, rm[n], rz[n], d);
-        const double q = dist_val(Q, rm[K + 1 + n], rz[K + 1 + n], d);
-        const double u = (double)uni[s * (K + 1) + n];
-        if (!(fma(u, q, -p) < 0.0)) break;   // reject: u*q >= p
+        sample_rows(s, tid, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
+        const double p = dist_val(P, rm[tid], rz[tid], d);
+        const double q = dist_val(Q, rm[K + 1 + tid], rz[K + 1 + tid], d);
+        const double u = (double)uni[s * (K + 1) + tid];
+        rej = !(fma(u, q, -p) < 0.0);   // reject: u*q >= p
       }
     }
-    s_nacc = n;
-    s_invalid = inv;
-    if (c == 0) {
-      ws.sinfo[2 * s] = n;
-      ws.sinfo[2 * s + 1] = inv;
-      ws.sst[4 * s + 0] = rm[n];
-      ws.sst[4 * s + 1] = rz[n];
-      ws.sst[4 * s + 2] = n < K ? rm[K + 1 + n] : 0.0;
-      ws.sst[4 * s + 3] = n < K ? rz[K + 1 + n] : 1.0;
+    const unsigned long long rmask = __ballot(rej);
+    const int n = inv ? 0 : (int)__builtin_ctzll(rmask);   // lanes >= K always reject (K <= 31)
+    if (tid == 0) {
+      s_nacc = n;
+      s_invalid = inv;
+      if (c == 0) {
+        ws.sinfo[2 * s] = n;
+        ws.sinfo[2 * s + 1] = inv;
+        ws.sst[4 * s + 0] = rm[n];
+        ws.sst[4 * s + 1] = rz[n];
+        ws.sst[4 * s + 2] = n < K ? rm[K + 1 + n] : 0.0;
+        ws.sst[4 * s + 3] = n < K ? rz[K + 1 + n] : 1.0;
+      }
     }
   }
   __syncthreads();
