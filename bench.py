@@ -208,6 +208,32 @@ def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
             "cpu": platform.processor() or platform.machine()}
 
 
+TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "lmhead_R5_hbm_traffic.md")
+
+
+def head_traffic(R):
+    """HBM bytes per vq8_lmhead_gemm call from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the copy-kernel
+    calibration), or None: for another R, or once a source the counters were
+    taken on has changed."""
+    import hashlib
+    if R != 5 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    text = open(TRAFFIC_PROFILE).read()
+    a = text.find("```json")
+    if a < 0:
+        return None
+    b = text.find("```", a + 7)
+    data = json.loads(text[a + 7:b])
+    for name, digest in data["sources_sha256"].items():
+        path = os.path.join(HERE, "bit_moe_tiny_amd", "csrc", name)
+        if not os.path.exists(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != digest:
+            return None
+    kib = sum(k["fetch_kib"] * data["fetch_factor"] + k["write_kib"] * data["write_factor"]
+              for k in data["kernels"].values())
+    return int(round(kib * 1024))
+
+
 def result_line(args, R, S, m, cpu=None):
     steps = len(m["step_ms"])
     total_s = m["total_ms"] / 1e3
@@ -246,8 +272,9 @@ def result_line(args, R, S, m, cpu=None):
         "moe_gbs": round(float(m["moe_bytes"].sum() / (m["moe_ms"].sum() / 1e3) / 1e9), 1),
         "hbm_frac_step": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "vq8_lmhead_gemm (staging + k_q8_lmhead)",
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": head_traffic(R),
+                     "kernel": "vq8_lmhead_gemm (one call: k_stage + k_q8_lmhead_dma)",
                      "bytes_per_launch": lm_bytes},
         "wall_s": round(m["wall_s"], 3),
     }
