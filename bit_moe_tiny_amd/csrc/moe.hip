@@ -542,6 +542,7 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
 // wave (item mod 8) adds them up and applies SwiGLU.  Two blocks share a CU
 // (four waves per SIMD, two of each block).
 constexpr int GP_WAVES = 8, GP_PARTS = 4;
+constexpr int GP_ZERO_BYTES = 8 * 512 + 64;   // zero operands of q2_block_c1: NQ <= 8 blocks
 
 struct GpCfg {
   bool ok;
@@ -565,7 +566,7 @@ static GpCfg gp_config(int hidden, bool use_lo, int R) {
   for (int q = 0; q < GP_PARTS; ++q)   // every window inside the row
     if ((c.nq * q & ~1) + 2 * dw > nb) return c;
   const size_t budget = (size_t)80 * 1024 - 512;   // two blocks per CU
-  const size_t red = (size_t)2 * GP_WAVES * 64 * 16 + 2 * XL_MAX_COLS * 4;
+  const size_t red = (size_t)2 * GP_WAVES * 64 * 16 + 2 * XL_MAX_COLS * 4 + GP_ZERO_BYTES;
   int cg = XL_MAX_COLS;
   while (cg > 1 && xl_bytes(cg, hidden, use_lo) + red > budget) --cg;
   if (xl_bytes(cg, hidden, use_lo) + red > budget) return c;
@@ -647,6 +648,10 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
   // the epilogue of the old descriptor's last item may still read its slot
   // while the next descriptor's scales are written
   float* rsc_slots = (float*)(lds + xl_bytes(CG, hidden, USE_LO) + (size_t)2 * GP_WAVES * 64 * 16);
+  // zeros read by the idle lanes of single-row operands (q2_block_c1): one
+  // part's worth of blocks, written once
+  _Float16* zeros = (_Float16*)(rsc_slots + 2 * XL_MAX_COLS);
+  for (int z = threadIdx.x; z < GP_ZERO_BYTES / 16; z += blockDim.x) ((uint4*)zeros)[z] = make_uint4(0, 0, 0, 0);
   auto wview = [&](int e) {
     const uint8_t* base = m == 0 ? (e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg)
                                  : (e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su);
@@ -709,21 +714,43 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
       dv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? dv[j + 1] : 0u, dv[j], dshift);
       mv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? mv[j + 1] : 0u, mv[j], dshift);
     }
+    // one activation row: sub-block selector operands (q2_block_c1); lane
+    // (c, g) is live for the steps of sub-block c == 4g + u.  The branch is
+    // uniform; both halves' loads are issued outside it.
+    const bool one = nc_cur == 1;
+    float ac = 0.f;
+    auto sel = [&](uint32_t* ph, uint32_t* pl) {   // byte offsets from lds
+      const uint32_t oh = (uint32_t)((const uint8_t*)xh - lds), ol = (uint32_t)((const uint8_t*)xl - lds);
+      const uint32_t oz = (uint32_t)((const uint8_t*)zeros - lds);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool live = nl == 4 * g + u;
+        ph[u] = live ? oh : oz - 128 * u;
+        pl[u] = live ? ol : oz - 128 * u;
+      }
+    };
     {
       uint32_t sct[4];
       xpose4(h0.sc, sct);
+      if (one) {
+        uint32_t ph[4], pl[4];
+        sel(ph, pl);
 #pragma unroll
-      for (int b = 0; b < N0; ++b) {
-        q2_block<USE_LO>(h0.qs[b], sct[b], win_val(dv, b), win_val(mv, b), xh + 256 * b, xl + 256 * b,
-                         xs + 32 * b, acc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (NQ <= 4) {
-#pragma unroll
-        for (int b = N0; b < NQ; ++b) {
+        for (int b = 0; b < NQ && b < 8; ++b) {
+          if (b >= N0 && NQ > 4) break;
           // (second-half blocks of a part of at most 4 use the first nibble load)
-          q2_block<USE_LO>(h1.qs[b - N0], sct[b], win_val(dv, b), win_val(mv, b), xh + 256 * b,
-                           xl + 256 * b, xs + 32 * b, acc);
+          const uint4& qs = b < N0 ? h0.qs[b] : h1.qs[b - N0 < H1::N ? b - N0 : 0];
+          q2_block_c1<USE_LO>(qs, sct[b & 3], win_val(dv, b), win_val(mv, b), g == 0, lds, ph, pl, 256 * b,
+                              xs + 32 * b, ac);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NQ && b < 8; ++b) {
+          if (b >= N0 && NQ > 4) break;
+          const uint4& qs = b < N0 ? h0.qs[b] : h1.qs[b - N0 < H1::N ? b - N0 : 0];
+          q2_block<USE_LO>(qs, sct[b & 3], win_val(dv, b), win_val(mv, b), xh + 256 * b, xl + 256 * b,
+                           xs + 32 * b, acc);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -732,15 +759,31 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
     if (NQ > 4) {
       uint32_t sct[4];
       xpose4(h1.sc, sct);
+      if (one) {
+        uint32_t ph[4], pl[4];
+        sel(ph, pl);
 #pragma unroll
-      for (int b = N0; b < NQ; ++b) {
-        q2_block<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), xh + 256 * b,
-                         xl + 256 * b, xs + 32 * b, acc);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int b = N0; b < NQ; ++b) {
+          q2_block_c1<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), g == 0, lds, ph, pl,
+                              256 * b, xs + 32 * b, ac);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int b = N0; b < NQ; ++b) {
+          q2_block<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), xh + 256 * b,
+                           xl + 256 * b, xs + 32 * b, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     issue1(h1);
-
+    if (one) {
+      // the row's total over its 4 lanes (g = 0..3), as column 0 of lane-row 0
+      ac += __shfl_xor(ac, 16, 64);
+      ac += __shfl_xor(ac, 32, 64);
+      acc[0] = g == 0 ? ac : 0.f;
+    }
     // partial sums of item i meet in buffer i & 1
     f4_t* rbuf = red + (size_t)(i & 1) * GP_WAVES * 64;
     rbuf[wv * 64 + lane] = acc;

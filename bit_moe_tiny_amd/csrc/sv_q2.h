@@ -237,6 +237,57 @@ __device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d,
   for (int e = 0; e < 4; ++e) acc[e] = fmaf(nd, dm[e], fmaf(d, dt[e], acc[e]));
 }
 
+// acc += one block for a single activation column (a descriptor of one row),
+// without per-weight scaling.  The A operand of row c is the column's values
+// on sub-block c and zero elsewhere: lane (c, g) is live at steps t with
+// 4g + t/2 == c, so ph[u] (u = t/2) addresses the block's activation operands
+// for the live lane and a zero region for the others (block offset and step
+// offset then land inside it; ph/pl are byte offsets from lds).  The B operand is the raw codes: each
+// 2-bit code masked in place reads as the fp16 subnormal 4^j q 2^-24 (the
+// matrix cores keep subnormals), and the activation image carries 4^-j.  The
+// result holds, per output row n and sub-block c, the unscaled partial sum of
+// that sub-block; the lane (n, g) scales its four sub-blocks 4g..4g+3 by their
+// nibbles in fp32.  Sums over the 4 lanes of a row are left to the caller;
+// the min term (the usual 16x16x16 product, identical in every lane's rows)
+// is added on lanes g == 0 only.
+template <bool USE_LO>
+__device__ __forceinline__ void q2_block_c1(const uint4& qs, uint32_t scw, float d, float dmin, bool g0,
+                                            const uint8_t* lds, const uint32_t* ph, const uint32_t* pl,
+                                            int boff, const _Float16* xs, float& ac) {
+  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f4_t D = zero;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int i = t >> 1, hs = t & 1;
+    const uint32_t dw = (i == 0 ? qs.x : i == 1 ? qs.y : i == 2 ? qs.z : qs.w) >> (8 * hs);
+    h8_t b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const h2_t p = as_h2(dw & sreg(0x00030003u << (2 * j)));
+      b[2 * j] = p.x;
+      b[2 * j + 1] = p.y;
+    }
+    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(lds + ph[i] + 2 * boff + 64 * t), b, D, 0, 0, 0);
+    if (USE_LO)
+      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(lds + pl[i] + 2 * boff + 64 * t), b, D, 0, 0, 0);
+  }
+  const uint32_t scb = scw & 0x0F0F0F0Fu;
+  const float u = fmaf((float)(scb >> 24), D[3],
+                       fmaf((float)((scb >> 16) & 0xFF), D[2],
+                            fmaf((float)((scb >> 8) & 0xFF), D[1], (float)(scb & 0xFF) * D[0])));
+  // min term
+  const h2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
+  const uint32_t hi = (scw >> 4) & 0x0F0F0F0Fu;
+  const h2_t m01 = q2_bytes01(hi) - k1024, m23 = q2_bytes23(hi) - k1024;
+  const h4_t m = {m01.x, m01.y, m23.x, m23.y};
+  const h8_t sx = *(const h8_t*)xs;
+  const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
+  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, m, zero, 0, 0, 0);
+  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, m, dm, 0, 0, 0);
+  ac = fmaf(d * 16777216.f, u, ac);   // 2^24: the codes' subnormal unit
+  if (g0) ac = fmaf(-dmin, dm[0], ac);
+}
+
 // fp16 value at position p (0..7) of an 8-value window held as 4 dwords.
 __device__ __forceinline__ float win_val(const uint32_t* w, int p) {
   return f16bits_to_f32((uint16_t)(w[p >> 1] >> (16 * (p & 1))));

@@ -13,9 +13,10 @@ configuration the benchmark times, on outputs the oracle computes one by one.
 * the cohort: 3 sequences x 5 rows = 15 rows through the same layer and head,
   per-sequence spec_accept;
 * the R = 1..16 stress sweep: every R against the oracle on sampled vocabulary
-  rows, and the MoE layer's rows checked for batch invariance (row r of an
-  R-row call equals row r of the 16-row call) plus sampled rows against the
-  oracle;
+  rows, and every row of every R-row MoE call against the oracle (the routing
+  bit-exact; the expert sums may round differently with the batch, since an
+  expert's rows are contracted one way when it has one row and another when
+  it has several);
 * a full-vocabulary rejection workload given as probabilities, where decisions
   and tokens must match the oracle exactly (identical fp32 p, q and u).
 """
@@ -187,7 +188,8 @@ def test_cohort_workload(sv, layer, head):
 # ----------------------------------------------------------------- sweep
 @pytest.fixture(scope="module")
 def sweep16(sv, layer, head):
-    """16-row inputs of the sweep and the GPU results of the 16-row calls."""
+    """16-row inputs of the sweep, the GPU results of the 16-row calls and the
+    oracle's MoE output for all 16 rows."""
     w, desc = layer
     buf, wdev = head
     rows = synth.moe_rows(16, synth.CFG_COHORT, sub=16)
@@ -195,35 +197,33 @@ def sweep16(sv, layer, head):
     say("sweep reference calls R=16")
     y16, ti16, _ = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
     z16 = _run_head(sv, wdev, h)
-    return rows, h, y16, ti16, z16
+    say("oracle MoE output of the 16 sweep rows")
+    y_or = _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, list(range(16)))
+    return rows, h, y16, ti16, z16, y_or
 
 
 def test_sweep_moe_r16_against_oracle(sv, layer, sweep16):
-    w, _ = layer
-    rows, _, y16, ti16, _ = sweep16
+    rows, _, y16, ti16, _, y_or = sweep16
     assert np.array_equal(ti16, oracle.route_topk(rows.router_logits, TOPK)[0])
-    check = [3, 15]
-    assert_close(y16[check], _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check),
-                 what="sweep R=16 moe y")
+    assert_close(y16, y_or, what="sweep R=16 moe y")
 
 
 @pytest.mark.parametrize("R", list(range(1, 16)))
-def test_sweep_moe_batch_invariance(sv, layer, sweep16, R):
-    """Row r of an R-row call equals row r of the 16-row call: each row's
-    output depends on that row alone, so the oracle check of the 16-row call
-    carries over (tolerance far below the parity bar)."""
+def test_sweep_moe_rows(sv, layer, sweep16, R):
+    """Every row of an R-row call against the oracle; the routing of row r
+    equals that of the 16-row call (it depends on that row alone)."""
     _, desc = layer
-    rows, _, y16, ti16, _ = sweep16
+    rows, _, _, ti16, _, y_or = sweep16
     say("vq2_moe_gemm sweep", R)
     y, ti, _ = _run_moe(sv, desc, rows.x_bf16[:R].copy(), rows.router_logits[:R].copy())
     assert np.array_equal(ti, ti16[:R])
-    assert_close(y, y16[:R], tol=1e-5, what=f"moe R={R} vs R=16")
+    assert_close(y, y_or[:R], what=f"moe R={R}")
 
 
 @pytest.mark.parametrize("R", list(range(1, 17)))
 def test_sweep_lm_head(sv, head, sweep16, R):
     buf, wdev = head
-    _, h, _, _, z16 = sweep16
+    _, h, _, _, z16, _ = sweep16
     say("vq8_lmhead_gemm sweep", R)
     z = _run_head(sv, wdev, h[:R].copy())
     cols = _vocab_sample(100 + R, 512)
