@@ -144,22 +144,29 @@ class Step:
 
 
 def measure(step, steps, warmup):
+    """Times `steps` steps with events at the two ends only (an event recorded
+    between kernels leaves a gap of several microseconds on the GPU timeline);
+    a second pass over the same batches, with events around each call, gives
+    the per-call breakdown."""
     import torch
     for i in range(warmup):
         step.run(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step.run(i, evs[i])
+        step.run(i)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step.run(i, evs[i])
+    torch.cuda.synchronize()
     moe = np.array([e[0].elapsed_time(e[1]) for e in evs])
     lm = np.array([e[1].elapsed_time(e[2]) for e in evs])
     acc = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -262,6 +269,8 @@ def result_line(args, R, S, m, cpu=None):
                          f"spec_accept, R={R} rows, S={S} sequence(s) x K={R // S - 1} drafts, T=0.8"),
             "R": R, "S": S, "K": R // S - 1, "batches": args.batches,
         },
+        # per-step spread and per-call times: the breakdown pass (events
+        # between the calls add their own gaps, so these exceed ms_per_step)
         "step_us": {"median": round(float(np.median(m["step_ms"])) * 1e3, 2),
                     "p10": round(float(np.percentile(m["step_ms"], 10)) * 1e3, 2),
                     "p90": round(float(np.percentile(m["step_ms"], 90)) * 1e3, 2)},
