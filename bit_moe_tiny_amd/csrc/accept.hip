@@ -8,40 +8,48 @@
 // p_i(d_i), tested exactly as the sign of fma(u, q, -p); the replacement or
 // bonus token is the first x whose running sum exceeds u_K times the total.
 //
-// Three launches, no host sync, no block waiting on another:
-//   k_acc_stats  grid (chunk, row): per 2048-entry chunk of every target and
-//                draft row, the chunk max of z/T and sum exp(z/T - max) in
-//                fp64 (or the plain sum for probability rows), plus a
-//                validity flag.  Spreads the vocabulary-wide reductions over
-//                many CUs.
-//   k_acc_chunk  grid (chunk, sequence): every block recombines its
-//                sequence's row statistics (same order in every block, so all
-//                agree bit for bit), replays the accept chain, and sums the
-//                sampling weights of its chunk (residual, or p_K for the
-//                bonus).
-//   k_acc_pick   one block per sequence: prefix over the chunk totals, the
-//                chunk that holds u_K * Z, a block scan inside it, outputs.
+// Two launches, no host sync, no block waiting on another:
+//   k_acc_stats   grid (chunk, row): per 2048-entry chunk of every target and
+//                 draft row, the chunk max of z/T and sum exp(z/T - max) in
+//                 fp64 (or the plain sum for probability rows), plus a
+//                 validity flag.  Spreads the vocabulary-wide reductions over
+//                 many CUs.
+//   k_acc_sample  grid (512-entry chunk, sequence): every block recombines
+//                 its sequence's row statistics (same order in every block, so
+//                 all agree bit for bit), replays the accept chain, and sums
+//                 the sampling weights of its chunk (residual, or p_K for the
+//                 bonus), per 2-entry thread segment and per chunk.  The last
+//                 block of the sequence to finish (a counter the first launch
+//                 clears) finds, with one wave, the chunk that holds u_K * Z
+//                 from the chunk totals, the segment inside it from the
+//                 per-thread sums, and the token among that segment's
+//                 entries, then writes the outputs.
 #include "sv_internal.h"
 
 namespace sv {
 
-constexpr int ACC_CHUNK = 2048;
-constexpr int ACC_PER = ACC_CHUNK / 256;
-constexpr int ACC_MAX_CH = 256;   // V <= 524288
+constexpr int ACC_T = 256;                    // threads per block
+constexpr int ACC_CHUNK = 2048;               // statistics chunk
+constexpr int ACC_PER = ACC_CHUNK / ACC_T;
+constexpr int ACC_MAX_CH = 256;               // V <= 524288
+constexpr int SMP_PER = 2;                    // sampling entries per thread
+constexpr int SMP_CHUNK = ACC_T * SMP_PER;    // sampling chunk
+constexpr int SMP_MAX_CH = ACC_MAX_CH * ACC_CHUNK / SMP_CHUNK;
 
 struct AccWs {
   double* cmax;     // [rows, CH]
   double* csum;     // [rows, CH]
   int* cbad;        // [rows, CH]
-  double* rsum;     // [S, CH]   sampling weight per chunk
-  double* sst;      // [S, 4]    pm, pz, qm, qz of the sampled row pair
-  int* sinfo;       // [S, 2]    n accepted, invalid
+  double* rsum;     // [S, CHs]        sampling weight per sampling chunk
+  double* tsum;     // [S, CHs, ACC_T] sampling weight per thread segment
+  unsigned* done;   // [S]            blocks of the sequence done sampling
 };
 
 static inline int acc_chunks(int V) { return (V + ACC_CHUNK - 1) / ACC_CHUNK; }
+static inline int smp_chunks(int V) { return (V + SMP_CHUNK - 1) / SMP_CHUNK; }
 
 static AccWs acc_carve(void* base, int S, int K, int V) {
-  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V);
+  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
   uint8_t* p = (uint8_t*)base;
   AccWs w;
   w.cmax = (double*)p;
@@ -51,28 +59,53 @@ static AccWs acc_carve(void* base, int S, int K, int V) {
   w.cbad = (int*)p;
   p += up256(rows * CH * 4);
   w.rsum = (double*)p;
-  p += up256((size_t)S * CH * 8);
-  w.sst = (double*)p;
-  p += up256((size_t)S * 4 * 8);
-  w.sinfo = (int*)p;
+  p += up256((size_t)S * CHs * 8);
+  w.tsum = (double*)p;
+  p += up256((size_t)S * CHs * ACC_T * 8);
+  w.done = (unsigned*)p;
   return w;
 }
 
 size_t accept_ws_bytes(int S, int K, int V) {
-  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V);
-  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256((size_t)S * CH * 8) +
-         up256((size_t)S * 4 * 8) + up256((size_t)S * 2 * 4);
+  const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
+  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256((size_t)S * CHs * 8) +
+         up256((size_t)S * CHs * ACC_T * 8) + up256((size_t)S * 4);
 }
 
 __device__ inline double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_allreduce(v, [](double a, double b) { return a + b; });
 }
 __device__ inline double wave_max_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_allreduce(v, [](double a, double b) { return fmax(a, b); });
+}
+
+// x from the lane CTRL names (DPP), 0 where the row/bank masks or the row
+// edge leave no source: 0x111/0x112/0x114/0x118 row_shr 1/2/4/8, 0x142
+// row_bcast 15, 0x143 row_bcast 31.
+template <int CTRL, int ROWS, int BANKS>
+__device__ __forceinline__ double xlane_z(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROWS, BANKS, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROWS, BANKS, true);
+  return __builtin_bit_cast(double, (uint64_t)lo | ((uint64_t)hi << 32));
+}
+
+// Wave-wide exclusive prefix sum in a fixed order (inclusive scan in 16-lane
+// rows by row shifts, then the row totals broadcast across rows);
+// *total = the wave's sum.
+__device__ inline double wave_excl_scan_d(double v, double* total) {
+  double x = v;
+  x += xlane_z<0x111, 0xF, 0xF>(x);
+  x += xlane_z<0x112, 0xF, 0xF>(x);
+  x += xlane_z<0x114, 0xF, 0xE>(x);
+  x += xlane_z<0x118, 0xF, 0xC>(x);
+  x += xlane_z<0x142, 0xA, 0xF>(x);
+  x += xlane_z<0x143, 0xC, 0xF>(x);
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  *total = __builtin_bit_cast(double, (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, 63) |
+                                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63) << 32));
+  const double ex = __shfl_up(x, 1, 64);
+  return (threadIdx.x & 63) == 0 ? 0.0 : ex;
 }
 
 // Block-wide fixed-order reductions (256 threads); `sh` holds 4 doubles.
@@ -138,6 +171,8 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
   __shared__ double sh[4];
   __shared__ int shb[4];
   const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
+  if (c == 0 && r == 0)   // the sampling launch's per-sequence counters
+    for (int i = threadIdx.x; i < S; i += blockDim.x) ws.done[i] = 0u;
   const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
   const int x0 = c * ACC_CHUNK;
   double a[ACC_PER];
@@ -208,39 +243,51 @@ __device__ inline void sample_rows(int s, int n, int S, int K, int V, const floa
   Q = n < K ? row_src(S * (K + 1) + s * K + n, S, K, V, target, tkind, Tp, draft, dkind, Tq) : P;
 }
 
-__global__ __launch_bounds__(256) void k_acc_chunk(int S, int K, int V, const float* target,
-                                                   int tkind, float Tp, const float* draft,
-                                                   int dkind, float Tq, const int32_t* drafts,
-                                                   const float* uni, AccWs ws) {
-  __shared__ double rm[2 * SV_MAX_DRAFTS + 1], rz[2 * SV_MAX_DRAFTS + 1];
-  __shared__ int rbad[2 * SV_MAX_DRAFTS + 1];
-  __shared__ int s_nacc, s_invalid;
-  __shared__ double sh[4];
-  const int c = blockIdx.x, s = blockIdx.y, CH = gridDim.x;
+// Row statistics of sequence s recombined from the chunk statistics: wave w
+// takes rows w, w+4, ... three at a time (their loads issued together), lane
+// l chunks l, l+64, ...; butterfly reductions, so every block gets the same
+// bits.
+__device__ inline void acc_rows(int s, int S, int K, int CH, int tkind, int dkind, const AccWs& ws,
+                                double* rm, double* rz, int* rbad) {
+  constexpr int RB = 3, CPL = ACC_MAX_CH / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nrows = 2 * K + 1;
-  const int tid = threadIdx.x;
-  // 1. recombine the sequence's row statistics: wave w takes rows w, w+4, ...,
-  //    lane l chunks l, l+64, ...; butterfly reductions, so the order (and
-  //    the result) is the same in every block
-  {
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int i = wv; i < nrows; i += 4) {
+  for (int i0 = wv; i0 < nrows; i0 += 4 * RB) {
+    double cm[RB][CPL], cs[RB][CPL];
+    int cb[RB];
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int i = i0 + 4 * j;
       const int r = i <= K ? s * (K + 1) + i : S * (K + 1) + s * K + (i - K - 1);
+      cb[j] = 0;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int cc = lane + 64 * k;
+        cm[j][k] = -INFINITY;
+        cs[j][k] = 0.0;
+        if (i < nrows && cc < CH) {
+          const size_t o = (size_t)r * CH + cc;
+          cm[j][k] = ws.cmax[o];
+          cs[j][k] = ws.csum[o];
+          cb[j] |= ws.cbad[o];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RB; ++j) {
+      const int i = i0 + 4 * j;
+      if (i >= nrows) break;   // uniform in the wave
       const bool logits = (i <= K ? tkind : dkind) == SV_LOGITS;
       double m = -INFINITY;
-      int bad = 0;
-      for (int cc = lane; cc < CH; cc += 64) {
-        m = fmax(m, ws.cmax[(size_t)r * CH + cc]);
-        bad |= ws.cbad[(size_t)r * CH + cc];
-      }
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) m = fmax(m, cm[j][k]);
       m = logits ? wave_max_d(m) : 0.0;
-      bad = __any(bad) ? 1 : 0;
       double z = 0.0;
-      for (int cc = lane; cc < CH; cc += 64) {
-        const double cs = ws.csum[(size_t)r * CH + cc];
-        z += logits ? cs * exp(ws.cmax[(size_t)r * CH + cc] - m) : cs;
-      }
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        if (lane + 64 * k < CH) z += logits ? cs[j][k] * exp(cm[j][k] - m) : cs[j][k];
       z = wave_sum_d(z);
+      const int bad = __any(cb[j]) ? 1 : 0;
       if (lane == 0) {
         rm[i] = m;
         rz[i] = z;
@@ -248,160 +295,234 @@ __global__ __launch_bounds__(256) void k_acc_chunk(int S, int K, int V, const fl
       }
     }
   }
-  __syncthreads();
-  // 2. validity and 3. the accept chain: wave 0 tests every draft at once
-  //    (lane i: draft i), the chain stops at the first rejection
-  if (tid < 64) {
-    int inv = 0;
-    for (int i = tid; i < nrows; i += 64) inv |= rbad[i];
-    for (int i = tid; i < K; i += 64) {
-      const int d = drafts[s * K + i];
-      inv |= !(d >= 0 && d < V);
-    }
-    for (int i = tid; i <= K; i += 64) {
-      const float u = uni[s * (K + 1) + i];
-      inv |= !(u >= 0.f && u < 1.f);
-    }
-    inv = __any(inv) ? 1 : 0;
-    int rej = 0;   // this lane's draft is rejected (lanes past K: rejected)
-    if (!inv) {
-      rej = 1;
-      if (tid < K) {
-        const int d = drafts[s * K + tid];
-        RowSrc P, Q;
-        sample_rows(s, tid, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
-        const double p = dist_val(P, rm[tid], rz[tid], d);
-        const double q = dist_val(Q, rm[K + 1 + tid], rz[K + 1 + tid], d);
-        const double u = (double)uni[s * (K + 1) + tid];
-        rej = !(fma(u, q, -p) < 0.0);   // reject: u*q >= p
+}
+
+// Sampling weight of this thread's segment of sampling chunk c: entries
+// c*SMP_CHUNK + tid*SMP_PER + 0..SMP_PER-1, summed in order.
+__device__ inline double seg_weight(int mode, const RowSrc& P, double pm, double pz,
+                                    const RowSrc& Q, double qm, double qz, int c, int V) {
+  double w = 0.0;
+#pragma unroll
+  for (int i = 0; i < SMP_PER; ++i) {
+    const int x = c * SMP_CHUNK + threadIdx.x * SMP_PER + i;
+    if (x < V) w += sample_weight(mode, P, pm, pz, Q, qm, qz, x);
+  }
+  return w;
+}
+
+// Running sums over n values v[0..n) in LDS, in order (lane l holds
+// v[l*per .. l*per+per-1]).  wave_prefix: the lane's exclusive prefix and
+// the total.  wave_cross: the first index at which the running sum from
+// `run` (the lane's starting sum) exceeds tt, and the running sum before it
+// (-1 if none); *lastpos = the last index with a positive value (-1 if none).
+// Wave-uniform results.
+__device__ inline double wave_prefix(const double* v, int n, int per, double* total) {
+  const int lane = threadIdx.x & 63;
+  double lt = 0.0;
+  for (int j = 0; j < per; ++j) {
+    const int k = lane * per + j;
+    if (k < n) lt += v[k];
+  }
+  return wave_excl_scan_d(lt, total);
+}
+
+__device__ inline int wave_cross(const double* v, int n, int per, double run, double tt, double* pre,
+                                 int* lastpos) {
+  const int lane = threadIdx.x & 63;
+  int cand = -1, lp = -1;
+  double cpre = 0.0;
+  for (int j = 0; j < per; ++j) {
+    const int k = lane * per + j;
+    if (k < n) {
+      const double x = v[k];
+      if (cand < 0 && run + x > tt) {
+        cand = k;
+        cpre = run;
       }
+      if (x > 0.0) lp = k;
+      run += x;
     }
-    const unsigned long long rmask = __ballot(rej);
-    const int n = inv ? 0 : (int)__builtin_ctzll(rmask);   // lanes >= K always reject (K <= 31)
-    if (tid == 0) {
-      s_nacc = n;
-      s_invalid = inv;
-      if (c == 0) {
-        ws.sinfo[2 * s] = n;
-        ws.sinfo[2 * s + 1] = inv;
-        ws.sst[4 * s + 0] = rm[n];
-        ws.sst[4 * s + 1] = rz[n];
-        ws.sst[4 * s + 2] = n < K ? rm[K + 1 + n] : 0.0;
-        ws.sst[4 * s + 3] = n < K ? rz[K + 1 + n] : 1.0;
+  }
+  const unsigned long long cm = __ballot(cand >= 0), pmask = __ballot(lp >= 0);
+  *lastpos = pmask ? __shfl(lp, 63 - __builtin_clzll(pmask), 64) : -1;
+  if (!cm) return -1;
+  const int fl = __builtin_ctzll(cm);
+  *pre = __shfl(cpre, fl, 64);
+  return __shfl(cand, fl, 64);
+}
+
+__global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int CH,
+                                                      const float* target, int tkind, float Tp,
+                                                      const float* draft, int dkind, float Tq,
+                                                      const int32_t* drafts, const float* uni,
+                                                      int32_t* out_tokens, int32_t* out_n, AccWs ws) {
+  __shared__ double rm[2 * SV_MAX_DRAFTS + 1], rz[2 * SV_MAX_DRAFTS + 1];
+  __shared__ int rbad[2 * SV_MAX_DRAFTS + 1];
+  __shared__ double sh[4];
+  __shared__ double cws[SMP_MAX_CH];   // the last block: chunk totals
+  __shared__ double parts[ACC_T];      // the last block: the hit chunk's segment totals
+  __shared__ double s_uk, s_z, s_base;
+  __shared__ int s_nacc, s_invalid, s_last, s_hit, s_found;
+  const int c = blockIdx.x, s = blockIdx.y, CHs = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // 0. wave 0, lane i: draft i's token and uniform and both rows' values at
+  //    the token, loaded before the statistics are read
+  int dk = -1, pre_bad = 0;
+  float uk = 0.f, vp = 0.f, vq = 0.f;
+  if (tid < 64) {
+    if (lane <= K) {
+      uk = uni[s * (K + 1) + lane];
+      pre_bad |= !(uk >= 0.f && uk < 1.f);
+    }
+    if (lane < K) {
+      dk = drafts[s * K + lane];
+      if (dk >= 0 && dk < V) {
+        vp = target[(size_t)(s * (K + 1) + lane) * V + dk];
+        vq = draft[(size_t)(s * K + lane) * V + dk];
+      } else {
+        pre_bad = 1;
       }
     }
   }
+  // 1. the sequence's row statistics
+  acc_rows(s, S, K, CH, tkind, dkind, ws, rm, rz, rbad);
   __syncthreads();
-  const int nacc = s_nacc;
-  // 4. this chunk's total sampling weight (residual, or p_K for the bonus)
+  // 2. validity and the accept chain: wave 0 tests every draft at once
+  //    (lane i: draft i), the chain stops at the first rejection
+  if (tid < 64) {
+    int inv = pre_bad;
+    for (int i = lane; i < 2 * K + 1; i += 64) inv |= rbad[i];
+    inv = __any(inv) ? 1 : 0;
+    int rej = 1;   // lanes past K: rejected (K <= 31)
+    if (!inv && lane < K) {
+      const double p = tkind == SV_LOGITS ? exp((double)vp / (double)Tp - rm[lane]) / rz[lane]
+                                          : (double)vp;
+      const double q = dkind == SV_LOGITS
+                           ? exp((double)vq / (double)Tq - rm[K + 1 + lane]) / rz[K + 1 + lane]
+                           : (double)vq;
+      rej = !(fma((double)uk, q, -p) < 0.0);   // reject: u*q >= p
+    }
+    const unsigned long long rmask = __ballot(rej);
+    if (lane == 0) {
+      s_nacc = inv ? 0 : (int)__builtin_ctzll(rmask);
+      s_invalid = inv;
+    }
+    if (lane == K) s_uk = (double)uk;
+  }
+  __syncthreads();
+  const int nacc = s_nacc, inv = s_invalid;
+  // 3. this chunk's sampling weights (residual, or p_K for the bonus), per
+  //    thread segment and per chunk
   RowSrc P, Q;
   sample_rows(s, nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
   const double pm = rm[nacc], pz = rz[nacc];
   const double qm = nacc < K ? rm[K + 1 + nacc] : 0.0, qz = nacc < K ? rz[K + 1 + nacc] : 1.0;
   const int mode = nacc < K ? MODE_RESID : MODE_P;
-  double w = 0.0;
-  if (!s_invalid) {
-    const int x0 = c * ACC_CHUNK;
-#pragma unroll
-    for (int i = 0; i < ACC_PER; ++i) {
-      const int x = x0 + tid * ACC_PER + i;
-      if (x < V) w += sample_weight(mode, P, pm, pz, Q, qm, qz, x);
-    }
-  }
+  double w = inv ? 0.0 : seg_weight(mode, P, pm, pz, Q, qm, qz, c, V);
+  // 4. the last block of the sequence to get here samples.  The sums go out
+  //    as device-scope stores (written through to the point of coherence of
+  //    all XCDs, not held in this XCD's L2) and every one has completed
+  //    before the block counts itself done; the last block reads them back
+  //    with device-scope loads
+  __hip_atomic_store(&ws.tsum[((size_t)s * CHs + c) * ACC_T + tid], w, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
   w = block_sum_d(w, sh);
-  if (tid == 0) ws.rsum[(size_t)s * CH + c] = w;
-}
-
-__global__ __launch_bounds__(256) void k_acc_pick(int S, int K, int V, int CH,
-                                                  const float* target, int tkind, float Tp,
-                                                  const float* draft, int dkind, float Tq,
-                                                  const int32_t* drafts, const float* uni,
-                                                  int32_t* out_tokens, int32_t* out_n, AccWs ws) {
-  __shared__ double sh[4];
-  __shared__ double s_base;
-  __shared__ int s_hit, s_pick, s_last;
-  const int s = blockIdx.x, tid = threadIdx.x;
-  const int nacc = ws.sinfo[2 * s], invalid = ws.sinfo[2 * s + 1];
+  if (tid == 0)
+    __hip_atomic_store(&ws.rsum[(size_t)s * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt_le(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(CHs - 1);
+  __syncthreads();
+  if (!s_last) return;
   int32_t* out = out_tokens + (size_t)s * (K + 1);
-  if (invalid) {
-    for (int i = tid; i <= K; i += 256) out[i] = -1;
+  if (inv) {
+    if (tid <= K) out[tid] = -1;
     if (tid == 0) out_n[s] = -1;
     return;
   }
-  RowSrc P, Q;
-  sample_rows(s, nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
-  const double pm = ws.sst[4 * s], pz = ws.sst[4 * s + 1], qm = ws.sst[4 * s + 2],
-               qz = ws.sst[4 * s + 3];
-  int mode = nacc < K ? MODE_RESID : MODE_P;
-  double cw = tid < CH ? ws.rsum[(size_t)s * CH + tid] : 0.0;
-  double Z;
-  double pre = block_excl_scan_d(cw, sh, &Z);
-  if (!(Z > 0.0)) {
-    // the residual vanished (only through rounding): sample p_i itself
-    mode = MODE_P;
-    cw = 0.0;
-    for (int cc = 0; cc < CH; ++cc) {
-      double t = 0.0;
-#pragma unroll
-      for (int i = 0; i < ACC_PER; ++i) {
-        const int x = cc * ACC_CHUNK + tid * ACC_PER + i;
-        if (x < V) t += sample_weight(mode, P, pm, pz, Q, qm, qz, x);
+  for (int cc = tid; cc < CHs; cc += ACC_T)
+    cws[cc] = __hip_atomic_load(&ws.rsum[(size_t)s * CHs + cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // the chunk holding tt = u_K * Z: the first whose running total exceeds
+  // it, failing that (rounding) the last chunk with weight
+  const int per = (CHs + 63) / 64;
+  auto find_chunk = [&]() {
+    if (tid < 64) {
+      double Z;
+      const double run = wave_prefix(cws, CHs, per, &Z);
+      double pre = 0.0;
+      int lastpos = -1;
+      const int hit = Z > 0.0 ? wave_cross(cws, CHs, per, run, s_uk * Z, &pre, &lastpos) : -1;
+      if (lane == 0) {
+        s_z = Z;
+        s_found = hit >= 0;
+        s_hit = hit >= 0 ? hit : max(lastpos, 0);
+        s_base = hit >= 0 ? pre : 0.0;
       }
-      t = block_sum_d(t, sh);
-      if (tid == cc) cw = t;
     }
-    pre = block_excl_scan_d(cw, sh, &Z);
+    __syncthreads();
+  };
+  find_chunk();
+  const bool redo = !(s_z > 0.0);
+  if (redo) {
+    // the residual vanished (only through rounding): sample p itself
+    for (int cc = 0; cc < CHs; ++cc) {
+      const double t = block_sum_d(seg_weight(MODE_P, P, pm, pz, Q, qm, qz, cc, V), sh);
+      if (tid == 0) cws[cc] = t;
+    }
+    __syncthreads();
+    find_chunk();
   }
-  const double target_t = (double)uni[s * (K + 1) + K] * Z;
-  // chunk holding the target: the first whose running total exceeds it
-  if (tid == 0) {
-    s_hit = 0x7fffffff;
-    s_last = -1;
-    s_pick = 0x7fffffff;
-  }
+  const int smode = redo ? MODE_P : mode;
+  const double tt = s_uk * s_z;
+  const int hit = s_hit;
+  parts[tid] = redo ? seg_weight(MODE_P, P, pm, pz, Q, qm, qz, hit, V)
+                    : __hip_atomic_load(&ws.tsum[((size_t)s * CHs + hit) * ACC_T + tid],
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (tid < CH && pre + cw > target_t) atomicMin(&s_hit, tid);
-  if (tid < CH && cw > 0.0) atomicMax(&s_last, tid);
-  __syncthreads();
-  const bool found_chunk = s_hit != 0x7fffffff;
-  // no chunk crossed (rounding): fall back to the last chunk with weight
-  const int hit = found_chunk ? s_hit : (s_last >= 0 ? s_last : 0);
-  if (tid == hit) s_base = pre;   // exclusive prefix of chunk `hit`
-  __syncthreads();
-  const double base = found_chunk ? s_base : 0.0;
-  // in-chunk scan, 8 consecutive entries per thread
-  double loc[ACC_PER];
-  double tot = 0.0;
-  int lastmine = -1;
+  if (tid >= 64) return;
+  // the thread segment inside it, the same way, then the entry: the first
+  // whose running sum exceeds tt, failing that (rounding) the last entry with
+  // weight of the segment, of the chunk
+  constexpr int TPL = ACC_T / 64;
+  double ptot;
+  const double prun = s_base + wave_prefix(parts, ACC_T, TPL, &ptot);
+  double tpre = 0.0;
+  int lastseg;
+  const int seg = wave_cross(parts, ACC_T, TPL, prun, tt, &tpre, &lastseg);
+  const bool found = s_found && seg >= 0;
+  const int thr = found ? seg : max(lastseg, 0);
+  int tok = -1;
+  {
+    double run = tpre;
+    int lp = -1;
 #pragma unroll
-  for (int i = 0; i < ACC_PER; ++i) {
-    const int x = hit * ACC_CHUNK + tid * ACC_PER + i;
-    loc[i] = x < V ? sample_weight(mode, P, pm, pz, Q, qm, qz, x) : 0.0;
-    tot += loc[i];
-    if (loc[i] > 0.0) lastmine = x;
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int x = hit * SMP_CHUNK + thr * SMP_PER + i;
+      if (x < V) {
+        const double wi = sample_weight(smode, P, pm, pz, Q, qm, qz, x);
+        run += wi;
+        if (wi > 0.0) lp = x;
+        if (found && tok < 0 && run > tt) tok = x;
+      }
+    }
+    if (tok < 0) tok = lp;
   }
-  double dummy;
-  double run = base + block_excl_scan_d(tot, sh, &dummy);
-  int mine = 0x7fffffff;
-#pragma unroll
-  for (int i = 0; i < ACC_PER; ++i) {
-    run += loc[i];
-    if (found_chunk && mine == 0x7fffffff && run > target_t) mine = hit * ACC_CHUNK + tid * ACC_PER + i;
+  if (tok < 0) {
+    // (rounding put the crossing in a segment without weight) the chunk's
+    // last entry with weight
+    int lp = -1;
+    for (int i = lane; i < SMP_CHUNK; i += 64) {
+      const int x = hit * SMP_CHUNK + i;
+      if (x < V && sample_weight(smode, P, pm, pz, Q, qm, qz, x) > 0.0) lp = x;
+    }
+    for (int o = 32; o >= 1; o >>= 1) lp = max(lp, __shfl_xor(lp, o, 64));
+    tok = lp;
   }
-  __syncthreads();
-  if (tid == 0) s_last = -1;
-  __syncthreads();
-  if (mine != 0x7fffffff) atomicMin(&s_pick, mine);
-  if (lastmine >= 0) atomicMax(&s_last, lastmine);
-  __syncthreads();
-  if (tid == 0) {
-    // none crossed (rounding): the last positive entry of the chunk
-    const int tok = s_pick != 0x7fffffff ? s_pick : s_last;
-    for (int i = 0; i < nacc; ++i) out[i] = drafts[s * K + i];
-    out[nacc] = tok;
-    for (int i = nacc + 1; i <= K; ++i) out[i] = -1;
-    out_n[s] = nacc;
-  }
+  if (lane <= K) out[lane] = lane < nacc ? dk : (lane == nacc ? tok : -1);
+  if (lane == 0) out_n[s] = nacc;
 }
 
 hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, float Tp,
@@ -409,17 +530,13 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
                          const float* u, int32_t* out_tokens, int32_t* out_n, void* wsp,
                          hipStream_t s) {
   const AccWs ws = acc_carve(wsp, S, K, V);
-  const int CH = acc_chunks(V);
+  const int CH = acc_chunks(V), CHs = smp_chunks(V);
   hipLaunchKernelGGL(k_acc_stats, dim3(CH, S * (2 * K + 1)), dim3(256), 0, s, S, K, V, target,
                      tkind, Tp, draft, dkind, Tq, ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_acc_chunk, dim3(CH, S), dim3(256), 0, s, S, K, V, target, tkind, Tp, draft,
-                     dkind, Tq, drafts, u, ws);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_acc_pick, dim3(S), dim3(256), 0, s, S, K, V, CH, target, tkind, Tp, draft,
-                     dkind, Tq, drafts, u, out_tokens, out_n, ws);
+  hipLaunchKernelGGL(k_acc_sample, dim3(CHs, S), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind,
+                     Tp, draft, dkind, Tq, drafts, u, out_tokens, out_n, ws);
   return hipGetLastError();
 }
 

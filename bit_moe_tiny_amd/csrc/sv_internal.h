@@ -30,6 +30,69 @@ __device__ __forceinline__ void barrier_lds() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// ------------------------------------------------------ cross-lane moves
+// Wave-wide reductions on the VALU: DPP moves inside 16-lane rows and the
+// permlane16/permlane32 swaps across rows, instead of LDS permutes.
+// xlane<CTRL>(x): lane i takes x from another lane under the DPP control
+// CTRL: 0xB1 quad_perm [1,0,3,2], 0x4E quad_perm [2,3,0,1], 0x141
+// row_half_mirror, 0x140 row_mirror.
+template <int CTRL>
+__device__ __forceinline__ uint32_t xlane(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double xlane(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = xlane<CTRL>((uint32_t)b), hi = xlane<CTRL>((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <int CTRL>
+__device__ __forceinline__ float xlane(float x) {
+  return __builtin_bit_cast(float, xlane<CTRL>(__builtin_bit_cast(uint32_t, x)));
+}
+
+// The permlane swaps pair the even and odd 16-lane rows (SPAN 16) or the two
+// 32-lane halves (SPAN 32): every lane gets (even / low part, odd / high
+// part) of its pair, so op(a, b) is the same expression in all lanes.
+template <int SPAN>
+__device__ __forceinline__ void xswap(uint32_t x, uint32_t& a, uint32_t& b) {
+  const auto r = SPAN == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                            : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  a = r[0];
+  b = r[1];
+}
+template <int SPAN>
+__device__ __forceinline__ void xswap(double x, double& a, double& b) {
+  const uint64_t v = __builtin_bit_cast(uint64_t, x);
+  uint32_t la, lb, ha, hb;
+  xswap<SPAN>((uint32_t)v, la, lb);
+  xswap<SPAN>((uint32_t)(v >> 32), ha, hb);
+  a = __builtin_bit_cast(double, (uint64_t)la | ((uint64_t)ha << 32));
+  b = __builtin_bit_cast(double, (uint64_t)lb | ((uint64_t)hb << 32));
+}
+template <int SPAN>
+__device__ __forceinline__ void xswap(float x, float& a, float& b) {
+  uint32_t ua, ub;
+  xswap<SPAN>(__builtin_bit_cast(uint32_t, x), ua, ub);
+  a = __builtin_bit_cast(float, ua);
+  b = __builtin_bit_cast(float, ub);
+}
+
+// op over the 64 lanes, the result in every lane (bit-identical in all
+// lanes and in every wave: a fixed pairing, commutative op).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+  v = op(v, xlane<0xB1>(v));
+  v = op(v, xlane<0x4E>(v));
+  v = op(v, xlane<0x141>(v));
+  v = op(v, xlane<0x140>(v));
+  T a, b;
+  xswap<16>(v, a, b);
+  v = op(a, b);
+  xswap<32>(v, a, b);
+  return op(a, b);
+}
+
 // s_waitcnt that waits until at most n vector-memory loads are outstanding
 // (n a compile-time constant after inlining), leaving the other counters alone.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {

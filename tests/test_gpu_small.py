@@ -185,3 +185,92 @@ def test_accept_many_sequences_probs(sv):
              else p[s * (K + 1) + K].astype(np.float64))
         assert sample_flag(w, u[s, K]), s
     assert set(np.unique(wn).tolist()) > {0}      # the cases mix accepts and rejects
+
+
+def _check_accept(S, K, V, target, tk, tp, draft, dk, tq, drafts, u, toks, nacc):
+    """GPU outputs against the oracle's: invalid sequences all -1; decisions
+    equal unless the oracle made one inside the flag band; tokens equal
+    unless the sampling target sits on a CDF boundary."""
+    wt, wn = oracle.spec_accept(S, K, V, target, tk, tp, draft, dk, tq, drafts, u)
+    tg = np.asarray(target, np.float32).reshape(S, K + 1, V)
+    dr = np.asarray(draft, np.float32).reshape(S, K, V) if K else None
+
+    def dist(row, kind, t):
+        return oracle.softmax_t(row, t) if kind == LOGITS else row.astype(np.float64)
+
+    for s in range(S):
+        if wn[s] < 0:
+            assert nacc[s] == -1 and np.all(toks[s] == -1), f"sequence {s}: {nacc[s]} {toks[s]}"
+            continue
+        p_rows = [dist(tg[s, i], tk, tp) for i in range(K + 1)]
+        q_rows = [dist(dr[s, i], dk, tq) for i in range(K)]
+        if accept_flags(p_rows, q_rows, drafts[s], u[s], int(wn[s])):
+            continue
+        assert nacc[s] == wn[s], f"sequence {s}: n_accepted {nacc[s]} vs oracle {wn[s]}"
+        if not np.array_equal(toks[s], wt[s]):
+            n = int(wn[s])
+            w = np.maximum(p_rows[n] - q_rows[n], 0.0) if n < K else p_rows[K]
+            if not w.sum() > 0:
+                w = p_rows[n]
+            assert sample_flag(w, u[s, K]), f"sequence {s}: tokens {toks[s]} vs oracle {wt[s]}"
+    return wn
+
+
+def _logit_inputs(key, S, K, V, noise, T):
+    g = synth.generator(key)
+    z = synth.normal(g, S * (K + 1) * V, 2.0).astype(np.float32).reshape(S * (K + 1), V)
+    zq = (z.reshape(S, K + 1, V)[:, :K].reshape(S * K, V).astype(np.float64)
+          + synth.normal(g, S * K * V, noise).reshape(S * K, V)).astype(np.float32)
+    drafts = synth.gumbel_drafts(zq, T, g).reshape(S, K)
+    u = synth.uniform24(g, S * (K + 1)).reshape(S, K + 1)
+    return z, zq, drafts, u
+
+
+def test_accept_bonus_only(sv):
+    """K = 0: one sample from p_0 per sequence (ragged last chunk)."""
+    g = synth.generator(130)
+    S, V = 3, 5000
+    z = synth.normal(g, S * V, 2.0).astype(np.float32).reshape(S, V)
+    u = synth.uniform24(g, S).reshape(S, 1)
+    drafts = np.zeros((S, 0), np.int32)
+    toks, nacc = _run_accept(sv, S, 0, V, z, LOGITS, 0.7, None, LOGITS, 0.7, drafts, u)
+    wn = _check_accept(S, 0, V, z, LOGITS, 0.7, None, LOGITS, 0.7, drafts, u, toks, nacc)
+    assert np.all(wn == 0)
+
+
+def test_accept_invalid_sequences(sv):
+    """A token outside [0, V), a uniform of 1, a NaN draft value and an
+    infinite target value each void their own sequence only."""
+    S, K, V = 5, 3, 4100
+    z, zq, drafts, u = _logit_inputs(131, S, K, V, 1.0, 1.0)
+    drafts[1, 2] = V
+    u[2, 0] = 1.0
+    zq[3 * K + 1, 77] = np.nan
+    z[4 * (K + 1) + K, 5] = np.inf
+    toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 1.0, zq, LOGITS, 1.0, drafts, u)
+    wn = _check_accept(S, K, V, z, LOGITS, 1.0, zq, LOGITS, 1.0, drafts, u, toks, nacc)
+    assert wn[0] >= 0 and np.all(wn[1:] == -1)
+
+
+def test_accept_residual_vanished(sv):
+    """q = p * (1 + 1e-5) as probabilities: a rejection leaves an all-zero
+    residual, so the replacement is sampled from p itself."""
+    g = synth.generator(132)
+    S, K, V = 2, 2, 3000
+    w = np.abs(synth.normal(g, S * (K + 1) * V, 1.0)).reshape(S * (K + 1), V) + 1e-3
+    p = (w / w.sum(1, keepdims=True)).astype(np.float32)
+    q = (p.reshape(S, K + 1, V)[:, :K].reshape(S * K, V) * np.float32(1.00001)).astype(np.float32)
+    assert np.all(q > p.reshape(S, K + 1, V)[:, :K].reshape(S * K, V))
+    drafts = np.array([[5, 9], [11, 13]], np.int32)
+    u = np.array([[0.999995, 0.5, 0.3], [0.1, 0.2, 0.6]], np.float32)
+    toks, nacc = _run_accept(sv, S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    wn = _check_accept(S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u, toks, nacc)
+    assert wn.tolist() == [0, 2]
+
+
+def test_accept_largest_vocabulary(sv):
+    """V = 524,288, the largest vocabulary the library takes (256 chunks)."""
+    S, K, V = 2, 2, 256 * 2048
+    z, zq, drafts, u = _logit_inputs(133, S, K, V, 1.5, 0.8)
+    toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.8, drafts, u)
+    _check_accept(S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.8, drafts, u, toks, nacc)
