@@ -62,13 +62,20 @@ _SIGS = {
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libspecverify.so (raises if it has not been built)."""
+    """Load libspecverify.so (raises if it has not been built).
+
+    torch is imported first: it carries its own HIP runtime under the same
+    soname as the system one, and whichever is loaded first serves the whole
+    process, so the library must bind to the runtime that owns torch's
+    streams and allocations (loaded the other way round, every launch on a
+    torch stream fails)."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m bit_moe_tiny_amd.build` "
                           "(there is no fallback implementation)")
+    import torch  # noqa: F401  (see above)
     lib = ctypes.CDLL(path)
     for name, (args, res) in _SIGS.items():
         fn = getattr(lib, name)
