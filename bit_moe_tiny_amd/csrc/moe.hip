@@ -8,11 +8,14 @@
 //                 expert's weights are read once ("MoE gate_up expert dedup",
 //                 ds4-on-spark README, introduction); the other blocks stage x
 //                 into the fp16 image the two-bit kernels read.
-//   k_q2_gateup   grid (16-row tile of inter, unit, column group), 8 waves:
-//                 gate and up x 4 K-quarters; the unit's rows are copied into
-//                 LDS once per block; the partial sums meet in LDS and one wave
-//                 applies SwiGLU ("fused gate+up+swiglu MoE decode", 1x Spark
-//                 tuned DSpark thread, Q&A answer 3).  h is kept in fp32.
+//   k_q2_gateup_p persistent, 2 blocks per CU of 8 waves (gate and up x 4
+//                 parts of hidden), each block a contiguous range of (work
+//                 item, 16-row tile of inter) with the next item's weight loads
+//                 in flight; the partial sums meet in LDS and one wave applies
+//                 SwiGLU ("fused gate+up+swiglu MoE decode", 1x Spark tuned
+//                 DSpark thread, Q&A answer 3).  h is kept in fp32.
+//   k_q2_gateup   the same per (tile, work item) block, for shapes the
+//                 persistent kernel does not take.
 //   k_q2_down     grid (128-row group of hidden, unit, column group), 8 waves
 //                 of one 16-row tile over all of inter; the block converts its
 //                 h rows into the LDS image itself; per-assignment outputs go
