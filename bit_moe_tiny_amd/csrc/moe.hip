@@ -348,7 +348,7 @@ __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, 
   if (blockIdx.x == 0) {
     route_and_group(logits, R, E, k, has_shared, cg_gu, cg_dn, idx_out, w_out, ws);
   } else {
-    stage_row<DT>(x, blockIdx.x - 1, XL_PERM, ws.x_img, sh);   // one block per row
+    stage_row<DT, PREP_THREADS>(x, blockIdx.x - 1, XL_PERM, ws.x_img, sh);   // one block per row
   }
 }
 

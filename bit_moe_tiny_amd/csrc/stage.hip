@@ -11,13 +11,15 @@
 
 namespace sv {
 
+constexpr int STAGE_THREADS = 256;
+
 template <int DT>
-__global__ __launch_bounds__(256) void k_stage(const void* src, int rows, int layout,
+__global__ __launch_bounds__(STAGE_THREADS) void k_stage(const void* src, int rows, int layout,
                                                const int* n_rows_dev, XImg img) {
-  __shared__ int sh[8];
+  __shared__ int sh[2 * STAGE_THREADS / 64];
   const int n_rows = n_rows_dev ? *n_rows_dev : rows;
   if ((int)blockIdx.x >= n_rows) return;
-  stage_row<DT>(src, blockIdx.x, layout, img, sh);
+  stage_row<DT, STAGE_THREADS>(src, blockIdx.x, layout, img, sh);
 }
 
 hipError_t launch_stage(const void* src, int dtype, int rows, int K, int layout,
@@ -25,10 +27,10 @@ hipError_t launch_stage(const void* src, int dtype, int rows, int K, int layout,
   (void)K;
   if (rows <= 0) return hipSuccess;
   if (dtype == SV_BF16)
-    hipLaunchKernelGGL(k_stage<SV_BF16>, dim3(rows), dim3(256), 0, s, src, rows, layout,
+    hipLaunchKernelGGL(k_stage<SV_BF16>, dim3(rows), dim3(STAGE_THREADS), 0, s, src, rows, layout,
                        n_rows_dev, img);
   else
-    hipLaunchKernelGGL(k_stage<SV_F32>, dim3(rows), dim3(256), 0, s, src, rows, layout,
+    hipLaunchKernelGGL(k_stage<SV_F32>, dim3(rows), dim3(STAGE_THREADS), 0, s, src, rows, layout,
                        n_rows_dev, img);
   return hipGetLastError();
 }

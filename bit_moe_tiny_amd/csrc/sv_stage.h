@@ -1,8 +1,6 @@
 // Device routines that stage activation rows into an XImg (layout and scaling
-// described in sv_internal.h).  One thread block per row: a first pass finds
-// the row's largest magnitude (its power-of-two scale), a second pass converts
-// the row block by block, 32 lanes -- half a wave -- per 256-element block,
-// each lane converting 8 elements.
+// described in sv_internal.h).  One thread block per row, 32 lanes -- half a
+// wave -- per 256-element block, each lane holding 8 elements.
 #pragma once
 
 #include "sv_internal.h"
@@ -45,107 +43,105 @@ __device__ __forceinline__ int row_exponent(float mx, int bad) {
   return esc;
 }
 
-// Largest magnitude of row `src` (K elements) and whether any is non-finite,
-// over the whole thread block.  `sh` holds 2 * (blockDim.x / 64) ints.
-template <int DT>
-__device__ inline int block_row_exponent(const void* src, int K, int* sh) {
-  float mx = 0.f;
-  int bad = 0;
-  for (int i = 4 * threadIdx.x; i < K; i += 4 * blockDim.x) {
-    float v[4];
-    load4_act<DT>(src, (size_t)i, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = fabsf(v[e]);
-      bad |= !(a <= 3.402823466e38f);   // inf or NaN
-      mx = fmaxf(mx, a);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    bad |= __shfl_xor(bad, o, 64);
-  }
-  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    sh[w] = __float_as_int(mx);
-    sh[nw + w] = bad;
-  }
-  __syncthreads();
-  for (int i = 0; i < nw; ++i) {
-    mx = fmaxf(mx, __int_as_float(sh[i]));
-    bad |= sh[nw + i];
-  }
-  return row_exponent(mx, bad);
-}
+constexpr int XIMG_MAX_K = 16384;   // longest row the staging routines take
 
-// Stage block kb of image row `row` from the row's source elements, scaled by
-// 2^esc.  l = lane index within the half-wave (0..31).
-template <int DT>
-__device__ inline void stage_block(const void* src, int row, int kb, int esc, int layout,
-                                   const XImg& img, int l) {
-  const int K = img.K;
-  const int k0 = kb * 256;
-  float v[8];
-  size_t dst;
-  if (layout == XL_PERM) {
-    // lane = chunk (t, g) of the block: element e = 2j + hb <-> k = 16 s + 4 hs + j + 8 hb
-    const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
-    float a[4], b[4];
-    load4_act<DT>(src, k0 + 16 * s + 4 * hs, a);
-    load4_act<DT>(src, k0 + 16 * s + 4 * hs + 8, b);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = a[j];
-      v[2 * j + 1] = b[j];
-    }
-    dst = (size_t)row * K + (size_t)(kb * 32 + l) * 8;
-  } else {
-    const int ka = k0 + 8 * l;
-    if (ka >= K) return;
-    load4_act<DT>(src, ka, v);
-    load4_act<DT>(src, ka + 4, v + 4);
-    dst = (size_t)row * K + ka;
-  }
-  h8_t hv, lv;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int sh = layout == XL_PERM ? esc - 2 * (e >> 1) : esc;   // 4^-j folded in (PERM)
-    _Float16 h, lo;
-    split16(ldexpf(v[e], sh), h, lo);
-    hv[e] = h;
-    lv[e] = lo;
-  }
-  *(h8_t*)(img.hi + dst) = hv;
-  *(h8_t*)(img.lo + dst) = lv;
-  if (layout == XL_PERM && l < 16) {   // sum of sub-block l (the min term)
-    float a[4], acc = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      load4_act<DT>(src, k0 + 16 * l + 4 * q, a);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc += ldexpf(a[i], esc);
-    }
-    _Float16 h, lo;
-    split16(acc, h, lo);
-    _Float16* sp = img.sx + (size_t)row * (K / 8) + (kb * 4 + (l >> 2)) * 8 + (l & 3);
-    sp[0] = h;
-    sp[4] = lo;
-  }
-}
-
-// The whole thread block stages row `row` of src ([rows, K], row-major).
-template <int DT>
+// The whole thread block (NT threads) stages row `row` of src ([rows, K],
+// row-major).  Every element is loaded once, into registers, with all loads
+// in flight together: half-wave h takes 256-element blocks h, h + NT/32, ...
+// (PERM: lane (t, g) holds elements 16 s + 4 hs + j and 16 s + 4 hs + 8 + j,
+// j = 0..3, of sub-block s = 4 g + t/2, hs = t & 1; PLAIN: lane l holds
+// elements 8 l .. 8 l + 7).  The row's largest magnitude is reduced over the
+// block (its power-of-two scale), then each lane converts its own elements;
+// a sub-block's 16-element sum is the lane's 8 plus those of lane l ^ 4.
+template <int DT, int NT>
 __device__ inline void stage_row(const void* src, int row, int layout, const XImg& img, int* sh) {
-  const int K = img.K;
+  constexpr int NHW = NT / 32, MAXB = (XIMG_MAX_K / 256 + NHW - 1) / NHW;
+  const int K = img.K, nbk = (K + 255) / 256;
+  const int l = threadIdx.x & 31, hw = threadIdx.x >> 5;
+  const bool perm = layout == XL_PERM;
+  const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
   const size_t base = (size_t)row * K;
   const void* rs = DT == SV_BF16 ? (const void*)((const uint16_t*)src + base)
                                  : (const void*)((const float*)src + base);
-  const int esc = block_row_exponent<DT>(rs, K, sh);
-  const int nbk = (K + 255) / 256;
-  for (int kb = threadIdx.x >> 5; kb < nbk; kb += blockDim.x >> 5)
-    stage_block<DT>(rs, row, kb, esc, layout, img, threadIdx.x & 31);
+  float v[MAXB][8];
+  float mx = 0.f;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int kb = hw + NHW * i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[i][e] = 0.f;
+    if (kb < nbk) {
+      const int k0 = kb * 256;
+      if (perm) {
+        float a[4], b[4];
+        load4_act<DT>(rs, k0 + 16 * s + 4 * hs, a);
+        load4_act<DT>(rs, k0 + 16 * s + 4 * hs + 8, b);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[i][2 * j] = a[j];
+          v[i][2 * j + 1] = b[j];
+        }
+      } else if (k0 + 8 * l < K) {
+        load4_act<DT>(rs, k0 + 8 * l, v[i]);
+        load4_act<DT>(rs, k0 + 8 * l + 4, v[i] + 4);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float a = fabsf(v[i][e]);
+      bad |= !(a <= 3.402823466e38f);   // inf or NaN
+      mx = fmaxf(mx, a);
+    }
+  mx = wave_allreduce(mx, [](float x, float y) { return fmaxf(x, y); });
+  bad = __any(bad) ? 1 : 0;
+  constexpr int NW = NT / 64;
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh[w] = __float_as_int(mx);
+    sh[NW + w] = bad;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    mx = fmaxf(mx, __int_as_float(sh[i]));
+    bad |= sh[NW + i];
+  }
+  const int esc = row_exponent(mx, bad);
+#pragma unroll
+  for (int i = 0; i < MAXB; ++i) {
+    const int kb = hw + NHW * i;
+    if (kb >= nbk) continue;   // (uniform in the half-wave)
+    const int k0 = kb * 256;
+    if (!perm && k0 + 8 * l >= K) continue;
+    const size_t dst = perm ? base + (size_t)(kb * 32 + l) * 8 : base + k0 + 8 * l;
+    h8_t hv, lv;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int shf = perm ? esc - 2 * (e >> 1) : esc;   // 4^-j folded in (PERM)
+      _Float16 h, lo;
+      split16(ldexpf(v[i][e], shf), h, lo);
+      hv[e] = h;
+      lv[e] = lo;
+      part += ldexpf(v[i][e], esc);
+    }
+    *(h8_t*)(img.hi + dst) = hv;
+    *(h8_t*)(img.lo + dst) = lv;
+    if (perm) {   // sum of sub-block s (the min term): this lane's 8 and lane l ^ 4's
+      const float sum = part + __shfl_xor(part, 4, 32);
+      if (hs == 0) {
+        _Float16 h, lo;
+        split16(sum, h, lo);
+        _Float16* sp = img.sx + (size_t)row * (K / 8) + (kb * 4 + g) * 8 + (t >> 1);
+        sp[0] = h;
+        sp[4] = lo;
+      }
+    }
+  }
   if (threadIdx.x == 0) img.rscale[row] = ldexpf(1.f, -esc);
 }
 
