@@ -320,8 +320,9 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 
 // ---------------------------------------------------------------------------
 // Weights streamed into LDS (block counts a multiple of 16, up to 8 columns;
-// 4 with fp32 inputs).  One block of 8 waves per CU, persistent over tiles:
-// in round r wave w of block b owns tile (r G + b) 8 + w.  K is swept in
+// 4 with fp32 inputs).  Two blocks of 4 waves per CU (each with its own
+// stage barrier, so a slow wave holds up 3 others, not 7), persistent over
+// tiles: in round r wave w of block b owns tile (r G + b) 4 + w.  K is swept in
 // stages of 16 blocks (512 k).  For each stage a wave copies its tile's 16
 // rows x 512 code bytes and 16 x 32 scale bytes into its own LDS buffer with
 // global_load_lds (full 128-byte lines, non-temporal: this is the pattern
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 // stage s+1 is in flight while stage s is computed; one barrier per stage.
 // Code rows are stored rotated by their row index in 16-byte units so that
 // the 16 rows of an MFMA operand read fall in distinct LDS banks.
-constexpr int LD_WAVES = 8;
+constexpr int LD_WAVES = 4;   // two blocks per CU
 constexpr int LD_SB = 16;                                   // blocks (of 32) per stage
 constexpr int LD_WBUF = 16 * LD_SB * 32;                    // code bytes per wave and stage (8 KB)
 constexpr int LD_DBUF = 16 * LD_SB * 2;                     // scale bytes per wave and stage (512)
@@ -351,7 +352,7 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t la) {
 }
 
 template <bool USE_LO>
-__global__ __launch_bounds__(LD_WAVES * 64, 1) void k_q8_lmhead_dma(Q8View W, int R, XImg img, float* logits,
+__global__ __launch_bounds__(LD_WAVES * 64, 2) void k_q8_lmhead_dma(Q8View W, int R, XImg img, float* logits,
                                                                     int ncols) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wv = wave_id();
@@ -475,9 +476,9 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
     }
     const size_t lb = ld_lds_bytes(R, use_lo);
     if (use_lo)
-      hipLaunchKernelGGL((k_q8_lmhead_dma<true>), dim3(ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
+      hipLaunchKernelGGL((k_q8_lmhead_dma<true>), dim3(2 * ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
     else
-      hipLaunchKernelGGL((k_q8_lmhead_dma<false>), dim3(ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
+      hipLaunchKernelGGL((k_q8_lmhead_dma<false>), dim3(2 * ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
     return hipGetLastError();
   }
   // (groups in pairs; windows of LM_WIN_GROUPS groups when K does not fit)
