@@ -320,9 +320,10 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 
 // ---------------------------------------------------------------------------
 // Weights streamed into LDS (block counts a multiple of 16, up to 8 columns;
-// 4 with fp32 inputs).  Two blocks of 4 waves per CU (each with its own
-// stage barrier, so a slow wave holds up 3 others, not 7), persistent over
-// tiles: in round r wave w of block b owns tile (r G + b) 4 + w.  K is swept in
+// 4 with fp32 inputs).  Blocks of LD_WAVES (4 or 8) waves, persistent over
+// tiles: in round r wave w of block b owns tile (r G + b) LD_WAVES + w.  Two
+// 4-wave blocks per CU where both fit in LDS (each with its own stage
+// barrier, so a slow wave holds up 3 others, not 7), else one of 8 waves.  K is swept in
 // stages of 16 blocks (512 k).  For each stage a wave copies its tile's 16
 // rows x 512 code bytes and 16 x 32 scale bytes into its own LDS buffer with
 // global_load_lds (full 128-byte lines, non-temporal: this is the pattern
@@ -331,15 +332,14 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 // stage s+1 is in flight while stage s is computed; one barrier per stage.
 // Code rows are stored rotated by their row index in 16-byte units so that
 // the 16 rows of an MFMA operand read fall in distinct LDS banks.
-constexpr int LD_WAVES = 4;   // two blocks per CU
 constexpr int LD_SB = 16;                                   // blocks (of 32) per stage
 constexpr int LD_WBUF = 16 * LD_SB * 32;                    // code bytes per wave and stage (8 KB)
 constexpr int LD_DBUF = 16 * LD_SB * 2;                     // scale bytes per wave and stage (512)
 constexpr int LD_XRS = LD_SB * 32 + 8;                      // activation row stride (fp16)
 constexpr int LD_XMAX = 8;                                  // columns (hi only; half with lo planes)
 
-static size_t ld_lds_bytes(int ncols, bool use_lo) {
-  return (size_t)LD_WAVES * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
+static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
+  return (size_t)waves * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
 }
 
 __device__ __forceinline__ void dma16(const void* src, uint32_t la) {
@@ -351,9 +351,9 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t la) {
                :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
 }
 
-template <bool USE_LO>
-__global__ __launch_bounds__(LD_WAVES * 64, 2) void k_q8_lmhead_dma(Q8View W, int R, XImg img, float* logits,
-                                                                    int ncols) {
+template <bool USE_LO, int LD_WAVES>
+__global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W, int R, XImg img,
+                                                                               float* logits, int ncols) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wv = wave_id();
   const int vocab = W.n_out, nb = W.nb, K = nb * 32;
@@ -474,11 +474,18 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
           hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
         ncu = 256;
     }
-    const size_t lb = ld_lds_bytes(R, use_lo);
-    if (use_lo)
-      hipLaunchKernelGGL((k_q8_lmhead_dma<true>), dim3(2 * ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
-    else
-      hipLaunchKernelGGL((k_q8_lmhead_dma<false>), dim3(2 * ncu), dim3(LD_WAVES * 64), lb, s, W, R, img, logits, R);
+    // two 4-wave blocks per CU when both fit in the CU's 160 KB of LDS
+    const bool two = 2 * ld_lds_bytes(4, R, use_lo) <= (size_t)160 * 1024;
+    const int waves = two ? 4 : 8;
+    const size_t lb = ld_lds_bytes(waves, R, use_lo);
+    const dim3 grid(two ? 2 * ncu : ncu), block(waves * 64);
+    if (use_lo) {
+      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<true, 4>), grid, block, lb, s, W, R, img, logits, R);
+      else hipLaunchKernelGGL((k_q8_lmhead_dma<true, 8>), grid, block, lb, s, W, R, img, logits, R);
+    } else {
+      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<false, 4>), grid, block, lb, s, W, R, img, logits, R);
+      else hipLaunchKernelGGL((k_q8_lmhead_dma<false, 8>), grid, block, lb, s, W, R, img, logits, R);
+    }
     return hipGetLastError();
   }
   // (groups in pairs; windows of LM_WIN_GROUPS groups when K does not fit)
