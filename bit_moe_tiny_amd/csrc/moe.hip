@@ -146,6 +146,22 @@ __device__ inline float wave_sum(float x) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), 63));
 }
 
+// Inclusive prefix sum over the 64 lanes on the DPP network (row shifts,
+// then the row totals broadcast across rows; lanes with no source add 0).
+template <int CTRL, int ROWS, int BANKS>
+__device__ inline int dpp_z(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, BANKS, true);
+}
+__device__ inline int wave_incl_scan(int x) {
+  x += dpp_z<0x111, 0xF, 0xF>(x);   // row_shr:1
+  x += dpp_z<0x112, 0xF, 0xF>(x);   // row_shr:2
+  x += dpp_z<0x114, 0xF, 0xE>(x);   // row_shr:4
+  x += dpp_z<0x118, 0xF, 0xC>(x);   // row_shr:8
+  x += dpp_z<0x142, 0xA, 0xF>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_z<0x143, 0xC, 0xF>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Order-preserving key of a logit: larger logit -> larger key; NaN -> 0, the
 // smallest (NaN ranks after every number, as in an ascending sort of -logit).
 __device__ inline uint32_t logit_key(float f) {
@@ -220,12 +236,7 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
   for (int u0 = 0; u0 < nu; u0 += 64) {
     const int u = u0 + lane;
     const int ng = u < nu ? (s_ucnt[u] + cg - 1) / cg : 0;
-    int incl = ng;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_incl_scan(ng);
     for (int j = 0; j < ng; ++j) {
       MoeWork w;
       w.expert = s_uexp[u];
@@ -236,7 +247,7 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
       for (int c = 0; c < MOE_WORK_COLS; ++c) w.rows[c] = c < w.ncols ? s_arow[w.a0 + c] : 0;
       work[base + incl - ng + j] = w;
     }
-    base += __shfl(incl, 63, 64);
+    base += __builtin_amdgcn_readlane(incl, 63);
   }
   if (lane == 0) *n_work = base;
 }
@@ -244,14 +255,14 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
                                 int cg_gu, int cg_dn, int32_t* idx_out, float* w_out, MoeWs ws) {
   __shared__ int s_idx[SV_MAX_ROWS * SV_MAX_TOPK];
-  __shared__ int cnt[SV_MAX_EXPERTS];
+  __shared__ unsigned long long s_rmask[SV_MAX_EXPERTS];   // rows that chose expert e (R <= 64)
   __shared__ int eoff[SV_MAX_EXPERTS];
   __shared__ int s_uexp[SV_MAX_EXPERTS + 1], s_uoff[SV_MAX_EXPERTS + 1], s_ucnt[SV_MAX_EXPERTS + 1];
   __shared__ int s_arow[SV_MAX_ROWS * (SV_MAX_TOPK + 1)];
   __shared__ int s_nu;
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   constexpr int NW = PREP_THREADS / 64;
-  for (int e = tid; e < E; e += PREP_THREADS) cnt[e] = 0;
+  for (int e = tid; e < E; e += PREP_THREADS) s_rmask[e] = 0ull;
   if (logits == nullptr) {  // one expert, no router: weight 1
     for (int i = tid; i < R * k; i += PREP_THREADS) {
       s_idx[i] = 0;
@@ -270,22 +281,14 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
     }
   }
   __syncthreads();
-  for (int i = tid; i < R * k; i += PREP_THREADS) atomicAdd(&cnt[s_idx[i]], 1);
+  for (int i = tid; i < R * k; i += PREP_THREADS) atomicOr(&s_rmask[s_idx[i]], 1ull << (i / k));
   __syncthreads();
   if (wv == 0) {  // touched experts in ascending order -> units, assignment offsets
     int base_u = 0, base_a = 0;
     for (int c0 = 0; c0 < E; c0 += 64) {
       const int e = c0 + lane;
-      const int ce = e < E ? cnt[e] : 0;
-      int fu = ce > 0 ? 1 : 0, fa = ce;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int tu = __shfl_up(fu, o, 64), ta = __shfl_up(fa, o, 64);
-        if (lane >= o) {
-          fu += tu;
-          fa += ta;
-        }
-      }
+      const int ce = e < E ? __popcll(s_rmask[e]) : 0;
+      const int fu = wave_incl_scan(ce > 0 ? 1 : 0), fa = wave_incl_scan(ce);
       const int u = base_u + fu - (ce > 0 ? 1 : 0);
       const int a = base_a + fa - ce;
       if (e < E) eoff[e] = a;
@@ -297,8 +300,8 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
         s_uoff[u] = a;
         s_ucnt[u] = ce;
       }
-      base_u += __shfl(fu, 63, 64);
-      base_a += __shfl(fa, 63, 64);
+      base_u += __builtin_amdgcn_readlane(fu, 63);
+      base_a += __builtin_amdgcn_readlane(fa, 63);
     }
     if (lane == 0) s_nu = base_u;
   }
@@ -306,8 +309,8 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   const int nu = s_nu;
   for (int i = tid; i < R * k; i += PREP_THREADS) {
     const int r = i / k, s = i - r * k, e = s_idx[i];
-    int rank = 0;  // rows before r that chose e (each row picks an expert at most once)
-    for (int j = 0; j < r * k; ++j) rank += s_idx[j] == e;
+    // rows before r that chose e (each row picks an expert at most once)
+    const int rank = __popcll(s_rmask[e] & ((1ull << r) - 1ull));
     const int a = eoff[e] + rank;
     ws.arow[a] = r;
     s_arow[a] = r;
