@@ -2,9 +2,28 @@
 // sequencing.  Nothing is enqueued unless every argument checks out.
 #include <math.h>
 
+#include <atomic>
+
 #include "sv_internal.h"
 
 using namespace sv;
+
+namespace sv {
+
+int cu_count() {
+  constexpr int MAX_DEV = 64;
+  static std::atomic<int> cache[MAX_DEV];   // 0 = not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::atomic<int>* slot = dev >= 0 && dev < MAX_DEV ? &cache[dev] : nullptr;
+  int n = slot ? slot->load(std::memory_order_relaxed) : 0;
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (slot) slot->store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace sv
 
 namespace {
 

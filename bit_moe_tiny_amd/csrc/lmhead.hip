@@ -467,13 +467,7 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
                             float* logits, hipStream_t s) {
   const Q8View W = q8_view(w, vocab, hidden);
   if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX / 2 : LD_XMAX)) {
-    static int ncu = 0;
-    if (ncu == 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
-        ncu = 256;
-    }
+    const int ncu = cu_count();
     // two 4-wave blocks per CU when both fit in the CU's 160 KB of LDS
     const bool two = 2 * ld_lds_bytes(4, R, use_lo) <= (size_t)160 * 1024;
     const int waves = two ? 4 : 8;

@@ -824,17 +824,6 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
   }
 }
 
-static int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 static size_t gu_lds(int hidden, bool use_lo, int CG) {
   const size_t x = xl_bytes(CG, hidden, use_lo), red = (size_t)GU_THREADS * 16;
   return x > red ? x : red;
@@ -849,7 +838,7 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, 
   const ExpertPtrs P = expert_ptrs(d);
   const GpCfg c = gp_config(d->hidden, use_lo, R);
   if (c.ok) {
-    const dim3 grid(2 * num_cus()), block(64 * GP_WAVES);
+    const dim3 grid(2 * cu_count()), block(64 * GP_WAVES);
 #define SV_GP(Q)                                                                                   \
   case Q:                                                                                          \
     if (use_lo)                                                                                    \

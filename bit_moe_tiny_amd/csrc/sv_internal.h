@@ -265,6 +265,11 @@ struct MoeWs {
 
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out);
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).  Persistent kernels size their grids with it; any value is correct,
+// only the speed depends on it.
+int cu_count();
+
 // ------------------------------------------------------------- launchers
 // All return hipSuccess or the launch error.
 hipError_t launch_stage(const void* src, int dtype, int rows, int K, int layout,

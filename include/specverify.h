@@ -20,7 +20,8 @@
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
  *    memory, including workspaces; the library never allocates, frees or
- *    synchronises, and keeps no mutable global state.
+ *    synchronises, and keeps no global state beyond a per-device cache of the
+ *    compute-unit count (used to size persistent grids).
  *  - Work is enqueued on `stream` (0 = the null stream).  Calls on different
  *    streams are independent when their workspaces and outputs are distinct.
  *  - Arguments are validated on the host before anything is enqueued; a
