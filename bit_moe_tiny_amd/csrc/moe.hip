@@ -18,8 +18,9 @@
 //                 persistent kernel does not take.
 //   k_q2_down     grid (128-row group of hidden, unit, column group), 8 waves
 //                 of one 16-row tile over all of inter; the block converts its
-//                 h rows into the LDS image itself; per-assignment outputs go
-//                 to the workspace.
+//                 h rows into the LDS image itself (fp16 high part and
+//                 remainder, which enter the products as two tile columns of
+//                 the row); per-assignment outputs go to the workspace.
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
 // Blocks never wait on each other inside a kernel: on a part whose L2 is split
@@ -970,13 +971,13 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hid
     if (tid >= ncols && tid < 16) L.rsc[tid] = 0.f;
     __syncthreads();
   };
-  q2_range_staged<WIDE_D, true>(D, n, 0, nbk, xl_view(L), min(nl, ncols - 1), lane, acc, issue,
-                                sync);
-  const f4_t rsc_c = *(const f4_t*)(L.rsc + 4 * g);
+  // tile column c = row c/2's high part (c even) or remainder (c odd)
+  q2_range_staged<WIDE_D, LO_FOLD>(D, n, 0, nbk, xl_view(L), min(nl >> 1, ncols - 1), lane, acc,
+                                   issue, sync);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * g + i;   // tile column; only 0..ncols-1 are real
-    if (c < ncols) ws.part[(size_t)(a0 + c) * hidden + n] = acc[i] * rsc_c[i];
+  for (int j = 0; j < 2; ++j) {
+    const int c = 2 * g + j;   // lane (n, g) holds tile columns 4g..4g+3: rows 2g, 2g+1
+    if (c < ncols) ws.part[(size_t)(a0 + c) * hidden + n] = (acc[2 * j] + acc[2 * j + 1]) * L.rsc[c];
   }
 }
 

@@ -108,15 +108,6 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 #undef SV_W
 }
 
-// 16-byte load with the non-temporal hint, for weights that are streamed
-// once: on this part such loads sustain a markedly higher read rate than
-// plain ones (they do not displace reusable lines from the caches).
-__device__ __forceinline__ uint4 ld_stream(const void* p) {
-  typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-  const u4v t = __builtin_nontemporal_load((const u4v*)p);
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
 // A global pointer to data that no kernel of this launch writes, in the
 // constant address space: uniform reads through it become scalar loads even
 // in kernels that store to global memory (the compiler cannot otherwise rule

@@ -210,10 +210,21 @@ __device__ __forceinline__ void xpose4(const uint4& v, uint32_t* r) {
   r[3] = d[1];
 }
 
+// How the remainder plane of the activation rows (XL::lo) enters a block:
+//   LO_NONE  not at all (the rows are fp16-exact);
+//   LO_STEP  a second product per step, into the same column;
+//   LO_FOLD  as a column of its own: tile column c holds row c/2's high part
+//            (c even) or its remainder (c odd), so one product per step
+//            covers both and the caller adds the two columns of a row (up to
+//            8 rows).  The min term takes the sums' high parts in even columns
+//            and their remainders in odd ones, one product for both.
+constexpr int LO_NONE = 0, LO_STEP = 1, LO_FOLD = 2;
+
 // acc += one block for this lane's column: xh/xl point at the block's
 // A operands of this lane (step t at +32 t elements), xs at its 4-sub-block
-// sum group.  The row scale is applied by the caller.
-template <bool USE_LO>
+// sum group (LO_FOLD: at the lane's half of it, and xh at its plane).  The
+// row scale is applied by the caller.
+template <int LOM>
 __device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d, float dmin,
                                          const _Float16* xh, const _Float16* xl,
                                          const _Float16* xs, f4_t& acc) {
@@ -225,13 +236,19 @@ __device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d,
   for (int t = 0; t < 8; ++t) {
     const h8_t b = q2_bop(qs, S, t, magic);
     dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + 32 * t), b, dt, 0, 0, 0);
-    if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + 32 * t), b, dt, 0, 0, 0);
+    if (LOM == LO_STEP)
+      dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xl + 32 * t), b, dt, 0, 0, 0);
   }
-  const h8_t sx = *(const h8_t*)xs;
-  const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
-  // the 16-element sums are never fp16-exact: their remainder is always used
-  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, S.m, zero, 0, 0, 0);
-  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, S.m, dm, 0, 0, 0);
+  f4_t dm;
+  if (LOM == LO_FOLD) {
+    dm = __builtin_amdgcn_mfma_f32_16x16x16f16(*(const h4_t*)xs, S.m, zero, 0, 0, 0);
+  } else {
+    const h8_t sx = *(const h8_t*)xs;
+    const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
+    // the 16-element sums are never fp16-exact: their remainder is always used
+    dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, S.m, zero, 0, 0, 0);
+    dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, S.m, dm, 0, 0, 0);
+  }
   const float nd = -dmin;
 #pragma unroll
   for (int e = 0; e < 4; ++e) acc[e] = fmaf(nd, dm[e], fmaf(d, dt[e], acc[e]));
@@ -294,7 +311,7 @@ __device__ __forceinline__ float win_val(const uint32_t* w, int p) {
 }
 
 // Blocks kb0..kb0+NBW-1 given their issued loads.
-template <int NBW, bool WIDE_D, bool USE_LO>
+template <int NBW, bool WIDE_D, int LOM>
 __device__ __forceinline__ void q2_chunk_compute(const Q2View& W, const Q2Chunk<NBW, WIDE_D>& c, int kb0,
                                         int n, const XL& X, int cr, int lane, f4_t& acc) {
   float dF[NBW], mF[NBW];
@@ -331,25 +348,26 @@ __device__ __forceinline__ void q2_chunk_compute(const Q2View& W, const Q2Chunk<
     }
   }
   const int g = lane >> 4;
-  const _Float16* xh = X.hi + (size_t)cr * X.rs + kb0 * 256 + g * 8;
+  const int piece = LOM == LO_FOLD ? (lane & 1) : 0;   // LO_FOLD: odd columns take the remainders
+  const _Float16* xh = X.hi + (size_t)piece * (X.lo - X.hi) + (size_t)cr * X.rs + kb0 * 256 + g * 8;
   const _Float16* xl = X.lo + (size_t)cr * X.rs + kb0 * 256 + g * 8;
-  const _Float16* xs = X.sx + (size_t)cr * X.sxs + kb0 * 32 + g * 8;
+  const _Float16* xs = X.sx + (size_t)cr * X.sxs + kb0 * 32 + g * 8 + 4 * piece;
   uint32_t sct[4];
 #pragma unroll
   for (int i = 0; i < NBW; ++i) {
     if (i % 4 == 0) xpose4(c.sc[i / 4], sct);
-    q2_block<USE_LO>(c.qs[i], sct[i % 4], dF[i], mF[i], xh + 256 * i, xl + 256 * i, xs + 32 * i,
+    q2_block<LOM>(c.qs[i], sct[i % 4], dF[i], mF[i], xh + 256 * i, xl + 256 * i, xs + 32 * i,
                      acc);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int NBW, bool WIDE_D, bool USE_LO>
+template <int NBW, bool WIDE_D, int LOM>
 __device__ __forceinline__ void q2_chunk(const Q2View& W, int n, int kb0, const XL& X, int cr, int lane,
                                 f4_t& acc) {
   Q2Chunk<NBW, WIDE_D> c;
   q2_chunk_load<NBW, WIDE_D>(W, n, kb0, lane >> 4, c);
-  q2_chunk_compute<NBW, WIDE_D, USE_LO>(W, c, kb0, n, X, cr, lane, acc);
+  q2_chunk_compute<NBW, WIDE_D, LOM>(W, c, kb0, n, X, cr, lane, acc);
 }
 
 // Length of the chunk starting at kb with `left` blocks to go: at most WB,
@@ -360,20 +378,20 @@ __device__ __forceinline__ int q2_chunk_len(int kb, int left) {
 }
 
 // Blocks [kb0, kb1) of row n, chunk by chunk.
-template <bool WIDE_D, bool USE_LO>
+template <bool WIDE_D, int LOM>
 __device__ __forceinline__ void q2_range(const Q2View& W, int n, int kb0, int kb1, const XL& X, int cr,
                                 int lane, f4_t& acc) {
   for (int kb = kb0; kb < kb1;) {
     const int len = q2_chunk_len<WIDE_D>(kb, kb1 - kb);
     switch (len) {
-      case 1: q2_chunk<1, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 2: q2_chunk<2, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 3: q2_chunk<3, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 4: q2_chunk<4, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 5: q2_chunk<5, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 6: q2_chunk<6, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      case 7: q2_chunk<7, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
-      default: q2_chunk<8, WIDE_D, USE_LO>(W, n, kb, X, cr, lane, acc); break;
+      case 1: q2_chunk<1, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 2: q2_chunk<2, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 3: q2_chunk<3, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 4: q2_chunk<4, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 5: q2_chunk<5, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 6: q2_chunk<6, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      case 7: q2_chunk<7, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
+      default: q2_chunk<8, WIDE_D, LOM>(W, n, kb, X, cr, lane, acc); break;
     }
     kb += len;
   }
@@ -393,7 +411,7 @@ constexpr int q2_chunk_nloads() {
 // loads are issued, then `sync(n)` (n = the number of weight loads issued
 // after issue()'s, so it can wait for exactly its own; it ends in a block
 // barrier), then the blocks are computed.  Every wave calls both exactly once.
-template <bool WIDE_D, bool USE_LO, typename F, typename G>
+template <bool WIDE_D, int LOM, typename F, typename G>
 __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0, int kb1,
                                                 const XL& X, int cr, int lane, f4_t& acc,
                                                 F&& issue, G&& sync) {
@@ -406,7 +424,7 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
     Q2Chunk<L, WIDE_D> c;                                               \
     q2_chunk_load<L, WIDE_D>(W, n, kb0, g, c);                          \
     sync(q2_chunk_nloads<L, WIDE_D>());                                 \
-    q2_chunk_compute<L, WIDE_D, USE_LO>(W, c, kb0, n, X, cr, lane, acc); \
+    q2_chunk_compute<L, WIDE_D, LOM>(W, c, kb0, n, X, cr, lane, acc);    \
     break;                                                              \
   }
   switch (len) {
@@ -421,7 +439,7 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
     default: sync(0); return;   // empty range
   }
 #undef SV_STAGED_CASE
-  q2_range<WIDE_D, USE_LO>(W, n, kb0 + len, kb1, X, cr, lane, acc);
+  q2_range<WIDE_D, LOM>(W, n, kb0 + len, kb1, X, cr, lane, acc);
 }
 
 // Block barrier that does not wait for outstanding vector-memory loads (the
