@@ -90,7 +90,7 @@ constexpr int DN_THREADS = 512;   // down: 8 waves, one 16-row tile each, all of
 constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave
 
 struct GpCfg;
-static GpCfg gp_config(int hidden, bool use_lo, int R);
+static GpCfg gp_config(int hidden, int inter, bool use_lo, int R);
 
 static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo);
 
@@ -562,10 +562,11 @@ struct GpCfg {
 // blocks); the part's values start at half (kb0 & 1) of it.
 __host__ __device__ constexpr int gp_dw(int nq) { return (nq + (nq & 1) + 1) / 2; }
 
-static GpCfg gp_config(int hidden, bool use_lo, int R) {
+static GpCfg gp_config(int hidden, int inter, bool use_lo, int R) {
   GpCfg c{};
   const int nb = hidden / 256;
   if (hidden % 256 != 0 || nb % GP_PARTS != 0) return c;
+  if ((size_t)inter * nb * 64 >= ((size_t)1 << 31)) return c;   // 32-bit load offsets (gp_load)
   c.nq = nb / GP_PARTS;
   if (c.nq < 1 || c.nq > 8) return c;
   const int dw = gp_dw(c.nq);
@@ -599,14 +600,18 @@ struct GpHalf {
   uint32_t dd[DW > 0 ? DW : 1];
 };
 
+// (32-bit offsets from the planes' uniform bases: the loads take a scalar
+// base and one offset register; the host keeps every plane under 2^31 bytes
+// for the kernels that use this)
 template <int NQ, bool FIRST>
 __device__ __forceinline__ void gp_load(const Q2View& W, size_t rb, int kb0, int g,
                                         GpHalf<NQ, FIRST>& h) {
   using H = GpHalf<NQ, FIRST>;
+  const uint32_t r0 = (uint32_t)rb;
   const int b0 = kb0 + (FIRST ? 0 : H::N0);
-  if (H::SC) h.sc = *(const uint4*)(W.sc + (rb + min(b0 + g, W.nb - 1)) * 16);
+  if (H::SC) h.sc = *(const uint4*)(W.sc + (r0 + (uint32_t)min(b0 + g, W.nb - 1)) * 16u);
   if (H::DW > 0) {
-    const uint16_t* dp = ((g & 1) ? W.dm : W.d) + rb + (kb0 & ~1);
+    const uint16_t* dp = ((g & 1) ? W.dm : W.d) + (r0 + (uint32_t)(kb0 & ~1));
     if (H::DW == 1) {
       h.dd[0] = *(const uint32_t*)dp;
     } else if (H::DW == 2) {
@@ -626,8 +631,9 @@ __device__ __forceinline__ void gp_load(const Q2View& W, size_t rb, int kb0, int
       h.dd[3] = v.w;
     }
   }
+  const uint8_t* q = W.qs + ((r0 + (uint32_t)b0) * 64u + 16u * (uint32_t)g);
 #pragma unroll
-  for (int i = 0; i < H::N; ++i) h.qs[i] = *(const uint4*)(W.qs + (rb + b0 + i) * 64 + 16 * g);
+  for (int i = 0; i < H::N; ++i) h.qs[i] = *(const uint4*)(q + 64 * i);
 }
 
 template <bool USE_LO, int NQ>
@@ -831,13 +837,13 @@ static size_t gu_lds(int hidden, bool use_lo, int CG) {
 }
 
 static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo) {
-  const GpCfg c = gp_config(d->hidden, use_lo, R);
+  const GpCfg c = gp_config(d->hidden, d->inter, use_lo, R);
   return c.ok ? c.cols : col_group(d->hidden, use_lo, R);
 }
 
 hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, hipStream_t s) {
   const ExpertPtrs P = expert_ptrs(d);
-  const GpCfg c = gp_config(d->hidden, use_lo, R);
+  const GpCfg c = gp_config(d->hidden, d->inter, use_lo, R);
   if (c.ok) {
     const dim3 grid(2 * cu_count()), block(64 * GP_WAVES);
 #define SV_GP(Q)                                                                                   \
