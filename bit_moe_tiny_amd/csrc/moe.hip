@@ -16,11 +16,13 @@
 //                 DSpark thread, Q&A answer 3).  h is kept in fp32.
 //   k_q2_gateup   the same per (tile, work item) block, for shapes the
 //                 persistent kernel does not take.
-//   k_q2_down     grid (128-row group of hidden, unit, column group), 8 waves
-//                 of one 16-row tile over all of inter; the block converts its
-//                 h rows into the LDS image itself (fp16 high part and
-//                 remainder, which enter the products as two tile columns of
-//                 the row); per-assignment outputs go to the workspace.
+//   k_q2_down     grid (128-row group of hidden, unit, column group of at
+//                 most 4 rows), 8 waves of one 16-row tile over all of inter,
+//                 on the int8 matrix cores: the block converts its h rows into
+//                 four fixed-point byte digits each (four tile columns per
+//                 row) in LDS, the weights enter as the bytes sc * q, every
+//                 block product is exact; per-assignment outputs go to the
+//                 workspace.
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
 // Blocks never wait on each other inside a kernel: on a part whose L2 is split
@@ -87,7 +89,8 @@ static int col_group(int K, bool use_lo, int R) {
 }
 
 constexpr int DN_THREADS = 512;   // down: 8 waves, one 16-row tile each, all of inter
-constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave
+constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave, at most
+constexpr int DN_MAX_ROWS = 4;    // rows of a down descriptor: one int8 tile of 4 digit columns each
 
 struct GpCfg;
 static GpCfg gp_config(int hidden, int inter, bool use_lo, int R);
@@ -95,7 +98,9 @@ static GpCfg gp_config(int hidden, int inter, bool use_lo, int R);
 static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo);
 
 static int down_cols(const sv_moe_desc* d, int R) {
-  int cg = col_group(d->inter, true, R);
+  int cg = DN_MAX_ROWS;
+  while (cg > 1 && xl8_bytes(cg, d->inter) > (size_t)LDS_BUDGET) --cg;
+  cg = cg < R ? cg : R;
   const int pair_cap = DN_PAIRS * (DN_THREADS / 32) / (d->inter / 256);
   if (cg > pair_cap) cg = pair_cap > 0 ? pair_cap : 1;
   return cg;
@@ -877,125 +882,176 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, 
 
 // ------------------------------------------------------------------ down
 
-// The block's h rows are read into registers before the weight loads are
-// issued (so their wait does not include the weights), then converted into
-// the LDS image: each row scaled by its own power of two, one half-wave per
-// (row, 256-block) pair, at most DN_PAIRS pairs per half-wave.
-template <bool WIDE_D>
-__global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter,
-                                                           MoeWs ws) {
+// h rows of a down descriptor into the int8 image (sv_q2.h, int8 form):
+// half-wave hw converts the (row, 256-block) pairs hw, hw + 16, ... (at most
+// PAIRS); lane l of a pair takes sub-block l/2, element positions j = 2(l&1)
+// and 2(l&1) + 1, at b = 0..3 (elements 16 sb + 4b + j), so that it writes
+// whole dwords of each digit plane.
+template <int PAIRS>
+struct DnH8 {
+  float2 v[PAIRS][4];
+};
+
+template <int PAIRS>
+__device__ __forceinline__ void dn8_h_load(const float* h, int a0, int ncols, int inter, DnH8<PAIRS>& v) {
+  const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
+  const int sb = l >> 1, jh = l & 1;
+  const int nbk = inter / 256, npairs = ncols * nbk;
+#pragma unroll
+  for (int i = 0; i < PAIRS; ++i) {
+    const int p = hw + (DN_THREADS / 32) * i;
+    if (p < npairs) {
+      const int c = p / nbk, kb = p - c * nbk;
+      const float* src = h + (size_t)(a0 + c) * inter + kb * 256 + 16 * sb + 2 * jh;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v.v[i][b] = *(const float2*)(src + 4 * b);
+    }
+  }
+}
+
+// Signed byte with the low 8 bits of x (sign-extended).
+__device__ __forceinline__ int sbyte(int x) { return (x << 24) >> 24; }
+
+template <int PAIRS>
+__device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _Float16* sx, float* csc, int ncols,
+                                              int inter, int* s_max) {
+  const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
+  const int sb = l >> 1, jh = l & 1;
+  const int nbk = inter / 256, npairs = ncols * nbk;
+  const int rs = inter + 16, sxs = inter / 16;
+#pragma unroll
+  for (int i = 0; i < PAIRS; ++i) {   // per-pair maxima
+    const int p = hw + (DN_THREADS / 32) * i;
+    if (p < npairs) {
+      float mx = 0.f;
+      int bad = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float x0 = fabsf(v.v[i][b].x), x1 = fabsf(v.v[i][b].y);
+        bad |= !(x0 <= 3.402823466e38f) | !(x1 <= 3.402823466e38f);
+        mx = fmaxf(mx, fmaxf(x0, x1));
+      }
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+        bad |= __shfl_xor(bad, o, 32);
+      }
+      if (l == 0) {
+        s_max[2 * p] = __float_as_int(mx);
+        s_max[2 * p + 1] = bad;
+      }
+    }
+  }
+  barrier_lds();   // (LDS only: the weight loads in flight are not waited for)
+#pragma unroll
+  for (int i = 0; i < PAIRS; ++i) {   // digits
+    const int p = hw + (DN_THREADS / 32) * i;
+    if (p < npairs) {
+      const int c = p / nbk, kb = p - c * nbk;
+      float mx = 0.f;
+      int bad = 0;
+      for (int j = 0; j < nbk; ++j) {
+        mx = fmaxf(mx, __int_as_float(s_max[2 * (c * nbk + j)]));
+        bad |= s_max[2 * (c * nbk + j) + 1];
+      }
+      // |h| 2^e < 2^29: the leading digit stays within +-65
+      int e = 0;
+      if (mx > 0.f && !bad) {
+        int E;
+        frexpf(mx, &E);   // mx in [2^(E-1), 2^E)
+        e = min(max(29 - E, -120), 120);
+      }
+      uint32_t w[4][2];   // [digit][j - 2 jh]
+      int ps[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) w[d][jj] = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float x = jj == 0 ? v.v[i][b].x : v.v[i][b].y;
+          const int a = bad ? 0 : (int)rintf(ldexpf(x, e));
+          const int p3 = sbyte(a), a1 = (a - p3) >> 8;
+          const int p2 = sbyte(a1), a2 = (a1 - p2) >> 8;
+          const int p1 = sbyte(a2), p0 = (a2 - p1) >> 8;
+          const int dg[4] = {p0, p1, p2, p3};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            w[d][jj] |= ((uint32_t)dg[d] & 0xFFu) << (8 * b);
+            ps[d] += dg[d];
+          }
+        }
+      }
+      // plane byte kb*256 + 64 t + 16 g + 4 j + b for sub-block sb = 4 g + t
+      const int off = kb * 256 + 64 * (sb & 3) + 16 * (sb >> 2) + 8 * jh;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        *(uint2*)(q + (size_t)(4 * c + d) * rs + off) = make_uint2(w[d][0], w[d][1]);
+        const int tot = ps[d] + __shfl_xor(ps[d], 1, 32);   // the partner lane's j
+        if (jh == 0) sx[(size_t)(4 * c + d) * sxs + kb * 16 + sb] = (_Float16)(float)tot;
+      }
+      if (kb == 0 && l < 4)
+        csc[4 * c + l] = bad ? __builtin_nanf("") : ldexpf(1.f, 24 - 8 * l - e);
+    }
+  }
+  for (int c = tid; c < 16; c += blockDim.x)
+    if (c >= 4 * ncols) csc[c] = 0.f;
+  barrier_lds();   // (LDS only: the weight loads in flight are not waited for)
+}
+
+// Down projection on the int8 matrix cores: one block per (128-row group of
+// hidden, descriptor of at most 4 rows), 8 waves of one 16-row tile over all
+// of inter; the block's h rows are read into registers before the weight
+// loads and converted into the LDS image (fixed-point digits, sv_q2.h).
+template <bool WIDE_D, int PAIRS>
+__global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_max[2 * DN_PAIRS * (DN_THREADS / 32)];   // per pair: max bits, bad flag
+  __shared__ int s_max[2 * PAIRS * (DN_THREADS / 32)];   // per pair: max bits, bad flag
   const int nwork = ws.meta->n_work_dn;
   const MoeWork wk = ws.work_dn[blockIdx.y];   // in bounds for every launched block
   if ((int)blockIdx.y >= nwork) return;
   const int e = wk.expert, a0 = wk.a0, ncols = wk.ncols;
-  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
+  const int lane = threadIdx.x & 63, wv = wave_id();
   const int nl = lane & 15, g = lane >> 4;
   const int n = (blockIdx.x * 8 + wv) * 16 + nl;
   const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
-  const XLw L = xl_make(lds, ncols, inter, true);
-  const int nbk = inter / 256, npairs = ncols * nbk;
-  const int l = tid & 31, hw = tid >> 5;
-  const int t = l >> 2, gg = l & 3, sb = 4 * gg + (t >> 1), hs = t & 1;
-  float4 pa[DN_PAIRS], pb[DN_PAIRS];
+  int8_t* q;
+  _Float16* sx;
+  float* csc;
+  xl8_carve(lds, ncols, inter, q, sx, csc);
+  XL8 X;
+  X.q = q;
+  X.sx = sx;
+  X.csc = csc;
+  X.rs = inter + 16;
+  X.sxs = inter / 16;
+  DnH8<PAIRS> hv;
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto issue = [&]() {
-#pragma unroll
-    for (int i = 0; i < DN_PAIRS; ++i) {
-      const int p = hw + (DN_THREADS / 32) * i;
-      if (p < npairs) {
-        const int c = p / nbk, kb = p - c * nbk;
-        const float* src = ws.h + (size_t)(a0 + c) * inter + kb * 256 + 16 * sb + 4 * hs;
-        pa[i] = *(const float4*)src;
-        pb[i] = *(const float4*)(src + 8);
-      }
-    }
-  };
-  auto sync = [&](int) {
-#pragma unroll
-    for (int i = 0; i < DN_PAIRS; ++i) {   // per-pair maxima
-      const int p = hw + (DN_THREADS / 32) * i;
-      if (p < npairs) {
-        const float a8[8] = {pa[i].x, pa[i].y, pa[i].z, pa[i].w, pb[i].x, pb[i].y, pb[i].z, pb[i].w};
-        float mx = 0.f;
-        int bad = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float av = fabsf(a8[k]);
-          bad |= !(av <= 3.402823466e38f);
-          mx = fmaxf(mx, av);
-        }
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) {
-          mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-          bad |= __shfl_xor(bad, o, 32);
-        }
-        if (l == 0) {
-          s_max[2 * p] = __float_as_int(mx);
-          s_max[2 * p + 1] = bad;
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < DN_PAIRS; ++i) {   // convert
-      const int p = hw + (DN_THREADS / 32) * i;
-      if (p < npairs) {
-        const int c = p / nbk, kb = p - c * nbk;
-        float mx = 0.f;
-        int bad = 0;
-        for (int j = 0; j < nbk; ++j) {
-          mx = fmaxf(mx, __int_as_float(s_max[2 * (c * nbk + j)]));
-          bad |= s_max[2 * (c * nbk + j) + 1];
-        }
-        const int esc = row_exponent(mx, bad);
-        const float v[8] = {pa[i].x, pb[i].x, pa[i].y, pb[i].y, pa[i].z, pb[i].z, pa[i].w, pb[i].w};
-        h8_t hv, lv;
-        float part = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float sv = ldexpf(v[k], esc - 2 * (k >> 1));   // 4^-j folded in
-          const _Float16 h = (_Float16)sv;
-          hv[k] = h;
-          lv[k] = (_Float16)(sv - (float)h);
-          part += ldexpf(v[k], esc);
-        }
-        const size_t dst = (size_t)c * L.rs + (size_t)(kb * 32 + l) * 8;
-        *(h8_t*)(L.hi + dst) = hv;
-        *(h8_t*)(L.lo + dst) = lv;
-        const float sum = part + __shfl_xor(part, 4, 32);   // the other half of sub-block sb
-        if (hs == 0) {
-          const _Float16 h = (_Float16)sum;
-          _Float16* sp = L.sx + (size_t)c * L.sxs + (kb * 4 + gg) * 8 + (t >> 1);
-          sp[0] = h;
-          sp[4] = (_Float16)(sum - (float)h);
-        }
-        if (kb == 0 && l == 0) L.rsc[c] = ldexpf(1.f, -esc);
-      }
-    }
-    if (tid >= ncols && tid < 16) L.rsc[tid] = 0.f;
-    __syncthreads();
-  };
-  // tile column c = row c/2's high part (c even) or remainder (c odd)
-  q2_range_staged<WIDE_D, LO_FOLD>(D, n, 0, nbk, xl_view(L), min(nl >> 1, ncols - 1), lane, acc,
-                                   issue, sync);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = 2 * g + j;   // lane (n, g) holds tile columns 4g..4g+3: rows 2g, 2g+1
-    if (c < ncols) ws.part[(size_t)(a0 + c) * hidden + n] = (acc[2 * j] + acc[2 * j + 1]) * L.rsc[c];
+  q2_range_staged_i8<WIDE_D>(
+      D, n, 0, inter / 256, X, ncols, lane, acc, [&]() { dn8_h_load(ws.h, a0, ncols, inter, hv); },
+      [&](int) { dn8_h_convert(hv, q, sx, csc, ncols, inter, s_max); });
+  // lane (n, g) holds tile columns 4g..4g+3: the four digits of row g
+  if (g < ncols) {
+    const f4_t sc = *(const f4_t*)(csc + 4 * g);
+    ws.part[(size_t)(a0 + g) * hidden + n] = ((sc[0] * acc[0] + sc[1] * acc[1]) + sc[2] * acc[2]) + sc[3] * acc[3];
   }
 }
 
 hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const int CG = down_cols(d, R);
+  const int CG = down_cols(d, R), nbk = d->inter / 256;
   const dim3 grid(d->hidden / 128, ws.max_work, 1);
-  const size_t lb = xl_bytes(CG, d->inter, true);
   const ExpertPtrs P = expert_ptrs(d);
-  if (q2_wide_d(d->inter / 256))
-    hipLaunchKernelGGL(k_q2_down<true>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws);
-  else
-    hipLaunchKernelGGL(k_q2_down<false>, grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws);
+  const size_t lb = xl8_bytes(CG, d->inter);
+  // staging registers for 2 (row, block) pairs per half-wave when that covers the rows
+  const bool wide = q2_wide_d(nbk), few = CG * nbk <= 2 * (DN_THREADS / 32);
+#define SV_DN(WD, PR) \
+  hipLaunchKernelGGL((k_q2_down<WD, PR>), grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws)
+  if (wide) {
+    if (few) SV_DN(true, 2); else SV_DN(true, DN_PAIRS);
+  } else {
+    if (few) SV_DN(false, 2); else SV_DN(false, DN_PAIRS);
+  }
+#undef SV_DN
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_moe_combine(d, R, ws, y, s);

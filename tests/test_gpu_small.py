@@ -96,7 +96,8 @@ def _small_moe(E, hidden, inter, shared, seed):
     (32, 8, 1024, 256, 16, True, "bf16"),
     (4, 4, 256, 256, 20, True, "bf16"),
     (12, 3, 768, 1024, 7, True, "bf16"),    # down: 4 blocks per row, 6 row groups
-    (6, 2, 1280, 1536, 9, True, "f32"),     # down: 6 blocks per row; shared expert in 2 column groups
+    (6, 2, 1280, 1536, 9, True, "f32"),     # down: 6 blocks per row; shared expert in 3 column groups
+    (2, 1, 256, 9216, 3, True, "f32"),      # down: 36 blocks per row, one row per column group
 ])
 def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
     (g, u, d), (sg, su, sd) = _small_moe(E, hidden, inter, shared, 104 + E)
