@@ -798,8 +798,7 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
     issue1(h1);
     if (one) {
       // the row's total over its 4 lanes (g = 0..3), as column 0 of lane-row 0
-      ac += __shfl_xor(ac, 16, 64);
-      ac += __shfl_xor(ac, 32, 64);
+      ac = rows_sum(ac);
       acc[0] = g == 0 ? ac : 0.f;
     }
     // partial sums of item i meet in buffer i & 1
@@ -931,11 +930,8 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
         bad |= !(x0 <= 3.402823466e38f) | !(x1 <= 3.402823466e38f);
         mx = fmaxf(mx, fmaxf(x0, x1));
       }
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) {
-        mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-        bad |= __shfl_xor(bad, o, 32);
-      }
+      mx = half_allreduce(mx, [](float a, float b) { return fmaxf(a, b); });
+      bad = (int)half_allreduce((uint32_t)bad, [](uint32_t a, uint32_t b) { return a | b; });
       if (l == 0) {
         s_max[2 * p] = __float_as_int(mx);
         s_max[2 * p + 1] = bad;
@@ -987,7 +983,7 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         *(uint2*)(q + (size_t)(4 * c + d) * rs + off) = make_uint2(w[d][0], w[d][1]);
-        const int tot = ps[d] + __shfl_xor(ps[d], 1, 32);   // the partner lane's j
+        const int tot = ps[d] + (int)xlane<0xB1>((uint32_t)ps[d]);   // the partner lane's j
         if (jh == 0) sx[(size_t)(4 * c + d) * sxs + kb * 16 + sb] = (_Float16)(float)tot;
       }
       if (kb == 0 && l < 4)

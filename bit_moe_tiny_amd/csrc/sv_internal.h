@@ -93,6 +93,29 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
   return op(a, b);
 }
 
+// op over each 32-lane half of the wave, the result in every lane of the half
+// (the same pairing in every half: bit-identical there).
+template <typename T, typename Op>
+__device__ __forceinline__ T half_allreduce(T v, Op op) {
+  v = op(v, xlane<0xB1>(v));
+  v = op(v, xlane<0x4E>(v));
+  v = op(v, xlane<0x141>(v));
+  v = op(v, xlane<0x140>(v));
+  T a, b;
+  xswap<16>(v, a, b);
+  return op(a, b);
+}
+
+// Sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows), in
+// every lane: (x0 + x1) + (x2 + x3).
+__device__ __forceinline__ float rows_sum(float v) {
+  float a, b;
+  xswap<16>(v, a, b);
+  v = a + b;
+  xswap<32>(v, a, b);
+  return a + b;
+}
+
 // s_waitcnt that waits until at most n vector-memory loads are outstanding
 // (n a compile-time constant after inlining), leaving the other counters alone.
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
