@@ -119,7 +119,9 @@ def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
 
 # ------------------------------------------------------------ lm head
 @pytest.mark.parametrize("vocab,hidden,R,dt", [(1000, 1024, 5, "bf16"), (77, 256, 3, "f32"),
-                                              (4096, 7168, 16, "bf16"), (33, 32, 40, "f32")])
+                                              (4096, 7168, 16, "bf16"), (33, 32, 40, "f32"),
+                                              (1999, 1024, 1, "f32"), (3001, 2048, 4, "bf16"),
+                                              (517, 3072, 2, "f32"), (700, 1024, 7, "bf16")])
 def test_small_lm_head(sv, vocab, hidden, R, dt):
     p = synth.q8_random(synth.generator(107, vocab, hidden), vocab, hidden, 0.01)
     buf = p.packed()
