@@ -207,6 +207,10 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
   for (int i = 0; i < PER; ++i)
     if (!(taken >> i & 1)) sum += expf(v[i] - mx);
   sum = wave_sum(sum);
+  // k rounds of (largest key, then the lowest index holding it); lane s keeps
+  // the s-th choice, and all k are written together afterwards
+  uint32_t my_key = 0;
+  int my_idx = 0;
   for (int s = 0; s < k; ++s) {
     uint32_t lk = 0;
 #pragma unroll
@@ -221,14 +225,18 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if (lane + 64 * i == bi) taken |= 1u << i;
-    if (lane == 0) {
-      const float w = expf(key_logit(gk) - mx) / sum;
-      s_idx[r * k + s] = bi;
-      ws.topk_idx[r * k + s] = bi;
-      ws.topk_w[r * k + s] = w;
-      if (idx_out) idx_out[r * k + s] = bi;
-      if (w_out) w_out[r * k + s] = w;
+    if (lane == s) {
+      my_key = gk;
+      my_idx = bi;
     }
+  }
+  if (lane < k) {
+    const float w = expf(key_logit(my_key) - mx) / sum;
+    s_idx[r * k + lane] = my_idx;
+    ws.topk_idx[r * k + lane] = my_idx;
+    ws.topk_w[r * k + lane] = w;
+    if (idx_out) idx_out[r * k + lane] = my_idx;
+    if (w_out) w_out[r * k + lane] = w;
   }
 }
 
