@@ -124,16 +124,6 @@ __device__ inline uint32_t wave_umax(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-__device__ inline uint32_t wave_umin(uint32_t v) {
-  v = min(v, dpp_u32<0x111, 0xF>(v));
-  v = min(v, dpp_u32<0x112, 0xF>(v));
-  v = min(v, dpp_u32<0x114, 0xF>(v));
-  v = min(v, dpp_u32<0x118, 0xF>(v));
-  v = min(v, dpp_u32<0x142, 0xA>(v));
-  v = min(v, dpp_u32<0x143, 0xC>(v));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // Sum in a fixed order (run-to-run identical): zeros are shifted in at row
 // edges and into the rows a broadcast step leaves alone.
 template <int CTRL, int ROWS>
@@ -217,11 +207,14 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
     for (int i = 0; i < PER; ++i)
       if (!(taken >> i & 1)) lk = max(lk, key[i]);
     const uint32_t gk = wave_umax(lk);
-    uint32_t li = 0xFFFFFFFFu;
+    // the lowest index holding gk: the first slot i with a match, then the
+    // lowest lane (index = lane + 64 i), from one ballot per slot
+    int bi = -1;
 #pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (!(taken >> i & 1) && key[i] == gk) li = min(li, (uint32_t)(lane + 64 * i));
-    const int bi = (int)wave_umin(li);
+    for (int i = 0; i < PER; ++i) {
+      const unsigned long long m = __ballot(!(taken >> i & 1) && key[i] == gk);
+      if (bi < 0 && m) bi = 64 * i + (int)__builtin_ctzll(m);
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i)
       if (lane + 64 * i == bi) taken |= 1u << i;
