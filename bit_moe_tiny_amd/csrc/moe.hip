@@ -60,6 +60,7 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.topk_idx = (int*)take(sizeof(int) * R * k);
   w.topk_w = (float*)take(sizeof(float) * R * k);
   w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
+  w.hmax = (uint32_t*)take(sizeof(uint32_t) * max_assign);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
   // column groups of at least one column: at most one item per unit plus one
   // per further column
@@ -170,6 +171,18 @@ __device__ inline float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Raises hmax[a] to |v| (bits; non-negative floats order as unsigned) with the
+// largest value over the lane's 16-lane row: every lane of the row calls it
+// (v = 0 where it has no value), lane 0 of the row does the atomic.
+__device__ inline void note_hmax(uint32_t* hmax, int a, float v, bool any) {
+  uint32_t m = __float_as_uint(fabsf(v));
+  m = max(m, xlane<0xB1>(m));
+  m = max(m, xlane<0x4E>(m));
+  m = max(m, xlane<0x141>(m));
+  m = max(m, xlane<0x140>(m));
+  if (any && (__lane_id() & 15) == 0) atomicMax(hmax + a, m);
+}
+
 // ---------------------------------------------------------------- routing
 constexpr int PREP_THREADS = 1024;
 
@@ -270,6 +283,7 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   constexpr int NW = PREP_THREADS / 64;
   for (int e = tid; e < E; e += PREP_THREADS) s_rmask[e] = 0ull;
+  for (int a = tid; a < ws.max_assign; a += PREP_THREADS) ws.hmax[a] = 0u;   // gate/up raises them
   if (logits == nullptr) {  // one expert, no router: weight 1
     for (int i = tid; i < R * k; i += PREP_THREADS) {
       s_idx[i] = 0;
@@ -533,11 +547,15 @@ __global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int h
   const f4_t us = ((red[256 + lane] + red[320 + lane]) + red[384 + lane]) + red[448 + lane];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = 4 * g + i;
-    if (c >= ncols) continue;
-    const float rs = ws.x_img.rscale[rows[c]];
-    const float gv = gs[i] * rs, uv = us[i] * rs;
-    ws.h[(size_t)(a0 + c) * inter + n] = gv / (1.f + expf(-gv)) * uv;
+    const int c = 4 * g + i;   // (uniform in the lane's 16-lane row)
+    float hv = 0.f;
+    if (c < ncols) {
+      const float rs = ws.x_img.rscale[rows[c]];
+      const float gv = gs[i] * rs, uv = us[i] * rs;
+      hv = gv / (1.f + expf(-gv)) * uv;
+      ws.h[(size_t)(a0 + c) * inter + n] = hv;
+    }
+    note_hmax(ws.hmax, a0 + c, hv, c < ncols);
   }
 }
 
@@ -815,10 +833,16 @@ __global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, 
       const int n = t * 16 + nl;
       // (lane groups g >= 2 hold columns 8..15, never present: kept in bounds)
       const float* rsv = rsc_slots + (w & 1) * XL_MAX_COLS + min(4 * g, XL_MAX_COLS - 4);
-      const int ne = min(4, nc_cur - 4 * g);
-      for (int e = 0; e < ne; ++e) {
-        const float gv = gs[e] * rsv[e], uv = us[e] * rsv[e];
-        ws.h[(size_t)(a0_cur + 4 * g + e) * inter + n] = gv / (1.f + __expf(-gv)) * uv;
+      const int ne = min(4, nc_cur - 4 * g);   // (uniform in the lane's 16-lane row)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float hv = 0.f;
+        if (e < ne) {
+          const float gv = gs[e] * rsv[e], uv = us[e] * rsv[e];
+          hv = gv / (1.f + __expf(-gv)) * uv;
+          ws.h[(size_t)(a0_cur + 4 * g + e) * inter + n] = hv;
+        }
+        note_hmax(ws.hmax, a0_cur + 4 * g + e, hv, e < ne);
       }
     }
     // next compute item; a new descriptor's rows replace the old ones once
@@ -886,14 +910,20 @@ hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, 
 // half-wave hw converts the (row, 256-block) pairs hw, hw + 16, ... (at most
 // PAIRS); lane l of a pair takes sub-block l/2, element positions j = 2(l&1)
 // and 2(l&1) + 1, at b = 0..3 (elements 16 sb + 4b + j), so that it writes
-// whole dwords of each digit plane.
+// whole dwords of each digit plane.  The row's scale comes from its largest
+// |h|, which the gate/up kernel left in hmax (loaded with the values).
 template <int PAIRS>
 struct DnH8 {
   float2 v[PAIRS][4];
+  uint32_t m[DN_MAX_ROWS];   // hmax bits of the descriptor's rows (uniform: scalar registers)
 };
 
 template <int PAIRS>
-__device__ __forceinline__ void dn8_h_load(const float* h, int a0, int ncols, int inter, DnH8<PAIRS>& v) {
+__device__ __forceinline__ void dn8_h_load(const float* h, const uint32_t* hmax, int a0, int ncols, int inter,
+                                           DnH8<PAIRS>& v) {
+  const auto hm = const_ptr(hmax + a0);
+#pragma unroll
+  for (int j = 0; j < DN_MAX_ROWS; ++j) v.m[j] = hm[min(j, ncols - 1)];
   const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
   const int sb = l >> 1, jh = l & 1;
   const int nbk = inter / 256, npairs = ncols * nbk;
@@ -914,43 +944,19 @@ __device__ __forceinline__ int sbyte(int x) { return (x << 24) >> 24; }
 
 template <int PAIRS>
 __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _Float16* sx, float* csc, int ncols,
-                                              int inter, int* s_max) {
+                                              int inter) {
   const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
   const int sb = l >> 1, jh = l & 1;
   const int nbk = inter / 256, npairs = ncols * nbk;
   const int rs = inter + 16, sxs = inter / 16;
 #pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {   // per-pair maxima
-    const int p = hw + (DN_THREADS / 32) * i;
-    if (p < npairs) {
-      float mx = 0.f;
-      int bad = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float x0 = fabsf(v.v[i][b].x), x1 = fabsf(v.v[i][b].y);
-        bad |= !(x0 <= 3.402823466e38f) | !(x1 <= 3.402823466e38f);
-        mx = fmaxf(mx, fmaxf(x0, x1));
-      }
-      mx = half_allreduce(mx, [](float a, float b) { return fmaxf(a, b); });
-      bad = (int)half_allreduce((uint32_t)bad, [](uint32_t a, uint32_t b) { return a | b; });
-      if (l == 0) {
-        s_max[2 * p] = __float_as_int(mx);
-        s_max[2 * p + 1] = bad;
-      }
-    }
-  }
-  barrier_lds();   // (LDS only: the weight loads in flight are not waited for)
-#pragma unroll
   for (int i = 0; i < PAIRS; ++i) {   // digits
     const int p = hw + (DN_THREADS / 32) * i;
     if (p < npairs) {
       const int c = p / nbk, kb = p - c * nbk;
-      float mx = 0.f;
-      int bad = 0;
-      for (int j = 0; j < nbk; ++j) {
-        mx = fmaxf(mx, __int_as_float(s_max[2 * (c * nbk + j)]));
-        bad |= s_max[2 * (c * nbk + j) + 1];
-      }
+      const uint32_t mb = c == 0 ? v.m[0] : c == 1 ? v.m[1] : c == 2 ? v.m[2] : v.m[3];
+      const float mx = __uint_as_float(mb);
+      const int bad = mb >= 0x7F800000u;   // an infinite or NaN value in the row
       // |h| 2^e < 2^29: the leading digit stays within +-65
       int e = 0;
       if (mx > 0.f && !bad) {
@@ -959,7 +965,6 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
         e = min(max(29 - E, -120), 120);
       }
       uint32_t w[4][2];   // [digit][j - 2 jh]
-      int ps[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
@@ -973,12 +978,15 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
           const int p1 = sbyte(a2), p0 = (a2 - p1) >> 8;
           const int dg[4] = {p0, p1, p2, p3};
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            w[d][jj] |= ((uint32_t)dg[d] & 0xFFu) << (8 * b);
-            ps[d] += dg[d];
-          }
+          for (int d = 0; d < 4; ++d) w[d][jj] |= ((uint32_t)dg[d] & 0xFFu) << (8 * b);
         }
       }
+      // digit sums of the lane's 8 elements: the signed bytes of its two words
+      int ps[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        ps[d] = __builtin_amdgcn_sdot4((int)w[d][0], 0x01010101, __builtin_amdgcn_sdot4((int)w[d][1], 0x01010101, 0, false),
+                                       false);
       // plane byte kb*256 + 64 t + 16 g + 4 j + b for sub-block sb = 4 g + t
       const int off = kb * 256 + 64 * (sb & 3) + 16 * (sb >> 2) + 8 * jh;
 #pragma unroll
@@ -1003,7 +1011,6 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
 template <bool WIDE_D, int PAIRS>
 __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ int s_max[2 * PAIRS * (DN_THREADS / 32)];   // per pair: max bits, bad flag
   const int nwork = ws.meta->n_work_dn;
   const MoeWork wk = ws.work_dn[blockIdx.y];   // in bounds for every launched block
   if ((int)blockIdx.y >= nwork) return;
@@ -1025,8 +1032,8 @@ __global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hid
   DnH8<PAIRS> hv;
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
   q2_range_staged_i8<WIDE_D>(
-      D, n, 0, inter / 256, X, ncols, lane, acc, [&]() { dn8_h_load(ws.h, a0, ncols, inter, hv); },
-      [&](int) { dn8_h_convert(hv, q, sx, csc, ncols, inter, s_max); });
+      D, n, 0, inter / 256, X, ncols, lane, acc, [&]() { dn8_h_load(ws.h, ws.hmax, a0, ncols, inter, hv); },
+      [&](int) { dn8_h_convert(hv, q, sx, csc, ncols, inter); });
   // lane (n, g) holds tile columns 4g..4g+3: the four digits of row g
   if (g < ncols) {
     const f4_t sc = *(const f4_t*)(csc + 4 * g);

@@ -270,6 +270,7 @@ struct MoeWs {
   int* topk_idx;      // [R, top_k]
   float* topk_w;      // [R, top_k]
   float* h;           // [max_assign, inter]  SwiGLU output
+  uint32_t* hmax;     // [max_assign]  bits of the largest |h| of each row (gate/up, atomic max)
   float* part;        // [max_assign, hidden] per-assignment down outputs
   MoeWork* work_gu;    // [max_work]
   MoeWork* work_dn;    // [max_work]
