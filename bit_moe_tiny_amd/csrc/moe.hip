@@ -3,7 +3,8 @@
 //
 // Launch sequence of one layer (all on the caller's stream, no host sync):
 //   k_moe_prep    block 0 routes all rows (top-k on logits, softmax weights;
-//                 one wave per row, wave-wide reductions on the DPP network)
+//                 one wave per row: a DPP maximum and one ballot per slot per
+//                 round)
 //                 and groups (row, slot) pairs by expert so each touched
 //                 expert's weights are read once ("MoE gate_up expert dedup",
 //                 ds4-on-spark README, introduction); the other blocks stage x
@@ -13,15 +14,18 @@
 //                 item, 16-row tile of inter) with the next item's weight loads
 //                 in flight; the partial sums meet in LDS and one wave applies
 //                 SwiGLU ("fused gate+up+swiglu MoE decode", 1x Spark tuned
-//                 DSpark thread, Q&A answer 3).  h is kept in fp32.
+//                 DSpark thread, Q&A answer 3).  h is kept in fp32, and each
+//                 h row's largest magnitude is raised by atomic max (the
+//                 down projection's scale; k_moe_prep clears it).
 //   k_q2_gateup   the same per (tile, work item) block, for shapes the
 //                 persistent kernel does not take.
 //   k_q2_down     grid (128-row group of hidden, unit, column group of at
 //                 most 4 rows), 8 waves of one 16-row tile over all of inter,
 //                 on the int8 matrix cores: the block converts its h rows into
 //                 four fixed-point byte digits each (four tile columns per
-//                 row) in LDS, the weights enter as the bytes sc * q, every
-//                 block product is exact; per-assignment outputs go to the
+//                 row; the scale from the row's recorded largest magnitude)
+//                 in LDS, the weights enter as the bytes sc * q, every block
+//                 product is exact; per-assignment outputs go to the
 //                 workspace.
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
