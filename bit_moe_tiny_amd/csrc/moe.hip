@@ -988,9 +988,10 @@ __device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _
       // digit sums of the lane's 8 elements: the signed bytes of its two words
       int ps[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
-        ps[d] = __builtin_amdgcn_sdot4((int)w[d][0], 0x01010101, __builtin_amdgcn_sdot4((int)w[d][1], 0x01010101, 0, false),
-                                       false);
+      for (int d = 0; d < 4; ++d) {
+        const int s1 = __builtin_amdgcn_sdot4((int)w[d][1], 0x01010101, 0, false);
+        ps[d] = __builtin_amdgcn_sdot4((int)w[d][0], 0x01010101, s1, false);
+      }
       // plane byte kb*256 + 64 t + 16 g + 4 j + b for sub-block sb = 4 g + t
       const int off = kb * 256 + 64 * (sb & 3) + 16 * (sb >> 2) + 8 * jh;
 #pragma unroll

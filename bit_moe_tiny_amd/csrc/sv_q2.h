@@ -442,8 +442,9 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
 // (v_mfma_i32_16x16x64_i8), for activation rows held as fixed-point digits:
 // each row r is scaled by 2^s_r and rounded to an integer a (|a| < 2^30),
 // written as four signed bytes a = 2^24 p0 + 2^16 p1 + 2^8 p2 + p3, and tile
-// column c = 4 r + i holds digit p_i of row r (up to 4 rows).  Weights enter as the bytes sc * q (at most 45, exact), so every
-// product and every sum inside a block is an exact integer.  Per block a lane
+// column c = 4 r + i holds digit p_i of row r (up to 4 rows).  Weights enter
+// as the bytes sc * q (at most 45, exact), so every product and every sum
+// inside a block is an exact integer.  Per block a lane
 // turns each of its 4 sub-block dwords into 4 byte vectors
 // ((w >> 2j) & 0x03030303) * sc -- byte b of vector j is code 4b + j -- one
 // step of 64 k per sub-block (step t = sub-block 4g + t of lane group g).  The
