@@ -320,23 +320,27 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 
 // ---------------------------------------------------------------------------
 // Weights streamed into LDS (block counts a multiple of 16, up to 8 columns;
-// 4 with fp32 inputs).  Blocks of LD_WAVES (4 or 8) waves, persistent over
-// tiles: in round r wave w of block b owns tile (r G + b) LD_WAVES + w.  Two
-// 4-wave blocks per CU where both fit in LDS (each with its own stage
-// barrier, so a slow wave holds up 3 others, not 7), else one of 8 waves.  K is swept in
-// stages of 16 blocks (512 k).  For each stage a wave copies its tile's 16
-// rows x 512 code bytes and 16 x 32 scale bytes into its own LDS buffer with
-// global_load_lds (full 128-byte lines, non-temporal: this is the pattern
-// that streams fastest on this part), and the block copies the activation
-// columns of the stage into a shared buffer.  Everything is double buffered:
-// stage s+1 is in flight while stage s is computed; one barrier per stage.
-// Code rows are stored rotated by their row index in 16-byte units so that
-// the 16 rows of an MFMA operand read fall in distinct LDS banks.
+// 4 with fp32 inputs; at most LD_MAX_ROUNDS tiles per wave).  Blocks of
+// LD_WAVES (4 or 8) waves, persistent over tiles: in round r wave w of block
+// b owns tile (r G + b) LD_WAVES + w.  Two 4-wave blocks per CU where both
+// fit in LDS (each with its own step barrier, so a slow wave holds up 3
+// others, not 7), else one of 8 waves.  K is swept in stages of 16 blocks
+// (512 k), stage-major: for each stage, the rounds' tiles one after another
+// (one accumulator per round), so the block copies a stage's activation
+// columns into its shared buffer once, not once per round.  For each step
+// (stage, round) a wave copies its tile's 16 rows x 512 code bytes and
+// 16 x 32 scale bytes into its own LDS buffer with global_load_lds (full
+// 128-byte lines, non-temporal: this is the pattern that streams fastest on
+// this part).  Everything is double buffered: step k+1 is in flight while
+// step k is computed; one barrier per step.  Code rows are stored rotated by
+// their row index in 16-byte units so that the 16 rows of an MFMA operand
+// read fall in distinct LDS banks.
 constexpr int LD_SB = 16;                                   // blocks (of 32) per stage
 constexpr int LD_WBUF = 16 * LD_SB * 32;                    // code bytes per wave and stage (8 KB)
 constexpr int LD_DBUF = 16 * LD_SB * 2;                     // scale bytes per wave and stage (512)
 constexpr int LD_XRS = LD_SB * 32 + 8;                      // activation row stride (fp16)
 constexpr int LD_XMAX = 8;                                  // columns (hi only; half with lo planes)
+constexpr int LD_MAX_ROUNDS = 4;                            // tiles per wave (one accumulator each)
 
 static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
   return (size_t)waves * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
@@ -371,10 +375,11 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
   const int cr = min(nl, ncols - 1);   // padding columns read the last real column; never stored
   const f4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-  // stage copies of (round r, stage st) into LDS buffer `buf` (the parity of
-  // the running stage count).  Wave-private code and scale rows; activation
-  // columns shared by the block (column c by wave c mod 8).
-  auto issue = [&](int r, int st, int buf) {
+  // copies for step (stage st, round r) into weight buffer `wb` (wave-private
+  // code and scale rows of the round's tile) and, for the first round of a
+  // stage, the stage's activation columns into activation buffer `xb`
+  // (shared by the block; column c by wave c mod LD_WAVES)
+  auto issue = [&](int st, int r, int wb, int xb) {
     const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
     if (tile < tiles) {
 #pragma unroll
@@ -382,37 +387,48 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
         const int row = 2 * i + (lane >> 5), c = lane & 31;
         const int n = min(tile * 16 + row, vocab - 1);
         const int8_t* src = W.qs + ((size_t)n * nb + st * LD_SB) * 32 + ((c + row) & 31) * 16;
-        dma16_nt(src, wbase + buf * LD_WBUF + i * 1024);
+        dma16_nt(src, wbase + wb * LD_WBUF + i * 1024);
       }
       if (lane < 32) {   // scales: two 16-byte pieces per row, lanes 0..31
         const int row = lane >> 1;
         const int n = min(tile * 16 + row, vocab - 1);
-        dma16(W.d + (size_t)n * nb + st * LD_SB + 8 * (lane & 1), dbase + buf * LD_DBUF);
+        dma16(W.d + (size_t)n * nb + st * LD_SB + 8 * (lane & 1), dbase + wb * LD_DBUF);
       }
     }
-    for (int c = wv; c < ncols * (USE_LO ? 2 : 1); c += LD_WAVES) {
-      const int pl = c >= ncols, cc = c - (pl ? ncols : 0);
-      const _Float16* src = (pl ? img.lo : img.hi) + (size_t)cc * K + st * LD_SB * 32 + 8 * lane;
-      dma16(src, xbase + (uint32_t)(((pl * 2 + buf) * ncols + cc) * LD_XRS * 2));
-    }
+    if (r == 0)
+      for (int c = wv; c < ncols * (USE_LO ? 2 : 1); c += LD_WAVES) {
+        const int pl = c >= ncols, cc = c - (pl ? ncols : 0);
+        const _Float16* src = (pl ? img.lo : img.hi) + (size_t)cc * K + st * LD_SB * 32 + 8 * lane;
+        dma16(src, xbase + (uint32_t)(((pl * 2 + xb) * ncols + cc) * LD_XRS * 2));
+      }
   };
 
-  issue(0, 0, 0);
-  int buf = 0;   // parity of the running stage count
-  for (int r = 0; r < rounds; ++r) {
-    const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
-    f4_t acc = zero;
-    for (int st = 0; st < ns; ++st, buf ^= 1) {
-      // this wave's copies of stage st are done; after the barrier everyone's
-      // are, and every wave is past stage st-1 (whose buffers the next copies reuse)
+  // Stage-major: for each 512-k stage, every round's tile in turn, so a
+  // stage's activation columns are copied once per block (not once per
+  // round); each round keeps its own accumulator.
+  f4_t acc[LD_MAX_ROUNDS];
+#pragma unroll
+  for (int r = 0; r < LD_MAX_ROUNDS; ++r) acc[r] = zero;
+  issue(0, 0, 0, 0);
+  int k = 0;   // running step count: weight buffer k & 1
+  for (int st = 0; st < ns; ++st) {
+#pragma unroll
+    for (int r = 0; r < LD_MAX_ROUNDS; ++r) {
+      if (r >= rounds) break;
+      // this wave's copies of step k are done; after the barrier everyone's
+      // are, and every wave is past step k-1 (whose buffers the next copies
+      // reuse; the activation buffer of stage st+1 was last read in st-1)
       wait_vmcnt_le(0);
       barrier_lds();
-      if (st + 1 < ns) issue(r, st + 1, buf ^ 1);
-      else if (r + 1 < rounds) issue(r + 1, 0, buf ^ 1);
+      if (r + 1 < rounds) issue(st, r + 1, (k + 1) & 1, st & 1);
+      else if (st + 1 < ns) issue(st + 1, 0, (k + 1) & 1, (st + 1) & 1);
+      const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
+      const int buf = k & 1, xbuf = st & 1;
+      ++k;
       if (tile >= tiles) continue;
       const uint8_t* wb = wl + buf * LD_WBUF + nl * (LD_SB * 32);
-      const _Float16* xh = xl16 + (size_t)(buf * ncols + cr) * LD_XRS + kofs;
-      const _Float16* xo = xl16 + (size_t)((2 + buf) * ncols + cr) * LD_XRS + kofs;
+      const _Float16* xh = xl16 + (size_t)(xbuf * ncols + cr) * LD_XRS + kofs;
+      const _Float16* xo = xl16 + (size_t)((2 + xbuf) * ncols + cr) * LD_XRS + kofs;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint4 dv = *(const uint4*)(dl + buf * LD_DBUF + nl * 32 + 16 * j);   // 8 block scales of row nl
@@ -431,19 +447,23 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
             if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xo + blk * 32), bw, dt, 0, 0, 0);
             const float d = f16b_to_f32((uint16_t)(w32 >> (16 * h)));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(d, dt[e], acc[e]);
+            for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(d, dt[e], acc[r][e]);
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);   // rounds one after another
     }
-    if (tile < tiles) {
-      const int n = tile * 16 + nl;
-      if (n < vocab) {
+  }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int cc = 4 * g + e;
-          if (cc < R) logits[(size_t)cc * vocab + n] = acc[e] * img.rscale[cc];
-        }
+  for (int r = 0; r < LD_MAX_ROUNDS; ++r) {
+    if (r >= rounds) break;
+    const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
+    const int n = tile * 16 + nl;
+    if (tile < tiles && n < vocab) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int cc = 4 * g + e;
+        if (cc < R) logits[(size_t)cc * vocab + n] = acc[r][e] * img.rscale[cc];
       }
     }
   }
@@ -466,11 +486,12 @@ static void launch_lm(int R, hipStream_t s, const Q8View& W, const XImg& img, fl
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo, XImg img,
                             float* logits, hipStream_t s) {
   const Q8View W = q8_view(w, vocab, hidden);
-  if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX / 2 : LD_XMAX)) {
-    const int ncu = cu_count();
-    // two 4-wave blocks per CU when both fit in the CU's 160 KB of LDS
-    const bool two = 2 * ld_lds_bytes(4, R, use_lo) <= (size_t)160 * 1024;
-    const int waves = two ? 4 : 8;
+  const int ncu = cu_count();
+  // two 4-wave blocks per CU when both fit in the CU's 160 KB of LDS
+  const bool two = 2 * ld_lds_bytes(4, R, use_lo) <= (size_t)160 * 1024;
+  const int waves = two ? 4 : 8;
+  const long rounds = ((vocab + 15) / 16 + (long)(two ? 2 * ncu : ncu) * waves - 1) / ((long)(two ? 2 * ncu : ncu) * waves);
+  if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX / 2 : LD_XMAX) && rounds <= LD_MAX_ROUNDS) {
     const size_t lb = ld_lds_bytes(waves, R, use_lo);
     const dim3 grid(two ? 2 * ncu : ncu), block(waves * 64);
     if (use_lo) {
