@@ -30,11 +30,12 @@ from .formats import (q2_fields, q2_dequant_units, q2_dequant_f32, q2_dequant_f6
                       q8_matrix_bytes)
 from .linalg import (gemm, silu, swiglu_expert, route_topk, moe_layer, plain_layer,
                      lm_head_logits)
-from .accept import softmax_t, first_exceeding, accept_sequence, spec_accept
+from .accept import (softmax_t, greedy_onehot, distribution, first_exceeding, accept_sequence,
+                     spec_accept)
 
 __all__ = [
     "q2_fields", "q2_dequant_units", "q2_dequant_f32", "q2_dequant_f64",
     "q8_fields", "q8_dequant_f32", "q8_dequant_f64", "q2_matrix_bytes", "q8_matrix_bytes",
     "gemm", "silu", "swiglu_expert", "route_topk", "moe_layer", "plain_layer",
-    "lm_head_logits", "softmax_t", "first_exceeding", "accept_sequence", "spec_accept",
+    "lm_head_logits", "softmax_t", "greedy_onehot", "distribution", "first_exceeding", "accept_sequence", "spec_accept",
 ]

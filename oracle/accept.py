@@ -26,7 +26,11 @@ budget (K accept uniforms plus one sampling uniform), inverse-CDF order
 bonus row.
 
 ``p`` and ``q`` come either from logits (softmax at temperature T, fp64) or are
-given as probabilities.  ``accept_sequence`` also runs on ``fractions.Fraction``
+given as probabilities.  T = 0 is greedy decoding (the same thread, page 1, post
+12: greedy outputs unchanged; *1x Spark tuned DSpark for DeepSeek-V4-Flash*,
+Q&A, the FP8 KV answer: the speculative self-check exact at temperature 0): the row is the one-hot distribution at its largest logit, the limit of the
+softmax as T falls to 0, with ties going to the lowest index (our reading; the
+limit itself would split the mass over tied maxima).  ``accept_sequence`` also runs on ``fractions.Fraction``
 inputs, where every step is exact; the parity pins enumerate it that way.
 """
 from __future__ import annotations
@@ -45,6 +49,25 @@ def softmax_t(z, temperature: float) -> np.ndarray:
     a = np.asarray(z, np.float32).astype(np.float64) / np.float64(np.float32(temperature))
     e = np.exp(a - a.max())
     return e / e.sum()
+
+
+def greedy_onehot(z) -> np.ndarray:
+    """The T = 0 distribution of one row of fp32 logits: 1 at the first index
+    holding the row's maximum, 0 elsewhere (fp64)."""
+    a = np.asarray(z, np.float32)
+    p = np.zeros(a.shape[0], np.float64)
+    p[int(np.argmax(a))] = 1.0   # numpy's argmax returns the first maximum
+    return p
+
+
+def distribution(row, kind: int, temperature: float) -> np.ndarray:
+    """p (or q) of one row: softmax at T, the T = 0 one-hot, or the given
+    probabilities (fp64)."""
+    if kind == PROBS:
+        return np.asarray(row, np.float32).astype(np.float64)
+    if np.float32(temperature) == 0:
+        return greedy_onehot(row)
+    return softmax_t(row, temperature)
 
 
 def first_exceeding(weights, u):
@@ -135,11 +158,8 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float,
         if not ok:
             continue
 
-        def dist(row, kind, t):
-            return softmax_t(row, t) if kind == LOGITS else row.astype(np.float64)
-
-        p_rows = [dist(target[s, i], target_kind, t_p) for i in range(K + 1)]
-        q_rows = [dist(draft[s, i], draft_kind, t_q) for i in range(K)]
+        p_rows = [distribution(target[s, i], target_kind, t_p) for i in range(K + 1)]
+        q_rows = [distribution(draft[s, i], draft_kind, t_q) for i in range(K)]
         n, out = accept_sequence(p_rows, q_rows, drafts[s].tolist(),
                                  [float(x) for x in uniforms[s]])
         nacc[s] = n

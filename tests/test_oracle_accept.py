@@ -235,3 +235,90 @@ def test_probs_mode_unnormalised_rows():
     n, toks = oracle.accept_sequence(p, q, [0], [0.5, 0.3])   # 0.125 < 0.2 accept
     # sums 1,2,4,8; target 0.3*8 = 2.4 -> first > 2.4 is x=2
     assert (n, toks) == (1, [0, 2])
+
+
+def _first_max(row):
+    vals = [float(v) for v in row]
+    return vals.index(max(vals))   # list.index: the first occurrence
+
+
+def _prefix_match(tl, drafts, S, K):
+    """Greedy decoding written out without the accept rule: drafts are kept
+    while each equals its target row's largest logit (the first one on ties);
+    the first disagreeing row, or row K, then gives its own largest logit."""
+    toks = np.full((S, K + 1), -1, np.int32)
+    nacc = np.zeros(S, np.int32)
+    for s in range(S):
+        best = [_first_max(tl[s * (K + 1) + i]) for i in range(K + 1)]
+        n = 0
+        while n < K and int(drafts[s][n]) == best[n]:
+            n += 1
+        toks[s, :n] = drafts[s, :n]
+        toks[s, n] = best[n]
+        nacc[s] = n
+    return toks, nacc
+
+
+def test_greedy_onehot_ties_to_lowest_index():
+    row = np.array([1.0, 3.0, -2.0, 3.0, 2.5], np.float32)
+    p = oracle.distribution(row, LOGITS, 0.0)
+    assert p.tolist() == [0.0, 1.0, 0.0, 0.0, 0.0]
+    assert np.array_equal(oracle.distribution(row, LOGITS, -0.0), p)
+    assert np.array_equal(oracle.greedy_onehot(row), p)
+    assert oracle.distribution(row, LOGITS, 1.0).argmax() == 1 and oracle.distribution(row, LOGITS, 1.0)[0] > 0
+
+
+def test_greedy_is_prefix_match():
+    """T_p = 0: for any q (softmax, greedy or given probabilities) and any
+    uniforms, the output is the longest prefix of drafts that agree with the
+    target's largest logit, then the largest logit at the first disagreement
+    (or of row K).  Small integer logits make ties common."""
+    rng = np.random.default_rng(21)
+    S, K, V = 60, 4, 12
+    tl = rng.integers(-3, 4, size=(S * (K + 1), V)).astype(np.float32)
+    dl = rng.normal(size=(S * K, V)).astype(np.float32)
+    drafts = rng.integers(0, V, size=(S, K)).astype(np.int32)
+    agree = rng.random((S, K)) < 0.75
+    for s in range(S):
+        for i in range(K):
+            if agree[s, i]:
+                drafts[s, i] = _first_max(tl[s * (K + 1) + i])
+    u = rng.random((S, K + 1)).astype(np.float32)
+    want_t, want_n = _prefix_match(tl, drafts, S, K)
+    assert set(want_n.tolist()) == set(range(K + 1))
+    qp = np.abs(dl) + 0.01
+    qp = (qp / qp.sum(1, keepdims=True)).astype(np.float32)
+    for draft, dk, t_q in ((dl, LOGITS, 1.0), (dl, LOGITS, 0.0), (qp, PROBS, 1.0)):
+        toks, nacc = oracle.spec_accept(S, K, V, tl, LOGITS, 0.0, draft, dk, t_q, drafts, u)
+        assert np.array_equal(nacc, want_n) and np.array_equal(toks, want_t)
+
+
+def test_greedy_is_the_low_temperature_limit():
+    """Distinct integer logits (gaps of at least 1): at T = 0.01 the softmax
+    puts all but e^-100 of the mass on the maximum, so with uniforms away
+    from 0 the outputs at T = 0.01 and at T = 0 agree, for both p and q."""
+    rng = np.random.default_rng(22)
+    S, K, V = 30, 3, 16
+    tl = np.stack([rng.permutation(V) for _ in range(S * (K + 1))]).astype(np.float32)
+    dl = np.stack([rng.permutation(V) for _ in range(S * K)]).astype(np.float32)
+    drafts = np.where(rng.random((S, K)) < 0.7, tl.reshape(S, K + 1, V)[:, :K].argmax(-1),
+                      rng.integers(0, V, size=(S, K))).astype(np.int32)
+    u = (0.01 + 0.98 * rng.random((S, K + 1))).astype(np.float32)
+    # a greedy drafter drafts its own largest logit (elsewhere q(d) = 0, and
+    # 0 < p(d) = e^-100 would accept at T = 0.01): its rows copy the target's
+    # for 70 % of the positions
+    same = rng.random((S * K, 1)) < 0.7
+    dl0 = np.where(same, tl.reshape(S, K + 1, V)[:, :K].reshape(S * K, V), dl)
+    drafts0 = dl0.argmax(-1).reshape(S, K).astype(np.int32)
+    for t_q, q, d in ((1.0, dl, drafts), (0.0, dl0, drafts0)):
+        cold = oracle.spec_accept(S, K, V, tl, LOGITS, 0.01, q, LOGITS, t_q, d, u)
+        zero = oracle.spec_accept(S, K, V, tl, LOGITS, 0.0, q, LOGITS, t_q, d, u)
+        assert np.array_equal(cold[0], zero[0]) and np.array_equal(cold[1], zero[1])
+        assert set(zero[1].tolist()) >= {0, K}
+    # q greedy, p soft: the draft is q's largest logit, accepted iff u < p(d)
+    d = int(dl[0].argmax())
+    p_rows = [oracle.softmax_t(tl[i], 1.0) for i in range(K + 1)]
+    q_rows = [oracle.distribution(dl[i], LOGITS, 0.0) for i in range(K)]
+    for uu in (0.0, float(p_rows[0][d]) * 0.999, float(p_rows[0][d]) * 1.001):
+        n, _ = oracle.accept_sequence(p_rows, q_rows, [d] + [0] * (K - 1), [uu] + [0.5] * K)
+        assert (n >= 1) == (uu < p_rows[0][d])
