@@ -36,6 +36,11 @@ constexpr int SMP_PER = 2;                    // sampling entries per thread
 constexpr int SMP_CHUNK = ACC_T * SMP_PER;    // sampling chunk
 constexpr int SMP_MAX_CH = ACC_MAX_CH * ACC_CHUNK / SMP_CHUNK;
 
+// A logits row at temperature 0 (greedy decoding): the one-hot distribution at
+// the row's first largest value.  Its statistics are the maximum and, in place
+// of the softmax denominator, that value's index.
+constexpr int ACC_ARGMAX = 2;
+
 struct AccWs {
   double* cmax;     // [rows, CH]
   double* csum;     // [rows, CH]
@@ -184,9 +189,9 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
     a[i] = -INFINITY;
     if (x < V) {
       const float v = src.p[x];
-      if (src.kind == SV_LOGITS) {
+      if (src.kind != SV_PROBS) {
         bad |= !(fabsf(v) <= 3.402823466e38f);
-        a[i] = (double)v / src.T;
+        a[i] = src.kind == SV_LOGITS ? (double)v / src.T : (double)v;
       } else {
         bad |= !(v >= 0.f && v <= 3.402823466e38f);
         a[i] = (double)v;
@@ -200,13 +205,22 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
 #pragma unroll
     for (int i = 0; i < ACC_PER; ++i)
       if (x0 + threadIdx.x + 256 * i < V && !bad) sum += exp(a[i] - mx);
+    sum = block_sum_d(sum, sh);
+  } else if (src.kind == ACC_ARGMAX) {
+    // the chunk's first index holding its maximum (a maximum of -index)
+    mx = block_max_d(mx, sh);
+    double fi = -INFINITY;
+#pragma unroll
+    for (int i = ACC_PER - 1; i >= 0; --i)
+      if (x0 + threadIdx.x + 256 * i < V && a[i] == mx) fi = -(double)(x0 + threadIdx.x + 256 * i);
+    sum = -block_max_d(fi, sh);
   } else {
     mx = 0.0;
 #pragma unroll
     for (int i = 0; i < ACC_PER; ++i)
       if (x0 + threadIdx.x + 256 * i < V) sum += a[i];
+    sum = block_sum_d(sum, sh);
   }
-  sum = block_sum_d(sum, sh);
   bad = __any(bad) ? 1 : 0;
   if ((threadIdx.x & 63) == 0) shb[threadIdx.x >> 6] = bad;
   __syncthreads();
@@ -220,6 +234,7 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
 
 // Distribution value of entry x of a row, given its recombined statistics.
 __device__ inline double dist_val(const RowSrc& s, double m, double z, int x) {
+  if (s.kind == ACC_ARGMAX) return x == (int)z ? 1.0 : 0.0;
   const float v = s.p[x];
   if (s.kind == SV_LOGITS) return exp((double)v / s.T - m) / z;
   return (double)v;
@@ -277,21 +292,31 @@ __device__ inline void acc_rows(int s, int S, int K, int CH, int tkind, int dkin
     for (int j = 0; j < RB; ++j) {
       const int i = i0 + 4 * j;
       if (i >= nrows) break;   // uniform in the wave
-      const bool logits = (i <= K ? tkind : dkind) == SV_LOGITS;
+      const int kind = i <= K ? tkind : dkind;
+      const bool logits = kind == SV_LOGITS;
       double m = -INFINITY;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) m = fmax(m, cm[j][k]);
-      m = logits ? wave_max_d(m) : 0.0;
+      m = kind != SV_PROBS ? wave_max_d(m) : 0.0;
       double z = 0.0;
+      if (kind == ACC_ARGMAX) {
+        // the first chunk holding the row's maximum gives the index
+        double f = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k)
-        if (lane + 64 * k < CH) z += logits ? cs[j][k] * exp(cm[j][k] - m) : cs[j][k];
-      z = wave_sum_d(z);
+        for (int k = 0; k < CPL; ++k)
+          if (lane + 64 * k < CH && cm[j][k] == m) f = fmax(f, -cs[j][k]);
+        z = -wave_max_d(f);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+          if (lane + 64 * k < CH) z += logits ? cs[j][k] * exp(cm[j][k] - m) : cs[j][k];
+        z = wave_sum_d(z);
+      }
       const int bad = __any(cb[j]) ? 1 : 0;
       if (lane == 0) {
         rm[i] = m;
         rz[i] = z;
-        rbad[i] = bad | (logits ? 0 : !(z > 0.0));
+        rbad[i] = bad | (kind == SV_PROBS ? !(z > 0.0) : 0);
       }
     }
   }
@@ -395,11 +420,12 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
     inv = __any(inv) ? 1 : 0;
     int rej = 1;   // lanes past K: rejected (K <= 31)
     if (!inv && lane < K) {
-      const double p = tkind == SV_LOGITS ? exp((double)vp / (double)Tp - rm[lane]) / rz[lane]
-                                          : (double)vp;
-      const double q = dkind == SV_LOGITS
-                           ? exp((double)vq / (double)Tq - rm[K + 1 + lane]) / rz[K + 1 + lane]
-                           : (double)vq;
+      const double p = tkind == SV_LOGITS    ? exp((double)vp / (double)Tp - rm[lane]) / rz[lane]
+                       : tkind == ACC_ARGMAX ? (dk == (int)rz[lane] ? 1.0 : 0.0)
+                                             : (double)vp;
+      const double q = dkind == SV_LOGITS ? exp((double)vq / (double)Tq - rm[K + 1 + lane]) / rz[K + 1 + lane]
+                       : dkind == ACC_ARGMAX ? (dk == (int)rz[K + 1 + lane] ? 1.0 : 0.0)
+                                             : (double)vq;
       rej = !(fma((double)uk, q, -p) < 0.0);   // reject: u*q >= p
     }
     const unsigned long long rmask = __ballot(rej);
@@ -531,6 +557,8 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
                          hipStream_t s) {
   const AccWs ws = acc_carve(wsp, S, K, V);
   const int CH = acc_chunks(V), CHs = smp_chunks(V);
+  if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
+  if (dkind == SV_LOGITS && Tq == 0.f) dkind = ACC_ARGMAX;
   hipLaunchKernelGGL(k_acc_stats, dim3(CH, S * (2 * K + 1)), dim3(256), 0, s, S, K, V, target,
                      tkind, Tp, draft, dkind, Tq, ws);
   hipError_t err = hipGetLastError();

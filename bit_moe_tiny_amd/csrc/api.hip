@@ -145,8 +145,8 @@ int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t ta
   if (!target || !uniforms || !out_tokens || !out_n_accepted || !ws) return SV_EINVAL;
   if (K > 0 && (!draft || !draft_tokens)) return SV_EINVAL;
   if (!kind_ok(target_kind) || (K > 0 && !kind_ok(draft_kind))) return SV_EINVAL;
-  if (target_kind == SV_LOGITS && !(isfinite(T_p) && T_p > 0.f)) return SV_EINVAL;
-  if (K > 0 && draft_kind == SV_LOGITS && !(isfinite(T_q) && T_q > 0.f)) return SV_EINVAL;
+  if (target_kind == SV_LOGITS && !(isfinite(T_p) && T_p >= 0.f)) return SV_EINVAL;
+  if (K > 0 && draft_kind == SV_LOGITS && !(isfinite(T_q) && T_q >= 0.f)) return SV_EINVAL;
   if (ws_bytes < accept_ws_bytes(S, K, V)) return SV_EWORKSPACE;
   return hip_status(launch_accept(S, K, V, target, target_kind, T_p, draft,
                                   K > 0 ? draft_kind : target_kind, T_q, draft_tokens, uniforms,

@@ -173,7 +173,10 @@ SV_API size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V);
  *
  *  target        [S*(K+1), V] fp32; row s*(K+1)+i is position i of sequence s
  *                (the K+1 verifier rows: [T1] page 2; [T3] "The break-even law")
- *  target_kind   SV_LOGITS: p = softmax(row / T_p); SV_PROBS: p = row as given
+ *  target_kind   SV_LOGITS: p = softmax(row / T_p), or for T_p == 0 (greedy
+ *                decoding: [T1] page 1, post 12; [T4] Q&A, the FP8 KV answer,
+ *                the self-check at temperature 0) the one-hot distribution at
+ *                the row's first largest value; SV_PROBS: p = row as given
  *  draft         [S*K, V] fp32, row s*K+i; q likewise with draft_kind / T_q;
  *                may be NULL when K == 0
  *  draft_tokens  [S, K] int32
@@ -191,7 +194,9 @@ SV_API size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V);
  *  Distributions are evaluated in fp64.  A sequence with a draft token outside
  *  [0, V), a uniform outside [0, 1), a non-finite value, or (SV_PROBS) a
  *  negative value or an all-zero row gets -1 in every output slot.
- *  T_p / T_q must be finite and > 0 for SV_LOGITS rows.  1 <= S, 0 <= K <=
+ *  T_p / T_q must be finite and >= 0 for SV_LOGITS rows (0: greedy; then the
+ *  output is the longest prefix of drafts equal to their rows' largest target
+ *  logits, followed by the largest logit of the next row).  1 <= S, 0 <= K <=
  *  SV_MAX_DRAFTS, 1 <= V.
  */
 SV_API int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,

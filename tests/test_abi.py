@@ -99,7 +99,7 @@ def test_calls_reject_bad_arguments_before_launch():
     args = lambda **k: [k.get("S", 1), k.get("K", 4), k.get("V", 32), fake, k.get("tk", 0),
                         k.get("tp", 1.0), k.get("draft", fake), k.get("dk", 0), k.get("tq", 1.0),
                         k.get("tok", fake), fake, fake, fake, fake, k.get("wsb", 1 << 20), None]
-    assert lib.spec_accept(*args(tp=0.0)) == sv.SV_EINVAL
+    assert lib.spec_accept(*args(tp=-0.5)) == sv.SV_EINVAL
     assert lib.spec_accept(*args(tq=float("nan"))) == sv.SV_EINVAL
     assert lib.spec_accept(*args(tk=3)) == sv.SV_EINVAL
     assert lib.spec_accept(*args(draft=None)) == sv.SV_EINVAL

@@ -200,8 +200,7 @@ def _check_accept(S, K, V, target, tk, tp, draft, dk, tq, drafts, u, toks, nacc)
     tg = np.asarray(target, np.float32).reshape(S, K + 1, V)
     dr = np.asarray(draft, np.float32).reshape(S, K, V) if K else None
 
-    def dist(row, kind, t):
-        return oracle.softmax_t(row, t) if kind == LOGITS else row.astype(np.float64)
+    dist = oracle.distribution
 
     for s in range(S):
         if wn[s] < 0:
@@ -279,3 +278,51 @@ def test_accept_largest_vocabulary(sv):
     z, zq, drafts, u = _logit_inputs(133, S, K, V, 1.5, 0.8)
     toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.8, drafts, u)
     _check_accept(S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.8, drafts, u, toks, nacc)
+
+
+def _greedy_inputs(key, S, K, V):
+    """Integer logits in [-50, 50): every row's maximum is tied at many
+    positions spread over many chunks.  Drafts equal the target row's first
+    maximum 3 times in 4, so every prefix length occurs."""
+    rng = np.random.default_rng(key)
+    z = rng.integers(-50, 50, size=(S * (K + 1), V)).astype(np.float32)
+    zq = rng.integers(-50, 50, size=(S * K, V)).astype(np.float32)
+    drafts = rng.integers(0, V, size=(S, K)).astype(np.int32)
+    first = z.reshape(S, K + 1, V)[:, :K].argmax(-1)
+    drafts = np.where(rng.random((S, K)) < 0.75, first, drafts).astype(np.int32)
+    u = synth.uniform24(synth.generator(key), S * (K + 1)).reshape(S, K + 1)
+    return z, zq, drafts, u
+
+
+@pytest.mark.parametrize("t_q", [1.0, 0.0])
+def test_accept_greedy_target(sv, t_q):
+    """T_p = 0 (greedy): exact agreement with the oracle, and with the
+    prefix-match form (drafts kept while they equal the target's first
+    largest logit, then that row's first largest logit)."""
+    S, K, V = 48, 4, 70000
+    z, zq, drafts, u = _greedy_inputs(140, S, K, V)
+    toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 0.0, zq, LOGITS, t_q, drafts, u)
+    wt, wn = oracle.spec_accept(S, K, V, z, LOGITS, 0.0, zq, LOGITS, t_q, drafts, u)
+    assert np.array_equal(nacc, wn) and np.array_equal(toks, wt)
+    best = z.reshape(S, K + 1, V).argmax(-1)
+    for s in range(S):
+        n = 0
+        while n < K and drafts[s, n] == best[s, n]:
+            n += 1
+        assert nacc[s] == n and toks[s, :n].tolist() == drafts[s, :n].tolist() and toks[s, n] == best[s, n]
+    assert set(nacc.tolist()) == set(range(K + 1))
+
+
+def test_accept_greedy_draft(sv):
+    """T_q = 0 with a soft target (T_p = 0.8): q is one-hot at the draft
+    row's first maximum and the drafts are those maxima."""
+    S, K, V = 16, 3, 9000
+    g = synth.generator(141)
+    z = synth.normal(g, S * (K + 1) * V, 2.0).astype(np.float32).reshape(S * (K + 1), V)
+    zq = (z.reshape(S, K + 1, V)[:, :K].reshape(S * K, V).astype(np.float64)
+          + synth.normal(g, S * K * V, 0.3).reshape(S * K, V)).astype(np.float32)
+    drafts = zq.argmax(-1).reshape(S, K).astype(np.int32)
+    u = synth.uniform24(g, S * (K + 1)).reshape(S, K + 1)
+    toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.0, drafts, u)
+    wn = _check_accept(S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.0, drafts, u, toks, nacc)
+    assert np.all(wn >= 0)
