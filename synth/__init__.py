@@ -281,6 +281,13 @@ def moe_rows(R: int, config_id: int = CFG_MOE, sub: int = 0) -> MoeRows:
     return MoeRows(lg, x)
 
 
+def router_weights(config_id: int = CFG_MOE, n_experts: int = N_ROUTED, hidden: int = HIDDEN) -> Q8Planes:
+    """Eight-bit router matrix [n_experts x hidden] (the router GEMV ahead of
+    the top-k): the vocabulary head's format, scales ~ fp16(|N(0, 3e-4^2)|) so
+    that the logits of unit-variance rows spread by about 2."""
+    return q8_random(generator(config_id, S_ROUTER, 1 << 20), n_experts, hidden, 3e-4)
+
+
 def lm_head_weights(config_id: int = CFG_LMHEAD, vocab: int = VOCAB, hidden: int = HIDDEN) -> Q8Planes:
     return q8_random(generator(config_id, S_WEIGHTS), vocab, hidden, 0.01)
 

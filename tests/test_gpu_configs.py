@@ -19,6 +19,9 @@ configuration the benchmark times, on outputs the oracle computes one by one.
   it has several);
 * a full-vocabulary rejection workload given as probabilities, where decisions
   and tokens must match the oracle exactly (identical fp32 p, q and u).
+* the eight-bit router GEMV ([256 x 7168], through the head's call) ahead of
+  the layer: every logit against the oracle, then the routing bit-exact on the
+  GPU's logits.
 """
 import numpy as np
 import pytest
@@ -144,6 +147,32 @@ def test_moe_layer_workload(sv, layer):
     check = [0, 4]
     want = _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check)
     assert_close(y[check], want, what="moe layer y")
+
+
+# ---------------------------------------------------------------- router
+def test_router_gemv_then_layer(sv, layer):
+    """The eight-bit router GEMV ahead of the top-k, as the vocabulary head's
+    call on a [256 x 7168] matrix: every logit against the oracle, then the
+    layer on the GPU's fp32 logits, its routing bit-exact against the oracle's
+    top-k of the same logits (the decision taken in the same precision on
+    both sides), and two rows of y against the oracle."""
+    w, desc = layer
+    rows = synth.moe_rows(5, synth.CFG_MOE)
+    wr = synth.router_weights().packed()
+    R = rows.x_bf16.shape[0]
+    z = empty((R, E), "f32")
+    say("vq8_lmhead_gemm router GEMV [256 x 7168] R=5")
+    sv.vq8_lmhead_gemm(dev(wr), E, H, dev(rows.x_bf16), z)
+    z = host(z)
+    assert_close(z, oracle.lm_head_logits(wr, E, H, rows.x_bf16, "bf16"), what="router logits")
+    say("vq2_moe_gemm on the router GEMV's logits R=5")
+    y, ti, tw = _run_moe(sv, desc, rows.x_bf16, z)
+    widx, ww = oracle.route_topk(z, TOPK)
+    assert np.array_equal(ti, widx)
+    assert_close(tw, ww, what="topk_w")
+    assert len(np.unique(ti)) > 2 * TOPK   # the rows route to different experts
+    check = [1, 3]
+    assert_close(y[check], _oracle_moe_rows(w, rows.x_bf16, z, check), what="moe layer y (router GEMV)")
 
 
 # ------------------------------------------------------------ vocab head
