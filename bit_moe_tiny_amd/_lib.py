@@ -192,7 +192,8 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float, dr
                 draft_kind: int, t_q: float, draft_tokens, uniforms, out_tokens, out_n_accepted,
                 ws=None, stream=None):
     """Accept/reject for S sequences of K drafts; fills out_tokens [S, K+1] and
-    out_n_accepted [S] (int32)."""
+    out_n_accepted [S] (int32).  A logits row at temperature 0 is greedy: the
+    one-hot distribution at its first largest value."""
     _dev_check(target, draft, draft_tokens, uniforms, out_tokens, out_n_accepted, ws)
     if ws is None:
         ws = _workspace(sv_accept_workspace_bytes(S, K, V), target)
