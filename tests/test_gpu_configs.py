@@ -190,6 +190,31 @@ def test_lm_head_workload_and_accept(sv, head, Tq):
     _check_accept(sv, z, S, K, T, Tq, acc)
 
 
+def test_lm_head_greedy(sv, head):
+    """Greedy decoding (T_p = T_q = 0) on the head's own logits at
+    V = 129,280, drafts from a greedy drafter (its largest draft logit): exact
+    against the oracle and against the prefix-match form."""
+    buf, wdev = head
+    R, S, K = 5, 1, 4
+    say("vq8_lmhead_gemm full head R=5, greedy spec_accept")
+    z = _run_head(sv, wdev, synth.lm_head_hidden(R))
+    acc = synth.accept_inputs(z, S, K, 0.3, 1.0, synth.CFG_LMHEAD, sub=7)
+    drafts = acc.draft_logits.reshape(S, K, V).argmax(-1).astype(np.int32)
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    sv.spec_accept(S, K, V, dev(z), sv.SV_LOGITS, 0.0, dev(acc.draft_logits), sv.SV_LOGITS, 0.0,
+                   dev(drafts), dev(acc.uniforms), toks, nacc)
+    toks, nacc = host(toks), host(nacc)
+    wt, wn = oracle.spec_accept(S, K, V, z, LOGITS, 0.0, acc.draft_logits, LOGITS, 0.0, drafts,
+                                acc.uniforms)
+    assert np.array_equal(nacc, wn) and np.array_equal(toks, wt)
+    best = z.argmax(-1)
+    n = 0
+    while n < K and drafts[0, n] == best[n]:
+        n += 1
+    assert nacc[0] == n and toks[0, :n].tolist() == drafts[0, :n].tolist() and toks[0, n] == best[n]
+
+
 # ---------------------------------------------------------------- cohort
 def test_cohort_workload(sv, layer, head):
     w, desc = layer
