@@ -99,6 +99,9 @@ def _check(fn: str, st: int):
 
 
 # ------------------------------------------------------------------ helpers
+# Every tensor is checked against what the C ABI will read or write through
+# its pointer (element type, shape, byte count) before the pointer is passed:
+# a mismatch would otherwise be an out-of-bounds device access.
 def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
@@ -116,13 +119,38 @@ def _act_dtype(t) -> int:
         return SV_F32
     if t.dtype == torch.bfloat16:
         return SV_BF16
-    raise TypeError(f"activation rows must be float32 or bfloat16, not {t.dtype}")
+    raise ValueError(f"activation rows must be float32 or bfloat16, not {t.dtype}")
+
+
+def _want(t, name: str, dtype: str, shape=None, min_bytes: Optional[int] = None):
+    """Checks tensor ``t`` (dtype one of 'f32', 'i32', 'u8', 'act' = f32 or
+    bf16) against the shape / byte count the C call assumes."""
+    import torch
+    if t is None:
+        raise ValueError(f"{name} is required")
+    dts = {"f32": (torch.float32,), "i32": (torch.int32,), "u8": (torch.uint8, torch.int8),
+           "act": (torch.float32, torch.bfloat16)}[dtype]
+    if t.dtype not in dts:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if min_bytes is not None and t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, at least {min_bytes} needed")
 
 
 def _dev_check(*ts):
+    """Contiguous tensors on the current HIP device (checked after shapes)."""
+    import torch
+    dev = None
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous device tensors")
+        if dev is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        if t.device != dev:
+            raise ValueError(f"tensor on {t.device}, but the current device is {dev}")
 
 
 def _workspace(nbytes: int, like):
@@ -141,7 +169,27 @@ def sv_q8_matrix_bytes(n_out: int, k_in: int) -> int:
 
 def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_gate, w_up=None,
              w_down=None, s_gate=None, s_up=None, s_down=None) -> MoeDesc:
-    """Layer description over device weight tensors (uint8 byte buffers)."""
+    """Layer description over device weight tensors (uint8 byte buffers), each
+    checked to hold the matrices the layer reads: n_experts expert-major
+    [inter x hidden] gate and up matrices and [hidden x inter] down matrices,
+    one of each for the shared expert (PLAIN: w_gate alone, [inter x hidden])."""
+    lib = load()
+    gu = lib.sv_q2_matrix_bytes(inter, hidden)
+    if ffn == SV_FFN_PLAIN:
+        _want(w_gate, "w_gate", "u8", min_bytes=gu)
+        if gu == 0:
+            raise ValueError(f"no two-bit matrix of shape [{inter} x {hidden}]")
+    else:
+        dn = lib.sv_q2_matrix_bytes(hidden, inter)
+        if gu == 0 or dn == 0 or n_experts < 1:
+            raise ValueError(f"no SwiGLU layer of hidden {hidden}, inter {inter}, {n_experts} experts")
+        _want(w_gate, "w_gate", "u8", min_bytes=n_experts * gu)
+        _want(w_up, "w_up", "u8", min_bytes=n_experts * gu)
+        _want(w_down, "w_down", "u8", min_bytes=n_experts * dn)
+        if s_gate is not None or s_up is not None or s_down is not None:
+            _want(s_gate, "s_gate", "u8", min_bytes=gu)
+            _want(s_up, "s_up", "u8", min_bytes=gu)
+            _want(s_down, "s_down", "u8", min_bytes=dn)
     _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
     d = MoeDesc(ffn, hidden, inter, n_experts, top_k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down))
@@ -165,10 +213,28 @@ def sv_accept_workspace_bytes(S: int, K: int, V: int) -> int:
 def vq2_moe_gemm(desc: MoeDesc, x, router_logits, y, topk_idx=None, topk_w=None, ws=None,
                  stream=None):
     """y[R, hidden] (PLAIN: [R, inter]) from rows x[R, hidden] (fp32 or bf16)."""
-    _dev_check(x, router_logits, y, topk_idx, topk_w, ws)
+    _want(x, "x", "act")
+    if x.dim() != 2:
+        raise ValueError(f"x: shape {tuple(x.shape)}, expected [R, {desc.hidden}]")
     R = x.shape[0]
+    _want(x, "x", "act", (R, desc.hidden))
+    plain = desc.ffn == SV_FFN_PLAIN
+    _want(y, "y", "f32", (R, desc.inter if plain else desc.hidden))
+    if router_logits is not None or (not plain and desc.n_experts > 1):
+        _want(router_logits, "router_logits", "f32", (R, desc.n_experts))
+    k = 1 if plain else desc.top_k
+    if topk_idx is not None:
+        _want(topk_idx, "topk_idx", "i32", (R, k))
+    if topk_w is not None:
+        _want(topk_w, "topk_w", "f32", (R, k))
+    need = sv_moe_workspace_bytes(desc, R)
+    if need == 0:
+        raise ValueError(f"invalid layer description or row count R = {R}")
+    if ws is not None:
+        _want(ws, "ws", "u8", min_bytes=need)
+    _dev_check(x, router_logits, y, topk_idx, topk_w, ws)
     if ws is None:
-        ws = _workspace(sv_moe_workspace_bytes(desc, R), x)
+        ws = _workspace(need, x)
     st = load().vq2_moe_gemm(ctypes.byref(desc), _ptr(x), _act_dtype(x), R, _ptr(router_logits),
                              _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws.numel(),
                              _stream(stream))
@@ -178,10 +244,21 @@ def vq2_moe_gemm(desc: MoeDesc, x, router_logits, y, topk_idx=None, topk_w=None,
 
 def vq8_lmhead_gemm(w, vocab: int, hidden: int, h, logits, ws=None, stream=None):
     """logits[R, vocab] from hidden rows h[R, hidden] (fp32 or bf16)."""
-    _dev_check(w, h, logits, ws)
+    _want(w, "w", "u8", min_bytes=max(sv_q8_matrix_bytes(vocab, hidden), 1))
+    _want(h, "h", "act")
+    if h.dim() != 2:
+        raise ValueError(f"h: shape {tuple(h.shape)}, expected [R, {hidden}]")
     R = h.shape[0]
+    _want(h, "h", "act", (R, hidden))
+    _want(logits, "logits", "f32", (R, vocab))
+    need = sv_lmhead_workspace_bytes(hidden, R)
+    if need == 0 or sv_q8_matrix_bytes(vocab, hidden) == 0:
+        raise ValueError(f"invalid head shape vocab {vocab} x hidden {hidden} or row count R = {R}")
+    if ws is not None:
+        _want(ws, "ws", "u8", min_bytes=need)
+    _dev_check(w, h, logits, ws)
     if ws is None:
-        ws = _workspace(sv_lmhead_workspace_bytes(hidden, R), h)
+        ws = _workspace(need, h)
     st = load().vq8_lmhead_gemm(_ptr(w), vocab, hidden, _ptr(h), _act_dtype(h), R, _ptr(logits),
                                 _ptr(ws), ws.numel(), _stream(stream))
     _check("vq8_lmhead_gemm", st)
@@ -194,9 +271,21 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float, dr
     """Accept/reject for S sequences of K drafts; fills out_tokens [S, K+1] and
     out_n_accepted [S] (int32).  A logits row at temperature 0 is greedy: the
     one-hot distribution at its first largest value."""
+    need = sv_accept_workspace_bytes(S, K, V)
+    if need == 0:
+        raise ValueError(f"invalid accept shape S = {S}, K = {K}, V = {V}")
+    _want(target, "target", "f32", (S * (K + 1), V))
+    if K > 0:
+        _want(draft, "draft", "f32", (S * K, V))
+        _want(draft_tokens, "draft_tokens", "i32", (S, K))
+    _want(uniforms, "uniforms", "f32", (S, K + 1))
+    _want(out_tokens, "out_tokens", "i32", (S, K + 1))
+    _want(out_n_accepted, "out_n_accepted", "i32", (S,))
+    if ws is not None:
+        _want(ws, "ws", "u8", min_bytes=need)
     _dev_check(target, draft, draft_tokens, uniforms, out_tokens, out_n_accepted, ws)
     if ws is None:
-        ws = _workspace(sv_accept_workspace_bytes(S, K, V), target)
+        ws = _workspace(need, target)
     st = load().spec_accept(S, K, V, _ptr(target), target_kind, t_p, _ptr(draft), draft_kind, t_q,
                             _ptr(draft_tokens), _ptr(uniforms), _ptr(out_tokens),
                             _ptr(out_n_accepted), _ptr(ws), ws.numel(), _stream(stream))
@@ -205,12 +294,22 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float, dr
 
 
 def vq2_dequant(w, n_out: int, k_in: int, out, stream=None):
+    nb = sv_q2_matrix_bytes(n_out, k_in)
+    if nb == 0:
+        raise ValueError(f"no two-bit matrix of shape [{n_out} x {k_in}]")
+    _want(w, "w", "u8", min_bytes=nb)
+    _want(out, "out", "f32", (n_out, k_in))
     _dev_check(w, out)
     _check("vq2_dequant", load().vq2_dequant(_ptr(w), n_out, k_in, _ptr(out), _stream(stream)))
     return out
 
 
 def vq8_dequant(w, n_out: int, k_in: int, out, stream=None):
+    nb = sv_q8_matrix_bytes(n_out, k_in)
+    if nb == 0:
+        raise ValueError(f"no eight-bit matrix of shape [{n_out} x {k_in}]")
+    _want(w, "w", "u8", min_bytes=nb)
+    _want(out, "out", "f32", (n_out, k_in))
     _dev_check(w, out)
     _check("vq8_dequant", load().vq8_dequant(_ptr(w), n_out, k_in, _ptr(out), _stream(stream)))
     return out

@@ -447,21 +447,26 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
   double w = inv ? 0.0 : seg_weight(mode, P, pm, pz, Q, qm, qz, c, V);
   // 4. the last block of the sequence to get here samples.  The sums go out
   //    as device-scope stores (written through to the point of coherence of
-  //    all XCDs, not held in this XCD's L2) and every one has completed
-  //    before the block counts itself done; the last block reads them back
-  //    with device-scope loads
+  //    all XCDs, not held in this XCD's L2); every thread then makes its
+  //    stores visible at device scope (a release fence, which also waits for
+  //    them to complete), the block meets, and one thread counts the block
+  //    done with a release increment.  The block that brings the count to
+  //    the total acquires before it reads the sums back (device-scope
+  //    loads): every other block's stores happen before its reads.
   __hip_atomic_store(&ws.tsum[((size_t)s * CHs + c) * ACC_T + tid], w, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
   w = block_sum_d(w, sh);
   if (tid == 0)
     __hip_atomic_store(&ws.rsum[(size_t)s * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   wait_vmcnt_le(0);
   __syncthreads();
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_last = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
              (unsigned)(CHs - 1);
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   int32_t* out = out_tokens + (size_t)s * (K + 1);
   if (inv) {
     if (tid <= K) out[tid] = -1;

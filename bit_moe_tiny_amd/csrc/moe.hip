@@ -165,9 +165,12 @@ __device__ inline int wave_incl_scan(int x) {
 
 // Order-preserving key of a logit: larger logit -> larger key; NaN -> 0, the
 // smallest (NaN ranks after every number, as in an ascending sort of -logit).
+// Both zeros are one value and get one key (that of +0), so that -0 and +0
+// tie and the lower index wins, as for any other pair of equal logits.
 __device__ inline uint32_t logit_key(float f) {
   const uint32_t u = __float_as_uint(f);
   if (f != f) return 0u;
+  if (f == 0.f) return 0x80000000u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

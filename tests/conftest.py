@@ -28,3 +28,15 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The worst row-relative error each floating-point comparison reached,
+    against its tolerance (the margin to the bar), in the order they ran."""
+    from tests.parity import MARGINS
+    if not MARGINS:
+        return
+    tr = terminalreporter
+    tr.section("parity margins: worst row-relative error / tolerance")
+    for what, worst, tol in MARGINS:
+        tr.write_line(f"{worst:10.3e} / {tol:.0e}  {what}")

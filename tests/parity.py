@@ -13,6 +13,10 @@ REL_TOL = 2e-3
 FLOOR = 1e-3
 FLAG_BAND = 1e-6
 
+# (what, worst row-relative error, tolerance) of every comparison made in this
+# process; printed at the end of the run (tests/conftest.py)
+MARGINS = []
+
 
 def rel_err_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
     got = np.asarray(got, np.float64)
@@ -29,6 +33,7 @@ def rel_err_rows(got: np.ndarray, want: np.ndarray) -> np.ndarray:
 def assert_close(got, want, tol: float = REL_TOL, what: str = ""):
     e = rel_err_rows(got, want)
     worst = float(e.max()) if e.size else 0.0
+    MARGINS.append((what, worst, tol))
     assert np.all(np.isfinite(np.asarray(got, np.float64))), f"{what}: non-finite output"
     assert worst <= tol, f"{what}: max row-relative error {worst:.3e} > {tol:.1e}"
     return worst

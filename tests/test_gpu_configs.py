@@ -4,14 +4,16 @@ configuration the benchmark times, on outputs the oracle computes one by one.
 * one SwiGLU expert (7168 -> 2048 -> 7168, two-bit) on R = 1, 2, 4, 8 bf16
   rows: every output against the oracle;
 * the full MoE layer (256 routed + 1 shared experts, top-8) on R = 5 rows:
-  routing indices bit-exact for every row, routing weights and two sampled rows
-  of y against the oracle;
-* the vocabulary head (129,280 x 7,168, eight-bit) on R = 5 rows: a sample of
-  vocabulary rows (head, tail and random) against the oracle, then spec_accept
-  at V = 129,280 and T = 0.8 on the GPU's logits (T_q = 0.8 and the T_q = 1
-  variant), decisions compared with the oracle's on identical inputs;
-* the cohort: 3 sequences x 5 rows = 15 rows through the same layer and head,
-  per-sequence spec_accept;
+  routing indices bit-exact for every row, routing weights and every row of y
+  against the oracle;
+* the vocabulary head (129,280 x 7,168, eight-bit) on R = 5 rows: every logit
+  against the oracle, then spec_accept at V = 129,280 and T = 0.8 on the GPU's
+  logits (T_q = 0.8 and the T_q = 1 variant), decisions compared with the
+  oracle's on identical inputs;
+* the cohort: 3 sequences x 5 rows = 15 rows through the same layer (every row
+  of y against the oracle) and head, per-sequence spec_accept;
+* run-to-run determinism: the layer, the head and spec_accept repeated on the
+  same inputs give bit-identical outputs;
 * the R = 1..16 stress sweep: every R against the oracle on sampled vocabulary
   rows, and every row of every R-row MoE call against the oracle (the routing
   bit-exact; the expert sums may round differently with the batch, since an
@@ -132,7 +134,7 @@ def test_expert_workload(sv, R):
     sv.vq2_moe_gemm(desc, dev(ex.x_bf16), None, y)
     x64 = oracle.linalg._exact_rows(ex.x_bf16, "bf16")
     want = oracle.swiglu_expert(g, u, d, H, I, x64)
-    assert_close(host(y), want, what=f"expert R={R}")
+    assert_close(host(y), want, what=f"one expert R={R} y (every output)")
 
 
 # ------------------------------------------------------------- MoE layer
@@ -143,10 +145,10 @@ def test_moe_layer_workload(sv, layer):
     y, ti, tw = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
     widx, ww = oracle.route_topk(rows.router_logits, TOPK)
     assert np.array_equal(ti, widx)
-    assert_close(tw, ww, what="topk_w")
-    check = [0, 4]
-    want = _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check)
-    assert_close(y[check], want, what="moe layer y")
+    assert_close(tw, ww, what="moe layer R=5 topk_w")
+    say("oracle MoE output, all 5 rows")
+    want = _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, list(range(5)))
+    assert_close(y, want, what="moe layer R=5 y (every row)")
 
 
 # ---------------------------------------------------------------- router
@@ -164,15 +166,16 @@ def test_router_gemv_then_layer(sv, layer):
     say("vq8_lmhead_gemm router GEMV [256 x 7168] R=5")
     sv.vq8_lmhead_gemm(dev(wr), E, H, dev(rows.x_bf16), z)
     z = host(z)
-    assert_close(z, oracle.lm_head_logits(wr, E, H, rows.x_bf16, "bf16"), what="router logits")
+    assert_close(z, oracle.lm_head_logits(wr, E, H, rows.x_bf16, "bf16"), what="router GEMV logits [256 x 7168] R=5")
     say("vq2_moe_gemm on the router GEMV's logits R=5")
     y, ti, tw = _run_moe(sv, desc, rows.x_bf16, z)
     widx, ww = oracle.route_topk(z, TOPK)
     assert np.array_equal(ti, widx)
-    assert_close(tw, ww, what="topk_w")
+    assert_close(tw, ww, what="router GEMV R=5 topk_w")
     assert len(np.unique(ti)) > 2 * TOPK   # the rows route to different experts
-    check = [1, 3]
-    assert_close(y[check], _oracle_moe_rows(w, rows.x_bf16, z, check), what="moe layer y (router GEMV)")
+    say("oracle MoE output on the router GEMV's logits, all 5 rows")
+    assert_close(y, _oracle_moe_rows(w, rows.x_bf16, z, list(range(R))),
+                 what="moe layer R=5 y on router GEMV logits (every row)")
 
 
 # ------------------------------------------------------------ vocab head
@@ -183,9 +186,9 @@ def test_lm_head_workload_and_accept(sv, head, Tq):
     h = synth.lm_head_hidden(R)
     say("vq8_lmhead_gemm full head R=5")
     z = _run_head(sv, wdev, h)
-    cols = _vocab_sample(31)
-    want = oracle.lm_head_logits(buf, V, H, h, "bf16", rows=cols)
-    assert_close(z[:, cols], want, what="lm head")
+    say("oracle head, every logit")
+    want = oracle.lm_head_logits(buf, V, H, h, "bf16")
+    assert_close(z, want, what=f"lm head R=5 (every logit, T_q={Tq} case)")
     acc = synth.accept_inputs(z, S, K, 1.5, Tq, synth.CFG_LMHEAD)
     _check_accept(sv, z, S, K, T, Tq, acc)
 
@@ -225,16 +228,16 @@ def test_cohort_workload(sv, layer, head):
     y, ti, tw = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
     widx, ww = oracle.route_topk(rows.router_logits, TOPK)
     assert np.array_equal(ti, widx)
-    assert_close(tw, ww, what="topk_w")
-    check = [7, 14]
-    assert_close(y[check], _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, check),
-                 what="cohort moe y")
+    assert_close(tw, ww, what="cohort R=15 topk_w")
+    say("oracle MoE output, all 15 cohort rows")
+    assert_close(y, _oracle_moe_rows(w, rows.x_bf16, rows.router_logits, list(range(R))),
+                 what="cohort R=15 moe y (every row)")
     h = synth.lm_head_hidden(R, synth.CFG_COHORT)
     say("vq8_lmhead_gemm cohort R=15")
     z = _run_head(sv, wdev, h)
     cols = _vocab_sample(32, 1024)
     assert_close(z[:, cols], oracle.lm_head_logits(buf, V, H, h, "bf16", rows=cols),
-                 what="cohort head")
+                 what="cohort head R=15 (1,024 sampled vocabulary rows)")
     acc = synth.accept_inputs(z, S, K, 1.5, T, synth.CFG_COHORT)
     _check_accept(sv, z, S, K, T, T, acc)
 
@@ -271,7 +274,7 @@ def test_sweep_moe_rows(sv, layer, sweep16, R):
     say("vq2_moe_gemm sweep", R)
     y, ti, _ = _run_moe(sv, desc, rows.x_bf16[:R].copy(), rows.router_logits[:R].copy())
     assert np.array_equal(ti, ti16[:R])
-    assert_close(y, y_or[:R], what=f"moe R={R}")
+    assert_close(y, y_or[:R], what=f"sweep moe R={R} y (every row)")
 
 
 @pytest.mark.parametrize("R", list(range(1, 17)))
@@ -282,7 +285,7 @@ def test_sweep_lm_head(sv, head, sweep16, R):
     z = _run_head(sv, wdev, h[:R].copy())
     cols = _vocab_sample(100 + R, 512)
     assert_close(z[:, cols], oracle.lm_head_logits(buf, V, H, h[:R], "bf16", rows=cols),
-                 what=f"head R={R}")
+                 what=f"sweep head R={R} (512 sampled vocabulary rows)")
     assert_close(z, z16[:R], tol=1e-5, what=f"head R={R} vs R=16")
 
 
@@ -318,3 +321,34 @@ def test_full_vocab_probs_exact(sv, S, K):
         pr = p[s * (K + 1) + n].astype(np.float64)
         wgt = np.maximum(pr - q[s * K + n], 0.0) if n < K else pr
         assert sample_flag(wgt, u[s, K]), f"sequence {s}: {gt[s]} vs {wt[s]}"
+
+
+# ----------------------------------------------------------- determinism
+def test_repeat_bit_identical(sv, layer, head):
+    """The three calls, repeated on the same inputs, give the same bits (every
+    summation order is fixed; no atomics decide a floating-point order)."""
+    _, desc = layer
+    _, wdev = head
+    R, S, K, T = 5, 1, 4, 0.8
+    rows = synth.moe_rows(R, synth.CFG_MOE)
+    h = synth.lm_head_hidden(R)
+    say("determinism: layer, head and accept three times each")
+    outs = []
+    for _ in range(3):
+        y, ti, tw = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
+        z = _run_head(sv, wdev, h)
+        outs.append((y, ti, tw, z))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+    z = outs[0][3]
+    acc = synth.accept_inputs(z, S, K, 1.5, T, synth.CFG_LMHEAD)
+    res = []
+    for _ in range(3):
+        toks = empty((S, K + 1), "i32")
+        nacc = empty((S,), "i32")
+        sv.spec_accept(S, K, V, dev(z), sv.SV_LOGITS, T, dev(acc.draft_logits), sv.SV_LOGITS, T,
+                       dev(acc.drafts), dev(acc.uniforms), toks, nacc)
+        res.append((host(toks), host(nacc)))
+    for r in res[1:]:
+        assert np.array_equal(r[0], res[0][0]) and np.array_equal(r[1], res[0][1])

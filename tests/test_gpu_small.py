@@ -113,8 +113,71 @@ def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
     sv.vq2_moe_gemm(desc, dev(x), dev(logits), y, ti, tw)
     want, widx, ww = oracle.moe_layer(g, u, d, sg, su, sd, E, k, hidden, inter, x, dt, logits)
     assert np.array_equal(host(ti), widx)
-    assert_close(host(tw), ww, what="topk_w")
-    assert_close(host(y), want, what="moe y")
+    assert_close(host(tw), ww, what=f"small moe E={E} k={k} {hidden}x{inter} R={R} {dt} topk_w")
+    assert_close(host(y), want, what=f"small moe E={E} k={k} {hidden}x{inter} R={R} shared={shared} {dt} y")
+
+
+# ------------------------------------------------------------ routing ties
+def _tie_logits(R, E, seed):
+    """Router rows built to exercise the tie-breaking rule (equal logits: the
+    lower index first), each kind of row twice:
+    integer logits in -3..3 (the top value tied at many indices in every
+    64-expert slot); all zeros with mixed signs except a few negatives (+0 and
+    -0 tie); zeros of both signs planted at indices 3 (-0), 5 (+0), 69 (-0),
+    132 (+0) and 200 (-0) among negatives; rows with -inf entries (fewer than
+    k finite logits in one row), rows with NaN entries (NaN ranks last), a row
+    with a +inf entry, and an all -inf row."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for _ in range(2):
+        rows.append(rng.integers(-3, 4, size=E).astype(np.float32))
+        z = np.where(rng.random(E) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        z[rng.choice(E, 40, replace=False)] = -rng.random(40).astype(np.float32) - 0.5
+        rows.append(z)
+        z = -rng.random(E).astype(np.float32) - 1.0
+        for i, v in ((3, -0.0), (5, 0.0), (69, -0.0), (132, 0.0), (200, -0.0)):
+            z[i] = np.float32(v)
+        rows.append(z)
+        z = rng.integers(-2, 3, size=E).astype(np.float32)
+        z[rng.choice(E, E - 5, replace=False)] = -np.inf
+        rows.append(z)
+        z = rng.integers(-2, 3, size=E).astype(np.float32)
+        z[rng.choice(E, 60, replace=False)] = np.nan
+        rows.append(z)
+    z = synth.normal_f32(synth.generator(seed), (E,))
+    z[17] = np.inf
+    rows.append(z)
+    rows.append(np.full(E, -np.inf, np.float32))
+    lg = np.stack(rows)[:R].astype(np.float32)
+    assert lg.shape == (R, E)
+    return lg
+
+
+def test_routing_ties_bit_exact(sv):
+    """256 experts, top-8: the indices match the oracle's exactly on rows full
+    of ties (across 64-lane slots and between -0 and +0) and on rows with
+    infinities and NaNs; the weights match where finite and are NaN at the
+    same places."""
+    E, k, hidden, inter, R = 256, 8, 256, 256, 12
+    (g, u, d), _ = _small_moe(E, hidden, inter, False, 150)
+    lg = _tie_logits(R, E, 151)
+    x = synth.normal_bf16(synth.generator(152), (R, hidden))
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, hidden, inter, E, k, dev(g), dev(u), dev(d))
+    y = empty((R, hidden), "f32")
+    ti = empty((R, k), "i32")
+    tw = empty((R, k), "f32")
+    say("vq2_moe_gemm routing ties E=256 k=8 R=12")
+    sv.vq2_moe_gemm(desc, dev(x), dev(lg), y, ti, tw)
+    gi, gw = host(ti), host(tw)
+    widx, ww = oracle.route_topk(lg, k)
+    assert np.array_equal(gi, widx), f"routing differs:\n{gi}\n{widx}"
+    assert np.array_equal(np.isnan(gw), np.isnan(ww))
+    fin = np.isfinite(ww)
+    assert np.allclose(gw[fin], ww[fin], rtol=1e-5, atol=0)
+    # the rows whose weights are all finite: the layer output against the oracle
+    ok = [r for r in range(R) if np.all(np.isfinite(ww[r]))]
+    want, _, _ = oracle.moe_layer(g, u, d, None, None, None, E, k, hidden, inter, x[ok], "bf16", lg[ok])
+    assert_close(host(y)[ok], want, what="moe y (tie rows)")
 
 
 # ------------------------------------------------------------ lm head
@@ -131,7 +194,7 @@ def test_small_lm_head(sv, vocab, hidden, R, dt):
     say("vq8_lmhead_gemm", vocab, hidden, R, dt)
     sv.vq8_lmhead_gemm(dev(buf), vocab, hidden, dev(h), out)
     want = oracle.lm_head_logits(buf, vocab, hidden, h, dt)
-    assert_close(host(out), want, what="lm head")
+    assert_close(host(out), want, what=f"small head {vocab}x{hidden} R={R} {dt}")
 
 
 # ------------------------------------------------------------- accept
