@@ -15,7 +15,8 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
-SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = range(5)
+SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP, SV_ESCRATCH = range(6)
+ACCEPT_SCRATCH_BYTES = 16 << 20   # SV_ACCEPT_SCRATCH_BYTES of the header
 SV_F32, SV_BF16 = 0, 1
 SV_FFN_PLAIN, SV_FFN_SWIGLU = 0, 1
 SV_LOGITS, SV_PROBS = 0, 1
@@ -23,7 +24,7 @@ SV_LOGITS, SV_PROBS = 0, 1
 EXPORTS = [
     "sv_api_version", "sv_status_str", "sv_q2_matrix_bytes", "sv_q8_matrix_bytes",
     "sv_moe_workspace_bytes", "vq2_moe_gemm", "sv_lmhead_workspace_bytes", "vq8_lmhead_gemm",
-    "sv_accept_workspace_bytes", "spec_accept", "vq2_dequant", "vq8_dequant",
+    "sv_accept_workspace_bytes", "spec_accept", "spec_accept_noalloc", "vq2_dequant", "vq8_dequant",
 ]
 
 
@@ -56,6 +57,8 @@ _SIGS = {
     "sv_accept_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "spec_accept": ([_i32, _i32, _i32, _vp, _i32, _f32, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp,
                      _sz, _vp], ctypes.c_int),
+    "spec_accept_noalloc": ([_i32, _i32, _i32, _vp, _i32, _f32, _vp, _i32, _f32, _vp, _vp, _vp, _vp,
+                             _vp], ctypes.c_int),
     "vq2_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "vq8_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
 }
@@ -290,6 +293,30 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float, dr
                             _ptr(draft_tokens), _ptr(uniforms), _ptr(out_tokens),
                             _ptr(out_n_accepted), _ptr(ws), ws.numel(), _stream(stream))
     _check("spec_accept", st)
+    return out_tokens, out_n_accepted
+
+
+def spec_accept_noalloc(S: int, K: int, V: int, target, target_kind: int, t_p: float, draft,
+                        draft_kind: int, t_q: float, draft_tokens, uniforms, out_tokens,
+                        out_n_accepted, stream=None):
+    """spec_accept on the library's static scratch array: no workspace, no
+    allocation (for callers that cannot allocate, e.g. under graph capture).
+    Calls that overlap on one GPU race; raises SvError(SV_ESCRATCH) when the
+    shape needs more than the array holds."""
+    if sv_accept_workspace_bytes(S, K, V) == 0:
+        raise ValueError(f"invalid accept shape S = {S}, K = {K}, V = {V}")
+    _want(target, "target", "f32", (S * (K + 1), V))
+    if K > 0:
+        _want(draft, "draft", "f32", (S * K, V))
+        _want(draft_tokens, "draft_tokens", "i32", (S, K))
+    _want(uniforms, "uniforms", "f32", (S, K + 1))
+    _want(out_tokens, "out_tokens", "i32", (S, K + 1))
+    _want(out_n_accepted, "out_n_accepted", "i32", (S,))
+    _dev_check(target, draft, draft_tokens, uniforms, out_tokens, out_n_accepted)
+    st = load().spec_accept_noalloc(S, K, V, _ptr(target), target_kind, t_p, _ptr(draft), draft_kind,
+                                    t_q, _ptr(draft_tokens), _ptr(uniforms), _ptr(out_tokens),
+                                    _ptr(out_n_accepted), _stream(stream))
+    _check("spec_accept_noalloc", st)
     return out_tokens, out_n_accepted
 
 

@@ -65,6 +65,7 @@ const char* sv_status_str(int status) {
     case SV_EUNSUPPORTED: return "unsupported";
     case SV_EWORKSPACE: return "workspace too small";
     case SV_EHIP: return "HIP launch failed";
+    case SV_ESCRATCH: return "request larger than the static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -137,17 +138,73 @@ size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V) {
   return accept_ws_bytes(S, K, V);
 }
 
-int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
-                float T_p, const float* draft, int32_t draft_kind, float T_q,
-                const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
-                int32_t* out_n_accepted, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// Scratch memory of spec_accept_noalloc: one copy per GPU, for the life of the
+// process.  In host code `scratch` only names the symbol; its device address
+// (different on every GPU) comes from hipGetSymbolAddress, looked up once per
+// device on that device's first call and cached.
+static __device__ __align__(256) uint8_t scratch[SV_ACCEPT_SCRATCH_BYTES];
+
+namespace {
+
+int accept_args_ok(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
+                   float T_p, const float* draft, int32_t draft_kind, float T_q,
+                   const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
+                   int32_t* out_n_accepted) {
   if (!accept_shape_ok(S, K, V)) return SV_EINVAL;
-  if (!target || !uniforms || !out_tokens || !out_n_accepted || !ws) return SV_EINVAL;
+  if (!target || !uniforms || !out_tokens || !out_n_accepted) return SV_EINVAL;
   if (K > 0 && (!draft || !draft_tokens)) return SV_EINVAL;
   if (!kind_ok(target_kind) || (K > 0 && !kind_ok(draft_kind))) return SV_EINVAL;
   if (target_kind == SV_LOGITS && !(isfinite(T_p) && T_p >= 0.f)) return SV_EINVAL;
   if (K > 0 && draft_kind == SV_LOGITS && !(isfinite(T_q) && T_q >= 0.f)) return SV_EINVAL;
+  return SV_OK;
+}
+
+constexpr int MAX_DEV = 64;
+std::atomic<void*> scratch_ptr[MAX_DEV];
+
+// Device address of this device's scratch array, or null (lookup failed).
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
+                float T_p, const float* draft, int32_t draft_kind, float T_q,
+                const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
+                int32_t* out_n_accepted, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = accept_args_ok(S, K, V, target, target_kind, T_p, draft, draft_kind, T_q,
+                                draft_tokens, uniforms, out_tokens, out_n_accepted);
+  if (st != SV_OK) return st;
+  if (!ws) return SV_EINVAL;
   if (ws_bytes < accept_ws_bytes(S, K, V)) return SV_EWORKSPACE;
+  return hip_status(launch_accept(S, K, V, target, target_kind, T_p, draft,
+                                  K > 0 ? draft_kind : target_kind, T_q, draft_tokens, uniforms,
+                                  out_tokens, out_n_accepted, ws, stream));
+}
+
+int spec_accept_noalloc(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
+                        float T_p, const float* draft, int32_t draft_kind, float T_q,
+                        const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
+                        int32_t* out_n_accepted, hipStream_t stream) {
+  const int st = accept_args_ok(S, K, V, target, target_kind, T_p, draft, draft_kind, T_q,
+                                draft_tokens, uniforms, out_tokens, out_n_accepted);
+  if (st != SV_OK) return st;
+  if (accept_ws_bytes(S, K, V) > SV_ACCEPT_SCRATCH_BYTES) return SV_ESCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return SV_EHIP;
+  // the same kernels as spec_accept, on the scratch array; the per-sequence
+  // counters they need at zero are cleared by the first of them
   return hip_status(launch_accept(S, K, V, target, target_kind, T_p, draft,
                                   K > 0 ? draft_kind : target_kind, T_q, draft_tokens, uniforms,
                                   out_tokens, out_n_accepted, ws, stream));

@@ -20,8 +20,9 @@
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
  *    memory, including workspaces; the library never allocates, frees or
- *    synchronises, and keeps no global state beyond a per-device cache of the
- *    compute-unit count (used to size persistent grids).
+ *    synchronises.  Its only global state: a per-device cache of the
+ *    compute-unit count (used to size persistent grids), and the static scratch
+ *    array of spec_accept_noalloc with its per-device address.
  *  - Work is enqueued on `stream` (0 = the null stream).  Calls on different
  *    streams are independent when their workspaces and outputs are distinct.
  *  - Arguments are validated on the host before anything is enqueued; a
@@ -54,7 +55,8 @@ enum sv_status {
   SV_EINVAL = 1,        /* invalid argument; nothing enqueued */
   SV_EUNSUPPORTED = 2,  /* valid but outside what this build implements */
   SV_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() */
-  SV_EHIP = 4           /* a HIP launch failed */
+  SV_EHIP = 4,          /* a HIP launch failed */
+  SV_ESCRATCH = 5       /* needs more than the library's static scratch buffer */
 };
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };   /* element type of activation rows */
@@ -203,6 +205,26 @@ SV_API int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int
                 float T_p, const float* draft, int32_t draft_kind, float T_q,
                 const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
                 int32_t* out_n_accepted, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * spec_accept without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, rule, outputs and validation as
+ * spec_accept; its scratch memory is a static device array of
+ * SV_ACCEPT_SCRATCH_BYTES inside the library (one per GPU, held until the
+ * process ends; its address is looked up on the first call on each device).
+ * Allocates nothing.  Returns SV_ESCRATCH, with nothing enqueued, when
+ * sv_accept_workspace_bytes(S, K, V) exceeds SV_ACCEPT_SCRATCH_BYTES (at
+ * V = 129,280 and K = 4: up to 31 sequences).  Every call on one GPU uses that
+ * GPU's one array: calls whose executions overlap on one GPU (different
+ * streams, or several host threads) race and give undefined results; calls
+ * ordered on one stream are safe.
+ */
+#define SV_ACCEPT_SCRATCH_BYTES ((size_t)16 << 20)
+SV_API int spec_accept_noalloc(int32_t S, int32_t K, int32_t V, const float* target,
+                int32_t target_kind, float T_p, const float* draft, int32_t draft_kind,
+                float T_q, const int32_t* draft_tokens, const float* uniforms,
+                int32_t* out_tokens, int32_t* out_n_accepted, hipStream_t stream);
 
 /*
  * Test exports: the dequantised weights [n_out, k_in] fp32.  Two-bit: the exact

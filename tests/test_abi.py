@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = sv.load()
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(sv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -106,6 +106,16 @@ def test_calls_reject_bad_arguments_before_launch():
     assert lib.spec_accept(*args(tok=None)) == sv.SV_EINVAL
     assert lib.spec_accept(*args(K=32)) == sv.SV_EINVAL
     assert lib.spec_accept(*args(wsb=8)) == sv.SV_EWORKSPACE
+    # the allocation-free variant: the same argument checks, and shapes whose
+    # scratch need exceeds the static array are refused before any HIP call
+    nargs = lambda **k: args(**k)[:13] + [None]
+    assert lib.spec_accept_noalloc(*nargs(tp=-0.5)) == sv.SV_EINVAL
+    assert lib.spec_accept_noalloc(*nargs(draft=None)) == sv.SV_EINVAL
+    assert lib.spec_accept_noalloc(*nargs(K=32)) == sv.SV_EINVAL
+    assert sv.sv_accept_workspace_bytes(40, 4, 129280) > sv.ACCEPT_SCRATCH_BYTES
+    assert sv.sv_accept_workspace_bytes(31, 4, 129280) <= sv.ACCEPT_SCRATCH_BYTES
+    assert lib.spec_accept_noalloc(*nargs(S=40, V=129280)) == sv.SV_ESCRATCH
+    assert "scratch" in sv.status_str(sv.SV_ESCRATCH)
     assert lib.vq2_dequant(fake, 10, 100, fake, None) == sv.SV_EINVAL
     assert lib.vq8_dequant(fake, 10, 33, fake, None) == sv.SV_EINVAL
 
