@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=3, help="routed experts in the oracle sample")
     ap.add_argument("--cpu-vocab", type=int, default=16384, help="vocab rows in the oracle sample")
+    ap.add_argument("--bw-probe-gib", type=float, default=2.0,
+                    help="buffer size of the read-bandwidth probe (0: skip it)")
+    ap.add_argument("--bw-probe-only", action="store_true",
+                    help="run only the read-bandwidth probe and print its JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, one plain device copy of this many MiB (fp32 x 1.0): "
                          "the known-size kernel that calibrates profiler byte counters")
@@ -174,6 +178,43 @@ def measure(step, steps, warmup):
     moe_b = np.array([step.moe_bytes(i) for i in range(steps)], np.float64)
     return dict(total_ms=total_ms, wall_s=wall, moe_ms=moe, lm_ms=lm, acc_ms=acc, step_ms=step_ms,
                 moe_bytes=moe_b)
+
+
+PROBE_MODES = {0: "plain loads to registers, full lines", 1: "global-to-LDS, non-temporal, full lines",
+               2: "global-to-LDS, full lines", 3: "global-to-LDS, 64-byte pieces",
+               4: "global-to-LDS, non-temporal, 64-byte pieces",
+               5: "global-to-LDS 4-byte loads, non-temporal (7 KB of every 28 KB group)"}
+
+
+def bw_probe(sv, gib: float, reps: int = 10):
+    """Read bandwidth of the part with the weight kernels' own load
+    instructions (sv_read_probe), each mode timed with HIP events on its launch
+    stream over `reps` launches on a buffer far larger than the last-level
+    cache: the median GB/s per mode."""
+    import torch
+    nbytes = int(gib * (1 << 30)) // sv.PROBE_GROUP_BYTES * sv.PROBE_GROUP_BYTES
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    sink = torch.empty(8 * torch.cuda.get_device_properties(0).multi_processor_count, dtype=torch.int32,
+                       device="cuda")
+    out = {}
+    for mode, what in PROBE_MODES.items():
+        sv.sv_read_probe(src, mode, sink)   # warm-up
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            nread = sv.sv_read_probe(src, mode, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        if mode == 5:
+            nread = nread // 4   # 7 KB of every 28 KB group
+        out[str(mode)] = {"what": what, "GB/s": round(nread / float(np.median(ts)) / 1e9, 1),
+                          "us": round(float(np.median(ts)) * 1e6, 1)}
+    del src
+    torch.cuda.synchronize()
+    return {"bytes": nbytes, "modes": out}
 
 
 def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
@@ -304,6 +345,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.bw_probe_only:
+        log(f"read-bandwidth probe on {args.bw_probe_gib} GiB")
+        print(json.dumps({"bw_probe": bw_probe(sv, args.bw_probe_gib)}), flush=True)
+        return
     t = time.time()
     log("generating 257 two-bit experts (3.7 GB) ...")
     (g, u, d), (sg, su, sd) = gen_moe_weights()

@@ -22,9 +22,11 @@ SV_FFN_PLAIN, SV_FFN_SWIGLU = 0, 1
 SV_LOGITS, SV_PROBS = 0, 1
 
 EXPORTS = [
-    "sv_api_version", "sv_status_str", "sv_q2_matrix_bytes", "sv_q8_matrix_bytes",
+    "sv_api_version", "sv_status_str", "sv_q2_matrix_bytes", "sv_q2_tiled_bytes", "sv_q2_tile",
+    "sv_q8_matrix_bytes",
     "sv_moe_workspace_bytes", "vq2_moe_gemm", "sv_lmhead_workspace_bytes", "vq8_lmhead_gemm",
     "sv_accept_workspace_bytes", "spec_accept", "spec_accept_noalloc", "vq2_dequant", "vq8_dequant",
+    "sv_read_probe",
 ]
 
 
@@ -48,6 +50,8 @@ _SIGS = {
     "sv_api_version": ([], ctypes.c_int),
     "sv_status_str": ([ctypes.c_int], ctypes.c_char_p),
     "sv_q2_matrix_bytes": ([_i32, _i32], _sz),
+    "sv_q2_tiled_bytes": ([_i32, _i32], _sz),
+    "sv_q2_tile": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "sv_q8_matrix_bytes": ([_i32, _i32], _sz),
     "sv_moe_workspace_bytes": ([ctypes.POINTER(MoeDesc), _i32], _sz),
     "vq2_moe_gemm": ([ctypes.POINTER(MoeDesc), _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -61,6 +65,7 @@ _SIGS = {
                              _vp], ctypes.c_int),
     "vq2_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "vq8_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "sv_read_probe": ([_vp, _sz, _i32, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -170,12 +175,53 @@ def sv_q8_matrix_bytes(n_out: int, k_in: int) -> int:
     return load().sv_q8_matrix_bytes(n_out, k_in)
 
 
+def sv_q2_tiled_bytes(n_out: int, k_in: int) -> int:
+    return load().sv_q2_tiled_bytes(n_out, k_in)
+
+
+def sv_q2_tile(src, n_out: int, k_in: int, parts: int, count: int = 1, out=None, stream=None):
+    """The `count` two-bit matrices [n_out x k_in] of the byte tensor ``src``
+    (back to back) in the expert-tiled layout with `parts` K ranges (4 for
+    gate and up, 1 for down); returns ``out`` (allocated when None)."""
+    import torch
+    a, b = sv_q2_matrix_bytes(n_out, k_in), sv_q2_tiled_bytes(n_out, k_in)
+    if a == 0 or b == 0 or count < 1 or not 1 <= parts <= 64:
+        raise ValueError(f"no tiled layout for {count} matrices [{n_out} x {k_in}], parts {parts}")
+    _want(src, "src", "u8", min_bytes=count * a)
+    if out is None:
+        out = torch.empty(count * b, dtype=torch.uint8, device=src.device)
+    _want(out, "out", "u8", min_bytes=count * b)
+    _dev_check(src, out)
+    _check("sv_q2_tile", load().sv_q2_tile(_ptr(src), _ptr(out), n_out, k_in, parts, count, _stream(stream)))
+    return out
+
+
+def _moe_weights(size, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate, s_up, s_down):
+    """The SwiGLU weight tensors hold the matrices the layer reads, `size`
+    giving the bytes of one matrix in their layout."""
+    gu, dn = size(inter, hidden), size(hidden, inter)
+    if gu == 0 or dn == 0 or n_experts < 1:
+        raise ValueError(f"no SwiGLU layer of hidden {hidden}, inter {inter}, {n_experts} experts")
+    _want(w_gate, "w_gate", "u8", min_bytes=n_experts * gu)
+    _want(w_up, "w_up", "u8", min_bytes=n_experts * gu)
+    _want(w_down, "w_down", "u8", min_bytes=n_experts * dn)
+    if s_gate is not None or s_up is not None or s_down is not None:
+        _want(s_gate, "s_gate", "u8", min_bytes=gu)
+        _want(s_up, "s_up", "u8", min_bytes=gu)
+        _want(s_down, "s_down", "u8", min_bytes=dn)
+    _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
+
+
 def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_gate, w_up=None,
-             w_down=None, s_gate=None, s_up=None, s_down=None) -> MoeDesc:
+             w_down=None, s_gate=None, s_up=None, s_down=None, tiled: bool = False) -> MoeDesc:
     """Layer description over device weight tensors (uint8 byte buffers), each
     checked to hold the matrices the layer reads: n_experts expert-major
     [inter x hidden] gate and up matrices and [hidden x inter] down matrices,
-    one of each for the shared expert (PLAIN: w_gate alone, [inter x hidden])."""
+    one of each for the shared expert (PLAIN: w_gate alone, [inter x hidden]).
+    SWIGLU weights are read in the expert-tiled layout: given in the plain
+    layout (tiled=False) they are regrouped once here, on the device, by
+    sv_q2_tile (gate and up with 4 parts, down with 1), and the description
+    keeps the tiled copies alive."""
     lib = load()
     gu = lib.sv_q2_matrix_bytes(inter, hidden)
     if ffn == SV_FFN_PLAIN:
@@ -183,16 +229,18 @@ def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_ga
         if gu == 0:
             raise ValueError(f"no two-bit matrix of shape [{inter} x {hidden}]")
     else:
-        dn = lib.sv_q2_matrix_bytes(hidden, inter)
-        if gu == 0 or dn == 0 or n_experts < 1:
-            raise ValueError(f"no SwiGLU layer of hidden {hidden}, inter {inter}, {n_experts} experts")
-        _want(w_gate, "w_gate", "u8", min_bytes=n_experts * gu)
-        _want(w_up, "w_up", "u8", min_bytes=n_experts * gu)
-        _want(w_down, "w_down", "u8", min_bytes=n_experts * dn)
-        if s_gate is not None or s_up is not None or s_down is not None:
-            _want(s_gate, "s_gate", "u8", min_bytes=gu)
-            _want(s_up, "s_up", "u8", min_bytes=gu)
-            _want(s_down, "s_down", "u8", min_bytes=dn)
+        if not tiled:
+            _moe_weights(lib.sv_q2_matrix_bytes, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate,
+                         s_up, s_down)
+            w_gate = sv_q2_tile(w_gate, inter, hidden, 4, n_experts)
+            w_up = sv_q2_tile(w_up, inter, hidden, 4, n_experts)
+            w_down = sv_q2_tile(w_down, hidden, inter, 1, n_experts)
+            if s_gate is not None and s_up is not None and s_down is not None:
+                s_gate = sv_q2_tile(s_gate, inter, hidden, 4)
+                s_up = sv_q2_tile(s_up, inter, hidden, 4)
+                s_down = sv_q2_tile(s_down, hidden, inter, 1)
+        _moe_weights(lib.sv_q2_tiled_bytes, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate, s_up,
+                     s_down)
     _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
     d = MoeDesc(ffn, hidden, inter, n_experts, top_k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                 _ptr(s_gate), _ptr(s_up), _ptr(s_down))
@@ -340,3 +388,18 @@ def vq8_dequant(w, n_out: int, k_in: int, out, stream=None):
     _dev_check(w, out)
     _check("vq8_dequant", load().vq8_dequant(_ptr(w), n_out, k_in, _ptr(out), _stream(stream)))
     return out
+
+
+PROBE_GROUP_BYTES = 16 * 1792   # SV_PROBE_GROUP_BYTES of the header
+
+
+def sv_read_probe(src, mode: int, sink, stream=None):
+    """Reads the byte buffer ``src`` once in access pattern ``mode`` (0..3; see
+    the header); ``sink`` is an int32 device tensor of at least 8 words per
+    compute unit.  Returns the number of bytes read."""
+    _want(src, "src", "u8", min_bytes=PROBE_GROUP_BYTES)
+    _want(sink, "sink", "i32")
+    _dev_check(src, sink)
+    _check("sv_read_probe", load().sv_read_probe(_ptr(src), src.numel(), mode, _ptr(sink), sink.numel(),
+                                                 _stream(stream)))
+    return src.numel() // PROBE_GROUP_BYTES * PROBE_GROUP_BYTES

@@ -75,6 +75,24 @@ size_t sv_q2_matrix_bytes(int32_t n_out, int32_t k_in) {
   return q2_bytes((size_t)n_out, (size_t)k_in);
 }
 
+size_t sv_q2_tiled_bytes(int32_t n_out, int32_t k_in) {
+  if (n_out < 16 || n_out % 16 || k_in < 256 || k_in % 256) return 0;
+  return q2_tiled_bytes((size_t)n_out, (size_t)k_in);
+}
+
+int sv_q2_tile(const void* src, void* dst, int32_t n_out, int32_t k_in, int32_t parts, int32_t count,
+               hipStream_t stream) {
+  if (!src || !dst || sv_q2_tiled_bytes(n_out, k_in) == 0 || parts < 1 || parts > 64 || count < 1)
+    return SV_EINVAL;
+  const size_t nblk = (size_t)count * (size_t)n_out * (size_t)(k_in / 256);
+  if (nblk / 256 + 1 > 0x7FFFFFFFu) return SV_EINVAL;   // (grid size)
+  const uint8_t *a = (const uint8_t*)src, *b = (const uint8_t*)dst;
+  const size_t na = (size_t)count * q2_bytes((size_t)n_out, (size_t)k_in);
+  const size_t nbt = (size_t)count * q2_tiled_bytes((size_t)n_out, (size_t)k_in);
+  if (a < b + nbt && b < a + na) return SV_EINVAL;   // overlapping buffers
+  return hip_status(launch_q2_tile(src, dst, n_out, k_in, parts, count, stream));
+}
+
 size_t sv_q8_matrix_bytes(int32_t n_out, int32_t k_in) {
   if (n_out < 1 || k_in < 32 || k_in % 32) return 0;
   return q8_bytes((size_t)n_out, (size_t)k_in);
@@ -102,12 +120,17 @@ int vq2_moe_gemm(const sv_moe_desc* d, const void* x, int32_t x_dtype, int32_t R
     if (st != SV_OK) return st;
     return hip_status(launch_q2_plain(d, R, use_lo, w, y, stream));
   }
+  if (!moe_shape_ok(d)) return SV_EUNSUPPORTED;
   st = hip_status(launch_moe_prep(d, R, d->n_experts > 1 ? router_logits : nullptr, x, x_dtype,
                                   topk_idx, topk_w, w, stream));
   if (st != SV_OK) return st;
-  st = hip_status(launch_q2_gateup(d, R, use_lo, w, stream));
+  st = hip_status(launch_moe_gateup(d, R, w, stream));
   if (st != SV_OK) return st;
-  return hip_status(launch_q2_down(d, R, w, y, stream));
+  st = hip_status(launch_hdig(d, R, w, stream));
+  if (st != SV_OK) return st;
+  st = hip_status(launch_moe_down(d, R, w, stream));
+  if (st != SV_OK) return st;
+  return hip_status(launch_moe_combine(d, R, w, y, stream));
 }
 
 size_t sv_lmhead_workspace_bytes(int32_t hidden, int32_t R) {
@@ -213,6 +236,13 @@ int spec_accept_noalloc(int32_t S, int32_t K, int32_t V, const float* target, in
 int vq2_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream) {
   if (!w || !out || sv_q2_matrix_bytes(n_out, k_in) == 0) return SV_EINVAL;
   return hip_status(launch_q2_dequant(w, n_out, k_in, out, stream));
+}
+
+int sv_read_probe(const void* src, size_t bytes, int32_t mode, uint32_t* sink, size_t sink_words,
+                  hipStream_t stream) {
+  if (!src || !sink || mode < 0 || mode > 5 || bytes < SV_PROBE_GROUP_BYTES) return SV_EINVAL;
+  if (sink_words < read_probe_sink_words()) return SV_EWORKSPACE;
+  return hip_status(launch_read_probe(src, bytes, mode, sink, stream));
 }
 
 int vq8_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream) {

@@ -346,14 +346,6 @@ static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
   return (size_t)waves * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
 }
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t la) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_nt(const void* src, uint32_t la) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
-}
 
 template <bool USE_LO, int LD_WAVES>
 __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W, int R, XImg img,

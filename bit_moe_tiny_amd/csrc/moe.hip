@@ -1,44 +1,33 @@
-// Routed two-bit MoE layer: routing + grouping, fused gate/up/SwiGLU, down
-// projection with a fixed-order weighted combine, and the one-matrix form.
+// Routed two-bit MoE layer: routing and grouping, the staging of x as byte
+// digits, and the weighted combine (the expert kernels are in moe_i8.hip);
+// also the one-matrix (PLAIN) form.
 //
-// Launch sequence of one layer (all on the caller's stream, no host sync):
+// Launch sequence of one SwiGLU layer (all on the caller's stream, no host
+// sync):
 //   k_moe_prep    block 0 routes all rows (top-k on logits, softmax weights;
 //                 one wave per row: a DPP maximum and one ballot per slot per
-//                 round)
-//                 and groups (row, slot) pairs by expert so each touched
+//                 round) and groups (row, slot) pairs by expert so each touched
 //                 expert's weights are read once ("MoE gate_up expert dedup",
-//                 ds4-on-spark README, introduction); the other blocks stage x
-//                 into the fp16 image the two-bit kernels read.
-//   k_q2_gateup_p persistent, 2 blocks per CU of 8 waves (gate and up x 4
-//                 parts of hidden), each block a contiguous range of (work
-//                 item, 16-row tile of inter) with the next item's weight loads
-//                 in flight; the partial sums meet in LDS and one wave applies
-//                 SwiGLU ("fused gate+up+swiglu MoE decode", 1x Spark tuned
-//                 DSpark thread, Q&A answer 3).  h is kept in fp32, and each
-//                 h row's largest magnitude is raised by atomic max (the
-//                 down projection's scale; k_moe_prep clears it).
-//   k_q2_gateup   the same per (tile, work item) block, for shapes the
-//                 persistent kernel does not take.
-//   k_q2_down     grid (128-row group of hidden, unit, column group of at
-//                 most 4 rows), 8 waves of one 16-row tile over all of inter,
-//                 on the int8 matrix cores: the block converts its h rows into
-//                 four fixed-point byte digits each (four tile columns per
-//                 row; the scale from the row's recorded largest magnitude)
-//                 in LDS, the weights enter as the bytes sc * q, every block
-//                 product is exact; per-assignment outputs go to the
-//                 workspace.
+//                 ds4-on-spark README, introduction), emitting the expert
+//                 kernels' descriptors; the other blocks write x as byte digits
+//                 (one block per row).
+//   k_gu8         gate/up + SwiGLU (moe_i8.hip)
+//   k_hdig        the down projection's input rows as digits (one block per
+//                 assignment; SwiGLU of the quarter sums for MOE_QUARTER units)
+//   k_dn8         down projection (moe_i8.hip)
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
-// Blocks never wait on each other inside a kernel: on a part whose L2 is split
-// across dies, a device-wide fence per block would cost far more than the
-// extra launch.
+#include "sv_digits.h"
 #include "sv_internal.h"
 #include "sv_q2.h"
 #include "sv_stage.h"
 
 namespace sv {
 
-constexpr int LDS_BUDGET = 80 * 1024 - 256;   // two 512-thread blocks per CU (160 KB LDS)
+constexpr int LDS_BUDGET = 80 * 1024 - 256;   // one-matrix path: two 512-thread blocks per CU
+
+// Column caps of the expert kernels' descriptors (moe_i8.hip).
+void moe8_caps(const sv_moe_desc* d, int* cap_allk, int* cap_quarter, int* cap_down);
 
 // ------------------------------------------------------------ workspace
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
@@ -64,15 +53,23 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.topk_idx = (int*)take(sizeof(int) * R * k);
   w.topk_w = (float*)take(sizeof(float) * R * k);
   w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
-  w.hmax = (uint32_t*)take(sizeof(uint32_t) * max_assign);
+  w.gpart = (float*)take(plain ? 0 : sizeof(float) * 8 * (size_t)max_assign * d->inter);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
-  // column groups of at least one column: at most one item per unit plus one
-  // per further column
+  // at most one descriptor per unit plus one per further column
   const int max_work = max_units + max_assign;
   w.work_gu = (MoeWork*)take(sizeof(MoeWork) * max_work);
   w.work_dn = (MoeWork*)take(sizeof(MoeWork) * max_work);
-  void* xb = take(ximg_bytes(R, d->hidden, XL_PERM));
-  if (p) w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
+  w.blk_gu = (int*)take(sizeof(int) * (MOE_MAX_GRID + 1));
+  w.blk_dn = (int*)take(sizeof(int) * (MOE_MAX_GRID + 1));
+  w.atype = (int*)take(sizeof(int) * max_assign);
+  void* hd = take(plain ? 0 : xdig_bytes(max_assign, d->inter));
+  void* xd = take(plain ? 0 : xdig_bytes(R, d->hidden));
+  void* xb = take(plain ? ximg_bytes(R, d->hidden, XL_PERM) : 0);
+  if (p) {
+    if (!plain) w.xd = xdig_carve(xd, R, d->hidden);
+    if (!plain) w.hd = xdig_carve(hd, max_assign, d->inter);
+    if (plain) w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
+  }
   w.max_units = max_units;
   w.max_assign = max_assign;
   w.max_work = max_work;
@@ -80,36 +77,15 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   return off;
 }
 
-// Activation rows are copied into LDS in 1 KB pieces.
-
-__host__ __device__ inline int xl_pieces_per_row(int K, bool use_lo) {
-  return ((2 * K + 1023) / 1024) * (use_lo ? 2 : 1) + (K / 4 + 1023) / 1024;
-}
-
-// Largest column group (rows per block) whose LDS copy fits the budget.
+// Largest column group (rows per block) of the one-matrix path whose LDS copy
+// fits the budget.
 static int col_group(int K, bool use_lo, int R) {
   int cg = XL_MAX_COLS;
   while (cg > 1 && xl_bytes(cg, K, use_lo) > (size_t)LDS_BUDGET) --cg;
   return cg < R ? cg : R;
 }
 
-constexpr int DN_THREADS = 512;   // down: 8 waves, one 16-row tile each, all of inter
-constexpr int DN_PAIRS = 4;       // staged (h row, 256-block) pairs per half-wave, at most
-constexpr int DN_MAX_ROWS = 4;    // rows of a down descriptor: one int8 tile of 4 digit columns each
-
-struct GpCfg;
-static GpCfg gp_config(int hidden, int inter, bool use_lo, int R);
-
-static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo);
-
-static int down_cols(const sv_moe_desc* d, int R) {
-  int cg = DN_MAX_ROWS;
-  while (cg > 1 && xl8_bytes(cg, d->inter) > (size_t)LDS_BUDGET) --cg;
-  cg = cg < R ? cg : R;
-  const int pair_cap = DN_PAIRS * (DN_THREADS / 32) / (d->inter / 256);
-  if (cg > pair_cap) cg = pair_cap > 0 ? pair_cap : 1;
-  return cg;
-}
+constexpr int DN_THREADS = 512;   // one-matrix path: 8 waves, one 16-row tile each
 
 // ---------------------------------------------------- wave reductions (DPP)
 // Reductions to lane 63 on the row-shift / row-broadcast network, then one
@@ -178,18 +154,6 @@ __device__ inline float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Raises hmax[a] to |v| (bits; non-negative floats order as unsigned) with the
-// largest value over the lane's 16-lane row: every lane of the row calls it
-// (v = 0 where it has no value), lane 0 of the row does the atomic.
-__device__ inline void note_hmax(uint32_t* hmax, int a, float v, bool any) {
-  uint32_t m = __float_as_uint(fabsf(v));
-  m = max(m, xlane<0xB1>(m));
-  m = max(m, xlane<0x4E>(m));
-  m = max(m, xlane<0x141>(m));
-  m = max(m, xlane<0x140>(m));
-  if (any && (__lane_id() & 15) == 0) atomicMax(hmax + a, m);
-}
-
 // ---------------------------------------------------------------- routing
 constexpr int PREP_THREADS = 1024;
 
@@ -254,33 +218,82 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 }
 
 // Block 0 of the prep kernel: top-k of every row, then grouping.
-// Work items of one expert kernel: each unit's assignments cut into groups
-// of at most cg columns (wave 0).
+// Descriptors of one expert kernel (wave 0): each unit's assignments in
+// column groups.  Gate/up: a unit of at most cap_allk rows is one MOE_ALLK
+// descriptor, a larger one is cut into MOE_QUARTER descriptors of at most
+// cap_big rows; down: groups of at most cap_big rows, typed like the unit's
+// gate/up work.  Then the item ranges of the kernel's G persistent blocks:
+// every descriptor has `items` items, each costing MOE_COST_1 (at most four
+// rows) or MOE_COST_2; block b starts at the first item whose cost offset is
+// at least floor(C b / G) (C the total cost), so the ranges are contiguous,
+// cover every item once and carry about equal cost.
 __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucnt, int nu,
-                          const int* s_arow, int cg, MoeWork* work, int* n_work) {
+                          const int* s_arow, bool gateup, int cap_allk, int cap_big, int items, int G,
+                          MoeWork* work, int* n_work, int* blk, int* s_cost, int* atype) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   for (int u0 = 0; u0 < nu; u0 += 64) {
     const int u = u0 + lane;
-    const int ng = u < nu ? (s_ucnt[u] + cg - 1) / cg : 0;
+    const int cnt = u < nu ? s_ucnt[u] : 0;
+    const int type = cnt <= cap_allk ? MOE_ALLK : MOE_QUARTER;
+    const int grp = (gateup && type == MOE_ALLK) ? cap_allk : cap_big;
+    const int ng = u < nu ? (cnt + grp - 1) / grp : 0;
     const int incl = wave_incl_scan(ng);
     for (int j = 0; j < ng; ++j) {
       MoeWork w;
       w.expert = s_uexp[u];
-      w.a0 = s_uoff[u] + j * cg;
-      w.ncols = min(cg, s_ucnt[u] - j * cg);
-      w.pad = 0;
+      w.a0 = s_uoff[u] + j * grp;
+      w.ncols = min(grp, cnt - j * grp);
+      w.type = type;
 #pragma unroll
       for (int c = 0; c < MOE_WORK_COLS; ++c) w.rows[c] = c < w.ncols ? s_arow[w.a0 + c] : 0;
       work[base + incl - ng + j] = w;
+      s_cost[base + incl - ng + j + 1] = w.ncols > 4 ? MOE_COST_2 : MOE_COST_1;
+      if (gateup)
+        for (int c = 0; c < w.ncols; ++c) atype[w.a0 + c] = type;
     }
     base += __builtin_amdgcn_readlane(incl, 63);
   }
-  if (lane == 0) *n_work = base;
+  const int nd = base;
+  if (lane == 0) *n_work = nd;
+  // s_cost[d] becomes the cost offset of descriptor d's first item
+  if (lane == 0) s_cost[0] = 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  int run = 0;
+  for (int d0 = 1; d0 <= nd; d0 += 64) {
+    const int d = d0 + lane;
+    const int c = d <= nd ? s_cost[d] * items : 0;
+    const int incl = wave_incl_scan(c);
+    if (d <= nd) s_cost[d] = run + incl;
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  const long C = run;
+  for (int b = lane; b <= G; b += 64) {
+    const int c = (int)(C * b / G);
+    int first;
+    if (c >= C) {
+      first = nd * items;
+    } else {   // the descriptor holding cost offset c: largest d with s_cost[d] <= c
+      int lo = 0, hi = nd - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cost[mid] <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      const int w = (s_cost[lo + 1] - s_cost[lo]) / items;
+      first = lo * items + (c - s_cost[lo] + w - 1) / w;
+    }
+    blk[b] = first;
+  }
 }
 
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
-                                int cg_gu, int cg_dn, int32_t* idx_out, float* w_out, MoeWs ws) {
+                                int cap_allk, int cap_quarter, int cap_down, int items_gu, int items_dn, int G,
+                                int32_t* idx_out, float* w_out, MoeWs ws) {
+  // cost offsets of the descriptors (at most one per unit plus one per further row)
+  __shared__ int s_cost_gu[SV_MAX_EXPERTS + 2 + SV_MAX_ROWS * (SV_MAX_TOPK + 1)];
+  __shared__ int s_cost_dn[SV_MAX_EXPERTS + 2 + SV_MAX_ROWS * (SV_MAX_TOPK + 1)];
   __shared__ int s_idx[SV_MAX_ROWS * SV_MAX_TOPK];
   __shared__ unsigned long long s_rmask[SV_MAX_EXPERTS];   // rows that chose expert e (R <= 64)
   __shared__ int eoff[SV_MAX_EXPERTS];
@@ -290,7 +303,6 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
   constexpr int NW = PREP_THREADS / 64;
   for (int e = tid; e < E; e += PREP_THREADS) s_rmask[e] = 0ull;
-  for (int a = tid; a < ws.max_assign; a += PREP_THREADS) ws.hmax[a] = 0u;   // gate/up raises them
   if (logits == nullptr) {  // one expert, no router: weight 1
     for (int i = tid; i < R * k; i += PREP_THREADS) {
       s_idx[i] = 0;
@@ -364,22 +376,148 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
     ws.meta->n_assign = R * k + has_shared * R;
   }
   __syncthreads();
-  if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, cg_gu, ws.work_gu,
-                         &ws.meta->n_work_gu);
-  if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, cg_dn, ws.work_dn,
-                         &ws.meta->n_work_dn);
+  if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, true, cap_allk, cap_quarter, items_gu,
+                         G, ws.work_gu, &ws.meta->n_work_gu, ws.blk_gu, s_cost_gu, ws.atype);
+  if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, false, cap_allk, cap_down, items_dn,
+                         G, ws.work_dn, &ws.meta->n_work_dn, ws.blk_dn, s_cost_dn, ws.atype);
+}
+
+// ------------------------------------------------------------ rows as digits
+// One block per row: thread t converts sub-blocks t, t + PREP_THREADS, ...
+// (16 values each, loaded once by load(sb, v)), after a block-wide maximum of
+// the row.
+template <typename Load>
+__device__ void stage_row_digits(int row, XDig xd, Load load) {
+  __shared__ uint32_t s_max;
+  __shared__ int s_bad;
+  const int K = xd.K, nsb = K / 16, tid = threadIdx.x;
+  constexpr int PER = (16384 / 16 + PREP_THREADS - 1) / PREP_THREADS;
+  float v[PER][16];
+  float mx = 0.f;
+  int bad = 0;
+  if (tid == 0) {
+    s_max = 0u;
+    s_bad = 0;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int sb = tid + PREP_THREADS * i;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[i][e] = 0.f;
+    if (sb < nsb) {
+      load(sb, v[i]);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float a = fabsf(v[i][e]);
+        bad |= !(a <= 3.402823466e38f);
+        mx = fmaxf(mx, a);
+      }
+    }
+  }
+  __syncthreads();
+  mx = wave_allreduce(mx, [](float a, float b) { return fmaxf(a, b); });
+  if ((tid & 63) == 0) atomicMax(&s_max, __float_as_uint(mx));
+  if (__any(bad) && (tid & 63) == 0) s_bad = 1;
+  __syncthreads();
+  const bool rbad = s_bad != 0;
+  const int s = rbad ? 0 : digit_exponent(__uint_as_float(s_max));
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int sb = tid + PREP_THREADS * i;
+    if (sb >= nsb) continue;
+    uint4 pl[NDIG];
+    int sums[NDIG];
+    subblock_digits(v[i], s, rbad, pl, sums);
+#pragma unroll
+    for (int p = 0; p < NDIG; ++p) {
+      *(uint4*)(xd.dig + ((size_t)row * NDIG + p) * K + subblock_offset(sb)) = pl[p];
+      xd.sx[((size_t)row * NDIG + p) * nsb + sb] = (_Float16)(float)sums[p];
+    }
+  }
+  if (tid == 0) xd.rsc[row] = rbad ? __builtin_nanf("") : ldexpf(1.f, -s);
+}
+
+// Row `row` of x (bf16 or fp32) as digits.
+template <int DT>
+__device__ void stage_digits(const void* x, int row, XDig xd) {
+  const int K = xd.K;
+  stage_row_digits(row, xd, [&](int sb, float (&v)[16]) {
+    const size_t o = (size_t)row * K + 16 * sb;
+    if (DT == SV_BF16) {
+      const uint4 a = *(const uint4*)((const uint16_t*)x + o);
+      const uint4 b = *(const uint4*)((const uint16_t*)x + o + 8);
+      const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[2 * j] = __uint_as_float(u[j] << 16);
+        v[2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 f = *(const float4*)((const float*)x + o + 4 * j);
+        v[4 * j] = f.x;
+        v[4 * j + 1] = f.y;
+        v[4 * j + 2] = f.z;
+        v[4 * j + 3] = f.w;
+      }
+    }
+  });
+}
+
+// The down projection's input of assignment a as digits: h (units of
+// MOE_ALLK) or silu(sum of the gate quarters) * (sum of the up quarters),
+// quarters summed in order (units of MOE_QUARTER).  One block per assignment.
+__global__ __launch_bounds__(PREP_THREADS) void k_hdig(MoeWs ws, int inter) {
+  const int a = blockIdx.x;
+  const int type = ws.atype[a];
+  const size_t qs = (size_t)ws.max_assign * inter;
+  stage_row_digits(a, ws.hd, [&](int sb, float (&v)[16]) {
+    const size_t o = (size_t)a * inter + 16 * sb;
+    if (type == MOE_ALLK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 f = *(const float4*)(ws.h + o + 4 * j);
+        v[4 * j] = f.x;
+        v[4 * j + 1] = f.y;
+        v[4 * j + 2] = f.z;
+        v[4 * j + 3] = f.w;
+      }
+      return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 gq[4], uq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gq[q] = *(const float4*)(ws.gpart + (size_t)q * qs + o + 4 * j);
+        uq[q] = *(const float4*)(ws.gpart + (size_t)(4 + q) * qs + o + 4 * j);
+      }
+      v[4 * j] = silu_mul(((gq[0].x + gq[1].x) + gq[2].x) + gq[3].x, ((uq[0].x + uq[1].x) + uq[2].x) + uq[3].x);
+      v[4 * j + 1] = silu_mul(((gq[0].y + gq[1].y) + gq[2].y) + gq[3].y, ((uq[0].y + uq[1].y) + uq[2].y) + uq[3].y);
+      v[4 * j + 2] = silu_mul(((gq[0].z + gq[1].z) + gq[2].z) + gq[3].z, ((uq[0].z + uq[1].z) + uq[2].z) + uq[3].z);
+      v[4 * j + 3] = silu_mul(((gq[0].w + gq[1].w) + gq[2].w) + gq[3].w, ((uq[0].w + uq[1].w) + uq[2].w) + uq[3].w);
+    }
+  });
+}
+
+hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s) {
+  (void)R;
+  hipLaunchKernelGGL(k_hdig, dim3(ws.max_assign), dim3(PREP_THREADS), 0, s, ws, d->inter);
+  return hipGetLastError();
 }
 
 template <int DT>
 __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, int R, int E, int k,
-                                                           int has_shared, int cg_gu, int cg_dn,
-                                                           int32_t* idx_out, float* w_out,
-                                                           const void* x, MoeWs ws) {
-  __shared__ int sh[2 * PREP_THREADS / 64];
+                                                           int has_shared, int cap_allk, int cap_quarter,
+                                                           int cap_down, int items_gu, int items_dn, int G,
+                                                           int32_t* idx_out, float* w_out, const void* x,
+                                                           MoeWs ws) {
   if (blockIdx.x == 0) {
-    route_and_group(logits, R, E, k, has_shared, cg_gu, cg_dn, idx_out, w_out, ws);
+    route_and_group(logits, R, E, k, has_shared, cap_allk, cap_quarter, cap_down, items_gu, items_dn, G, idx_out,
+                    w_out, ws);
   } else {
-    stage_row<DT, PREP_THREADS>(x, blockIdx.x - 1, XL_PERM, ws.x_img, sh);   // one block per row
+    stage_digits<DT>(x, blockIdx.x - 1, ws.xd);   // one block per row
   }
 }
 
@@ -388,19 +526,24 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
   const int has_shared = d->s_gate ? 1 : 0;
   const dim3 grid(1 + R);
-  const int cg_gu = gateup_cols(d, R, x_dtype == SV_F32), cg_dn = down_cols(d, R);
+  int ca, cq, cd;
+  moe8_caps(d, &ca, &cq, &cd);
+  const int items_gu = d->inter / 16, items_dn = d->hidden / 128, G = moe_grid();
   if (x_dtype == SV_BF16)
-    hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
-                       d->n_experts, d->top_k, has_shared, cg_gu, cg_dn, topk_idx_out, topk_w_out,
-                       x, ws);
+    hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R, d->n_experts,
+                       d->top_k, has_shared, ca, cq, cd, items_gu, items_dn, G, topk_idx_out, topk_w_out, x, ws);
   else
-    hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(PREP_THREADS), 0, s, router_logits, R,
-                       d->n_experts, d->top_k, has_shared, cg_gu, cg_dn, topk_idx_out, topk_w_out,
-                       x, ws);
+    hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(PREP_THREADS), 0, s, router_logits, R, d->n_experts,
+                       d->top_k, has_shared, ca, cq, cd, items_gu, items_dn, G, topk_idx_out, topk_w_out, x, ws);
   return hipGetLastError();
 }
 
-// ------------------------------------------------------------ LDS staging
+// ------------------------------------------------ one-matrix path staging
+// Activation rows are copied into LDS in 1 KB pieces.
+__host__ __device__ inline int xl_pieces_per_row(int K, bool use_lo) {
+  return ((2 * K + 1023) / 1024) * (use_lo ? 2 : 1) + (K / 4 + 1023) / 1024;
+}
+
 struct XLw {   // writable view of the LDS rows
   _Float16 *hi, *lo, *sx;
   float* rsc;
@@ -494,579 +637,6 @@ __device__ __forceinline__ void xl_img_dma(const XImg& img, const int* rows, int
     const XLPiece p = xl_piece(img, L, xl_row(rows, row0, c), c, q - c * per_c, use_lo);
     dma_piece(p.src, p.la, p.bytes);
   }
-}
-
-// ------------------------------------------------------------- gate / up
-struct ExpertPtrs {
-  const uint8_t *g, *u, *dn;     // routed, expert-major
-  const uint8_t *sg, *su, *sd;   // shared
-  size_t bytes_gu, bytes_d;
-};
-
-static ExpertPtrs expert_ptrs(const sv_moe_desc* d) {
-  ExpertPtrs P;
-  P.g = (const uint8_t*)d->w_gate;
-  P.u = (const uint8_t*)d->w_up;
-  P.dn = (const uint8_t*)d->w_down;
-  P.sg = (const uint8_t*)d->s_gate;
-  P.su = (const uint8_t*)d->s_up;
-  P.sd = (const uint8_t*)d->s_down;
-  P.bytes_gu = q2_bytes(d->inter, d->hidden);
-  P.bytes_d = q2_bytes(d->hidden, d->inter);
-  return P;
-}
-
-constexpr int GU_THREADS = 512;   // 8 waves: (gate, up) x 4 K-quarters of one 16-row tile
-
-template <bool USE_LO, bool WIDE_D>
-__global__ __launch_bounds__(GU_THREADS, 4) void k_q2_gateup(ExpertPtrs P, int hidden, int inter,
-                                                             MoeWs ws) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int tile = blockIdx.x;
-  const int nwork = ws.meta->n_work_gu;
-  const MoeWork wk = ws.work_gu[blockIdx.y];   // in bounds for every launched block
-  if ((int)blockIdx.y >= nwork) return;
-  const int e = wk.expert, a0 = wk.a0, ncols = wk.ncols;
-  const int* rows = ws.work_gu[blockIdx.y].rows;   // activation rows of the block's columns
-  const int tid = threadIdx.x, lane = tid & 63, wv = wave_id();
-  const int m = wv >> 2, q = wv & 3;
-  const int nl = lane & 15, g = lane >> 4;
-  const int n = tile * 16 + nl;
-  const int nb = hidden / 256;
-  const uint8_t* base = m == 0 ? (e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg)
-                               : (e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su);
-  const Q2View W = q2_view(base, inter, hidden);
-  const XLw L = xl_make(lds, ncols, hidden, USE_LO);
-  f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  auto issue = [&]() { xl_img_dma(ws.x_img, rows, 0, ncols, USE_LO, L); };
-  auto sync = [&](int nload) {
-    wait_vmcnt_le(nload);   // this wave's copies (older than its nload weight loads) have landed
-    barrier_keep_loads();
-  };
-  q2_range_staged<WIDE_D, USE_LO>(W, n, nb * q / 4, nb * (q + 1) / 4, xl_view(L), min(nl, ncols - 1),
-                                  lane, acc, issue, sync);
-  __syncthreads();   // every wave is done with the rows: reuse LDS for the partial sums
-  f4_t* red = (f4_t*)lds;
-  red[wv * 64 + lane] = acc;
-  __syncthreads();
-  if (wv != 0) return;
-  const f4_t gs = ((red[lane] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
-  const f4_t us = ((red[256 + lane] + red[320 + lane]) + red[384 + lane]) + red[448 + lane];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 4 * g + i;   // (uniform in the lane's 16-lane row)
-    float hv = 0.f;
-    if (c < ncols) {
-      const float rs = ws.x_img.rscale[rows[c]];
-      const float gv = gs[i] * rs, uv = us[i] * rs;
-      hv = gv / (1.f + expf(-gv)) * uv;
-      ws.h[(size_t)(a0 + c) * inter + n] = hv;
-    }
-    note_hmax(ws.hmax, a0 + c, hv, c < ncols);
-  }
-}
-
-// ------------------------------------------------ gate / up, persistent
-// Blocks of 8 waves: wave (m, q) = (matrix gate/up, K part q of 4), each part
-// NQ = nb / 4 consecutive 256-element blocks.  Block b owns the contiguous
-// item range [b I / G, (b + 1) I / G) of the I = n_work * (inter/16) items
-// (work descriptor, 16-row tile), which are ordered by descriptor, and every
-// wave works on its (m, q) share of each item in turn.  A wave issues the
-// next item's loads while it computes the current item -- the loads of the
-// first half of its part once that half is computed, the rest after the
-// second half -- so its loads stay in flight across items and across the
-// per-item barrier.  The activation rows are copied into LDS only when the
-// descriptor changes.  Partial sums meet in a double-buffered LDS area;
-// wave (item mod 8) adds them up and applies SwiGLU.  Two blocks share a CU
-// (four waves per SIMD, two of each block).
-constexpr int GP_WAVES = 8, GP_PARTS = 4;
-constexpr int GP_ZERO_BYTES = 8 * 512 + 64;   // zero operands of q2_block_c1: NQ <= 8 blocks
-
-struct GpCfg {
-  bool ok;
-  int nq, cols;
-  size_t lds;
-};
-
-// d/dmin window of a part starting at block kb0: 2 DW values from the even
-// block w0 = kb0 & ~1 (even lane-rows d, odd lane-rows dmin, one dword per 2
-// blocks); the part's values start at half (kb0 & 1) of it.
-__host__ __device__ constexpr int gp_dw(int nq) { return (nq + (nq & 1) + 1) / 2; }
-
-static GpCfg gp_config(int hidden, int inter, bool use_lo, int R) {
-  GpCfg c{};
-  const int nb = hidden / 256;
-  if (hidden % 256 != 0 || nb % GP_PARTS != 0) return c;
-  if ((size_t)inter * nb * 64 >= ((size_t)1 << 31)) return c;   // 32-bit load offsets (gp_load)
-  c.nq = nb / GP_PARTS;
-  if (c.nq < 1 || c.nq > 8) return c;
-  const int dw = gp_dw(c.nq);
-  if (dw > 4) return c;
-  for (int q = 0; q < GP_PARTS; ++q)   // every window inside the row
-    if ((c.nq * q & ~1) + 2 * dw > nb) return c;
-  const size_t budget = (size_t)80 * 1024 - 512;   // two blocks per CU
-  const size_t red = (size_t)2 * GP_WAVES * 64 * 16 + 2 * XL_MAX_COLS * 4 + GP_ZERO_BYTES;
-  int cg = XL_MAX_COLS;
-  while (cg > 1 && xl_bytes(cg, hidden, use_lo) + red > budget) --cg;
-  if (xl_bytes(cg, hidden, use_lo) + red > budget) return c;
-  c.cols = cg < R ? cg : R;
-  c.lds = xl_bytes(c.cols, hidden, use_lo) + red;
-  c.ok = true;
-  return c;
-}
-
-// The loads of one half of a part: N code blocks, plus (first half) the
-// block scales and the scale nibbles of the first 4 blocks, or (second half
-// of a part of more than 4 blocks) the nibbles of blocks 4..7.  Nibble loads:
-// lane-row g gets block base + g (clamped to the row).
-template <int NQ, bool FIRST>
-struct GpHalf {
-  static constexpr int N0 = NQ > 4 ? 4 : (NQ + 1) / 2;
-  static constexpr int N = FIRST ? N0 : NQ - N0;
-  static constexpr bool SC = FIRST || NQ > 4;
-  static constexpr int DW = FIRST ? gp_dw(NQ) : 0;
-  static constexpr int LOADS = N + (SC ? 1 : 0) + (DW > 0 ? 1 : 0);
-  uint4 qs[N > 0 ? N : 1];
-  uint4 sc;
-  uint32_t dd[DW > 0 ? DW : 1];
-};
-
-// (32-bit offsets from the planes' uniform bases: the loads take a scalar
-// base and one offset register; the host keeps every plane under 2^31 bytes
-// for the kernels that use this)
-template <int NQ, bool FIRST>
-__device__ __forceinline__ void gp_load(const Q2View& W, size_t rb, int kb0, int g,
-                                        GpHalf<NQ, FIRST>& h) {
-  using H = GpHalf<NQ, FIRST>;
-  const uint32_t r0 = (uint32_t)rb;
-  const int b0 = kb0 + (FIRST ? 0 : H::N0);
-  if (H::SC) h.sc = *(const uint4*)(W.sc + (r0 + (uint32_t)min(b0 + g, W.nb - 1)) * 16u);
-  if (H::DW > 0) {
-    const uint16_t* dp = ((g & 1) ? W.dm : W.d) + (r0 + (uint32_t)(kb0 & ~1));
-    if (H::DW == 1) {
-      h.dd[0] = *(const uint32_t*)dp;
-    } else if (H::DW == 2) {
-      const uint2 v = *(const uint2*)dp;
-      h.dd[0] = v.x;
-      h.dd[1] = v.y;
-    } else if (H::DW == 3) {
-      const uint3 v = *(const uint3*)dp;
-      h.dd[0] = v.x;
-      h.dd[1] = v.y;
-      h.dd[2] = v.z;
-    } else {
-      const uint4 v = *(const uint4*)dp;
-      h.dd[0] = v.x;
-      h.dd[1] = v.y;
-      h.dd[2] = v.z;
-      h.dd[3] = v.w;
-    }
-  }
-  const uint8_t* q = W.qs + ((r0 + (uint32_t)b0) * 64u + 16u * (uint32_t)g);
-#pragma unroll
-  for (int i = 0; i < H::N; ++i) h.qs[i] = *(const uint4*)(q + 64 * i);
-}
-
-template <bool USE_LO, int NQ>
-__global__ __launch_bounds__(GP_WAVES * 64, 4) void k_q2_gateup_p(ExpertPtrs P, int hidden, int inter,
-                                                                  int CG, MoeWs ws) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  using H0 = GpHalf<NQ, true>;
-  using H1 = GpHalf<NQ, false>;
-  constexpr int N0 = H0::N0, DW = H0::DW;
-  const int T = inter / 16;
-  const long total = (long)ws.meta->n_work_gu * T;
-  // (the 64-bit divisions run on the vector unit: make the results uniform so
-  // that descriptor reads are scalar loads)
-  const int i0 = __builtin_amdgcn_readfirstlane((int)(total * blockIdx.x / gridDim.x));
-  const int i1 = __builtin_amdgcn_readfirstlane((int)(total * (blockIdx.x + 1) / gridDim.x));
-  if (i0 >= i1) return;
-  const int lane = threadIdx.x & 63, wv = wave_id();
-  const int m = wv >= GP_PARTS, q = wv & (GP_PARTS - 1);
-  const int nl = lane & 15, g = lane >> 4;
-  const int nb = hidden / 256, kb0 = NQ * q;
-  const uint32_t dshift = 16 * (kb0 & 1);   // the part's first value: half (kb0 & 1) of the window
-  const auto work = const_ptr(ws.work_gu);   // descriptor reads as scalar loads
-  f4_t* red = (f4_t*)(lds + xl_bytes(CG, hidden, USE_LO));
-  // row scales of a descriptor's columns, in LDS slot (descriptor index & 1):
-  // the epilogue of the old descriptor's last item may still read its slot
-  // while the next descriptor's scales are written
-  float* rsc_slots = (float*)(lds + xl_bytes(CG, hidden, USE_LO) + (size_t)2 * GP_WAVES * 64 * 16);
-  // zeros read by the idle lanes of single-row operands (q2_block_c1): one
-  // part's worth of blocks, written once
-  _Float16* zeros = (_Float16*)(rsc_slots + 2 * XL_MAX_COLS);
-  for (int z = threadIdx.x; z < GP_ZERO_BYTES / 16; z += blockDim.x) ((uint4*)zeros)[z] = make_uint4(0, 0, 0, 0);
-  auto wview = [&](int e) {
-    const uint8_t* base = m == 0 ? (e >= 0 ? P.g + (size_t)e * P.bytes_gu : P.sg)
-                                 : (e >= 0 ? P.u + (size_t)e * P.bytes_gu : P.su);
-    return q2_view(base, inter, hidden);
-  };
-
-  // load cursor: the item whose weights are issued next (stays on the last
-  // item of the range once there: those loads re-read cached lines and keep
-  // the compiler's load counting identical on every path)
-  int lw = __builtin_amdgcn_readfirstlane(i0 / T), lt = i0 - lw * T, li = i0;
-  Q2View LW = wview(work[lw].expert);
-  auto issue0 = [&](H0& h) { gp_load<NQ, true>(LW, (size_t)(lt * 16 + nl) * nb, kb0, g, h); };
-  auto issue1 = [&](H1& h) {
-    gp_load<NQ, false>(LW, (size_t)(lt * 16 + nl) * nb, kb0, g, h);
-    if (li + 1 < i1) {
-      ++li;
-      if (++lt == T) {
-        lt = 0;
-        ++lw;
-        LW = wview(work[lw].expert);
-      }
-    }
-  };
-
-  // compute cursor
-  int w = lw, t = lt;
-  int a0_cur = work[w].a0, nc_cur = work[w].ncols;
-  auto row_scales = [&]() {
-    if (wv == 0 && lane < XL_MAX_COLS)
-      rsc_slots[(w & 1) * XL_MAX_COLS + lane] = lane < nc_cur ? ws.x_img.rscale[work[w].rows[lane]] : 0.f;
-  };
-  row_scales();
-  // the first descriptor's activation copies, then the first item's weights
-  xl_img_dma(ws.x_img, (const int*)work[w].rows, 0, nc_cur, USE_LO, xl_make(lds, nc_cur, hidden, USE_LO));
-  H0 h0;
-  H1 h1;
-  issue0(h0);
-  issue1(h1);
-  wait_vmcnt_le(H0::LOADS + H1::LOADS);   // this wave's activation copies are done
-  barrier_lds();
-
-  for (int i = i0; i < i1; ++i) {
-    const XLw L = xl_make(lds, nc_cur, hidden, USE_LO);   // rebuilt, not carried
-    const int cr = min(nl, nc_cur - 1);
-    const _Float16* xh = L.hi + (size_t)cr * L.rs + kb0 * 256 + g * 8;
-    const _Float16* xl = L.lo + (size_t)cr * L.rs + kb0 * 256 + g * 8;
-    const _Float16* xs = L.sx + (size_t)cr * L.sxs + kb0 * 32 + g * 8;
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // block scales: both halves of the window to every lane, aligned so that
-    // value b belongs to block kb0 + b
-    uint32_t dv[DW], mv[DW];
-#pragma unroll
-    for (int j = 0; j < DW; ++j) {
-      const auto sw = __builtin_amdgcn_permlane16_swap(h0.dd[j], h0.dd[j], false, false);
-      dv[j] = sw[0];
-      mv[j] = sw[1];
-    }
-#pragma unroll
-    for (int j = 0; j < DW; ++j) {
-      dv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? dv[j + 1] : 0u, dv[j], dshift);
-      mv[j] = __builtin_amdgcn_alignbit(j + 1 < DW ? mv[j + 1] : 0u, mv[j], dshift);
-    }
-    // one activation row: sub-block selector operands (q2_block_c1); lane
-    // (c, g) is live for the steps of sub-block c == 4g + u.  The branch is
-    // uniform; both halves' loads are issued outside it.
-    const bool one = nc_cur == 1;
-    float ac = 0.f;
-    auto sel = [&](uint32_t* ph, uint32_t* pl) {   // byte offsets from lds
-      const uint32_t oh = (uint32_t)((const uint8_t*)xh - lds), ol = (uint32_t)((const uint8_t*)xl - lds);
-      const uint32_t oz = (uint32_t)((const uint8_t*)zeros - lds);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool live = nl == 4 * g + u;
-        ph[u] = live ? oh : oz - 128 * u;
-        pl[u] = live ? ol : oz - 128 * u;
-      }
-    };
-    {
-      uint32_t sct[4];
-      xpose4(h0.sc, sct);
-      if (one) {
-        uint32_t ph[4], pl[4];
-        sel(ph, pl);
-#pragma unroll
-        for (int b = 0; b < NQ && b < 8; ++b) {
-          if (b >= N0 && NQ > 4) break;
-          // (second-half blocks of a part of at most 4 use the first nibble load)
-          const uint4& qs = b < N0 ? h0.qs[b] : h1.qs[b - N0 < H1::N ? b - N0 : 0];
-          q2_block_c1<USE_LO>(qs, sct[b & 3], win_val(dv, b), win_val(mv, b), g == 0, lds, ph, pl, 256 * b,
-                              xs + 32 * b, ac);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < NQ && b < 8; ++b) {
-          if (b >= N0 && NQ > 4) break;
-          const uint4& qs = b < N0 ? h0.qs[b] : h1.qs[b - N0 < H1::N ? b - N0 : 0];
-          q2_block<USE_LO>(qs, sct[b & 3], win_val(dv, b), win_val(mv, b), xh + 256 * b, xl + 256 * b,
-                           xs + 32 * b, acc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    issue0(h0);
-    if (NQ > 4) {
-      uint32_t sct[4];
-      xpose4(h1.sc, sct);
-      if (one) {
-        uint32_t ph[4], pl[4];
-        sel(ph, pl);
-#pragma unroll
-        for (int b = N0; b < NQ; ++b) {
-          q2_block_c1<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), g == 0, lds, ph, pl,
-                              256 * b, xs + 32 * b, ac);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-#pragma unroll
-        for (int b = N0; b < NQ; ++b) {
-          q2_block<USE_LO>(h1.qs[b - N0], sct[b - N0], win_val(dv, b), win_val(mv, b), xh + 256 * b,
-                           xl + 256 * b, xs + 32 * b, acc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    }
-    issue1(h1);
-    if (one) {
-      // the row's total over its 4 lanes (g = 0..3), as column 0 of lane-row 0
-      ac = rows_sum(ac);
-      acc[0] = g == 0 ? ac : 0.f;
-    }
-    // partial sums of item i meet in buffer i & 1
-    f4_t* rbuf = red + (size_t)(i & 1) * GP_WAVES * 64;
-    rbuf[wv * 64 + lane] = acc;
-    barrier_lds();
-    if (wv == (i & (GP_WAVES - 1))) {
-      // (addressed from the lane id, which the compiler recomputes instead of
-      // keeping a register live across the item)
-      const f4_t* rl = red + (size_t)(i & 1) * GP_WAVES * 64 + __lane_id();
-      const f4_t gs = ((rl[0] + rl[64]) + rl[128]) + rl[192];
-      const f4_t us = ((rl[256] + rl[320]) + rl[384]) + rl[448];
-      const int n = t * 16 + nl;
-      // (lane groups g >= 2 hold columns 8..15, never present: kept in bounds)
-      const float* rsv = rsc_slots + (w & 1) * XL_MAX_COLS + min(4 * g, XL_MAX_COLS - 4);
-      const int ne = min(4, nc_cur - 4 * g);   // (uniform in the lane's 16-lane row)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float hv = 0.f;
-        if (e < ne) {
-          const float gv = gs[e] * rsv[e], uv = us[e] * rsv[e];
-          hv = gv / (1.f + __expf(-gv)) * uv;
-          ws.h[(size_t)(a0_cur + 4 * g + e) * inter + n] = hv;
-        }
-        note_hmax(ws.hmax, a0_cur + 4 * g + e, hv, e < ne);
-      }
-    }
-    // next compute item; a new descriptor's rows replace the old ones once
-    // every wave is past item i
-    if (++t == T && i + 1 < i1) {
-      t = 0;
-      ++w;
-      a0_cur = work[w].a0;
-      nc_cur = work[w].ncols;
-      xl_img_dma(ws.x_img, (const int*)work[w].rows, 0, nc_cur, USE_LO, xl_make(lds, nc_cur, hidden, USE_LO));
-      row_scales();
-      wait_vmcnt_le(0);
-      barrier_lds();
-    }
-  }
-}
-
-static size_t gu_lds(int hidden, bool use_lo, int CG) {
-  const size_t x = xl_bytes(CG, hidden, use_lo), red = (size_t)GU_THREADS * 16;
-  return x > red ? x : red;
-}
-
-static int gateup_cols(const sv_moe_desc* d, int R, bool use_lo) {
-  const GpCfg c = gp_config(d->hidden, d->inter, use_lo, R);
-  return c.ok ? c.cols : col_group(d->hidden, use_lo, R);
-}
-
-hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, hipStream_t s) {
-  const ExpertPtrs P = expert_ptrs(d);
-  const GpCfg c = gp_config(d->hidden, d->inter, use_lo, R);
-  if (c.ok) {
-    const dim3 grid(2 * cu_count()), block(64 * GP_WAVES);
-#define SV_GP(Q)                                                                                   \
-  case Q:                                                                                          \
-    if (use_lo)                                                                                    \
-      hipLaunchKernelGGL((k_q2_gateup_p<true, Q>), grid, block, c.lds, s, P, d->hidden, d->inter,  \
-                         c.cols, ws);                                                              \
-    else                                                                                           \
-      hipLaunchKernelGGL((k_q2_gateup_p<false, Q>), grid, block, c.lds, s, P, d->hidden, d->inter, \
-                         c.cols, ws);                                                              \
-    break;
-    switch (c.nq) { SV_GP(1) SV_GP(2) SV_GP(3) SV_GP(4) SV_GP(5) SV_GP(6) SV_GP(7) SV_GP(8) default: break; }
-#undef SV_GP
-    return hipGetLastError();
-  }
-  const int CG = gateup_cols(d, R, use_lo);
-  const dim3 grid(d->inter / 16, ws.max_work, 1);
-  const size_t lb = gu_lds(d->hidden, use_lo, CG);
-  const bool wide = q2_wide_d(d->hidden / 256);
-#define SV_GU(LO, WD)                                                                              \
-  hipLaunchKernelGGL((k_q2_gateup<LO, WD>), grid, dim3(GU_THREADS), lb, s, P, d->hidden, d->inter, \
-                     ws)
-  if (use_lo) {
-    if (wide) SV_GU(true, true); else SV_GU(true, false);
-  } else {
-    if (wide) SV_GU(false, true); else SV_GU(false, false);
-  }
-#undef SV_GU
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ down
-
-// h rows of a down descriptor into the int8 image (sv_q2.h, int8 form):
-// half-wave hw converts the (row, 256-block) pairs hw, hw + 16, ... (at most
-// PAIRS); lane l of a pair takes sub-block l/2, element positions j = 2(l&1)
-// and 2(l&1) + 1, at b = 0..3 (elements 16 sb + 4b + j), so that it writes
-// whole dwords of each digit plane.  The row's scale comes from its largest
-// |h|, which the gate/up kernel left in hmax (loaded with the values).
-template <int PAIRS>
-struct DnH8 {
-  float2 v[PAIRS][4];
-  uint32_t m[DN_MAX_ROWS];   // hmax bits of the descriptor's rows (uniform: scalar registers)
-};
-
-template <int PAIRS>
-__device__ __forceinline__ void dn8_h_load(const float* h, const uint32_t* hmax, int a0, int ncols, int inter,
-                                           DnH8<PAIRS>& v) {
-  const auto hm = const_ptr(hmax + a0);
-#pragma unroll
-  for (int j = 0; j < DN_MAX_ROWS; ++j) v.m[j] = hm[min(j, ncols - 1)];
-  const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
-  const int sb = l >> 1, jh = l & 1;
-  const int nbk = inter / 256, npairs = ncols * nbk;
-#pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {
-    const int p = hw + (DN_THREADS / 32) * i;
-    if (p < npairs) {
-      const int c = p / nbk, kb = p - c * nbk;
-      const float* src = h + (size_t)(a0 + c) * inter + kb * 256 + 16 * sb + 2 * jh;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) v.v[i][b] = *(const float2*)(src + 4 * b);
-    }
-  }
-}
-
-// Signed byte with the low 8 bits of x (sign-extended).
-__device__ __forceinline__ int sbyte(int x) { return (x << 24) >> 24; }
-
-template <int PAIRS>
-__device__ __forceinline__ void dn8_h_convert(const DnH8<PAIRS>& v, int8_t* q, _Float16* sx, float* csc, int ncols,
-                                              int inter) {
-  const int tid = threadIdx.x, l = tid & 31, hw = tid >> 5;
-  const int sb = l >> 1, jh = l & 1;
-  const int nbk = inter / 256, npairs = ncols * nbk;
-  const int rs = inter + 16, sxs = inter / 16;
-#pragma unroll
-  for (int i = 0; i < PAIRS; ++i) {   // digits
-    const int p = hw + (DN_THREADS / 32) * i;
-    if (p < npairs) {
-      const int c = p / nbk, kb = p - c * nbk;
-      const uint32_t mb = c == 0 ? v.m[0] : c == 1 ? v.m[1] : c == 2 ? v.m[2] : v.m[3];
-      const float mx = __uint_as_float(mb);
-      const int bad = mb >= 0x7F800000u;   // an infinite or NaN value in the row
-      // |h| 2^e < 2^29: the leading digit stays within +-65
-      int e = 0;
-      if (mx > 0.f && !bad) {
-        int E;
-        frexpf(mx, &E);   // mx in [2^(E-1), 2^E)
-        e = min(max(29 - E, -120), 120);
-      }
-      uint32_t w[4][2];   // [digit][j - 2 jh]
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) w[d][jj] = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float x = jj == 0 ? v.v[i][b].x : v.v[i][b].y;
-          const int a = bad ? 0 : (int)rintf(ldexpf(x, e));
-          const int p3 = sbyte(a), a1 = (a - p3) >> 8;
-          const int p2 = sbyte(a1), a2 = (a1 - p2) >> 8;
-          const int p1 = sbyte(a2), p0 = (a2 - p1) >> 8;
-          const int dg[4] = {p0, p1, p2, p3};
-#pragma unroll
-          for (int d = 0; d < 4; ++d) w[d][jj] |= ((uint32_t)dg[d] & 0xFFu) << (8 * b);
-        }
-      }
-      // digit sums of the lane's 8 elements: the signed bytes of its two words
-      int ps[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int s1 = __builtin_amdgcn_sdot4((int)w[d][1], 0x01010101, 0, false);
-        ps[d] = __builtin_amdgcn_sdot4((int)w[d][0], 0x01010101, s1, false);
-      }
-      // plane byte kb*256 + 64 t + 16 g + 4 j + b for sub-block sb = 4 g + t
-      const int off = kb * 256 + 64 * (sb & 3) + 16 * (sb >> 2) + 8 * jh;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        *(uint2*)(q + (size_t)(4 * c + d) * rs + off) = make_uint2(w[d][0], w[d][1]);
-        const int tot = ps[d] + (int)xlane<0xB1>((uint32_t)ps[d]);   // the partner lane's j
-        if (jh == 0) sx[(size_t)(4 * c + d) * sxs + kb * 16 + sb] = (_Float16)(float)tot;
-      }
-      if (kb == 0 && l < 4)
-        csc[4 * c + l] = bad ? __builtin_nanf("") : ldexpf(1.f, 24 - 8 * l - e);
-    }
-  }
-  for (int c = tid; c < 16; c += blockDim.x)
-    if (c >= 4 * ncols) csc[c] = 0.f;
-  barrier_lds();   // (LDS only: the weight loads in flight are not waited for)
-}
-
-// Down projection on the int8 matrix cores: one block per (128-row group of
-// hidden, descriptor of at most 4 rows), 8 waves of one 16-row tile over all
-// of inter; the block's h rows are read into registers before the weight
-// loads and converted into the LDS image (fixed-point digits, sv_q2.h).
-template <bool WIDE_D, int PAIRS>
-__global__ __launch_bounds__(DN_THREADS, 4) void k_q2_down(ExpertPtrs P, int hidden, int inter, MoeWs ws) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int nwork = ws.meta->n_work_dn;
-  const MoeWork wk = ws.work_dn[blockIdx.y];   // in bounds for every launched block
-  if ((int)blockIdx.y >= nwork) return;
-  const int e = wk.expert, a0 = wk.a0, ncols = wk.ncols;
-  const int lane = threadIdx.x & 63, wv = wave_id();
-  const int nl = lane & 15, g = lane >> 4;
-  const int n = (blockIdx.x * 8 + wv) * 16 + nl;
-  const Q2View D = q2_view(e >= 0 ? P.dn + (size_t)e * P.bytes_d : P.sd, hidden, inter);
-  int8_t* q;
-  _Float16* sx;
-  float* csc;
-  xl8_carve(lds, ncols, inter, q, sx, csc);
-  XL8 X;
-  X.q = q;
-  X.sx = sx;
-  X.csc = csc;
-  X.rs = inter + 16;
-  X.sxs = inter / 16;
-  DnH8<PAIRS> hv;
-  f4_t acc = {0.f, 0.f, 0.f, 0.f};
-  q2_range_staged_i8<WIDE_D>(
-      D, n, 0, inter / 256, X, ncols, lane, acc, [&]() { dn8_h_load(ws.h, ws.hmax, a0, ncols, inter, hv); },
-      [&](int) { dn8_h_convert(hv, q, sx, csc, ncols, inter); });
-  // lane (n, g) holds tile columns 4g..4g+3: the four digits of row g
-  if (g < ncols) {
-    const f4_t sc = *(const f4_t*)(csc + 4 * g);
-    ws.part[(size_t)(a0 + g) * hidden + n] = ((sc[0] * acc[0] + sc[1] * acc[1]) + sc[2] * acc[2]) + sc[3] * acc[3];
-  }
-}
-
-hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const int CG = down_cols(d, R), nbk = d->inter / 256;
-  const dim3 grid(d->hidden / 128, ws.max_work, 1);
-  const ExpertPtrs P = expert_ptrs(d);
-  const size_t lb = xl8_bytes(CG, d->inter);
-  // staging registers for 2 (row, block) pairs per half-wave when that covers the rows
-  const bool wide = q2_wide_d(nbk), few = CG * nbk <= 2 * (DN_THREADS / 32);
-#define SV_DN(WD, PR) \
-  hipLaunchKernelGGL((k_q2_down<WD, PR>), grid, dim3(DN_THREADS), lb, s, P, d->hidden, d->inter, ws)
-  if (wide) {
-    if (few) SV_DN(true, 2); else SV_DN(true, DN_PAIRS);
-  } else {
-    if (few) SV_DN(false, 2); else SV_DN(false, DN_PAIRS);
-  }
-#undef SV_DN
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_moe_combine(d, R, ws, y, s);
 }
 
 // --------------------------------------------------------------- combine

@@ -131,6 +131,50 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 #undef SV_W
 }
 
+// silu(g) * u in fp32 (the SwiGLU of the expert layers).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+// ---------------------------------------------------- global-to-LDS loads
+// One wave instruction: lane l copies 4 or 16 bytes from its own global
+// address `src` to LDS byte address la + 4 l or la + 16 l (la wave-uniform).
+// Written as inline assembly because the compiler, seeing such a load
+// outstanding, would wait for every vector load before the next use; callers
+// wait with explicit vmcnt counts instead.  nt: the non-temporal hint, for
+// data read exactly once (full 128-byte lines stream fastest with it).
+__device__ __forceinline__ void dma16(const void* src, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+
+// The same with a wave-uniform base address in scalar registers and a 32-bit
+// per-lane byte offset (the address is base + off): a loop that streams a
+// fixed per-lane pattern moves only the scalar base.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16s_nt(const void* base, uint32_t off, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4s(const void* base, uint32_t off, uint32_t la) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory", "m0");
+}
+
+// LDS byte address of a generic pointer into the LDS aperture.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 // A global pointer to data that no kernel of this launch writes, in the
 // constant address space: uniform reads through it become scalar loads even
 // in kernels that store to global memory (the compiler cannot otherwise rule
@@ -156,6 +200,9 @@ __host__ __device__ inline size_t q2_bytes(size_t n_out, size_t k_in) {
   size_t nblk = n_out * (k_in / 256);
   return up256(nblk * 64) + up256(nblk * 16) + 2 * up256(nblk * 2);
 }
+
+// Expert-tiled two-bit matrix (sv_q2_tile): 84 bytes per 256 weights.
+__host__ __device__ inline size_t q2_tiled_bytes(size_t n_out, size_t k_in) { return n_out * (k_in / 256) * 84; }
 
 __host__ __device__ inline Q2View q2_view(const void* base, int n_out, int k_in) {
   const uint8_t* p = (const uint8_t*)base;
@@ -242,21 +289,66 @@ inline XImg ximg_carve(void* base, size_t rows, int K, int layout) {
   return x;
 }
 
+// ------------------------------------------------------ activation digits
+// Rows prepared for the int8 matrix cores: each row r is scaled by its own
+// power of two 2^s_r (its largest magnitude lands in [2^29, 2^30)), rounded to
+// integers a and written as four signed bytes a = 2^24 p0 + 2^16 p1 + 2^8 p2 +
+// p3 (balanced digits: p1..p3 in -128..127, |p0| <= 64).  Plane i holds digit
+// p_i of every element, in the byte order the two-bit contraction consumes:
+// byte kb*256 + 64 t + 16 g + 4 j + b <-> element kb*256 + (4g + t)*16 + 4b + j
+// (block kb, sub-block 4g + t, the 16 bytes one lane group reads at step t).
+// sx holds each digit plane's sums over the 16 elements of a sub-block (exact
+// integers, |sum| <= 2048, exact in fp16) for the min term.  rsc = 2^-s_r, or
+// NaN for a row with a non-finite value (whose digits are all zero).
+struct XDig {
+  int8_t* dig;      // [rows][4][K]
+  _Float16* sx;     // [rows][4][K/16]
+  float* rsc;       // [rows]
+  int K;
+};
+
+__host__ __device__ inline size_t xdig_bytes(size_t rows, size_t K) {
+  return up256(rows * 4 * K) + up256(rows * 4 * (K / 16) * 2) + up256(rows * 4);
+}
+
+inline XDig xdig_carve(void* base, size_t rows, int K) {
+  uint8_t* p = (uint8_t*)base;
+  XDig x;
+  x.K = K;
+  x.dig = (int8_t*)p;
+  p += up256(rows * 4 * K);
+  x.sx = (_Float16*)p;
+  p += up256(rows * 4 * (K / 16) * 2);
+  x.rsc = (float*)p;
+  return x;
+}
+
 // ----------------------------------------------------------- MoE workspace
 // Device-side routing/grouping results written by the prep kernel.
 struct MoeMeta {
   int n_units;    // touched routed experts + shared
   int n_assign;   // (row, slot) assignments incl. shared rows
-  int n_work_gu;  // work items of the gate/up kernel
-  int n_work_dn;  // work items of the down kernel
+  int n_work_gu;  // descriptors of the gate/up kernel
+  int n_work_dn;  // descriptors of the down kernel
 };
 
-// One block's work in the expert kernels: an expert (-1 = shared), the first
-// of its assignments the block covers, how many (its columns), and the
-// activation row of each -- everything a block needs in one 48-byte load.
+// One descriptor of the expert kernels: a column group of one unit (an
+// expert, -1 = shared): its first assignment a0, its ncols assignments and
+// the activation row of each.  type (gate/up): MOE_ALLK -- the rows' digits
+// over all of K stay resident and the block's waves split K (SwiGLU in the
+// block); MOE_QUARTER -- the block's waves take four tiles of one quarter of
+// K, partial sums go to the workspace and SwiGLU happens where the down
+// projection reads them.  Down descriptors carry the type of their unit's
+// gate/up work (where h comes from).  One 48-byte load per descriptor.
 constexpr int MOE_WORK_COLS = 8;
+constexpr int MOE_MAX_GRID = 1024;   // persistent blocks of an expert kernel, at most
+// Relative cost of an expert-kernel item whose descriptor has at most four
+// rows (one column tile) and more (two column tiles, the weight tile shared):
+// the block ranges are cut to equal cost with these weights.
+constexpr int MOE_COST_1 = 5, MOE_COST_2 = 8;
+enum { MOE_ALLK = 0, MOE_QUARTER = 1 };
 struct MoeWork {
-  int expert, a0, ncols, pad;
+  int expert, a0, ncols, type;
   int rows[MOE_WORK_COLS];
 };
 
@@ -269,12 +361,17 @@ struct MoeWs {
   int* amap;          // [R, top_k+1]  assignment of (row, slot); slot top_k = shared
   int* topk_idx;      // [R, top_k]
   float* topk_w;      // [R, top_k]
-  float* h;           // [max_assign, inter]  SwiGLU output
-  uint32_t* hmax;     // [max_assign]  bits of the largest |h| of each row (gate/up, atomic max)
+  float* h;           // [max_assign, inter]  SwiGLU output (units of MOE_ALLK)
+  float* gpart;       // [2][4][max_assign, inter]  gate / up quarter sums (units of MOE_QUARTER)
   float* part;        // [max_assign, hidden] per-assignment down outputs
-  MoeWork* work_gu;    // [max_work]
-  MoeWork* work_dn;    // [max_work]
-  XImg x_img;         // staged x  [R, hidden]
+  MoeWork* work_gu;   // [max_work]
+  MoeWork* work_dn;   // [max_work]
+  int* blk_gu;        // [MOE_MAX_GRID + 1] first item of each persistent gate/up block
+  int* blk_dn;        // [MOE_MAX_GRID + 1] the same for the down kernel
+  int* atype;         // [max_assign] MOE_ALLK / MOE_QUARTER: where assignment a's SwiGLU output is
+  XDig hd;            // the down projection's input rows as digits  [max_assign, inter]
+  XDig xd;            // x as digits  [R, hidden]
+  XImg x_img;         // x staged for the one-matrix (PLAIN) path  [R, hidden]
   int max_units, max_assign, max_work;
 };
 
@@ -294,10 +391,16 @@ hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logi
                            float* topk_w_out, MoeWs ws, hipStream_t s);
 hipError_t launch_q2_plain(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws, float* y,
                            hipStream_t s);
-hipError_t launch_q2_gateup(const sv_moe_desc* d, int R, bool use_lo, MoeWs ws,
-                            hipStream_t s);
-hipError_t launch_q2_down(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
+// Persistent blocks of the expert kernels (the device's compute units, at
+// most MOE_MAX_GRID).
+int moe_grid();
+hipError_t launch_moe_gateup(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
+hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
+hipError_t launch_moe_down(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
+// Whether the streamed int8 expert kernels take this layer (LDS limits).
+bool moe_shape_ok(const sv_moe_desc* d);
+hipError_t launch_q2_tile(const void* src, void* dst, int n_out, int k_in, int parts, int count, hipStream_t s);
 hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool use_lo,
                             XImg img, float* logits, hipStream_t s);
 hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, float Tp,
@@ -305,6 +408,8 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
                          const float* u, int32_t* out_tokens, int32_t* out_n, void* ws,
                          hipStream_t s);
 size_t accept_ws_bytes(int S, int K, int V);
+hipError_t launch_read_probe(const void* src, size_t bytes, int mode, uint32_t* sink, hipStream_t s);
+size_t read_probe_sink_words();
 hipError_t launch_q2_dequant(const void* w, int n_out, int k_in, float* out, hipStream_t s);
 hipError_t launch_q8_dequant(const void* w, int n_out, int k_in, float* out, hipStream_t s);
 

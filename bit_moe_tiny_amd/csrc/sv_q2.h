@@ -243,57 +243,6 @@ __device__ __forceinline__ void q2_block(const uint4& qs, uint32_t scw, float d,
   for (int e = 0; e < 4; ++e) acc[e] = fmaf(nd, dm[e], fmaf(d, dt[e], acc[e]));
 }
 
-// acc += one block for a single activation column (a descriptor of one row),
-// without per-weight scaling.  The A operand of row c is the column's values
-// on sub-block c and zero elsewhere: lane (c, g) is live at steps t with
-// 4g + t/2 == c, so ph[u] (u = t/2) addresses the block's activation operands
-// for the live lane and a zero region for the others (block offset and step
-// offset then land inside it; ph/pl are byte offsets from lds).  The B operand is the raw codes: each
-// 2-bit code masked in place reads as the fp16 subnormal 4^j q 2^-24 (the
-// matrix cores keep subnormals), and the activation image carries 4^-j.  The
-// result holds, per output row n and sub-block c, the unscaled partial sum of
-// that sub-block; the lane (n, g) scales its four sub-blocks 4g..4g+3 by their
-// nibbles in fp32.  Sums over the 4 lanes of a row are left to the caller;
-// the min term (the usual 16x16x16 product, identical in every lane's rows)
-// is added on lanes g == 0 only.
-template <bool USE_LO>
-__device__ __forceinline__ void q2_block_c1(const uint4& qs, uint32_t scw, float d, float dmin, bool g0,
-                                            const uint8_t* lds, const uint32_t* ph, const uint32_t* pl,
-                                            int boff, const _Float16* xs, float& ac) {
-  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f4_t D = zero;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int i = t >> 1, hs = t & 1;
-    const uint32_t dw = (i == 0 ? qs.x : i == 1 ? qs.y : i == 2 ? qs.z : qs.w) >> (8 * hs);
-    h8_t b;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const h2_t p = as_h2(dw & sreg(0x00030003u << (2 * j)));
-      b[2 * j] = p.x;
-      b[2 * j + 1] = p.y;
-    }
-    D = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(lds + ph[i] + 2 * boff + 64 * t), b, D, 0, 0, 0);
-    if (USE_LO)
-      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(lds + pl[i] + 2 * boff + 64 * t), b, D, 0, 0, 0);
-  }
-  const uint32_t scb = scw & 0x0F0F0F0Fu;
-  const float u = fmaf((float)(scb >> 24), D[3],
-                       fmaf((float)((scb >> 16) & 0xFF), D[2],
-                            fmaf((float)((scb >> 8) & 0xFF), D[1], (float)(scb & 0xFF) * D[0])));
-  // min term
-  const h2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-  const uint32_t hi = (scw >> 4) & 0x0F0F0F0Fu;
-  const h2_t m01 = q2_bytes01(hi) - k1024, m23 = q2_bytes23(hi) - k1024;
-  const h4_t m = {m01.x, m01.y, m23.x, m23.y};
-  const h8_t sx = *(const h8_t*)xs;
-  const h4_t sxh = {sx[0], sx[1], sx[2], sx[3]}, sxl = {sx[4], sx[5], sx[6], sx[7]};
-  f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxh, m, zero, 0, 0, 0);
-  dm = __builtin_amdgcn_mfma_f32_16x16x16f16(sxl, m, dm, 0, 0, 0);
-  ac = fmaf(d * 16777216.f, u, ac);   // 2^24: the codes' subnormal unit
-  if (g0) ac = fmaf(-dmin, dm[0], ac);
-}
-
 // fp16 value at position p (0..7) of an 8-value window held as 4 dwords.
 __device__ __forceinline__ float win_val(const uint32_t* w, int p) {
   return f16bits_to_f32((uint16_t)(w[p >> 1] >> (16 * (p & 1))));
@@ -435,169 +384,6 @@ __device__ __forceinline__ void q2_range_staged(const Q2View& W, int n, int kb0,
   }
 #undef SV_STAGED_CASE
   q2_range<WIDE_D, LOM>(W, n, kb0 + len, kb1, X, cr, lane, acc);
-}
-
-// ------------------------------------------------------------ int8 form
-// The same block contraction on the int8 matrix cores
-// (v_mfma_i32_16x16x64_i8), for activation rows held as fixed-point digits:
-// each row r is scaled by 2^s_r and rounded to an integer a (|a| < 2^30),
-// written as four signed bytes a = 2^24 p0 + 2^16 p1 + 2^8 p2 + p3, and tile
-// column c = 4 r + i holds digit p_i of row r (up to 4 rows).  Weights enter
-// as the bytes sc * q (at most 45, exact), so every product and every sum
-// inside a block is an exact integer.  Per block a lane
-// turns each of its 4 sub-block dwords into 4 byte vectors
-// ((w >> 2j) & 0x03030303) * sc -- byte b of vector j is code 4b + j -- one
-// step of 64 k per sub-block (step t = sub-block 4g + t of lane group g).  The
-// min term is the usual 16x16x16 product of the digits' sub-block sums (exact
-// integers, at most 2048 in magnitude, exact in fp16) with the m nibbles.
-//
-// LDS image of a tile column (written by the down projection's stager):
-//   q   [K] int8: block kb, step t, lane group g, byte 4j + b = digit of
-//       element kb*256 + (4g + t)*16 + 4b + j  (byte offset kb*256 + 64t +
-//       16g + 4j + b); columns XL8::rs bytes apart
-//   sx  [K/16] fp16 per column: the digit sums of each sub-block
-//   csc [16] fp32: per tile column, 2^(24 - 8i - s_r) (0 beyond the rows)
-typedef int i4_t __attribute__((ext_vector_type(4)));
-
-// Materialises an accumulator at this point: otherwise the compiler sinks each
-// block's scaling into the (conditional) output stores and keeps every block's
-// products live until then.
-__device__ __forceinline__ void pin4(f4_t& a) {
-  asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]));
-}
-
-struct XL8 {
-  const int8_t* q;
-  const _Float16* sx;
-  const float* csc;
-  int rs, sxs;
-};
-
-__host__ __device__ inline size_t xl8_bytes(int nrows, int K) {
-  const int cols = 4 * nrows;
-  return up16((size_t)cols * (K + 16)) + up16((size_t)cols * (K / 16) * 2) + 16 * 4;
-}
-
-template <typename P>
-__device__ __forceinline__ void xl8_carve(P* base, int nrows, int K, int8_t*& q, _Float16*& sx,
-                                          float*& csc) {
-  uint8_t* p = (uint8_t*)base;
-  const int cols = 4 * nrows;
-  q = (int8_t*)p;
-  p += up16((size_t)cols * (K + 16));
-  sx = (_Float16*)p;
-  p += up16((size_t)cols * (K / 16) * 2);
-  csc = (float*)p;
-}
-
-// Weight bytes of step t (sub-block dword w, scale sc): the B operand.
-__device__ __forceinline__ i4_t q2_bop_i8(uint32_t w, uint32_t sc) {
-  const uint32_t m = 0x03030303u;
-  i4_t b;
-  b[0] = (int)((w & m) * sc);
-  b[1] = (int)(((w >> 2) & m) * sc);
-  b[2] = (int)(((w >> 4) & m) * sc);
-  b[3] = (int)(((w >> 6) & m) * sc);
-  return b;
-}
-
-// acc += one block.  xa: the lane's A bytes of the block (step t at +64 t);
-// xs: its 4 sub-block sums.
-__device__ __forceinline__ void q2_block_i8(const uint4& qs, uint32_t scw, float d, float dmin,
-                                            const int8_t* xa, const _Float16* xs, f4_t& acc) {
-  const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-  i4_t D = {0, 0, 0, 0};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t w = t == 0 ? qs.x : t == 1 ? qs.y : t == 2 ? qs.z : qs.w;
-    D = __builtin_amdgcn_mfma_i32_16x16x64_i8(*(const i4_t*)(xa + 64 * t), q2_bop_i8(w, (scw >> (8 * t)) & 0x0Fu),
-                                              D, 0, 0, 0);
-  }
-  const h2_t k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-  const uint32_t hi = (scw >> 4) & 0x0F0F0F0Fu;
-  const h2_t m01 = q2_bytes01(hi) - k1024, m23 = q2_bytes23(hi) - k1024;
-  const h4_t m = {m01.x, m01.y, m23.x, m23.y};
-  const f4_t dm = __builtin_amdgcn_mfma_f32_16x16x16f16(*(const h4_t*)xs, m, zero, 0, 0, 0);
-  const float nd = -dmin;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) acc[e] = fmaf(nd, dm[e], fmaf(d, (float)D[e], acc[e]));
-}
-
-// Blocks of a chunk given its issued loads (int8 form).
-// Tile column of lane l: digit l & 3 of row (l & 15) / 4 (rows past the
-// descriptor's nrows repeat its last row; their outputs are not written).
-template <int NBW, bool WIDE_D>
-__device__ __forceinline__ void q2_chunk_compute_i8(const Q2View& W, const Q2Chunk<NBW, WIDE_D>& c, int kb0,
-                                                    int n, const XL8& X, int nrows, int lane, f4_t& acc) {
-  float dF[NBW], mF[NBW];
-  q2_chunk_scales<NBW, WIDE_D>(W, c, kb0, n, dF, mF);
-  const int g = lane >> 4;
-  // (from the lane id here, not carried from the kernel's start)
-  const int nl = __lane_id() & 15, c0 = 4 * min(nl >> 2, nrows - 1) + (nl & 3);
-  const int8_t* xa = X.q + (size_t)c0 * X.rs + kb0 * 256 + g * 16;
-  const _Float16* xs = X.sx + (size_t)c0 * X.sxs + kb0 * 16 + g * 4;
-  uint32_t sct[4];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    if (i % 4 == 0) xpose4(c.sc[i / 4], sct);
-    q2_block_i8(c.qs[i], sct[i % 4], dF[i], mF[i], xa + 256 * i, xs + 16 * i, acc);
-    pin4(acc);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Blocks [kb0, kb1) of row n in the int8 form, the first chunk staged as in
-// q2_range_staged (issue(), the chunk's weight loads, sync(), compute), the
-// rest chunk by chunk.
-template <bool WIDE_D, typename F, typename G>
-__device__ __forceinline__ void q2_range_staged_i8(const Q2View& W, int n, int kb0, int kb1, const XL8& X,
-                                                   int nrows, int lane, f4_t& acc, F&& issue, G&& sync) {
-  const int g = lane >> 4;
-  issue();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the weight loads stay after issue()'s loads
-  const int len0 = q2_chunk_len<WIDE_D>(kb0, kb1 - kb0);
-#define SV_I8_FIRST(L)                                                                 \
-  case L: {                                                                            \
-    Q2Chunk<L, WIDE_D> c;                                                              \
-    q2_chunk_load<L, WIDE_D>(W, n, kb0, g, c);                                         \
-    sync(q2_chunk_nloads<L, WIDE_D>());                                                \
-    q2_chunk_compute_i8<L, WIDE_D>(W, c, kb0, n, X, nrows, lane, acc);                 \
-    break;                                                                             \
-  }
-  switch (len0) {
-    SV_I8_FIRST(1)
-    SV_I8_FIRST(2)
-    SV_I8_FIRST(3)
-    SV_I8_FIRST(4)
-    SV_I8_FIRST(5)
-    SV_I8_FIRST(6)
-    SV_I8_FIRST(7)
-    SV_I8_FIRST(8)
-    default: sync(0); return;   // empty range
-  }
-#undef SV_I8_FIRST
-  for (int kb = kb0 + len0; kb < kb1;) {
-    const int len = q2_chunk_len<WIDE_D>(kb, kb1 - kb);
-#define SV_I8_NEXT(L)                                                                  \
-  case L: {                                                                            \
-    Q2Chunk<L, WIDE_D> c;                                                              \
-    q2_chunk_load<L, WIDE_D>(W, n, kb, g, c);                                          \
-    q2_chunk_compute_i8<L, WIDE_D>(W, c, kb, n, X, nrows, lane, acc);                  \
-    break;                                                                             \
-  }
-    switch (len) {
-      SV_I8_NEXT(1)
-      SV_I8_NEXT(2)
-      SV_I8_NEXT(3)
-      SV_I8_NEXT(4)
-      SV_I8_NEXT(5)
-      SV_I8_NEXT(6)
-      SV_I8_NEXT(7)
-      default: SV_I8_NEXT(8)
-    }
-#undef SV_I8_NEXT
-    kb += len;
-  }
 }
 
 // Block barrier that does not wait for outstanding vector-memory loads (the

@@ -68,7 +68,7 @@ enum sv_ffn {
 
 enum sv_dist { SV_LOGITS = 0, SV_PROBS = 1 };  /* how a distribution row is given */
 
-#define SV_API_VERSION 1
+#define SV_API_VERSION 2
 #define SV_MAX_ROWS 64        /* R limit of the GEMM calls */
 #define SV_MAX_TOPK 16
 #define SV_MAX_EXPERTS 1024
@@ -95,6 +95,41 @@ SV_API const char* sv_status_str(int status);
 SV_API size_t sv_q2_matrix_bytes(int32_t n_out, int32_t k_in);
 
 /*
+ * Expert-tiled two-bit matrix: the blocks of a two-bit matrix regrouped so
+ * that everything one step of the SwiGLU expert kernels reads -- codes,
+ * nibbles, d and dmin of one or two blocks of 16 consecutive output rows --
+ * is one contiguous chunk (whole 128-byte lines instead of pieces of four
+ * planes).  The layout is the library's own (decode is bound by streaming the
+ * weights: [T3] "Roofline"); values and block format are unchanged.
+ * n_out % 16 == 0, k_in % 256 == 0, nb = k_in/256.  `parts` is the number of
+ * K ranges the kernels split a row into (4 for gate and up, 1 for down): part
+ * p covers blocks [nb*p/parts, nb*(p+1)/parts) (integer division).  A part's
+ * blocks form steps: one block first when the part starts at an odd block,
+ * then aligned pairs (2k, 2k+1), then one block when one is left.  The step of
+ * tile t (rows 16t .. 16t+15) starting at block kb with nblk blocks is the
+ * chunk of 1344*nblk bytes at byte 1344*(t*nb + kb):
+ *   codes   [16 rows][64*nblk B]: 16-byte piece c of row r (bytes 16c ..
+ *           16c+15 of its nblk*64 code bytes) at r*64*nblk + 16*((c+r) mod 4*nblk)
+ *   nibbles [16 rows][16*nblk B] from byte 1024*nblk
+ *   d       [16 rows][nblk] fp16 from byte 1280*nblk
+ *   dmin    [16 rows][nblk] fp16 from byte 1312*nblk
+ * sv_q2_tiled_bytes returns the size (84 bytes per 256 weights, no padding) or
+ * 0 for invalid shapes.
+ */
+SV_API size_t sv_q2_tiled_bytes(int32_t n_out, int32_t k_in);
+
+/*
+ * Regroups `count` two-bit matrices [n_out x k_in] stored back to back in the
+ * layout above (src, each sv_q2_matrix_bytes long) into the expert-tiled
+ * layout (dst, each sv_q2_tiled_bytes long), on `stream`.  src and dst are
+ * device buffers that must not overlap; the call only enqueues the copy.
+ * Returns SV_EINVAL for invalid shapes, parts outside 1..64, count < 1 or null
+ * pointers.
+ */
+SV_API int sv_q2_tile(const void* src, void* dst, int32_t n_out, int32_t k_in, int32_t parts, int32_t count,
+                      hipStream_t stream);
+
+/*
  * Eight-bit block matrix ("Q8_0" for the output head in [T3], introduction):
  * [n_out x k_in], k_in % 32 == 0; blocks of 32 int8 codes with one fp16 scale;
  * block b = n*(k_in/32) + kb.  Planes: codes nblk*32 int8, then d nblk fp16,
@@ -104,11 +139,14 @@ SV_API size_t sv_q8_matrix_bytes(int32_t n_out, int32_t k_in);
 
 /*
  * Description of one MoE layer (host struct, read only during the call).
- *  SV_FFN_SWIGLU: w_gate, w_up: n_experts matrices [inter x hidden] each;
- *    w_down: n_experts matrices [hidden x inter]; s_gate/s_up/s_down: the
- *    shared expert (always on, combine weight 1) or all NULL.
- *  SV_FFN_PLAIN: w_gate is one [inter x hidden] matrix; the other five NULL;
- *    n_experts = top_k = 1.
+ *  SV_FFN_SWIGLU: w_gate, w_up: n_experts matrices [inter x hidden] each,
+ *    expert-tiled with parts = 4 (sv_q2_tile), back to back
+ *    sv_q2_tiled_bytes(inter, hidden) apart; w_down: n_experts matrices
+ *    [hidden x inter], expert-tiled with parts = 1; s_gate/s_up/s_down: the
+ *    shared expert in the same layouts (always on, combine weight 1) or all
+ *    NULL.
+ *  SV_FFN_PLAIN: w_gate is one [inter x hidden] two-bit matrix (plain
+ *    layout); the other five NULL; n_experts = top_k = 1.
  *  hidden % 256 == 0 and inter % 256 == 0 for SWIGLU; PLAIN needs
  *  hidden % 256 == 0 and inter >= 1.
  */
@@ -233,6 +271,24 @@ SV_API int spec_accept_noalloc(int32_t S, int32_t K, int32_t V, const float* tar
  */
 SV_API int vq2_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream);
 SV_API int vq8_dequant(const void* w, int32_t n_out, int32_t k_in, float* out, hipStream_t stream);
+
+/*
+ * Tooling: a read-bandwidth probe, the measured denominator of the roofline
+ * fractions ([T3] "Roofline": a bandwidth probe sets the achievable rate).
+ * Reads floor(bytes / SV_PROBE_GROUP_BYTES) groups of 16 rows x 1792 bytes
+ * (the code plane of a 16-row tile of a 7168-wide two-bit matrix) from `src`
+ * once, each wave a contiguous range, 1 KB per wave instruction, in pattern
+ * `mode`: 0 loads into registers over full 128-byte lines; 1 global-to-LDS
+ * loads, non-temporal, full lines; 2 the same with the default cache policy;
+ * 3 global-to-LDS loads in 64-byte pieces (16 rows x 64 B per instruction);
+ * 4 the same, non-temporal; 5 global-to-LDS 4-byte loads, non-temporal, 256
+ * contiguous bytes per instruction (the first 7 KB of every group only).
+ * `sink` [sink_words] receives one word per wave (at most 8 per compute
+ * unit); SV_EWORKSPACE if sink_words is smaller.
+ */
+#define SV_PROBE_GROUP_BYTES ((size_t)16 * 1792)
+SV_API int sv_read_probe(const void* src, size_t bytes, int32_t mode, uint32_t* sink,
+                         size_t sink_words, hipStream_t stream);
 
 #ifdef __cplusplus
 }

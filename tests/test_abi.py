@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = sv.load()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 16
     assert set(names) == set(sv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.api_version() == 1
+    assert sv.api_version() == 2
     assert sv.status_str(sv.SV_OK) == "ok"
     assert "workspace" in sv.status_str(sv.SV_EWORKSPACE)
     assert sv.status_str(99) == "unknown status"
@@ -46,6 +46,29 @@ def test_q2_matrix_bytes_agree_with_oracle(n, k):
 @pytest.mark.parametrize("n,k", [(129280, 7168), (1, 32), (7, 64)])
 def test_q8_matrix_bytes_agree_with_oracle(n, k):
     assert sv.sv_q8_matrix_bytes(n, k) == oracle.q8_matrix_bytes(n, k)
+
+
+@pytest.mark.parametrize("n,k", [(2048, 7168), (7168, 2048), (16, 256), (48, 768)])
+def test_q2_tiled_bytes_are_84_per_256_weights(n, k):
+    assert sv.sv_q2_tiled_bytes(n, k) == 84 * n * k // 256
+
+
+def test_q2_tiled_bytes_reject_invalid_shapes():
+    for n, k in ((8, 256), (24, 256), (0, 256), (16, 100), (16, 0)):
+        assert sv.sv_q2_tiled_bytes(n, k) == 0, (n, k)
+
+
+def test_q2_tile_validates_on_the_host():
+    lib = sv.load()
+    a, b = 0x10000000, 0x20000000
+    assert lib.sv_q2_tile(None, b, 32, 512, 4, 1, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, None, 32, 512, 4, 1, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, b, 24, 512, 4, 1, None) == sv.SV_EINVAL      # rows not a multiple of 16
+    assert lib.sv_q2_tile(a, b, 32, 500, 4, 1, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, b, 32, 512, 0, 1, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, b, 32, 512, 65, 1, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, b, 32, 512, 4, 0, None) == sv.SV_EINVAL
+    assert lib.sv_q2_tile(a, a + 64, 32, 512, 4, 1, None) == sv.SV_EINVAL  # overlapping buffers
 
 
 def test_invalid_shapes_give_zero_sizes():
@@ -116,6 +139,8 @@ def test_calls_reject_bad_arguments_before_launch():
     assert sv.sv_accept_workspace_bytes(31, 4, 129280) <= sv.ACCEPT_SCRATCH_BYTES
     assert lib.spec_accept_noalloc(*nargs(S=40, V=129280)) == sv.SV_ESCRATCH
     assert "scratch" in sv.status_str(sv.SV_ESCRATCH)
+    assert lib.sv_read_probe(fake, 1 << 20, 6, fake, 1 << 16, None) == sv.SV_EINVAL
+    assert lib.sv_read_probe(fake, 100, 0, fake, 1 << 16, None) == sv.SV_EINVAL
     assert lib.vq2_dequant(fake, 10, 100, fake, None) == sv.SV_EINVAL
     assert lib.vq8_dequant(fake, 10, 33, fake, None) == sv.SV_EINVAL
 

@@ -41,6 +41,55 @@ def test_q2_dequant_bit_exact(sv, n, k):
         pytest.fail(f"{rows.size} mismatches; (n,k,q,sc,m,d*2^24,dmin*2^24,got,want): {info}")
 
 
+def _tiled_layout(buf, n, k, parts):
+    """The expert-tiled layout as the header states it, written out with
+    numpy loops from the plain planes (an independent restatement of the
+    chunk formula, not a copy of the kernel's indexing)."""
+    nb = k // 256
+    nblk = n * nb
+    up = lambda x: (x + 255) // 256 * 256
+    qs = buf[:nblk * 64].reshape(n, nb, 64)
+    o = up(nblk * 64)
+    sc = buf[o:o + nblk * 16].reshape(n, nb, 16)
+    o += up(nblk * 16)
+    d = buf[o:o + nblk * 2].reshape(n, nb, 2)
+    o += up(nblk * 2)
+    dm = buf[o:o + nblk * 2].reshape(n, nb, 2)
+    out = np.zeros(nblk * 84, np.uint8)
+    for t in range(n // 16):
+        rows = slice(16 * t, 16 * t + 16)
+        for p in range(parts):
+            b0, b1 = nb * p // parts, nb * (p + 1) // parts
+            kb = b0
+            while kb < b1:
+                m = 1 if (kb % 2 or kb + 1 >= b1) else 2
+                base = 1344 * (t * nb + kb)
+                pieces = qs[rows, kb:kb + m].reshape(16, 4 * m, 16)
+                for r in range(16):
+                    for c in range(4 * m):
+                        at = base + r * 64 * m + 16 * ((c + r) % (4 * m))
+                        out[at:at + 16] = pieces[r, c]
+                out[base + 1024 * m:base + 1280 * m] = sc[rows, kb:kb + m].reshape(-1)
+                out[base + 1280 * m:base + 1312 * m] = d[rows, kb:kb + m].reshape(-1)
+                out[base + 1312 * m:base + 1344 * m] = dm[rows, kb:kb + m].reshape(-1)
+                kb += m
+    return out
+
+
+@pytest.mark.parametrize("n,k,parts", [(32, 7168, 4), (16, 2048, 1), (32, 1792, 4), (48, 768, 4),
+                                       (16, 2304, 1), (32, 2304, 3)])
+def test_q2_tile_layout_bit_exact(sv, n, k, parts):
+    """sv_q2_tile writes every byte where the documented chunk layout puts it
+    (two matrices back to back: the second one's offset is checked too)."""
+    mats = [synth.q2_random(synth.generator(109, n, k, i), n, k, 0.02).packed() for i in range(2)]
+    say("sv_q2_tile", n, k, parts)
+    got = host(sv.sv_q2_tile(dev(np.concatenate(mats)), n, k, parts, 2))
+    want = np.concatenate([_tiled_layout(m, n, k, parts) for m in mats])
+    assert got.shape == want.shape
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8].tolist()}"
+
+
 @pytest.mark.parametrize("n,k", [(777, 1024), (16, 7168)])
 def test_q8_dequant_bit_exact(sv, n, k):
     p = synth.q8_random(synth.generator(101, n, k), n, k, 0.01)
