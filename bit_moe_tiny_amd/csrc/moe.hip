@@ -224,7 +224,7 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 // cap_big rows; down: groups of at most cap_big rows, typed like the unit's
 // gate/up work.  Then the item ranges of the kernel's G persistent blocks:
 // every descriptor has `items` items, each costing MOE_COST_1 (at most four
-// rows) or MOE_COST_2; block b starts at the first item whose cost offset is
+// rows) or MOE_COST_2_*; block b starts at the first item whose cost offset is
 // at least floor(C b / G) (C the total cost), so the ranges are contiguous,
 // cover every item once and carry about equal cost.
 __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucnt, int nu,
@@ -248,7 +248,7 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
 #pragma unroll
       for (int c = 0; c < MOE_WORK_COLS; ++c) w.rows[c] = c < w.ncols ? s_arow[w.a0 + c] : 0;
       work[base + incl - ng + j] = w;
-      s_cost[base + incl - ng + j + 1] = w.ncols > 4 ? MOE_COST_2 : MOE_COST_1;
+      s_cost[base + incl - ng + j + 1] = w.ncols > 4 ? (gateup ? MOE_COST_2_GU : MOE_COST_2_DN) : MOE_COST_1;
       if (gateup)
         for (int c = 0; c < w.ncols; ++c) atype[w.a0 + c] = type;
     }

@@ -343,9 +343,11 @@ struct MoeMeta {
 constexpr int MOE_WORK_COLS = 8;
 constexpr int MOE_MAX_GRID = 1024;   // persistent blocks of an expert kernel, at most
 // Relative cost of an expert-kernel item whose descriptor has at most four
-// rows (one column tile) and more (two column tiles, the weight tile shared):
-// the block ranges are cut to equal cost with these weights.
-constexpr int MOE_COST_1 = 5, MOE_COST_2 = 8;
+// rows (one column tile) and more (two column tiles, the weight tile shared),
+// as measured per kernel: the block ranges are cut to equal cost with these
+// weights.
+constexpr int MOE_COST_1 = 10;
+constexpr int MOE_COST_2_GU = 16, MOE_COST_2_DN = 19;
 enum { MOE_ALLK = 0, MOE_QUARTER = 1 };
 struct MoeWork {
   int expert, a0, ncols, type;
