@@ -13,12 +13,18 @@ between two device synchronisations; value = algorithmic weight bytes of the
 timed steps (the routed experts each batch actually touches, the shared
 expert, the vocabulary head) / elapsed time.
 
-Prints ONE JSON line (rank 0, N = 1).  --sweep prints one line per R instead.
+Prints ONE JSON line (rank 0, N = 1).  Besides the headline (R = 5, S = 1)
+the line carries, unless --no-extras: one entry per R = 1..16 and the
+three-sequence cohort (R = 15, S = 3), single-expert calls at R = 1, 2, 4, 8
+beside an empty-launch floor, live per-kernel times of one R = 5 step with a
+roofline entry per expert kernel, the read-bandwidth probe, and SHA-256
+digests of the generated inputs.  --sweep prints one line per R instead.
 """
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import json
 import os
 import platform
@@ -58,6 +64,9 @@ def parse():
                     help="buffer size of the read-bandwidth probe (0: skip it)")
     ap.add_argument("--bw-probe-only", action="store_true",
                     help="run only the read-bandwidth probe and print its JSON line")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline: no per-R entries, cohort, single-expert calls or kernel times")
+    ap.add_argument("--extra-steps", type=int, default=20, help="timed steps of each per-R / cohort entry")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, one plain device copy of this many MiB (fp32 x 1.0): "
                          "the known-size kernel that calibrates profiler byte counters")
@@ -81,6 +90,17 @@ def gen_moe_weights(threads: int = 8):
     return routed, bufs[E]
 
 
+def sha256_of(arrays, threads: int = 8) -> str:
+    """SHA-256 over the SHA-256 digests of the arrays' bytes, in order (each
+    array hashed on its own thread)."""
+    def one(a):
+        a = np.ascontiguousarray(a)
+        return hashlib.sha256(a.tobytes() if a.size == 0 else memoryview(a).cast("B")).digest()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(one, arrays))
+    return hashlib.sha256(b"".join(parts)).hexdigest()
+
+
 def to_dev(a):
     import torch
     a = np.ascontiguousarray(a)
@@ -99,9 +119,11 @@ class Step:
         self.T = temperature
         V, H = synth.VOCAB, synth.HIDDEN
         self.batches = []
+        self.host_inputs = []
         for b in range(n_batches):
             rows = synth.moe_rows(R, synth.CFG_MOE, sub=100 * R + b)
             h = synth.lm_head_hidden(R, synth.CFG_LMHEAD, sub=100 * R + b)
+            self.host_inputs += [rows.x_bf16, rows.router_logits, h]
             self.batches.append(dict(x=to_dev(rows.x_bf16), logits=to_dev(rows.router_logits),
                                      h=to_dev(h)))
         self.y = torch.empty((R, H), dtype=torch.float32, device="cuda")
@@ -123,6 +145,7 @@ class Step:
             bt["draft"] = to_dev(acc.draft_logits) if self.K else None
             bt["drafts"] = to_dev(acc.drafts) if self.K else None
             bt["u"] = to_dev(acc.uniforms)
+            self.host_inputs += [acc.drafts, acc.uniforms] + ([acc.draft_logits] if self.K else [])
 
     def run(self, b, ev=None):
         sv, bt = self.sv, self.batches[b % len(self.batches)]
@@ -217,6 +240,126 @@ def bw_probe(sv, gib: float, reps: int = 10):
     return {"bytes": nbytes, "modes": out}
 
 
+# ------------------------------------------------------------------ extras
+def entry(R, S, m):
+    """Compact per-R record: step time, weight GB/s, roofline fraction and
+    the per-call times of the breakdown pass."""
+    steps = len(m["step_ms"])
+    total_s = m["total_ms"] / 1e3
+    gbs = float((m["moe_bytes"] + Q8_HEAD_BYTES).sum() / total_s / 1e9)
+    return {"R": R, "S": S, "K": R // S - 1, "ms_per_step": round(total_s * 1e3 / steps, 4),
+            "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "call_us": {"vq2_moe_gemm": round(float(m["moe_ms"].mean()) * 1e3, 2),
+                        "vq8_lmhead_gemm": round(float(m["lm_ms"].mean()) * 1e3, 2),
+                        "spec_accept": round(float(m["acc_ms"].mean()) * 1e3, 2)},
+            "moe_GB/s": round(float(m["moe_bytes"].sum() / (m["moe_ms"].sum() / 1e3) / 1e9), 1)}
+
+
+def launch_floor(n_launch: int, reps: int = 200):
+    """Time of n_launch back-to-back minimal kernel launches on the current
+    stream (a one-element fill each), median over reps: the fixed cost every
+    call of that many kernels pays whatever its size."""
+    import torch
+    t = torch.empty(1, dtype=torch.float32, device="cuda")
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_launch):
+            t.fill_(1.0)
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)) * 1e3
+
+
+def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24, reps: int = 48):
+    """Config C1 shape: one SwiGLU expert (E = 1, no shared) with all R rows.
+    The calls rotate over `copies` resident experts (24 x 14.45 MB exceeds
+    the 256 MB last-level cache, so the weights stream from HBM); median of
+    the event-timed calls, beside the floor of the same number of empty
+    launches (the call is 5 kernels)."""
+    import torch
+    wg, wu, wd = desc._keep[0], desc._keep[1], desc._keep[2]
+    gu, dn = sv.sv_q2_tiled_bytes(synth.INTER, synth.HIDDEN), sv.sv_q2_tiled_bytes(synth.HIDDEN, synth.INTER)
+    descs = [sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, 1, 1, wg[e * gu:(e + 1) * gu],
+                         wu[e * gu:(e + 1) * gu], wd[e * dn:(e + 1) * dn], tiled=True)
+             for e in range(copies)]
+    floor = launch_floor(5)
+    out = []
+    for R in Rs:
+        x = to_dev(synth.expert(R).x_bf16)
+        y = torch.empty((R, synth.HIDDEN), dtype=torch.float32, device="cuda")
+        ws = torch.empty(sv.sv_moe_workspace_bytes(descs[0], R), dtype=torch.uint8, device="cuda")
+        for d in descs:   # warm-up
+            sv.vq2_moe_gemm(d, x, None, y, ws=ws)
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sv.vq2_moe_gemm(descs[i % copies], x, None, y, ws=ws)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        us = float(np.median(ts)) * 1e3
+        out.append({"R": R, "us": round(us, 2), "GB/s": round(Q2_EXPERT_BYTES / us / 1e3, 1),
+                    "frac": round(Q2_EXPERT_BYTES / us / 1e3 / PEAK_HBM_GBS, 4)})
+    return {"bytes": Q2_EXPERT_BYTES, "launches": 5, "empty_launch_floor_us": round(floor, 2),
+            "rows": out}
+
+
+KERNEL_KEYS = {"gate/up": "k_gu8", "down": "k_dn8", "down input digits": "k_hdig", "routing": "k_moe_prep",
+               "combine": "k_moe_combine", "head": "k_q8_lmhead", "head staging": "k_stage",
+               "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample"}
+
+
+def kernel_times(step, steps: int = 10):
+    """Average device time per launch of each kernel over `steps` steps,
+    from torch's profiler (it records the library's launches on the same
+    stream); with the algorithmic bytes of the two expert kernels, their
+    roofline entries.  None when the profiler is unavailable."""
+    import torch
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(steps):
+                step.run(i)
+            torch.cuda.synchronize()
+        avg = {}
+        for ev in prof.key_averages():
+            dev_us = getattr(ev, "device_time_total", None)
+            if dev_us is None:
+                dev_us = getattr(ev, "cuda_time_total", 0.0)
+            if ev.count and dev_us:
+                for what, key in KERNEL_KEYS.items():
+                    if key in ev.key:
+                        a = avg.setdefault(what, {"kernel": ev.key.split("(")[0].replace("void ", ""),
+                                                  "launches": 0, "us_total": 0.0})
+                        a["launches"] += ev.count
+                        a["us_total"] += dev_us
+    except Exception as exc:  # pragma: no cover - profiler support differs between builds
+        log(f"kernel times unavailable: {exc!r}")
+        return None
+    out = {}
+    for what, a in avg.items():
+        out[what] = {"kernel": a["kernel"], "launches": a["launches"],
+                     "us": round(a["us_total"] / a["launches"], 2)}
+    # algorithmic bytes per launch of the expert kernels: each touched expert's
+    # matrices once (gate + up for the first, down for the second)
+    per = Q2_EXPERT_BYTES // 3
+    experts = float(np.mean([len(np.unique(step.tidx[i % len(step.batches)].cpu().numpy())) + 1
+                             for i in range(steps)]))
+    roof = []
+    for what, nbytes in (("gate/up", 2 * per * experts), ("down", per * experts)):
+        if what in out:
+            gbs = nbytes / (out[what]["us"] * 1e-6) / 1e9
+            roof.append({"kernel": out[what]["kernel"], "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes_per_launch": int(nbytes)})
+    return {"steps": steps, "R": step.R, "kernels": out, "roofline_expert_kernels": roof}
+
+
 def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
     """The oracle, unchanged, on a bounded sample of the same workload."""
     import threadpoolctl
@@ -245,6 +388,14 @@ def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
     dt = time.perf_counter() - t0
     nbytes = (len(experts) + 1) * Q2_EXPERT_BYTES + n_vocab * synth.HIDDEN * 34 // 32
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    model = platform.processor() or platform.machine()
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     gbs = nbytes / dt / 1e9
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"{len(experts)} routed experts (their routed rows) + the shared expert on "
@@ -253,7 +404,8 @@ def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
                        f"of weights in {dt:.2f} s"),
             "seconds": round(dt, 3),
             "est_step_s": round(step_bytes_mean / (gbs * 1e9), 2),
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": model, "host_cpus": os.cpu_count(),
+            "threads_note": "cores = threads of the BLAS pool the oracle's matrix products ran on"}
 
 
 TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "lmhead_R5_hbm_traffic.md")
@@ -352,10 +504,14 @@ def main():
     t = time.time()
     log("generating 257 two-bit experts (3.7 GB) ...")
     (g, u, d), (sg, su, sd) = gen_moe_weights()
+    digests = {"moe_weights": sha256_of([g, u, d, sg, su, sd])}
     wg, wu, wd, wsg, wsu, wsd = (to_dev(a) for a in (g, u, d, sg, su, sd))
     del g, u, d
     log(f"experts resident ({time.time() - t:.1f} s); generating the vocabulary head (985 MB) ...")
-    wq8 = to_dev(synth.lm_head_weights().packed())
+    q8 = synth.lm_head_weights().packed()
+    digests["head_weights"] = sha256_of([q8])
+    wq8 = to_dev(q8)
+    del q8
     log(f"head resident ({time.time() - t:.1f} s)")
     desc = sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, synth.N_ROUTED, synth.TOP_K,
                        wg, wu, wd, wsg, wsu, wsd)
@@ -370,7 +526,28 @@ def main():
             log("cpu_baseline: timing the oracle on a bounded sample ...")
             cpu = cpu_baseline(float((m["moe_bytes"] + Q8_HEAD_BYTES).mean()), R, args.cpu_experts,
                                args.cpu_vocab)
-        print(json.dumps(result_line(args, R, S, m, cpu)), flush=True)
+        line = result_line(args, R, S, m, cpu)
+        if not args.sweep:
+            digests["step_inputs"] = sha256_of(step.host_inputs)
+            line["inputs_sha256"] = digests
+            if not args.no_extras:
+                log("kernel times of one step (profiler) ...")
+                line["kernel_times"] = kernel_times(step)
+                del step
+                ents = []
+                for r2, s2 in [(r, 1) for r in range(1, 17)] + [(15, 3)]:
+                    st = Step(sv, desc, wq8, r2, s2, 3, args.temperature)
+                    ents.append(entry(r2, s2, measure(st, args.extra_steps, 3)))
+                    log(f"entry R={r2} S={s2}: {ents[-1]['ms_per_step']} ms per step")
+                    del st
+                line["per_R"] = [e for e in ents if e["S"] == 1]
+                line["cohort"] = [e for e in ents if e["S"] == 3][0]
+                log("single-expert calls ...")
+                line["single_expert"] = single_expert(sv, desc)
+            if args.bw_probe_gib > 0:
+                log(f"read-bandwidth probe on {args.bw_probe_gib} GiB ...")
+                line["bw_probe"] = bw_probe(sv, args.bw_probe_gib)
+        print(json.dumps(line), flush=True)
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -13,7 +13,7 @@
 //                 (one block per row).
 //   k_gu8         gate/up + SwiGLU (moe_i8.hip)
 //   k_hdig        the down projection's input rows as digits (one block per
-//                 assignment; SwiGLU of the quarter sums for MOE_QUARTER units)
+//                 assignment: SwiGLU of the gate/up quarter sums)
 //   k_dn8         down projection (moe_i8.hip)
 //   k_moe_combine y = fixed-order weighted sum of the per-assignment outputs:
 //                 slots 0..k-1, then the shared expert.
@@ -52,7 +52,6 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.amap = (int*)take(sizeof(int) * R * (k + 1));
   w.topk_idx = (int*)take(sizeof(int) * R * k);
   w.topk_w = (float*)take(sizeof(float) * R * k);
-  w.h = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->inter);
   w.gpart = (float*)take(plain ? 0 : sizeof(float) * 8 * (size_t)max_assign * d->inter);
   w.part = (float*)take(plain ? 0 : sizeof(float) * (size_t)max_assign * d->hidden);
   // at most one descriptor per unit plus one per further column
@@ -61,7 +60,6 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   w.work_dn = (MoeWork*)take(sizeof(MoeWork) * max_work);
   w.blk_gu = (int*)take(sizeof(int) * (MOE_MAX_GRID + 1));
   w.blk_dn = (int*)take(sizeof(int) * (MOE_MAX_GRID + 1));
-  w.atype = (int*)take(sizeof(int) * max_assign);
   void* hd = take(plain ? 0 : xdig_bytes(max_assign, d->inter));
   void* xd = take(plain ? 0 : xdig_bytes(R, d->hidden));
   void* xb = take(plain ? ximg_bytes(R, d->hidden, XL_PERM) : 0);
@@ -229,7 +227,7 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 // cover every item once and carry about equal cost.
 __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucnt, int nu,
                           const int* s_arow, bool gateup, int cap_allk, int cap_big, int items, int G,
-                          MoeWork* work, int* n_work, int* blk, int* s_cost, int* atype) {
+                          MoeWork* work, int* n_work, int* blk, int* s_cost) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   for (int u0 = 0; u0 < nu; u0 += 64) {
@@ -249,8 +247,6 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
       for (int c = 0; c < MOE_WORK_COLS; ++c) w.rows[c] = c < w.ncols ? s_arow[w.a0 + c] : 0;
       work[base + incl - ng + j] = w;
       s_cost[base + incl - ng + j + 1] = w.ncols > 4 ? (gateup ? MOE_COST_2_GU : MOE_COST_2_DN) : MOE_COST_1;
-      if (gateup)
-        for (int c = 0; c < w.ncols; ++c) atype[w.a0 + c] = type;
     }
     base += __builtin_amdgcn_readlane(incl, 63);
   }
@@ -377,9 +373,9 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
   }
   __syncthreads();
   if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, true, cap_allk, cap_quarter, items_gu,
-                         G, ws.work_gu, &ws.meta->n_work_gu, ws.blk_gu, s_cost_gu, ws.atype);
+                         G, ws.work_gu, &ws.meta->n_work_gu, ws.blk_gu, s_cost_gu);
   if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, false, cap_allk, cap_down, items_dn,
-                         G, ws.work_dn, &ws.meta->n_work_dn, ws.blk_dn, s_cost_dn, ws.atype);
+                         G, ws.work_dn, &ws.meta->n_work_dn, ws.blk_dn, s_cost_dn);
 }
 
 // ------------------------------------------------------------ rows as digits
@@ -465,26 +461,14 @@ __device__ void stage_digits(const void* x, int row, XDig xd) {
   });
 }
 
-// The down projection's input of assignment a as digits: h (units of
-// MOE_ALLK) or silu(sum of the gate quarters) * (sum of the up quarters),
-// quarters summed in order (units of MOE_QUARTER).  One block per assignment.
+// The down projection's input of assignment a as digits: silu(sum of the
+// gate quarters) * (sum of the up quarters), quarters summed in order (the
+// SwiGLU of the gate/up kernels' quarter sums).  One block per assignment.
 __global__ __launch_bounds__(PREP_THREADS) void k_hdig(MoeWs ws, int inter) {
   const int a = blockIdx.x;
-  const int type = ws.atype[a];
   const size_t qs = (size_t)ws.max_assign * inter;
   stage_row_digits(a, ws.hd, [&](int sb, float (&v)[16]) {
     const size_t o = (size_t)a * inter + 16 * sb;
-    if (type == MOE_ALLK) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 f = *(const float4*)(ws.h + o + 4 * j);
-        v[4 * j] = f.x;
-        v[4 * j + 1] = f.y;
-        v[4 * j + 2] = f.z;
-        v[4 * j + 3] = f.w;
-      }
-      return;
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float4 gq[4], uq[4];

@@ -30,13 +30,14 @@
 // range of items (all 8 waves on one item at a time):
 //   k_gu8, MOE_ALLK descriptor (a unit of <= cap_allk rows): item = one
 //     16-row tile of inter; wave (m, q): matrix m (gate, up), quarter q of
-//     hidden.  The rows' digits over all of hidden stay in LDS; the quarter
-//     sums meet in LDS, one wave applies SwiGLU and writes h.
+//     hidden.  The rows' digits over all of hidden stay in LDS.
 //   k_gu8, MOE_QUARTER descriptor (a unit with more rows, e.g. the shared
 //     expert): item = (quarter q, four 16-row tiles); wave (m, j): matrix m,
 //     tile j of four, over quarter q; the rows' digits over that quarter stay
-//     in LDS; the quarter sums go to the workspace and SwiGLU happens where
-//     the down projection reads them -- every weight tile is still read once.
+//     in LDS.
+//   Either way every wave writes its quarter sums to the workspace; k_hdig
+//     sums the quarters in order and applies SwiGLU.  Every weight tile is
+//     read once.
 //   k_dn8: item = eight 16-row tiles of hidden for one descriptor (at most
 //     cap_down rows), wave j: tile j over all of inter.  The block copies the
 //     descriptor's rows of the down input's digit image (written once per
@@ -56,7 +57,7 @@ constexpr int M8_CHUNK = 1344;                               // tiled bytes of o
 constexpr int M8_SLOT = 2 * M8_CHUNK;                        // one two-block step
 constexpr int M8_DMA = 3;                                    // wave instructions per step
 constexpr size_t M8_RINGS = (size_t)M8_WAVES * M8_RING * M8_SLOT;
-constexpr size_t M8_RED = (size_t)2 * M8_WAVES * 64 * 4 + 64;   // quarter sums of two items; row scales
+constexpr size_t M8_RED = 64;                                // gate/up: row scales of the descriptor's columns
 constexpr size_t M8_MISC = 256;                              // down: row maxima, flags, scales
 constexpr size_t M8_LDS_MAX = 160 * 1024;
 constexpr int M8_CAP_ALLK = 2;                               // rows of a MOE_ALLK descriptor, at most
@@ -415,8 +416,7 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8(ExpertPtrs P, int nb, int
   const int n = lane & 15, g = lane >> 4;
   uint8_t* ring = lds + (size_t)w * M8_RING * M8_SLOT;
   const uint32_t ring_la = lds_addr(ring);
-  float* red = (float*)(lds + M8_RINGS);
-  float* s_rsc = red + 2 * M8_WAVES * 64;   // row scales of the current descriptor's columns
+  float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_RED;
   const uint32_t voff = 16u * (uint32_t)lane;
   const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
@@ -523,22 +523,9 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8(ExpertPtrs P, int nb, int
     for (int ct = 0; ct < 2; ++ct) acc[ct] = (f4_t){0.f, 0.f, 0.f, 0.f};
     if (nc <= 4) m8_item<1>(ring, cslot, cu.b0, cu.b1, rb0, A, acc, issue);
     else m8_item<2>(ring, cslot, cu.b0, cu.b1, rb0, A, acc, issue);
-    if (cc.type == MOE_ALLK) {
-      // quarter sums of the tile meet in LDS; wave (it mod 8) applies SwiGLU
-      float* rb = red + (size_t)(it & 1) * M8_WAVES * 64;
-      rb[w * 64 + lane] = m8_value(acc[0]);
-      barrier_lds();
-      if (w == (it & (M8_WAVES - 1))) {
-        const float* rl = rb + lane;
-        const float gs = ((rl[0] + rl[64]) + rl[128]) + rl[192];
-        const float us = ((rl[256] + rl[320]) + rl[384]) + rl[448];
-        if (g < nc) {
-          const float rs = s_rsc[g];
-          ws.h[(size_t)(a0 + g) * inter + cu.tile * 16 + n] = silu_mul(gs * rs, us * rs);
-        }
-      }
-    } else {
+    {
       // this wave's quarter sums of its tile, per row slot, to the workspace
+      // (k_hdig sums the quarters and applies SwiGLU)
       const int nct = (nc + 3) / 4;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -575,8 +562,7 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8f(ExpertPtrs P, int inter,
   const int n = lane & 15, g = lane >> 4;
   uint8_t* ring = lds + (size_t)w * M8_RING * M8_SLOT;
   const uint32_t ring_la = lds_addr(ring);
-  float* red = (float*)(lds + M8_RINGS);
-  float* s_rsc = red + 2 * M8_WAVES * 64;
+  float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_RED;
   const uint32_t voff = 16u * (uint32_t)lane;
   const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
@@ -695,21 +681,9 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8f(ExpertPtrs P, int inter,
       if (NQ == 7 && odd) m8_fitem<PO, 2>(ring, A, acc, nx);
       else m8_fitem<PE, 2>(ring, A, acc, nx);
     }
-    if (cc.type == MOE_ALLK) {
-      // quarter sums of the tile meet in LDS; wave (it mod 8) applies SwiGLU
-      float* rb = red + (size_t)(it & 1) * M8_WAVES * 64;
-      rb[w * 64 + lane] = m8_value(acc[0]);
-      barrier_lds();
-      if (w == (it & (M8_WAVES - 1))) {
-        const float* rl = rb + lane;
-        const float gs = ((rl[0] + rl[64]) + rl[128]) + rl[192];
-        const float us = ((rl[256] + rl[320]) + rl[384]) + rl[448];
-        if (g < nc) {
-          const float rs = s_rsc[g];
-          ws.h[(size_t)(a0 + g) * inter + cu.tile * 16 + n] = silu_mul(gs * rs, us * rs);
-        }
-      }
-    } else {
+    {
+      // this wave's quarter sums of its tile, per row slot, to the workspace
+      // (k_hdig sums the quarters and applies SwiGLU)
       const int nct = (nc + 3) / 4;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {

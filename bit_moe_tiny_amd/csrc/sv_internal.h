@@ -335,11 +335,11 @@ struct MoeMeta {
 // One descriptor of the expert kernels: a column group of one unit (an
 // expert, -1 = shared): its first assignment a0, its ncols assignments and
 // the activation row of each.  type (gate/up): MOE_ALLK -- the rows' digits
-// over all of K stay resident and the block's waves split K (SwiGLU in the
-// block); MOE_QUARTER -- the block's waves take four tiles of one quarter of
-// K, partial sums go to the workspace and SwiGLU happens where the down
-// projection reads them.  Down descriptors carry the type of their unit's
-// gate/up work (where h comes from).  One 48-byte load per descriptor.
+// over all of K stay resident and the block's waves split K; MOE_QUARTER --
+// the block's waves take four tiles of one quarter of K.  Either way the
+// quarter sums go to the workspace and SwiGLU happens when the down
+// projection's input is staged (k_hdig).  Down descriptors carry their unit's
+// gate/up type.  One 48-byte load per descriptor.
 constexpr int MOE_WORK_COLS = 8;
 constexpr int MOE_MAX_GRID = 1024;   // persistent blocks of an expert kernel, at most
 // Relative cost of an expert-kernel item whose descriptor has at most four
@@ -363,14 +363,12 @@ struct MoeWs {
   int* amap;          // [R, top_k+1]  assignment of (row, slot); slot top_k = shared
   int* topk_idx;      // [R, top_k]
   float* topk_w;      // [R, top_k]
-  float* h;           // [max_assign, inter]  SwiGLU output (units of MOE_ALLK)
-  float* gpart;       // [2][4][max_assign, inter]  gate / up quarter sums (units of MOE_QUARTER)
+  float* gpart;       // [2][4][max_assign, inter]  gate / up quarter sums
   float* part;        // [max_assign, hidden] per-assignment down outputs
   MoeWork* work_gu;   // [max_work]
   MoeWork* work_dn;   // [max_work]
   int* blk_gu;        // [MOE_MAX_GRID + 1] first item of each persistent gate/up block
   int* blk_dn;        // [MOE_MAX_GRID + 1] the same for the down kernel
-  int* atype;         // [max_assign] MOE_ALLK / MOE_QUARTER: where assignment a's SwiGLU output is
   XDig hd;            // the down projection's input rows as digits  [max_assign, inter]
   XDig xd;            // x as digits  [R, hidden]
   XImg x_img;         // x staged for the one-matrix (PLAIN) path  [R, hidden]
