@@ -360,6 +360,112 @@ def kernel_times(step, steps: int = 10):
     return {"steps": steps, "R": step.R, "kernels": out, "roofline_expert_kernels": roof}
 
 
+class LayerStack:
+    """A verifier step over L stacked MoE layers: per layer the eight-bit
+    router GEMV ([256 x 7168], through the head's call) on the layer's input,
+    the routed layer, its output feeding the next layer (fp32); then the
+    vocabulary head on the last output and spec_accept (S = 1, K = R - 1).
+    The layers share one expert set and router (a synthetic stand-in: the
+    work per layer is the same as with distinct weights, the touched experts
+    differ with the inputs)."""
+
+    def __init__(self, sv, desc, wq8, wrouter, R, L, temperature):
+        import torch
+        self.sv, self.desc, self.wq8, self.wr = sv, desc, wq8, wrouter
+        self.R, self.L, self.K, self.T = R, L, R - 1, temperature
+        V, H, E = synth.VOCAB, synth.HIDDEN, synth.N_ROUTED
+        self.x0 = to_dev(synth.moe_rows(R, synth.CFG_MOE, sub=900 + R).x_bf16)
+        self.ys = [torch.empty((R, H), dtype=torch.float32, device="cuda") for _ in range(L)]
+        self.lg = [torch.empty((R, E), dtype=torch.float32, device="cuda") for _ in range(L)]
+        self.tidx = torch.empty((R, synth.TOP_K), dtype=torch.int32, device="cuda")
+        self.z = torch.empty((R, V), dtype=torch.float32, device="cuda")
+        self.toks = torch.empty((1, R), dtype=torch.int32, device="cuda")
+        self.nacc = torch.empty((1,), dtype=torch.int32, device="cuda")
+        self.ws_moe = torch.empty(sv.sv_moe_workspace_bytes(desc, R), dtype=torch.uint8, device="cuda")
+        self.ws_lm = torch.empty(sv.sv_lmhead_workspace_bytes(H, R), dtype=torch.uint8, device="cuda")
+        self.ws_acc = torch.empty(sv.sv_accept_workspace_bytes(1, self.K, V), dtype=torch.uint8, device="cuda")
+        self.draft = self.drafts = None
+        self.u = torch.zeros((1, R), dtype=torch.float32, device="cuda")
+        self.run()                       # target logits of the stack, then the draft side
+        torch.cuda.synchronize()
+        acc = synth.accept_inputs(self.z.cpu().numpy(), 1, self.K, 1.5, temperature, synth.CFG_LMHEAD, sub=900 + R)
+        self.draft = to_dev(acc.draft_logits) if self.K else None
+        self.drafts = to_dev(acc.drafts) if self.K else None
+        self.u = to_dev(acc.uniforms)
+
+    launches_per_layer = 2 + 5          # router GEMV (staging + head kernel) + the MoE layer
+
+    def launches(self):
+        return self.L * self.launches_per_layer + 2 + 2
+
+    def run(self):
+        sv, H, V, E = self.sv, synth.HIDDEN, synth.VOCAB, synth.N_ROUTED
+        x = self.x0
+        for l in range(self.L):
+            sv.vq8_lmhead_gemm(self.wr, E, H, x, self.lg[l], ws=self.ws_lm)
+            sv.vq2_moe_gemm(self.desc, x, self.lg[l], self.ys[l], self.tidx, None, ws=self.ws_moe)
+            x = self.ys[l]
+        sv.vq8_lmhead_gemm(self.wq8, V, H, x, self.z, ws=self.ws_lm)
+        if self.u is not None and (self.K == 0 or self.draft is not None):
+            sv.spec_accept(1, self.K, V, self.z, sv.SV_LOGITS, self.T, self.draft, sv.SV_LOGITS, self.T,
+                           self.drafts, self.u, self.toks, self.nacc, ws=self.ws_acc)
+
+
+def time_eager_and_graph(fn, reps: int = 30):
+    """Median event-timed duration of fn() run eagerly and as a captured HIP
+    graph replay (torch.cuda.CUDAGraph), in microseconds."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+
+    def timed(call):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e3
+
+    eager = timed(fn)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    graph = timed(g.replay)
+    del g
+    return eager, graph
+
+
+def graph_steps(sv, desc, wq8, Rs=(1, 5, 16), L: int = 4):
+    """The verifier step (one MoE layer + head + accept) and an L-layer step
+    (router GEMV + MoE per layer, then head + accept), each timed eagerly and
+    as a graph replay at every R."""
+    import torch
+    wr = to_dev(synth.router_weights().packed())
+    out = []
+    for R in Rs:
+        st = Step(sv, desc, wq8, R, 1, 1, 0.8)
+        e1, g1 = time_eager_and_graph(lambda: st.run(0))
+        del st
+        stack = LayerStack(sv, desc, wq8, wr, R, L, 0.8)
+        eL, gL = time_eager_and_graph(stack.run)
+        out.append({"R": R, "step_us": {"eager": round(e1, 2), "graph": round(g1, 2)},
+                    f"stack{L}_us": {"eager": round(eL, 2), "graph": round(gL, 2),
+                                     "launches": stack.launches()}})
+        del stack
+        torch.cuda.synchronize()
+    return {"layers": L, "rows": out}
+
+
 def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
     """The oracle, unchanged, on a bounded sample of the same workload."""
     import threadpoolctl
@@ -544,6 +650,8 @@ def main():
                 line["cohort"] = [e for e in ents if e["S"] == 3][0]
                 log("single-expert calls ...")
                 line["single_expert"] = single_expert(sv, desc)
+                log("eager and graph-replayed steps ...")
+                line["graph_steps"] = graph_steps(sv, desc, wq8)
             if args.bw_probe_gib > 0:
                 log(f"read-bandwidth probe on {args.bw_probe_gib} GiB ...")
                 line["bw_probe"] = bw_probe(sv, args.bw_probe_gib)
