@@ -264,24 +264,26 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
     run += __builtin_amdgcn_readlane(incl, 63);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
-  const long C = run;
-  for (int b = lane; b <= G; b += 64) {
-    const int c = (int)(C * b / G);
-    int first;
-    if (c >= C) {
-      first = nd * items;
-    } else {   // the descriptor holding cost offset c: largest d with s_cost[d] <= c
-      int lo = 0, hi = nd - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_cost[mid] <= c) lo = mid;
-        else hi = mid - 1;
-      }
-      const int w = (s_cost[lo + 1] - s_cost[lo]) / items;
-      first = lo * items + (c - s_cost[lo] + w - 1) / w;
-    }
-    blk[b] = first;
+  const int C = run;
+  if (C == 0) {
+    for (int b = lane; b <= G; b += 64) blk[b] = 0;
+    return;
   }
+  // block b starts in descriptor d when s_cost[d] <= floor(C b / G) <
+  // s_cost[d + 1], i.e. for b in [ceil(s_cost[d] G / C), ceil(s_cost[d+1] G / C)):
+  // each descriptor writes its own blocks (every product here is below 2^53,
+  // and a quotient that is not an integer is at least 1/C away from one, so
+  // the fp64 floor and ceil are exact)
+  const double dG = (double)G, dC = (double)C;
+  for (int d = lane; d < nd; d += 64) {
+    const int P0 = s_cost[d], P1 = s_cost[d + 1], w = (P1 - P0) / items;
+    const int b0 = (int)ceil((double)P0 * dG / dC), b1 = (int)ceil((double)P1 * dG / dC);
+    for (int b = b0; b < b1; ++b) {
+      const int c = (int)floor(dC * (double)b / dG);
+      blk[b] = d * items + (c - P0 + w - 1) / w;
+    }
+  }
+  if (lane == 0) blk[G] = nd * items;
 }
 
 __device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
