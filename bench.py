@@ -514,7 +514,7 @@ def cpu_baseline(step_bytes_mean, R, n_experts, n_vocab):
             "threads_note": "cores = threads of the BLAS pool the oracle's matrix products ran on"}
 
 
-TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "lmhead_R5_hbm_traffic.md")
+TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "verifier_step_R5_hbm_traffic.md")
 
 
 def head_traffic(R):
