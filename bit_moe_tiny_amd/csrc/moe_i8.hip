@@ -64,11 +64,14 @@ constexpr int M8_CAP_ALLK = 2;                               // rows of a MOE_AL
 
 // -------------------------------------------------------------- geometry
 // LDS region of activation digits: ncols rows x 4 planes over nbr blocks,
-// planes nbr*256 + 16 bytes apart (the padding moves neighbouring planes to
-// other banks), then the planes' sub-block sums (nbr*16 fp16 each).
-__host__ __device__ inline int m8_ps(int nbr) { return nbr * 256 + 16; }
+// planes nbr*256 + 32 bytes apart, then the planes' sub-block sums (nbr*16
+// fp16 each), nbr*32 + 16 bytes apart.  The paddings put the 16-byte (8-byte)
+// pieces one operand read takes from different planes in different banks of
+// the 64-bank LDS (measured: without them the reads take twice the cycles).
+__host__ __device__ inline int m8_ps(int nbr) { return nbr * 256 + 32; }
+__host__ __device__ inline int m8_ss(int nbr) { return nbr * 32 + 16; }
 __host__ __device__ inline size_t m8_area(int nc, int nbr) {
-  return (size_t)nc * NDIG * ((size_t)m8_ps(nbr) + (size_t)nbr * 32);
+  return (size_t)nc * NDIG * ((size_t)m8_ps(nbr) + (size_t)m8_ss(nbr));
 }
 
 static size_t gu_lds_bytes(int nc_allk, int nc_quarter, int nb) {
@@ -154,7 +157,7 @@ __device__ __forceinline__ M8A m8_aptr(const uint8_t* reg, int nc, int nbr, int 
   for (int ct = 0; ct < 2; ++ct) {
     const int slot = min(4 * ct + (c >> 2), nc - 1), pl = slot * NDIG + (c & 3);
     p.a[ct] = (const int8_t*)(reg + (size_t)pl * m8_ps(nbr) + 16 * g);
-    p.s[ct] = sx + (size_t)pl * nbr * 16 + 4 * g;
+    p.s[ct] = sx + (size_t)pl * (m8_ss(nbr) / 2) + 4 * g;
   }
   return p;
 }
@@ -184,8 +187,8 @@ __device__ __forceinline__ i4_t m8_bop(uint32_t w, uint32_t sc2) {
 // their sums of both blocks -- so that the wave waits once, then the blocks'
 // matrix products are interleaved (independent accumulators).  Slot offsets
 // follow the chunk layout: codes of row n, piece c at 64 NB n + 16 ((c + n)
-// mod 4 NB); nibbles at 1024 NB + 16 NB n; d, dmin at 1280 NB and 1312 NB,
-// NB halves per row.
+// mod 4 NB); the nibble dword g of block b, row n at 1024 NB + 4 (16 (4 b +
+// g) + n); d, dmin at 1280 NB and 1312 NB, NB halves per row.
 template <int NB, int NCT>
 __device__ __forceinline__ void m8_step_compute(const uint8_t* slot, int kbl, const M8A& A, f4_t (&acc)[2]) {
   const int lane = __lane_id(), n = lane & 15, g = lane >> 4;
@@ -196,7 +199,7 @@ __device__ __forceinline__ void m8_step_compute(const uint8_t* slot, int kbl, co
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     qs[b] = *(const uint4*)(slot + n * 64 * NB + (((4 * b + g + n) & (4 * NB - 1)) << 4));
-    scw[b] = *(const uint32_t*)(slot + 1024 * NB + n * 16 * NB + b * 16 + 4 * g);
+    scw[b] = *(const uint32_t*)(slot + 1024 * NB + ((b * 4 + g) * 16 + n) * 4);
   }
   uint32_t dw, mw;
   if (NB == 2) {
@@ -344,7 +347,7 @@ __device__ void m8_load_x(const XDig& xd, const int* rows, int nc, int rb0, int 
     for (int i = 0; i < NDIG; ++i) {
       const int pl = c * NDIG + i;
       m8_copy(xd.dig + ((size_t)r * NDIG + i) * K + (size_t)rb0 * 256, la + (uint32_t)pl * m8_ps(nbr), nbr * 256, q);
-      m8_copy(xd.sx + ((size_t)r * NDIG + i) * (K / 16) + (size_t)rb0 * 16, las + (uint32_t)pl * nbr * 32, nbr * 32, q);
+      m8_copy(xd.sx + ((size_t)r * NDIG + i) * (K / 16) + (size_t)rb0 * 16, las + (uint32_t)pl * m8_ss(nbr), nbr * 32, q);
     }
   }
 }
@@ -928,7 +931,12 @@ __global__ __launch_bounds__(256) void k_q2_tile(const uint8_t* src, uint8_t* ds
     const int pc = 4 * j + c, pos = (pc + r) & (4 * nblk - 1);
     *(uint4*)(ch + r * 64 * nblk + 16 * pos) = qs[c];
   }
-  *(uint4*)(ch + 1024 * nblk + r * 16 * nblk + 16 * j) = *(const uint4*)(W.sc + ((size_t)n * nb + kb) * 16);
+  {
+    const uint4 sc = *(const uint4*)(W.sc + ((size_t)n * nb + kb) * 16);
+    const uint32_t w4[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *(uint32_t*)(ch + 1024 * nblk + ((j * 4 + g) * 16 + r) * 4) = w4[g];
+  }
   *(uint16_t*)(ch + 1280 * nblk + 2 * (r * nblk + j)) = W.d[(size_t)n * nb + kb];
   *(uint16_t*)(ch + 1312 * nblk + 2 * (r * nblk + j)) = W.dm[(size_t)n * nb + kb];
 }

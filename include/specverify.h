@@ -110,7 +110,9 @@ SV_API size_t sv_q2_matrix_bytes(int32_t n_out, int32_t k_in);
  * chunk of 1344*nblk bytes at byte 1344*(t*nb + kb):
  *   codes   [16 rows][64*nblk B]: 16-byte piece c of row r (bytes 16c ..
  *           16c+15 of its nblk*64 code bytes) at r*64*nblk + 16*((c+r) mod 4*nblk)
- *   nibbles [16 rows][16*nblk B] from byte 1024*nblk
+ *   nibbles [nblk][4][16 rows] dwords from byte 1024*nblk: dword g (nibble
+ *           bytes 4g .. 4g+3) of block j of the step, row r, at
+ *           1024*nblk + 4*(16*(4j + g) + r)
  *   d       [16 rows][nblk] fp16 from byte 1280*nblk
  *   dmin    [16 rows][nblk] fp16 from byte 1312*nblk
  * sv_q2_tiled_bytes returns the size (84 bytes per 256 weights, no padding) or

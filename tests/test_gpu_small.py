@@ -69,7 +69,8 @@ def _tiled_layout(buf, n, k, parts):
                     for c in range(4 * m):
                         at = base + r * 64 * m + 16 * ((c + r) % (4 * m))
                         out[at:at + 16] = pieces[r, c]
-                out[base + 1024 * m:base + 1280 * m] = sc[rows, kb:kb + m].reshape(-1)
+                nib = sc[rows, kb:kb + m].reshape(16, m, 4, 4)          # [row][block][dword g][byte]
+                out[base + 1024 * m:base + 1280 * m] = nib.transpose(1, 2, 0, 3).reshape(-1)
                 out[base + 1280 * m:base + 1312 * m] = d[rows, kb:kb + m].reshape(-1)
                 out[base + 1312 * m:base + 1344 * m] = dm[rows, kb:kb + m].reshape(-1)
                 kb += m
