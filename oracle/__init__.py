@@ -19,7 +19,9 @@ What it computes, and from where (page titles of the sources):
 * the p/q accept/reject rule with residual resampling and the bonus token
   (``accept``) -- *Optimizing DeepSeek-V4-Flash on a single NVIDIA GB10/GX10
   with DSpark speculative decoding*, post 1 (the paragraph under the analyzer
-  output), taken step by step.
+  output), taken step by step; target-sample matching -- *1x Spark tuned
+  DSpark for DeepSeek-V4-Flash*, the losslessness paragraph; the yield-quench
+  accounting -- *ds4-on-spark* README, "The break-even law".
 
 Parity pins (tests marked ``not gpu``) tie every function to facts that do not
 come from this code: hand-computed blocks, exact rational arithmetic, closed
@@ -31,11 +33,13 @@ from .formats import (q2_fields, q2_dequant_units, q2_dequant_f32, q2_dequant_f6
 from .linalg import (gemm, silu, swiglu_expert, route_topk, moe_layer, plain_layer,
                      lm_head_logits)
 from .accept import (softmax_t, greedy_onehot, distribution, first_exceeding, accept_sequence,
-                     spec_accept)
+                     spec_accept, target_sample_sequence, spec_accept_target_sample,
+                     yield_quench)
 
 __all__ = [
     "q2_fields", "q2_dequant_units", "q2_dequant_f32", "q2_dequant_f64",
     "q8_fields", "q8_dequant_f32", "q8_dequant_f64", "q2_matrix_bytes", "q8_matrix_bytes",
     "gemm", "silu", "swiglu_expert", "route_topk", "moe_layer", "plain_layer",
     "lm_head_logits", "softmax_t", "greedy_onehot", "distribution", "first_exceeding", "accept_sequence", "spec_accept",
+    "target_sample_sequence", "spec_accept_target_sample", "yield_quench",
 ]

@@ -1,5 +1,6 @@
-"""The p/q accept/reject rule with residual resampling (oracle; test
-infrastructure only).
+"""The accept rules of the verifier step (oracle; test infrastructure only):
+the p/q accept/reject rule with residual resampling, target-sample matching,
+and the per-step accounting of the yield-quench policy.
 
 Source: *Optimizing DeepSeek-V4-Flash on a single NVIDIA GB10/GX10 with DSpark
 speculative decoding*, post 1, the paragraph under the analyzer output: the
@@ -165,3 +166,91 @@ def spec_accept(S: int, K: int, V: int, target, target_kind: int, t_p: float,
         nacc[s] = n
         toks[s, :len(out)] = out
     return toks, nacc
+
+
+def target_sample_sequence(p_rows: Sequence, drafts: Sequence[int],
+                           u: Sequence) -> Tuple[int, List[int]]:
+    """Target-sample matching for one sequence: p_rows K+1 distributions,
+    drafts K, u K+1.
+
+    Source: *1x Spark tuned DSpark for DeepSeek-V4-Flash*, the paragraph on
+    losslessness under "The break-even law, and why speculation can't hurt you
+    here": the verify rows are the only source of tokens; the accept loop
+    draws the target's own token from each verify row with the request's
+    sampler and random stream.  Steps: for i = 0 .. K, t_i = the inverse-CDF
+    sample of p_i at u_i (the first x whose running sum exceeds u_i times the
+    row total, as for the p/q rule's sample); while i < K and t_i equals
+    draft i the draft stands and the walk moves on to row i+1; the first t_i
+    that differs (or t_K) is emitted and ends the step.  The draft rows q are
+    not used.  Returns (n_accepted, emitted tokens: n_accepted drafts, then
+    t_n)."""
+    K = len(drafts)
+    out: List[int] = []
+    for i in range(K + 1):
+        t = first_exceeding(p_rows[i], u[i])
+        out.append(t)
+        if i == K or t != int(drafts[i]):
+            return i, out
+    raise AssertionError("unreachable")
+
+
+def spec_accept_target_sample(S: int, K: int, V: int, target, target_kind: int, t_p: float,
+                              drafts, uniforms):
+    """Batched target-sample matching with the library's argument order:
+    target [S*(K+1), V] fp32 (row s*(K+1)+i), drafts [S, K] int32, uniforms
+    [S, K+1] fp32 (u[s][i] samples row i).  Returns (out_tokens int32
+    [S, K+1] padded with -1, n_accepted int32 [S]); invalid inputs (a token
+    outside [0, V), a uniform outside [0, 1), a non-finite value, a negative
+    or all-zero probability row) give -1 everywhere for that sequence."""
+    target = np.asarray(target, np.float32).reshape(S, K + 1, V)
+    drafts = np.asarray(drafts, np.int64).reshape(S, K)
+    uniforms = np.asarray(uniforms, np.float32).reshape(S, K + 1)
+    toks = np.full((S, K + 1), -1, np.int32)
+    nacc = np.full(S, -1, np.int32)
+    for s in range(S):
+        ok = all(_row_valid(target[s, i], target_kind) for i in range(K + 1))
+        ok = ok and bool(np.all((drafts[s] >= 0) & (drafts[s] < V)))
+        ok = ok and bool(np.all((uniforms[s] >= 0) & (uniforms[s] < 1)))
+        if not ok:
+            continue
+        p_rows = [distribution(target[s, i], target_kind, t_p) for i in range(K + 1)]
+        n, out = target_sample_sequence(p_rows, drafts[s].tolist(), [float(x) for x in uniforms[s]])
+        nacc[s] = n
+        toks[s, :len(out)] = out
+    return toks, nacc
+
+
+def yield_quench(n_accepted_steps: Sequence[int], guard, threshold):
+    """The per-request accounting of the yield-quench policy over a run of
+    verify steps.
+
+    Source: *ds4-on-spark* README, "The break-even law" (a verify step costs
+    about as much as `guard` plain decode steps, so it pays only when it
+    commits more tokens than that; the controller sums the regret
+    guard - tokens-per-step over the verify steps and turns speculation off
+    for the rest of the request once the sum exceeds a few plain-step
+    times), and *1x Spark tuned DSpark for DeepSeek-V4-Flash*, "The break-even
+    law, and why speculation can't hurt you here" (the realised regret
+    guard - tokens committed, accumulated per verify step; the quench is
+    terminal).  Steps, for each step's accepted-draft count n (-1: the
+    sequence's inputs were invalid, nothing committed, not counted): tokens
+    committed t = n + 1; steps += 1; tokens += t; regret += guard - t; once
+    regret > threshold the request is quenched at that step and later steps
+    are not counted.  Readings (listed in the design notes): the sum is not
+    clamped at zero (a request that runs ahead banks credit), "exceeds" is
+    strict, and the regret is a plain running sum in the arithmetic of its
+    inputs (fp64 floats, or exact Fractions).
+
+    Returns (steps, tokens, regret, quench_step or None)."""
+    steps = tokens = 0
+    regret = guard - guard   # zero in the inputs' arithmetic
+    for n in n_accepted_steps:
+        if n < 0:
+            continue
+        t = int(n) + 1
+        steps += 1
+        tokens += t
+        regret = regret + (guard - t)
+        if regret > threshold:
+            return steps, tokens, regret, steps
+    return steps, tokens, regret, None
