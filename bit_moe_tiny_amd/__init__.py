@@ -8,6 +8,8 @@ from ._lib import (ACCEPT_SCRATCH_BYTES, EXPORTS, LIB_PATH, MoeDesc, SV_BF16, SV
                    SV_ESCRATCH, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_F32, SV_FFN_PLAIN,
                    SV_FFN_SWIGLU, SV_LOGITS, SV_OK, SV_PROBS, SvError, api_version, load, moe_desc,
                    spec_accept, spec_accept_noalloc, sv_read_probe, PROBE_GROUP_BYTES,
+                   SpecAccount, spec_accept_target_sample, sv_accept_tsm_workspace_bytes,
+                   sv_spec_account,
                    status_str, sv_accept_workspace_bytes, sv_lmhead_workspace_bytes,
                    sv_moe_workspace_bytes, sv_q2_matrix_bytes, sv_q2_tile, sv_q2_tiled_bytes,
                    sv_q8_matrix_bytes, vq2_dequant,
@@ -19,6 +21,7 @@ __all__ = [
     "sv_lmhead_workspace_bytes", "sv_accept_workspace_bytes", "vq2_moe_gemm",
     "vq8_lmhead_gemm", "spec_accept", "spec_accept_noalloc", "vq2_dequant", "vq8_dequant",
     "sv_read_probe", "PROBE_GROUP_BYTES",
+    "SpecAccount", "spec_accept_target_sample", "sv_accept_tsm_workspace_bytes", "sv_spec_account",
     "ACCEPT_SCRATCH_BYTES", "SV_OK", "SV_EINVAL", "SV_EUNSUPPORTED", "SV_EWORKSPACE", "SV_EHIP",
     "SV_ESCRATCH", "SV_F32", "SV_BF16",
     "SV_FFN_PLAIN", "SV_FFN_SWIGLU", "SV_LOGITS", "SV_PROBS",

@@ -26,7 +26,7 @@ EXPORTS = [
     "sv_q8_matrix_bytes",
     "sv_moe_workspace_bytes", "vq2_moe_gemm", "sv_lmhead_workspace_bytes", "vq8_lmhead_gemm",
     "sv_accept_workspace_bytes", "spec_accept", "spec_accept_noalloc", "vq2_dequant", "vq8_dequant",
-    "sv_read_probe",
+    "sv_read_probe", "sv_accept_tsm_workspace_bytes", "spec_accept_target_sample", "sv_spec_account",
 ]
 
 
@@ -41,6 +41,13 @@ class MoeDesc(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class SpecAccount(ctypes.Structure):
+    """sv_spec_account_t: per-sequence step accounting of the yield-quench
+    policy (zero-initialised before a request's first step)."""
+    _fields_ = [("steps", ctypes.c_int64), ("tokens", ctypes.c_int64), ("regret", ctypes.c_double),
+                ("quenched", ctypes.c_int32), ("quench_step", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -66,6 +73,11 @@ _SIGS = {
     "vq2_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "vq8_dequant": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "sv_read_probe": ([_vp, _sz, _i32, _vp, _sz, _vp], ctypes.c_int),
+    "sv_accept_tsm_workspace_bytes": ([_i32, _i32, _i32], _sz),
+    "spec_accept_target_sample": ([_i32, _i32, _i32, _vp, _i32, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                                  ctypes.c_int),
+    "sv_spec_account": ([_vp, _i32, _i32, ctypes.c_double, ctypes.c_double, ctypes.POINTER(SpecAccount)],
+                        ctypes.c_int),
 }
 
 
@@ -366,6 +378,54 @@ def spec_accept_noalloc(S: int, K: int, V: int, target, target_kind: int, t_p: f
                                     _ptr(out_n_accepted), _stream(stream))
     _check("spec_accept_noalloc", st)
     return out_tokens, out_n_accepted
+
+
+def sv_accept_tsm_workspace_bytes(S: int, K: int, V: int) -> int:
+    return load().sv_accept_tsm_workspace_bytes(S, K, V)
+
+
+def spec_accept_target_sample(S: int, K: int, V: int, target, target_kind: int, t_p: float,
+                              draft_tokens, uniforms, out_tokens, out_n_accepted, ws=None, stream=None):
+    """Target-sample matching for S sequences of K drafts: every verify row's
+    own sample at its uniform, drafts kept while they match; fills out_tokens
+    [S, K+1] and out_n_accepted [S] (int32).  No draft distribution."""
+    need = sv_accept_tsm_workspace_bytes(S, K, V)
+    if need == 0:
+        raise ValueError(f"invalid accept shape S = {S}, K = {K}, V = {V}")
+    _want(target, "target", "f32", (S * (K + 1), V))
+    if K > 0:
+        _want(draft_tokens, "draft_tokens", "i32", (S, K))
+    _want(uniforms, "uniforms", "f32", (S, K + 1))
+    _want(out_tokens, "out_tokens", "i32", (S, K + 1))
+    _want(out_n_accepted, "out_n_accepted", "i32", (S,))
+    if ws is not None:
+        _want(ws, "ws", "u8", min_bytes=need)
+    _dev_check(target, draft_tokens if K > 0 else None, uniforms, out_tokens, out_n_accepted, ws)
+    if ws is None:
+        ws = _workspace(need, target)
+    st = load().spec_accept_target_sample(S, K, V, _ptr(target), target_kind, t_p,
+                                          _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms),
+                                          _ptr(out_tokens), _ptr(out_n_accepted), _ptr(ws), ws.numel(),
+                                          _stream(stream))
+    _check("spec_accept_target_sample", st)
+    return out_tokens, out_n_accepted
+
+
+def sv_spec_account(n_accepted, K: int, guard: float, threshold: float, state=None):
+    """One verify step of the yield-quench accounting (host): n_accepted is a
+    host sequence of S int32 values as an accept call wrote them; ``state`` a
+    ctypes array of S SpecAccount (created zeroed when None).  Returns
+    ``state``."""
+    import numpy as np
+    n = np.ascontiguousarray(np.asarray(n_accepted, dtype=np.int32).reshape(-1))
+    S = int(n.shape[0])
+    if state is None:
+        state = (SpecAccount * S)()
+    if len(state) != S:
+        raise ValueError(f"state holds {len(state)} sequences, n_accepted {S}")
+    _check("sv_spec_account", load().sv_spec_account(n.ctypes.data, S, K, float(guard), float(threshold),
+                                                     ctypes.cast(state, ctypes.POINTER(SpecAccount))))
+    return state
 
 
 def vq2_dequant(w, n_out: int, k_in: int, out, stream=None):

@@ -8,7 +8,12 @@
 // p_i(d_i), tested exactly as the sign of fma(u, q, -p); the replacement or
 // bonus token is the first x whose running sum exceeds u_K times the total.
 //
-// Two launches, no host sync, no block waiting on another:
+// Target-sample matching (the second rule, "1x Spark tuned DSpark for
+// DeepSeek-V4-Flash", the losslessness paragraph): every verify row's own
+// inverse-CDF sample at its uniform; drafts stand while they equal these
+// samples, the first that differs (or row K's) is emitted last.
+//
+// Two launches per rule, no host sync, no block waiting on another:
 //   k_acc_stats   grid (chunk, row): per 2048-entry chunk of every target and
 //                 draft row, the chunk max of z/T and sum exp(z/T - max) in
 //                 fp64 (or the plain sum for probability rows), plus a
@@ -24,6 +29,10 @@
 //                 from the chunk totals, the segment inside it from the
 //                 per-thread sums, and the token among that segment's
 //                 entries, then writes the outputs.
+//   k_tsm_sample  (target-sample matching) grid (512-entry chunk, target row):
+//                 the same chunk sums for p of one row; the last block of a row
+//                 samples it; the last row of a sequence to be sampled takes
+//                 the prefix of matching drafts and writes the outputs.
 #include "sv_internal.h"
 
 namespace sv {
@@ -172,12 +181,12 @@ __device__ inline RowSrc row_src(int r, int S, int K, int V, const float* target
 
 __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const float* target,
                                                    int tkind, float Tp, const float* draft,
-                                                   int dkind, float Tq, AccWs ws) {
+                                                   int dkind, float Tq, AccWs ws, int n_clear) {
   __shared__ double sh[4];
   __shared__ int shb[4];
   const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
-  if (c == 0 && r == 0)   // the sampling launch's per-sequence counters
-    for (int i = threadIdx.x; i < S; i += blockDim.x) ws.done[i] = 0u;
+  if (c == 0 && r == 0)   // the sampling launch's counters
+    for (int i = threadIdx.x; i < n_clear; i += blockDim.x) ws.done[i] = 0u;
   const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
   const int x0 = c * ACC_CHUNK;
   double a[ACC_PER];
@@ -258,6 +267,36 @@ __device__ inline void sample_rows(int s, int n, int S, int K, int V, const floa
   Q = n < K ? row_src(S * (K + 1) + s * K + n, S, K, V, target, tkind, Tp, draft, dkind, Tq) : P;
 }
 
+// One row's statistics from lane-held chunk statistics (lane l: chunks l,
+// l + 64, ...): the maximum and the softmax denominator rescaled to it (the
+// plain sum for probability rows; for a greedy row the first index holding
+// the maximum), fixed-order butterfly reductions.
+template <int CPL>
+__device__ inline void row_reduce(const double (&cm)[CPL], const double (&cs)[CPL], int CH, int kind,
+                                  double* m_out, double* z_out) {
+  const int lane = threadIdx.x & 63;
+  double m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) m = fmax(m, cm[k]);
+  m = kind != SV_PROBS ? wave_max_d(m) : 0.0;
+  double z = 0.0;
+  if (kind == ACC_ARGMAX) {
+    // the first chunk holding the row's maximum gives the index
+    double f = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+      if (lane + 64 * k < CH && cm[k] == m) f = fmax(f, -cs[k]);
+    z = -wave_max_d(f);
+  } else {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+      if (lane + 64 * k < CH) z += kind == SV_LOGITS ? cs[k] * exp(cm[k] - m) : cs[k];
+    z = wave_sum_d(z);
+  }
+  *m_out = m;
+  *z_out = z;
+}
+
 // Row statistics of sequence s recombined from the chunk statistics: wave w
 // takes rows w, w+4, ... three at a time (their loads issued together), lane
 // l chunks l, l+64, ...; butterfly reductions, so every block gets the same
@@ -293,25 +332,8 @@ __device__ inline void acc_rows(int s, int S, int K, int CH, int tkind, int dkin
       const int i = i0 + 4 * j;
       if (i >= nrows) break;   // uniform in the wave
       const int kind = i <= K ? tkind : dkind;
-      const bool logits = kind == SV_LOGITS;
-      double m = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) m = fmax(m, cm[j][k]);
-      m = kind != SV_PROBS ? wave_max_d(m) : 0.0;
-      double z = 0.0;
-      if (kind == ACC_ARGMAX) {
-        // the first chunk holding the row's maximum gives the index
-        double f = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-          if (lane + 64 * k < CH && cm[j][k] == m) f = fmax(f, -cs[j][k]);
-        z = -wave_max_d(f);
-      } else {
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-          if (lane + 64 * k < CH) z += logits ? cs[j][k] * exp(cm[j][k] - m) : cs[j][k];
-        z = wave_sum_d(z);
-      }
+      double m, z;
+      row_reduce<CPL>(cm[j], cs[j], CH, kind, &m, &z);
       const int bad = __any(cb[j]) ? 1 : 0;
       if (lane == 0) {
         rm[i] = m;
@@ -374,6 +396,76 @@ __device__ inline int wave_cross(const double* v, int n, int per, double run, do
   const int fl = __builtin_ctzll(cm);
   *pre = __shfl(cpre, fl, 64);
   return __shfl(cand, fl, 64);
+}
+
+// The sampled chunk, run by the block whose LDS holds the chunk totals
+// cws[0..CHs): wave 0 finds the first chunk whose running total exceeds
+// tt = u Z, failing that (rounding) the last chunk with weight.  Sets *z
+// (the total Z), *found, *hit and *base (the running total before the hit
+// chunk); ends with a block barrier.
+__device__ inline void find_chunk(const double* cws, int CHs, double u, double* z, int* found, int* hit,
+                                  double* base) {
+  if (threadIdx.x < 64) {
+    const int per = (CHs + 63) / 64;
+    double Z;
+    const double run = wave_prefix(cws, CHs, per, &Z);
+    double pre = 0.0;
+    int lastpos = -1;
+    const int h = Z > 0.0 ? wave_cross(cws, CHs, per, run, u * Z, &pre, &lastpos) : -1;
+    if ((threadIdx.x & 63) == 0) {
+      *z = Z;
+      *found = h >= 0;
+      *hit = h >= 0 ? h : max(lastpos, 0);
+      *base = h >= 0 ? pre : 0.0;
+    }
+  }
+  __syncthreads();
+}
+
+// The sampled entry of chunk `hit`, by wave 0, given the per-thread segment
+// weights parts[0..ACC_T) of that chunk in LDS: the thread segment whose
+// running sum (from base) first exceeds tt, then the entry inside it, failing
+// that (rounding) the last entry with weight of the segment, of the chunk.
+__device__ inline int seg_token(const double* parts, double base, bool found_chunk, double tt, int hit,
+                                int mode, const RowSrc& P, double pm, double pz, const RowSrc& Q, double qm,
+                                double qz, int V) {
+  const int lane = threadIdx.x & 63;
+  constexpr int TPL = ACC_T / 64;
+  double ptot;
+  const double prun = base + wave_prefix(parts, ACC_T, TPL, &ptot);
+  double tpre = 0.0;
+  int lastseg;
+  const int seg = wave_cross(parts, ACC_T, TPL, prun, tt, &tpre, &lastseg);
+  const bool found = found_chunk && seg >= 0;
+  const int thr = found ? seg : max(lastseg, 0);
+  int tok = -1;
+  {
+    double run = tpre;
+    int lp = -1;
+#pragma unroll
+    for (int i = 0; i < SMP_PER; ++i) {
+      const int x = hit * SMP_CHUNK + thr * SMP_PER + i;
+      if (x < V) {
+        const double wi = sample_weight(mode, P, pm, pz, Q, qm, qz, x);
+        run += wi;
+        if (wi > 0.0) lp = x;
+        if (found && tok < 0 && run > tt) tok = x;
+      }
+    }
+    if (tok < 0) tok = lp;
+  }
+  if (tok < 0) {
+    // (rounding put the crossing in a segment without weight) the chunk's
+    // last entry with weight
+    int lp = -1;
+    for (int i = lane; i < SMP_CHUNK; i += 64) {
+      const int x = hit * SMP_CHUNK + i;
+      if (x < V && sample_weight(mode, P, pm, pz, Q, qm, qz, x) > 0.0) lp = x;
+    }
+    for (int o = 32; o >= 1; o >>= 1) lp = max(lp, __shfl_xor(lp, o, 64));
+    tok = lp;
+  }
+  return tok;
 }
 
 __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int CH,
@@ -476,26 +568,8 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
   for (int cc = tid; cc < CHs; cc += ACC_T)
     cws[cc] = __hip_atomic_load(&ws.rsum[(size_t)s * CHs + cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  // the chunk holding tt = u_K * Z: the first whose running total exceeds
-  // it, failing that (rounding) the last chunk with weight
-  const int per = (CHs + 63) / 64;
-  auto find_chunk = [&]() {
-    if (tid < 64) {
-      double Z;
-      const double run = wave_prefix(cws, CHs, per, &Z);
-      double pre = 0.0;
-      int lastpos = -1;
-      const int hit = Z > 0.0 ? wave_cross(cws, CHs, per, run, s_uk * Z, &pre, &lastpos) : -1;
-      if (lane == 0) {
-        s_z = Z;
-        s_found = hit >= 0;
-        s_hit = hit >= 0 ? hit : max(lastpos, 0);
-        s_base = hit >= 0 ? pre : 0.0;
-      }
-    }
-    __syncthreads();
-  };
-  find_chunk();
+  // the chunk holding tt = u_K * Z
+  find_chunk(cws, CHs, s_uk, &s_z, &s_found, &s_hit, &s_base);
   const bool redo = !(s_z > 0.0);
   if (redo) {
     // the residual vanished (only through rounding): sample p itself
@@ -504,7 +578,7 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
       if (tid == 0) cws[cc] = t;
     }
     __syncthreads();
-    find_chunk();
+    find_chunk(cws, CHs, s_uk, &s_z, &s_found, &s_hit, &s_base);
   }
   const int smode = redo ? MODE_P : mode;
   const double tt = s_uk * s_z;
@@ -514,44 +588,8 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (tid >= 64) return;
-  // the thread segment inside it, the same way, then the entry: the first
-  // whose running sum exceeds tt, failing that (rounding) the last entry with
-  // weight of the segment, of the chunk
-  constexpr int TPL = ACC_T / 64;
-  double ptot;
-  const double prun = s_base + wave_prefix(parts, ACC_T, TPL, &ptot);
-  double tpre = 0.0;
-  int lastseg;
-  const int seg = wave_cross(parts, ACC_T, TPL, prun, tt, &tpre, &lastseg);
-  const bool found = s_found && seg >= 0;
-  const int thr = found ? seg : max(lastseg, 0);
-  int tok = -1;
-  {
-    double run = tpre;
-    int lp = -1;
-#pragma unroll
-    for (int i = 0; i < SMP_PER; ++i) {
-      const int x = hit * SMP_CHUNK + thr * SMP_PER + i;
-      if (x < V) {
-        const double wi = sample_weight(smode, P, pm, pz, Q, qm, qz, x);
-        run += wi;
-        if (wi > 0.0) lp = x;
-        if (found && tok < 0 && run > tt) tok = x;
-      }
-    }
-    if (tok < 0) tok = lp;
-  }
-  if (tok < 0) {
-    // (rounding put the crossing in a segment without weight) the chunk's
-    // last entry with weight
-    int lp = -1;
-    for (int i = lane; i < SMP_CHUNK; i += 64) {
-      const int x = hit * SMP_CHUNK + i;
-      if (x < V && sample_weight(smode, P, pm, pz, Q, qm, qz, x) > 0.0) lp = x;
-    }
-    for (int o = 32; o >= 1; o >>= 1) lp = max(lp, __shfl_xor(lp, o, 64));
-    tok = lp;
-  }
+  // the thread segment inside it, then the entry
+  const int tok = seg_token(parts, s_base, s_found, tt, hit, smode, P, pm, pz, Q, qm, qz, V);
   if (lane <= K) out[lane] = lane < nacc ? dk : (lane == nacc ? tok : -1);
   if (lane == 0) out_n[s] = nacc;
 }
@@ -565,11 +603,178 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
   if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
   if (dkind == SV_LOGITS && Tq == 0.f) dkind = ACC_ARGMAX;
   hipLaunchKernelGGL(k_acc_stats, dim3(CH, S * (2 * K + 1)), dim3(256), 0, s, S, K, V, target,
-                     tkind, Tp, draft, dkind, Tq, ws);
+                     tkind, Tp, draft, dkind, Tq, ws, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_acc_sample, dim3(CHs, S), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind,
                      Tp, draft, dkind, Tq, drafts, u, out_tokens, out_n, ws);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------- target-sample matching
+struct TsmWs {
+  double* cmax;     // [rows, CH]
+  double* csum;     // [rows, CH]
+  int* cbad;        // [rows, CH]
+  double* rsum;     // [rows, CHs]  p mass per sampling chunk
+  int* tok;         // [rows]       each row's sample (-1: invalid row or uniform)
+  unsigned* done;   // [rows + S]   blocks of each row done, then rows of each sequence done
+};
+
+static TsmWs tsm_carve(void* base, int S, int K, int V) {
+  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
+  uint8_t* p = (uint8_t*)base;
+  TsmWs w;
+  w.cmax = (double*)p;
+  p += up256(rows * CH * 8);
+  w.csum = (double*)p;
+  p += up256(rows * CH * 8);
+  w.cbad = (int*)p;
+  p += up256(rows * CH * 4);
+  w.rsum = (double*)p;
+  p += up256(rows * CHs * 8);
+  w.tok = (int*)p;
+  p += up256(rows * 4);
+  w.done = (unsigned*)p;
+  return w;
+}
+
+size_t accept_tsm_ws_bytes(int S, int K, int V) {
+  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
+  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256(rows * CHs * 8) + up256(rows * 4) +
+         up256((rows + S) * 4);
+}
+
+// Row r's statistics from its chunk statistics, by wave 0 (the same
+// reduction as the p/q rule's rows).
+__device__ inline void tsm_row_stats(int r, int CH, int kind, const TsmWs& ws, double* m, double* z, int* bad) {
+  constexpr int CPL = ACC_MAX_CH / 64;
+  const int lane = threadIdx.x & 63;
+  double cm[CPL], cs[CPL];
+  int cb = 0;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const int cc = lane + 64 * k;
+    cm[k] = -INFINITY;
+    cs[k] = 0.0;
+    if (cc < CH) {
+      const size_t o = (size_t)r * CH + cc;
+      cm[k] = ws.cmax[o];
+      cs[k] = ws.csum[o];
+      cb |= ws.cbad[o];
+    }
+  }
+  row_reduce<CPL>(cm, cs, CH, kind, m, z);
+  *bad = (__any(cb) ? 1 : 0) | (kind == SV_PROBS ? !(*z > 0.0) : 0);
+}
+
+__global__ __launch_bounds__(ACC_T) void k_tsm_sample(int S, int K, int V, int CH, const float* target,
+                                                      int tkind, float Tp, const int32_t* drafts,
+                                                      const float* uni, int32_t* out_tokens, int32_t* out_n,
+                                                      TsmWs ws) {
+  __shared__ double sh[4];
+  __shared__ double cws[SMP_MAX_CH];   // the last block of the row: chunk totals
+  __shared__ double parts[ACC_T];      // the last block of the row: the hit chunk's segment totals
+  __shared__ double s_m, s_zr, s_z, s_base;
+  __shared__ int s_bad, s_last, s_hit, s_found;
+  const int c = blockIdx.x, r = blockIdx.y, CHs = gridDim.x;
+  const int s = r / (K + 1), i = r - s * (K + 1);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int rows = S * (K + 1);
+  // 1. the row's statistics
+  if (tid < 64) {
+    double m, z;
+    int bad;
+    tsm_row_stats(r, CH, tkind, ws, &m, &z, &bad);
+    if (lane == 0) {
+      s_m = m;
+      s_zr = z;
+      s_bad = bad;
+    }
+  }
+  __syncthreads();
+  RowSrc P;
+  P.p = target + (size_t)r * V;
+  P.kind = tkind;
+  P.T = (double)Tp;
+  const double pm = s_m, pz = s_zr;
+  const int bad = s_bad;
+  // 2. this chunk's mass of p; the last block of the row to finish samples it
+  //    (publication as in k_acc_sample: device-scope stores, release fence,
+  //    release increment; the last block acquires)
+  double w = bad ? 0.0 : seg_weight(MODE_P, P, pm, pz, P, 0.0, 1.0, c, V);
+  w = block_sum_d(w, sh);
+  if (tid == 0)
+    __hip_atomic_store(&ws.rsum[(size_t)r * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_vmcnt_le(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&ws.done[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(CHs - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // 3. row r's sample at u_i (block-uniform branch)
+  const float uf = uni[(size_t)s * (K + 1) + i];
+  const bool ok = !bad && uf >= 0.f && uf < 1.f;
+  int tok = -1;
+  if (ok) {
+    for (int cc = tid; cc < CHs; cc += ACC_T)
+      cws[cc] = __hip_atomic_load(&ws.rsum[(size_t)r * CHs + cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    find_chunk(cws, CHs, (double)uf, &s_z, &s_found, &s_hit, &s_base);
+    parts[tid] = seg_weight(MODE_P, P, pm, pz, P, 0.0, 1.0, s_hit, V);
+    __syncthreads();
+    if (tid < 64)
+      tok = seg_token(parts, s_base, s_found, (double)uf * s_z, s_hit, MODE_P, P, pm, pz, P, 0.0, 1.0, V);
+  }
+  if (tid >= 64) return;
+  // 4. publish it; the last row of the sequence to be sampled decides
+  if (lane == 0) __hip_atomic_store(&ws.tok[r], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  wait_vmcnt_le(0);
+  unsigned prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&ws.done[rows + s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __builtin_amdgcn_readfirstlane(prev);
+  if (prev != (unsigned)K) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  int ti = -1, di = -1, inv = 0;
+  if (lane <= K) {
+    ti = __hip_atomic_load(&ws.tok[s * (K + 1) + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    inv |= ti < 0;
+  }
+  if (lane < K) {
+    di = drafts[s * K + lane];
+    inv |= !(di >= 0 && di < V);
+  }
+  inv = __any(inv) ? 1 : 0;
+  // the first row whose sample differs from its draft (row K always "differs")
+  const unsigned long long mism = __ballot(lane < K ? ti != di : 1);
+  const int n = (int)__builtin_ctzll(mism);
+  int32_t* out = out_tokens + (size_t)s * (K + 1);
+  if (lane <= K) out[lane] = inv ? -1 : lane < n ? di : (lane == n ? ti : -1);
+  if (lane == 0) out_n[s] = inv ? -1 : n;
+}
+
+hipError_t launch_accept_tsm(int S, int K, int V, const float* target, int tkind, float Tp,
+                             const int32_t* drafts, const float* u, int32_t* out_tokens, int32_t* out_n,
+                             void* wsp, hipStream_t s) {
+  const TsmWs tw = tsm_carve(wsp, S, K, V);
+  AccWs aw{};
+  aw.cmax = tw.cmax;
+  aw.csum = tw.csum;
+  aw.cbad = tw.cbad;
+  aw.done = tw.done;
+  const int CH = acc_chunks(V), CHs = smp_chunks(V), rows = S * (K + 1);
+  if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
+  // target rows only (row index < S (K+1)); no draft rows are read
+  hipLaunchKernelGGL(k_acc_stats, dim3(CH, rows), dim3(256), 0, s, S, K, V, target, tkind, Tp,
+                     (const float*)nullptr, tkind, Tp, aw, rows + S);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_tsm_sample, dim3(CHs, rows), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind, Tp,
+                     drafts, u, out_tokens, out_n, tw);
   return hipGetLastError();
 }
 

@@ -161,6 +161,52 @@ size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V) {
   return accept_ws_bytes(S, K, V);
 }
 
+// Target-sample matching launches one block row per target row only.
+static bool tsm_shape_ok(int32_t S, int32_t K, int32_t V) {
+  if (S < 1 || K < 0 || K > SV_MAX_DRAFTS || V < 1 || V > 256 * 2048) return false;
+  return (long long)S * (K + 1) <= 65535;
+}
+
+size_t sv_accept_tsm_workspace_bytes(int32_t S, int32_t K, int32_t V) {
+  if (!tsm_shape_ok(S, K, V)) return 0;
+  return accept_tsm_ws_bytes(S, K, V);
+}
+
+int spec_accept_target_sample(int32_t S, int32_t K, int32_t V, const float* target,
+                              int32_t target_kind, float T_p, const int32_t* draft_tokens,
+                              const float* uniforms, int32_t* out_tokens, int32_t* out_n_accepted,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!tsm_shape_ok(S, K, V)) return SV_EINVAL;
+  if (!target || !uniforms || !out_tokens || !out_n_accepted || !ws) return SV_EINVAL;
+  if (K > 0 && !draft_tokens) return SV_EINVAL;
+  if (!kind_ok(target_kind)) return SV_EINVAL;
+  if (target_kind == SV_LOGITS && !(isfinite(T_p) && T_p >= 0.f)) return SV_EINVAL;
+  if (ws_bytes < accept_tsm_ws_bytes(S, K, V)) return SV_EWORKSPACE;
+  return hip_status(launch_accept_tsm(S, K, V, target, target_kind, T_p, draft_tokens, uniforms,
+                                      out_tokens, out_n_accepted, ws, stream));
+}
+
+int sv_spec_account(const int32_t* n_accepted, int32_t S, int32_t K, double guard, double threshold,
+                    sv_spec_account_t* state) {
+  if (!n_accepted || !state || S < 1 || K < 0 || K > SV_MAX_DRAFTS) return SV_EINVAL;
+  if (!isfinite(guard) || !isfinite(threshold)) return SV_EINVAL;
+  for (int32_t s = 0; s < S; ++s)
+    if (n_accepted[s] < -1 || n_accepted[s] > K) return SV_EINVAL;
+  for (int32_t s = 0; s < S; ++s) {
+    sv_spec_account_t& a = state[s];
+    if (a.quenched || n_accepted[s] < 0) continue;
+    const int64_t t = (int64_t)n_accepted[s] + 1;
+    a.steps += 1;
+    a.tokens += t;
+    a.regret += guard - (double)t;
+    if (a.regret > threshold) {
+      a.quenched = 1;
+      a.quench_step = (int32_t)a.steps;
+    }
+  }
+  return SV_OK;
+}
+
 }  // extern "C"
 
 // Scratch memory of spec_accept_noalloc: one copy per GPU, for the life of the

@@ -408,6 +408,10 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
                          const float* u, int32_t* out_tokens, int32_t* out_n, void* ws,
                          hipStream_t s);
 size_t accept_ws_bytes(int S, int K, int V);
+hipError_t launch_accept_tsm(int S, int K, int V, const float* target, int tkind, float Tp,
+                             const int32_t* drafts, const float* u, int32_t* out_tokens, int32_t* out_n,
+                             void* ws, hipStream_t s);
+size_t accept_tsm_ws_bytes(int S, int K, int V);
 hipError_t launch_read_probe(const void* src, size_t bytes, int mode, uint32_t* sink, hipStream_t s);
 size_t read_probe_sink_words();
 hipError_t launch_q2_dequant(const void* w, int n_out, int k_in, float* out, hipStream_t s);

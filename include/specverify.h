@@ -12,10 +12,13 @@
  *  [T3] "ds4-on-spark" README (introduction: block formats of the weights,
  *       expert dedup; "Roofline": decode is weight-streaming bound; "Under the
  *       hood": routed experts stay quantised with inline dequantisation; "The
- *       break-even law": one committed row plus four draft rows per verify).
+ *       break-even law": one committed row plus four draft rows per verify,
+ *       the break-even guard and the yield-quench controller).
  *  [T4] "1x Spark tuned DSpark for DeepSeek-V4-Flash: 35 tok/s, 800+ prefill,
  *       and fast multi-agent serving", forum thread (Q&A answer 3: fused
- *       gate+up+SwiGLU MoE decode, fused router).
+ *       gate+up+SwiGLU MoE decode, fused router; "The break-even law, and why
+ *       speculation can't hurt you here": the realised regret per verify step,
+ *       and the verify rows as the only token source).
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked (host).  The caller owns all
@@ -68,7 +71,7 @@ enum sv_ffn {
 
 enum sv_dist { SV_LOGITS = 0, SV_PROBS = 1 };  /* how a distribution row is given */
 
-#define SV_API_VERSION 2
+#define SV_API_VERSION 3
 #define SV_MAX_ROWS 64        /* R limit of the GEMM calls */
 #define SV_MAX_TOPK 16
 #define SV_MAX_EXPERTS 1024
@@ -239,12 +242,68 @@ SV_API size_t sv_accept_workspace_bytes(int32_t S, int32_t K, int32_t V);
  *  T_p / T_q must be finite and >= 0 for SV_LOGITS rows (0: greedy; then the
  *  output is the longest prefix of drafts equal to their rows' largest target
  *  logits, followed by the largest logit of the next row).  1 <= S, 0 <= K <=
- *  SV_MAX_DRAFTS, 1 <= V.
+ *  SV_MAX_DRAFTS, 1 <= V <= 524,288, S (2K+1) <= 65,535.
  */
 SV_API int spec_accept(int32_t S, int32_t K, int32_t V, const float* target, int32_t target_kind,
                 float T_p, const float* draft, int32_t draft_kind, float T_q,
                 const int32_t* draft_tokens, const float* uniforms, int32_t* out_tokens,
                 int32_t* out_n_accepted, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes spec_accept_target_sample needs (0 if invalid). */
+SV_API size_t sv_accept_tsm_workspace_bytes(int32_t S, int32_t K, int32_t V);
+
+/*
+ * Target-sample matching ([T4] "The break-even law, and why speculation can't
+ * hurt you here", the paragraph on losslessness: the verify forward is the only
+ * token source; the accept loop draws the target's own token from each verify
+ * row with the request's sampler and random stream).  For S sequences of K
+ * drafts: t_i = the first x (vocabulary order) whose running sum of p_i
+ * exceeds u[s][i] times the row total, for every row i = 0..K; n = the first
+ * i < K with t_i != draft i (K if none); the outputs are drafts 0..n-1, then
+ * t_n, then -1 padding.  No draft distribution is read.  target,
+ * target_kind, T_p, draft_tokens, uniforms ([S, K+1]: u[s][i] samples row i),
+ * out_tokens, out_n_accepted, validation, and the -1 marking of sequences with
+ * invalid data are as for spec_accept; draft_tokens may be NULL when K == 0.
+ * With T_p == 0 (greedy rows) the output equals spec_accept's.  1 <= S,
+ * 0 <= K <= SV_MAX_DRAFTS, 1 <= V <= 524,288, S (K+1) <= 65,535.
+ */
+SV_API int spec_accept_target_sample(int32_t S, int32_t K, int32_t V, const float* target,
+                int32_t target_kind, float T_p, const int32_t* draft_tokens,
+                const float* uniforms, int32_t* out_tokens, int32_t* out_n_accepted,
+                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step accounting of the yield-quench policy ([T3] "The break-even law": a
+ * verify step costs about `guard` plain decode steps, so it pays only when it
+ * commits more tokens than that; the controller sums guard - tokens per step
+ * and turns speculation off for the rest of the request once the sum exceeds a
+ * few plain-step times; [T4] "The break-even law, and why speculation can't
+ * hurt you here": the realised regret guard - tokens committed, summed per
+ * verify step, a terminal quench).  A HOST function over one verify step's
+ * out_n_accepted, copied to host memory.
+ *
+ *  n_accepted  [S] (host) int32, as an accept call wrote it: -1 marks a
+ *              sequence whose inputs were invalid (nothing committed; the step
+ *              is not counted); otherwise 0..K
+ *  state       [S] (host), in/out; zero-initialised before a request's first
+ *              step
+ *
+ * For each sequence not yet quenched with n >= 0: t = n + 1 tokens
+ * committed; steps += 1; tokens += t; regret += guard - t (fp64, not clamped
+ * at zero, so early gains are banked); if regret > threshold: quenched = 1,
+ * quench_step = steps.  Quenched sequences are left as they are.  SV_EINVAL,
+ * with no state changed, for null pointers, S < 1, K outside 0..SV_MAX_DRAFTS,
+ * an n outside -1..K, or a non-finite guard or threshold.
+ */
+typedef struct {
+  int64_t steps;         /* verify steps counted */
+  int64_t tokens;        /* tokens committed by them */
+  double regret;         /* sum of guard - tokens committed */
+  int32_t quenched;      /* 1 once regret exceeded the threshold */
+  int32_t quench_step;   /* the step at which it did (0 while not quenched) */
+} sv_spec_account_t;
+SV_API int sv_spec_account(const int32_t* n_accepted, int32_t S, int32_t K, double guard,
+                           double threshold, sv_spec_account_t* state);
 
 /*
  * spec_accept without a workspace argument, for callers that cannot allocate

@@ -60,3 +60,43 @@ def sample_flag(weights: np.ndarray, u: float) -> bool:
         return False
     t = float(u) * z
     return bool(np.any(np.abs(c - t) < FLAG_BAND * z))
+
+
+def check_target_sample(S, K, V, target, tk, tp, drafts, u, toks, nacc):
+    """GPU target-sample matching against the oracle on the same inputs:
+    invalid sequences all -1; otherwise n_accepted and tokens equal, except
+    from the first row the oracle sampled whose u * Z lies within 1e-6 * Z of
+    a CDF boundary (before that row the outputs must still agree).  Returns
+    (oracle n_accepted, number of flagged sequences)."""
+    import oracle
+    wt, wn = oracle.spec_accept_target_sample(S, K, V, target, tk, tp, drafts, u)
+    tg = np.asarray(target, np.float32).reshape(S, K + 1, V)
+    flagged = 0
+    for s in range(S):
+        if wn[s] < 0:
+            assert nacc[s] == -1 and np.all(toks[s] == -1), f"sequence {s}: {nacc[s]} {toks[s]}"
+            continue
+        n = int(wn[s])
+        fl = [sample_flag(oracle.distribution(tg[s, i], tk, tp), u[s, i]) for i in range(n + 1)]
+        if any(fl):
+            j = fl.index(True)
+            assert nacc[s] >= j and np.array_equal(toks[s, :j], wt[s, :j]), f"sequence {s}"
+            flagged += 1
+            continue
+        assert nacc[s] == n and np.array_equal(toks[s], wt[s]), (
+            f"sequence {s}: n {nacc[s]} tokens {toks[s]} vs oracle {n} {wt[s]}")
+    return wn, flagged
+
+
+def matching_drafts(S, K, V, target, tk, tp, u, p_match, rng):
+    """Drafts that equal the target's own sample of their row (the oracle's,
+    at the same uniform) with probability p_match, else uniform tokens: inputs
+    for target-sample matching whose accepted prefixes take every length."""
+    import oracle
+    tg = np.asarray(target, np.float32).reshape(S, K + 1, V)
+    d = rng.integers(0, V, size=(S, K)).astype(np.int32)
+    for s in range(S):
+        for i in range(K):
+            if rng.random() < p_match:
+                d[s, i] = oracle.first_exceeding(oracle.distribution(tg[s, i], tk, tp), float(u[s, i]))
+    return d

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = sv.load()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 19
     assert set(names) == set(sv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert sv.api_version() == 2
+    assert sv.api_version() == 3
     assert sv.status_str(sv.SV_OK) == "ok"
     assert "workspace" in sv.status_str(sv.SV_EWORKSPACE)
     assert sv.status_str(99) == "unknown status"
@@ -143,6 +143,70 @@ def test_calls_reject_bad_arguments_before_launch():
     assert lib.sv_read_probe(fake, 100, 0, fake, 1 << 16, None) == sv.SV_EINVAL
     assert lib.vq2_dequant(fake, 10, 100, fake, None) == sv.SV_EINVAL
     assert lib.vq8_dequant(fake, 10, 33, fake, None) == sv.SV_EINVAL
+    # target-sample matching: the same shape, kind, temperature and workspace checks
+    targs = lambda **k: [k.get("S", 1), k.get("K", 4), k.get("V", 32), k.get("target", fake),
+                         k.get("tk", 0), k.get("tp", 1.0), k.get("tok", fake), fake, fake, fake,
+                         k.get("ws", fake), k.get("wsb", 1 << 20), None]
+    assert lib.spec_accept_target_sample(*targs(tp=-1.0)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(tp=float("inf"))) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(tk=2)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(tok=None)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(target=None)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(ws=None)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(K=32)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(V=0)) == sv.SV_EINVAL
+    assert lib.spec_accept_target_sample(*targs(wsb=8)) == sv.SV_EWORKSPACE
+    assert sv.sv_accept_tsm_workspace_bytes(1, 0, 1) > 0
+    assert sv.sv_accept_tsm_workspace_bytes(0, 4, 32) == 0
+    assert sv.sv_accept_tsm_workspace_bytes(1, 4, 256 * 2048 + 1) == 0
+
+
+def test_spec_account_matches_the_oracle():
+    """The host accounting against oracle.yield_quench, step by step, on
+    random runs of accepted-draft counts (with invalid -1 steps); fp64 on
+    both sides in the same order, so the regrets agree exactly."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(17)
+    S, K, steps = 64, 4, 40
+    guard, th = 2.16, 4.0
+    p_acc = rng.uniform(0.2, 0.95, size=S)
+    runs = np.where(rng.random((steps, S)) < 0.05, -1,
+                    np.minimum(rng.geometric(1 - p_acc[None, :], size=(steps, S)) - 1, K)).astype(np.int32)
+    state = None
+    for k in range(steps):
+        state = sv.sv_spec_account(runs[k], K, guard, th, state)
+    quenched = 0
+    for s in range(S):
+        st, tok, reg, q = oracle.yield_quench(runs[:, s].tolist(), guard, th)
+        a = state[s]
+        assert (a.steps, a.tokens, a.regret) == (st, tok, reg), s
+        assert a.quenched == (q is not None) and a.quench_step == (q or 0), s
+        quenched += a.quenched
+    assert 0 < quenched < S
+
+
+def test_spec_account_rejects_bad_arguments():
+    import numpy as np
+    lib = sv.load()
+    st = (sv.SpecAccount * 2)()
+    st[0].regret = 1.5
+    n = np.array([1, 5], np.int32)
+    ptr = ctypes.cast(st, ctypes.POINTER(sv.SpecAccount))
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, 2.16, 4.0, ptr) == sv.SV_EINVAL   # 5 > K
+    assert st[0].regret == 1.5 and st[0].steps == 0                                     # nothing changed
+    n[1] = -2
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, 2.16, 4.0, ptr) == sv.SV_EINVAL
+    n[1] = -1
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, float("nan"), 4.0, ptr) == sv.SV_EINVAL
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, 2.16, float("inf"), ptr) == sv.SV_EINVAL
+    assert lib.sv_spec_account(n.ctypes.data, 0, 4, 2.16, 4.0, ptr) == sv.SV_EINVAL
+    assert lib.sv_spec_account(n.ctypes.data, 2, 32, 2.16, 4.0, ptr) == sv.SV_EINVAL
+    assert lib.sv_spec_account(None, 2, 4, 2.16, 4.0, ptr) == sv.SV_EINVAL
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, 2.16, 4.0, None) == sv.SV_EINVAL
+    assert lib.sv_spec_account(n.ctypes.data, 2, 4, 2.16, 4.0, ptr) == sv.SV_OK
+    assert (st[0].steps, st[0].tokens, st[1].steps) == (1, 2, 0)
+    assert st[0].regret == 1.5 + (2.16 - 2)
 
 
 def test_binding_has_no_fallback(tmp_path):

@@ -23,7 +23,9 @@ configuration the benchmark times, on outputs the oracle computes one by one.
   and tokens must match the oracle exactly (identical fp32 p, q and u).
 * the eight-bit router GEMV ([256 x 7168], through the head's call) ahead of
   the layer: every logit against the oracle, then the routing bit-exact on the
-  GPU's logits.
+  GPU's logits;
+* target-sample matching at V = 129,280 on the head's own logits (the cohort
+  shape, 3 sequences x 4 drafts, and one sequence of 15 drafts).
 """
 import numpy as np
 import pytest
@@ -32,7 +34,8 @@ import oracle
 import synth
 from oracle.accept import LOGITS, PROBS
 from tests.gpu_util import dev, empty, host, say
-from tests.parity import accept_flags, assert_close, sample_flag
+from tests.parity import (accept_flags, assert_close, check_target_sample, matching_drafts,
+                          sample_flag)
 
 pytestmark = pytest.mark.gpu
 
@@ -287,6 +290,23 @@ def test_sweep_lm_head(sv, head, sweep16, R):
     assert_close(z[:, cols], oracle.lm_head_logits(buf, V, H, h[:R], "bf16", rows=cols),
                  what=f"sweep head R={R} (512 sampled vocabulary rows)")
     assert_close(z, z16[:R], tol=1e-5, what=f"head R={R} vs R=16")
+
+
+@pytest.mark.parametrize("S,K,T", [(3, 4, 0.8), (1, 15, 1.0)])
+def test_target_sample_full_vocab(sv, sweep16, S, K, T):
+    """Target-sample matching on the head's 16 logit rows of the sweep
+    (V = 129,280), drafts equal to the target's own sample 70 % of the time:
+    outputs against the oracle on the same logits."""
+    z = sweep16[4][:S * (K + 1)]
+    g = synth.generator(160, S, K)
+    u = synth.uniform24(g, S * (K + 1)).reshape(S, K + 1)
+    drafts = matching_drafts(S, K, V, z, LOGITS, T, u, 0.7, np.random.default_rng(160 + K))
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    say("spec_accept_target_sample full vocab", S, K, T)
+    sv.spec_accept_target_sample(S, K, V, dev(z), sv.SV_LOGITS, T, dev(drafts), dev(u), toks, nacc)
+    wn, flagged = check_target_sample(S, K, V, z, LOGITS, T, drafts, u, host(toks), host(nacc))
+    assert np.all(wn >= 0) and flagged == 0
 
 
 # ----------------------------------------------- full-vocabulary rejection

@@ -9,7 +9,8 @@ import oracle
 import synth
 from oracle.accept import LOGITS, PROBS
 from tests.gpu_util import dev, empty, host, say
-from tests.parity import accept_flags, assert_close, sample_flag
+from tests.parity import (accept_flags, assert_close, check_target_sample, matching_drafts,
+                          sample_flag)
 
 pytestmark = pytest.mark.gpu
 
@@ -439,3 +440,124 @@ def test_accept_greedy_draft(sv):
     toks, nacc = _run_accept(sv, S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.0, drafts, u)
     wn = _check_accept(S, K, V, z, LOGITS, 0.8, zq, LOGITS, 0.0, drafts, u, toks, nacc)
     assert np.all(wn >= 0)
+
+
+# ------------------------------------------------- target-sample matching
+def _run_tsm(sv, S, K, V, target, tk, tp, drafts, u):
+    toks = empty((S, K + 1), "i32")
+    nacc = empty((S,), "i32")
+    say("spec_accept_target_sample", S, K, V, tk, tp)
+    sv.spec_accept_target_sample(S, K, V, dev(target), tk, tp, dev(drafts) if K else None, dev(u),
+                                 toks, nacc)
+    return host(toks), host(nacc)
+
+
+def test_tsm_many_sequences_probs(sv):
+    """Random probability rows (zeros included), drafts equal to the
+    target's own sample 3 times in 4: agreement with the oracle, every prefix
+    length present."""
+    rng = np.random.default_rng(31)
+    S, K, V = 200, 5, 50
+    w = rng.random((S * (K + 1), V)) * (rng.random((S * (K + 1), V)) > 0.3)
+    w[:, 0] += 1e-3
+    p = (w / w.sum(1, keepdims=True)).astype(np.float32)
+    u = synth.uniform24(synth.generator(150), S * (K + 1)).reshape(S, K + 1)
+    drafts = matching_drafts(S, K, V, p, PROBS, 1.0, u, 0.75, rng)
+    toks, nacc = _run_tsm(sv, S, K, V, p, PROBS, 1.0, drafts, u)
+    wn, flagged = check_target_sample(S, K, V, p, PROBS, 1.0, drafts, u, toks, nacc)
+    assert set(wn.tolist()) == set(range(K + 1)) and flagged <= 2
+
+
+def test_tsm_logits_ragged_and_invalid(sv):
+    """Logit rows at T = 0.8 over V = 4,100 (three chunks, a ragged one); a
+    token outside [0, V), a uniform of 1 and an infinite target value each
+    void their own sequence only."""
+    rng = np.random.default_rng(32)
+    S, K, V = 7, 3, 4100
+    z, _, _, u = _logit_inputs(151, S, K, V, 1.0, 0.8)
+    drafts = matching_drafts(S, K, V, z, LOGITS, 0.8, u, 0.8, rng)
+    drafts[1, 2] = V
+    u[2, 0] = 1.0
+    z[4 * (K + 1) + K, 5] = np.inf
+    toks, nacc = _run_tsm(sv, S, K, V, z, LOGITS, 0.8, drafts, u)
+    wn, _ = check_target_sample(S, K, V, z, LOGITS, 0.8, drafts, u, toks, nacc)
+    assert wn[1] == -1 and wn[2] == -1 and wn[4] == -1 and np.all(wn[[0, 3, 5, 6]] >= 0)
+
+
+def test_tsm_no_drafts_equals_bonus_sample(sv):
+    """K = 0: the same sample as spec_accept's bonus token, bit for bit."""
+    g = synth.generator(152)
+    S, V = 6, 9000
+    z = synth.normal(g, S * V, 2.0).astype(np.float32).reshape(S, V)
+    u = synth.uniform24(g, S).reshape(S, 1)
+    empty_d = np.zeros((S, 0), np.int32)
+    a = _run_tsm(sv, S, 0, V, z, LOGITS, 0.7, empty_d, u)
+    b = _run_accept(sv, S, 0, V, z, LOGITS, 0.7, None, LOGITS, 0.7, empty_d, u)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    check_target_sample(S, 0, V, z, LOGITS, 0.7, empty_d, u, *a)
+
+
+def test_tsm_greedy_equals_pq_greedy(sv):
+    """T_p = 0: target-sample matching and the p/q rule give the same output
+    (the longest prefix of drafts equal to their rows' first maxima, then the
+    next row's first maximum), exactly, at V = 70,000 with ties across chunks."""
+    S, K, V = 48, 4, 70000
+    z, zq, drafts, u = _greedy_inputs(153, S, K, V)
+    a = _run_tsm(sv, S, K, V, z, LOGITS, 0.0, drafts, u)
+    b = _run_accept(sv, S, K, V, z, LOGITS, 0.0, zq, LOGITS, 1.0, drafts, u)
+    wt, wn = oracle.spec_accept_target_sample(S, K, V, z, LOGITS, 0.0, drafts, u)
+    assert np.array_equal(a[0], wt) and np.array_equal(a[1], wn)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert set(wn.tolist()) == set(range(K + 1))
+
+
+def test_tsm_largest_vocabulary(sv):
+    """V = 524,288 (256 statistics chunks, 1,024 sampling chunks per row)."""
+    rng = np.random.default_rng(34)
+    S, K, V = 2, 2, 256 * 2048
+    z, _, _, u = _logit_inputs(154, S, K, V, 1.5, 0.8)
+    drafts = matching_drafts(S, K, V, z, LOGITS, 0.8, u, 0.9, rng)
+    toks, nacc = _run_tsm(sv, S, K, V, z, LOGITS, 0.8, drafts, u)
+    check_target_sample(S, K, V, z, LOGITS, 0.8, drafts, u, toks, nacc)
+
+
+def _chi_square(counts, probs):
+    n = counts.sum()
+    e = n * probs
+    keep = e > 0
+    assert np.all(counts[~keep] == 0)
+    return float(((counts[keep] - e[keep]) ** 2 / e[keep]).sum()), int(keep.sum()) - 1
+
+
+def test_sampler_chi_square(sv):
+    """The samplers' output distribution on the GPU: 16,384 sequences share
+    one target row (V = 40, T = 1); the bonus tokens of spec_accept (K = 0)
+    and the first emitted tokens of target-sample matching (K = 2, fixed
+    drafts: lossless, so distributed as p_0 whatever the drafts) are binned
+    and tested with chi-square against p_0 (threshold 96: the 1e-6 tail for
+    39 degrees of freedom is 96.1); the acceptance of draft 0 must also match
+    p_0(draft 0) within 5 standard deviations."""
+    S, V = 16384, 40
+    g = synth.generator(155)
+    row = synth.normal(g, V, 1.5).astype(np.float32)
+    p0 = oracle.softmax_t(row, 1.0)
+    u1 = synth.uniform24(g, S).reshape(S, 1)
+    toks, nacc = _run_accept(sv, S, 0, V, np.tile(row, (S, 1)), LOGITS, 1.0, None, LOGITS, 1.0,
+                             np.zeros((S, 0), np.int32), u1)
+    assert np.all(nacc == 0)
+    chi, dof = _chi_square(np.bincount(toks[:, 0], minlength=V).astype(np.float64), p0)
+    print(f"\n[chi2] spec_accept K=0: {chi:.1f} on {dof} dof")
+    assert dof == V - 1 and chi < 96.0
+    K = 2
+    rows = np.tile(np.stack([row, row[::-1].copy(), row]), (S, 1)).astype(np.float32)
+    d0 = int(np.argsort(p0)[-3])
+    drafts = np.tile(np.array([[d0, 7]], np.int32), (S, 1))
+    u3 = synth.uniform24(g, S * (K + 1)).reshape(S, K + 1)
+    toks, nacc = _run_tsm(sv, S, K, V, rows, LOGITS, 1.0, drafts, u3)
+    assert np.all(nacc >= 0)
+    chi, dof = _chi_square(np.bincount(toks[:, 0], minlength=V).astype(np.float64), p0)
+    acc = float((nacc >= 1).mean())
+    sd = float(np.sqrt(p0[d0] * (1 - p0[d0]) / S))
+    print(f"[chi2] target-sample matching, first token: {chi:.1f} on {dof} dof; "
+          f"draft 0 accepted {acc:.4f} vs p0 {p0[d0]:.4f}")
+    assert chi < 96.0 and abs(acc - p0[d0]) < 5 * sd
