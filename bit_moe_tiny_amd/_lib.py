@@ -20,6 +20,7 @@ ACCEPT_SCRATCH_BYTES = 16 << 20   # SV_ACCEPT_SCRATCH_BYTES of the header
 SV_F32, SV_BF16 = 0, 1
 SV_FFN_PLAIN, SV_FFN_SWIGLU = 0, 1
 SV_LOGITS, SV_PROBS = 0, 1
+SV_Q2, SV_Q8 = 0, 1
 
 EXPORTS = [
     "sv_api_version", "sv_status_str", "sv_q2_matrix_bytes", "sv_q2_tiled_bytes", "sv_q2_tile",
@@ -40,7 +41,8 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [("ffn", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("s_format", ctypes.c_int32)]
 
 
 class SpecAccount(ctypes.Structure):
@@ -208,24 +210,29 @@ def sv_q2_tile(src, n_out: int, k_in: int, parts: int, count: int = 1, out=None,
     return out
 
 
-def _moe_weights(size, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate, s_up, s_down):
+def _moe_weights(size, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate, s_up, s_down, s_size=None):
     """The SwiGLU weight tensors hold the matrices the layer reads, `size`
-    giving the bytes of one matrix in their layout."""
+    giving the bytes of one matrix in their layout (`s_size` that of the
+    shared expert's, when its format differs)."""
     gu, dn = size(inter, hidden), size(hidden, inter)
+    sgu, sdn = (gu, dn) if s_size is None else (s_size(inter, hidden), s_size(hidden, inter))
     if gu == 0 or dn == 0 or n_experts < 1:
         raise ValueError(f"no SwiGLU layer of hidden {hidden}, inter {inter}, {n_experts} experts")
     _want(w_gate, "w_gate", "u8", min_bytes=n_experts * gu)
     _want(w_up, "w_up", "u8", min_bytes=n_experts * gu)
     _want(w_down, "w_down", "u8", min_bytes=n_experts * dn)
     if s_gate is not None or s_up is not None or s_down is not None:
-        _want(s_gate, "s_gate", "u8", min_bytes=gu)
-        _want(s_up, "s_up", "u8", min_bytes=gu)
-        _want(s_down, "s_down", "u8", min_bytes=dn)
+        if sgu == 0 or sdn == 0:
+            raise ValueError(f"no shared expert of hidden {hidden}, inter {inter} in this format")
+        _want(s_gate, "s_gate", "u8", min_bytes=sgu)
+        _want(s_up, "s_up", "u8", min_bytes=sgu)
+        _want(s_down, "s_down", "u8", min_bytes=sdn)
     _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
 
 
 def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_gate, w_up=None,
-             w_down=None, s_gate=None, s_up=None, s_down=None, tiled: bool = False) -> MoeDesc:
+             w_down=None, s_gate=None, s_up=None, s_down=None, tiled: bool = False,
+             shared_format: int = SV_Q2) -> MoeDesc:
     """Layer description over device weight tensors (uint8 byte buffers), each
     checked to hold the matrices the layer reads: n_experts expert-major
     [inter x hidden] gate and up matrices and [hidden x inter] down matrices,
@@ -233,7 +240,8 @@ def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_ga
     SWIGLU weights are read in the expert-tiled layout: given in the plain
     layout (tiled=False) they are regrouped once here, on the device, by
     sv_q2_tile (gate and up with 4 parts, down with 1), and the description
-    keeps the tiled copies alive."""
+    keeps the tiled copies alive.  shared_format SV_Q8: the shared expert's
+    matrices are eight-bit (plain eight-bit layout, used as given)."""
     lib = load()
     gu = lib.sv_q2_matrix_bytes(inter, hidden)
     if ffn == SV_FFN_PLAIN:
@@ -241,21 +249,25 @@ def moe_desc(ffn: int, hidden: int, inter: int, n_experts: int, top_k: int, w_ga
         if gu == 0:
             raise ValueError(f"no two-bit matrix of shape [{inter} x {hidden}]")
     else:
+        if shared_format not in (SV_Q2, SV_Q8):
+            raise ValueError(f"shared_format {shared_format}: expected SV_Q2 or SV_Q8")
+        q8 = shared_format == SV_Q8
+        s_size = lib.sv_q8_matrix_bytes if q8 else None
         if not tiled:
             _moe_weights(lib.sv_q2_matrix_bytes, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate,
-                         s_up, s_down)
+                         s_up, s_down, s_size)
             w_gate = sv_q2_tile(w_gate, inter, hidden, 4, n_experts)
             w_up = sv_q2_tile(w_up, inter, hidden, 4, n_experts)
             w_down = sv_q2_tile(w_down, hidden, inter, 1, n_experts)
-            if s_gate is not None and s_up is not None and s_down is not None:
+            if not q8 and s_gate is not None and s_up is not None and s_down is not None:
                 s_gate = sv_q2_tile(s_gate, inter, hidden, 4)
                 s_up = sv_q2_tile(s_up, inter, hidden, 4)
                 s_down = sv_q2_tile(s_down, hidden, inter, 1)
         _moe_weights(lib.sv_q2_tiled_bytes, hidden, inter, n_experts, w_gate, w_up, w_down, s_gate, s_up,
-                     s_down)
+                     s_down, s_size)
     _dev_check(w_gate, w_up, w_down, s_gate, s_up, s_down)
     d = MoeDesc(ffn, hidden, inter, n_experts, top_k, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-                _ptr(s_gate), _ptr(s_up), _ptr(s_down))
+                _ptr(s_gate), _ptr(s_up), _ptr(s_down), shared_format if ffn != SV_FFN_PLAIN else SV_Q2)
     d._keep = (w_gate, w_up, w_down, s_gate, s_up, s_down)   # keep tensors alive
     return d
 

@@ -47,6 +47,7 @@ int moe_check(const sv_moe_desc* d, int R) {
   if (!d->w_gate || !d->w_up || !d->w_down) return SV_EINVAL;
   const int ns = (d->s_gate != nullptr) + (d->s_up != nullptr) + (d->s_down != nullptr);
   if (ns != 0 && ns != 3) return SV_EINVAL;
+  if (ns == 3 && d->s_format != SV_Q2 && d->s_format != SV_Q8) return SV_EINVAL;
   return SV_OK;
 }
 
@@ -130,6 +131,10 @@ int vq2_moe_gemm(const sv_moe_desc* d, const void* x, int32_t x_dtype, int32_t R
   if (st != SV_OK) return st;
   st = hip_status(launch_moe_down(d, R, w, stream));
   if (st != SV_OK) return st;
+  if (shared_q8(d)) {
+    st = hip_status(launch_shared_q8(d, R, x, x_dtype, w, stream));
+    if (st != SV_OK) return st;
+  }
   return hip_status(launch_moe_combine(d, R, w, y, stream));
 }
 

@@ -63,10 +63,20 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   void* hd = take(plain ? 0 : xdig_bytes(max_assign, d->inter));
   void* xd = take(plain ? 0 : xdig_bytes(R, d->hidden));
   void* xb = take(plain ? ximg_bytes(R, d->hidden, XL_PERM) : 0);
+  const bool q8s = shared_q8(d);
+  void* sxb = take(q8s ? ximg_bytes(R, d->hidden, XL_PLAIN) : 0);
+  void* shb = take(q8s ? ximg_bytes(R, d->inter, XL_PLAIN) : 0);
+  w.sg = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
+  w.su = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
+  w.sh = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
   if (p) {
     if (!plain) w.xd = xdig_carve(xd, R, d->hidden);
     if (!plain) w.hd = xdig_carve(hd, max_assign, d->inter);
     if (plain) w.x_img = ximg_carve(xb, R, d->hidden, XL_PERM);
+    if (q8s) {
+      w.sx_img = ximg_carve(sxb, R, d->hidden, XL_PLAIN);
+      w.sh_img = ximg_carve(shb, R, d->inter, XL_PLAIN);
+    }
   }
   w.max_units = max_units;
   w.max_assign = max_assign;
@@ -286,7 +296,10 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
   if (lane == 0) blk[G] = nd * items;
 }
 
-__device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared,
+// has_shared: the layer has a shared expert (its R assignments follow the
+// routed ones); shared_work: the two-bit expert kernels compute it (not when
+// it is eight-bit).
+__device__ void route_and_group(const float* logits, int R, int E, int k, int has_shared, int shared_work,
                                 int cap_allk, int cap_quarter, int cap_down, int items_gu, int items_dn, int G,
                                 int32_t* idx_out, float* w_out, MoeWs ws) {
   // cost offsets of the descriptors (at most one per unit plus one per further row)
@@ -374,9 +387,10 @@ __device__ void route_and_group(const float* logits, int R, int E, int k, int ha
     ws.meta->n_assign = R * k + has_shared * R;
   }
   __syncthreads();
-  if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, true, cap_allk, cap_quarter, items_gu,
+  const int nwu = nu + (has_shared && shared_work ? 1 : 0);   // units the expert kernels compute
+  if (wv == 0) emit_work(s_uexp, s_uoff, s_ucnt, nwu, s_arow, true, cap_allk, cap_quarter, items_gu,
                          G, ws.work_gu, &ws.meta->n_work_gu, ws.blk_gu, s_cost_gu);
-  if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nu + has_shared, s_arow, false, cap_allk, cap_down, items_dn,
+  if (wv == 1) emit_work(s_uexp, s_uoff, s_ucnt, nwu, s_arow, false, cap_allk, cap_down, items_dn,
                          G, ws.work_dn, &ws.meta->n_work_dn, ws.blk_dn, s_cost_dn);
 }
 
@@ -488,19 +502,22 @@ __global__ __launch_bounds__(PREP_THREADS) void k_hdig(MoeWs ws, int inter) {
 }
 
 hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s) {
-  (void)R;
-  hipLaunchKernelGGL(k_hdig, dim3(ws.max_assign), dim3(PREP_THREADS), 0, s, ws, d->inter);
+  // the eight-bit shared expert's assignments (the last R) have no quarter sums
+  const int na = shared_q8(d) ? ws.max_assign - R : ws.max_assign;
+  hipLaunchKernelGGL(k_hdig, dim3(na), dim3(PREP_THREADS), 0, s, ws, d->inter);
   return hipGetLastError();
 }
 
 template <int DT>
 __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, int R, int E, int k,
-                                                           int has_shared, int cap_allk, int cap_quarter,
+                                                           int has_shared, int shared_work, int cap_allk,
+                                                           int cap_quarter,
                                                            int cap_down, int items_gu, int items_dn, int G,
                                                            int32_t* idx_out, float* w_out, const void* x,
                                                            MoeWs ws) {
   if (blockIdx.x == 0) {
-    route_and_group(logits, R, E, k, has_shared, cap_allk, cap_quarter, cap_down, items_gu, items_dn, G, idx_out,
+    route_and_group(logits, R, E, k, has_shared, shared_work, cap_allk, cap_quarter, cap_down, items_gu, items_dn,
+                    G, idx_out,
                     w_out, ws);
   } else {
     stage_digits<DT>(x, blockIdx.x - 1, ws.xd);   // one block per row
@@ -510,17 +527,19 @@ __global__ __launch_bounds__(PREP_THREADS) void k_moe_prep(const float* logits, 
 hipError_t launch_moe_prep(const sv_moe_desc* d, int R, const float* router_logits,
                            const void* x, int x_dtype, int32_t* topk_idx_out,
                            float* topk_w_out, MoeWs ws, hipStream_t s) {
-  const int has_shared = d->s_gate ? 1 : 0;
+  const int has_shared = d->s_gate ? 1 : 0, shared_work = shared_q8(d) ? 0 : 1;
   const dim3 grid(1 + R);
   int ca, cq, cd;
   moe8_caps(d, &ca, &cq, &cd);
   const int items_gu = d->inter / 16, items_dn = d->hidden / 128, G = moe_grid();
   if (x_dtype == SV_BF16)
     hipLaunchKernelGGL(k_moe_prep<SV_BF16>, grid, dim3(PREP_THREADS), 0, s, router_logits, R, d->n_experts,
-                       d->top_k, has_shared, ca, cq, cd, items_gu, items_dn, G, topk_idx_out, topk_w_out, x, ws);
+                       d->top_k, has_shared, shared_work, ca, cq, cd, items_gu, items_dn, G, topk_idx_out,
+                       topk_w_out, x, ws);
   else
     hipLaunchKernelGGL(k_moe_prep<SV_F32>, grid, dim3(PREP_THREADS), 0, s, router_logits, R, d->n_experts,
-                       d->top_k, has_shared, ca, cq, cd, items_gu, items_dn, G, topk_idx_out, topk_w_out, x, ws);
+                       d->top_k, has_shared, shared_work, ca, cq, cd, items_gu, items_dn, G, topk_idx_out,
+                       topk_w_out, x, ws);
   return hipGetLastError();
 }
 
@@ -664,6 +683,29 @@ hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, h
   hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden / 4 + 255) / 256, R), dim3(256), 0, s,
                      d->hidden, d->top_k, d->s_gate ? 1 : 0, ws, y);
   return hipGetLastError();
+}
+
+// ------------------------------------------------ eight-bit shared expert
+// h = silu(g) * u over the R x inter outputs of the shared gate / up products.
+__global__ __launch_bounds__(256) void k_swiglu_rows(const float* g, const float* u, float* h, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) h[i] = silu_mul(g[i], u[i]);
+}
+
+hipError_t launch_shared_q8(const sv_moe_desc* d, int R, const void* x, int x_dtype, MoeWs ws,
+                            hipStream_t s) {
+  const int H = d->hidden, I = d->inter;
+  hipError_t e = launch_stage(x, x_dtype, R, H, XL_PLAIN, nullptr, ws.sx_img, s);
+  if (e != hipSuccess) return e;
+  const bool lo = x_dtype == SV_F32;   // bf16 rows are exact in the fp16 high part
+  if ((e = launch_q8_lmhead(d->s_gate, I, H, R, lo, ws.sx_img, ws.sg, s)) != hipSuccess) return e;
+  if ((e = launch_q8_lmhead(d->s_up, I, H, R, lo, ws.sx_img, ws.su, s)) != hipSuccess) return e;
+  const int n = R * I;
+  hipLaunchKernelGGL(k_swiglu_rows, dim3((n + 255) / 256), dim3(256), 0, s, ws.sg, ws.su, ws.sh, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_stage(ws.sh, SV_F32, R, I, XL_PLAIN, nullptr, ws.sh_img, s)) != hipSuccess) return e;
+  // the shared assignments are R*k .. R*k+R-1, row r at R*k + r
+  return launch_q8_lmhead(d->s_down, H, I, R, true, ws.sh_img, ws.part + (size_t)R * d->top_k * H, s);
 }
 
 // ----------------------------------------------------------------- plain

@@ -372,8 +372,17 @@ struct MoeWs {
   XDig hd;            // the down projection's input rows as digits  [max_assign, inter]
   XDig xd;            // x as digits  [R, hidden]
   XImg x_img;         // x staged for the one-matrix (PLAIN) path  [R, hidden]
+  // eight-bit shared expert: x and h staged for the head kernels, the
+  // gate / up outputs and h = silu(g) * u, all [R, *]
+  XImg sx_img, sh_img;
+  float *sg, *su, *sh;
   int max_units, max_assign, max_work;
 };
+
+// Whether the layer's shared expert runs on the eight-bit path.
+inline bool shared_q8(const sv_moe_desc* d) {
+  return d->ffn == SV_FFN_SWIGLU && d->s_gate != nullptr && d->s_format == SV_Q8;
+}
 
 size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out);
 
@@ -398,6 +407,10 @@ hipError_t launch_moe_gateup(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t 
 hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
 hipError_t launch_moe_down(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
+// The eight-bit shared expert: its outputs into the shared assignments' rows
+// of ws.part.
+hipError_t launch_shared_q8(const sv_moe_desc* d, int R, const void* x, int x_dtype, MoeWs ws,
+                            hipStream_t s);
 // Whether the streamed int8 expert kernels take this layer (LDS limits).
 bool moe_shape_ok(const sv_moe_desc* d);
 hipError_t launch_q2_tile(const void* src, void* dst, int n_out, int k_in, int parts, int count, hipStream_t s);

@@ -71,6 +71,8 @@ enum sv_ffn {
 
 enum sv_dist { SV_LOGITS = 0, SV_PROBS = 1 };  /* how a distribution row is given */
 
+enum sv_wfmt { SV_Q2 = 0, SV_Q8 = 1 };         /* block format of the shared expert */
+
 #define SV_API_VERSION 3
 #define SV_MAX_ROWS 64        /* R limit of the GEMM calls */
 #define SV_MAX_TOPK 16
@@ -148,8 +150,14 @@ SV_API size_t sv_q8_matrix_bytes(int32_t n_out, int32_t k_in);
  *    expert-tiled with parts = 4 (sv_q2_tile), back to back
  *    sv_q2_tiled_bytes(inter, hidden) apart; w_down: n_experts matrices
  *    [hidden x inter], expert-tiled with parts = 1; s_gate/s_up/s_down: the
- *    shared expert in the same layouts (always on, combine weight 1) or all
- *    NULL.
+ *    shared expert (always on, combine weight 1) or all NULL.  s_format
+ *    SV_Q2: the shared matrices in the routed experts' layouts; SV_Q8: the
+ *    shared matrices eight-bit (the format the pages' model keeps its shared
+ *    expert in: [T3] introduction, the quantisation recipe; [T1] page 1, post
+ *    14, the target file's name), s_gate/s_up [inter x hidden] and s_down
+ *    [hidden x inter] in the plain eight-bit layout below, each computed with
+ *    the vocabulary head's kernels (activation rows staged as fp16 high +
+ *    remainder).  Ignored when there is no shared expert.
  *  SV_FFN_PLAIN: w_gate is one [inter x hidden] two-bit matrix (plain
  *    layout); the other five NULL; n_experts = top_k = 1.
  *  hidden % 256 == 0 and inter % 256 == 0 for SWIGLU; PLAIN needs
@@ -159,6 +167,7 @@ typedef struct {
   int32_t ffn, hidden, inter, n_experts, top_k;
   const void *w_gate, *w_up, *w_down;
   const void *s_gate, *s_up, *s_down;
+  int32_t s_format;   /* sv_wfmt of s_gate / s_up / s_down */
 } sv_moe_desc;
 
 /* Workspace bytes vq2_moe_gemm needs for this layer and R rows (0 if invalid). */
@@ -185,9 +194,10 @@ SV_API size_t sv_moe_workspace_bytes(const sv_moe_desc* d, int32_t R);
  *  FFN(x) = W_d(silu(W_g x) * (W_u x)) and fp32 intermediates.  Summation
  *  order is fixed, so results are run-to-run deterministic.  Accuracy: every
  *  element of y within 2e-3 relative of the exact value, or of 1e-3 of its
- *  row's largest magnitude where that is larger (x enters the gate/up products
- *  with ~22 significant bits per element, h enters the down projection as a
- *  ~30-bit fixed-point value per row).
+ *  row's largest magnitude where that is larger (x and h enter the two-bit
+ *  products as ~30-bit fixed-point values per row, exact for bf16 x within
+ *  2^-22 of the row's largest magnitude; the eight-bit shared expert takes
+ *  its rows as fp16 high + remainder, ~22 significant bits).
  */
 SV_API int vq2_moe_gemm(const sv_moe_desc* d, const void* x, int32_t x_dtype, int32_t R,
                  const float* router_logits, float* y, int32_t* topk_idx, float* topk_w,

@@ -51,12 +51,15 @@ def silu(g: np.ndarray) -> np.ndarray:
     return out
 
 
-def swiglu_expert(w_gate, w_up, w_down, hidden: int, inter: int, x64: np.ndarray) -> np.ndarray:
-    """One SwiGLU expert on fp64 rows x64 [r, hidden] -> [r, hidden]."""
-    g = gemm(q2_dequant_f64(w_gate, inter, hidden), x64)
-    u = gemm(q2_dequant_f64(w_up, inter, hidden), x64)
+def swiglu_expert(w_gate, w_up, w_down, hidden: int, inter: int, x64: np.ndarray,
+                  fmt: str = "q2") -> np.ndarray:
+    """One SwiGLU expert on fp64 rows x64 [r, hidden] -> [r, hidden]; its
+    matrices two-bit (fmt "q2") or eight-bit ("q8")."""
+    deq = {"q2": q2_dequant_f64, "q8": q8_dequant_f64}[fmt]
+    g = gemm(deq(w_gate, inter, hidden), x64)
+    u = gemm(deq(w_up, inter, hidden), x64)
     h = silu(g) * u
-    return gemm(q2_dequant_f64(w_down, hidden, inter), h)
+    return gemm(deq(w_down, hidden, inter), h)
 
 
 def route_topk(logits: np.ndarray, k: int):
@@ -80,10 +83,13 @@ def _slice_expert(buf, e: int, nbytes: int):
 
 
 def moe_layer(w_gate, w_up, w_down, s_gate, s_up, s_down, n_experts: int, top_k: int,
-              hidden: int, inter: int, x, x_dtype: str, router_logits):
+              hidden: int, inter: int, x, x_dtype: str, router_logits, shared_format: str = "q2"):
     """Routed + shared SwiGLU MoE layer.
 
-    w_* hold ``n_experts`` expert-major matrices; s_* the shared expert (or None).
+    w_* hold ``n_experts`` expert-major two-bit matrices; s_* the shared
+    expert (or None), two-bit or, with shared_format "q8", eight-bit (the
+    format the pages' model keeps it in: *ds4-on-spark* README, introduction,
+    the quantisation recipe).
     Returns (y fp64 [R, hidden], topk_idx int32 [R, k], topk_w fp64 [R, k]).
     """
     x64 = _exact_rows(x, x_dtype)
@@ -104,7 +110,7 @@ def moe_layer(w_gate, w_up, w_down, s_gate, s_up, s_down, n_experts: int, top_k:
             for s in np.nonzero(idx[r] == e)[0]:
                 y[r] += wts[r, s] * ye[j]
     if s_gate is not None:
-        y += swiglu_expert(s_gate, s_up, s_down, hidden, inter, x64)
+        y += swiglu_expert(s_gate, s_up, s_down, hidden, inter, x64, shared_format)
     return y, idx, wts
 
 

@@ -288,6 +288,17 @@ def router_weights(config_id: int = CFG_MOE, n_experts: int = N_ROUTED, hidden: 
     return q8_random(generator(config_id, S_ROUTER, 1 << 20), n_experts, hidden, 3e-4)
 
 
+def shared_q8_weights(config_id: int = CFG_MOE, hidden: int = HIDDEN, inter: int = INTER,
+                      sigma: float = 2e-3):
+    """An eight-bit shared expert: gate, up [inter x hidden] and down
+    [hidden x inter] in the vocabulary head's format, codes uniform on
+    -127..127 and scales ~ fp16(|N(0, sigma^2)|), so that the weights spread
+    about as much as the two-bit experts' (rms ~ 0.15)."""
+    g = generator(config_id, S_WEIGHTS, 1 << 21)
+    return (q8_random(g, inter, hidden, sigma), q8_random(g, inter, hidden, sigma),
+            q8_random(g, hidden, inter, sigma))
+
+
 def lm_head_weights(config_id: int = CFG_LMHEAD, vocab: int = VOCAB, hidden: int = HIDDEN) -> Q8Planes:
     return q8_random(generator(config_id, S_WEIGHTS), vocab, hidden, 0.01)
 

@@ -86,7 +86,7 @@ def _desc(**kw):
     base.update(kw)
     d = sv.MoeDesc(base["ffn"], base["hidden"], base["inter"], base["n_experts"], base["top_k"],
                    base.get("w_gate", 0x1000), base.get("w_up", 0x1000), base.get("w_down", 0x1000),
-                   base.get("s_gate"), base.get("s_up"), base.get("s_down"))
+                   base.get("s_gate"), base.get("s_up"), base.get("s_down"), base.get("s_format", 0))
     return d
 
 
@@ -102,6 +102,12 @@ def test_moe_workspace_sizes():
     assert sv.sv_moe_workspace_bytes(_desc(ffn=sv.SV_FFN_PLAIN, inter=512, hidden=256, n_experts=1,
                                            top_k=1, w_up=None, w_down=None), 4) > 0
     assert sv.sv_moe_workspace_bytes(_desc(ffn=7), 4) == 0
+    # the shared expert's format: SV_Q2 or SV_Q8 (eight-bit needs its staging and output space)
+    assert sv.sv_moe_workspace_bytes(_desc(s_gate=1, s_up=1, s_down=1, s_format=2), 5) == 0
+    q2s = sv.sv_moe_workspace_bytes(_desc(s_gate=1, s_up=1, s_down=1, s_format=sv.SV_Q2), 5)
+    q8s = sv.sv_moe_workspace_bytes(_desc(s_gate=1, s_up=1, s_down=1, s_format=sv.SV_Q8), 5)
+    assert q8s > q2s > 0
+    assert sv.sv_moe_workspace_bytes(_desc(s_format=5), 5) > 0      # ignored without a shared expert
 
 
 def test_calls_reject_bad_arguments_before_launch():

@@ -154,6 +154,27 @@ def test_moe_layer_workload(sv, layer):
     assert_close(y, want, what="moe layer R=5 y (every row)")
 
 
+@pytest.mark.parametrize("R", [5, 16])
+def test_moe_layer_eight_bit_shared(sv, layer, R):
+    """The full layer with its shared expert in eight-bit blocks (the
+    format of the pages' model): the 256 routed experts of the workload, an
+    eight-bit shared expert of the same shape; every row of y against the
+    oracle."""
+    w, _ = layer
+    say("eight-bit shared expert, layer R =", R)
+    sq = [m.packed() for m in synth.shared_q8_weights()]
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, H, I, E, TOPK, *(dev(a) for a in (w.gate, w.up, w.down)),
+                       *(dev(a) for a in sq), shared_format=sv.SV_Q8)
+    rows = synth.moe_rows(R, synth.CFG_MOE, sub=40 + R)
+    y, ti, _ = _run_moe(sv, desc, rows.x_bf16, rows.router_logits)
+    widx, _ = oracle.route_topk(rows.router_logits, TOPK)
+    assert np.array_equal(ti, widx)
+    say("oracle MoE output with the eight-bit shared expert, all rows")
+    want, _, _ = oracle.moe_layer(w.gate, w.up, w.down, *sq, E, TOPK, H, I, rows.x_bf16, "bf16",
+                                  rows.router_logits, shared_format="q8")
+    assert_close(y, want, what=f"moe layer q8 shared R={R} y (every row)")
+
+
 # ---------------------------------------------------------------- router
 def test_router_gemv_then_layer(sv, layer):
     """The eight-bit router GEMV ahead of the top-k, as the vocabulary head's

@@ -168,6 +168,33 @@ def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
     assert_close(host(y), want, what=f"small moe E={E} k={k} {hidden}x{inter} R={R} shared={shared} {dt} y")
 
 
+@pytest.mark.parametrize("E,k,hidden,inter,R,dt", [
+    (16, 4, 512, 256, 5, "bf16"),
+    (8, 2, 256, 512, 3, "f32"),
+    (32, 8, 1024, 256, 16, "bf16"),
+    (6, 2, 1280, 1536, 9, "f32"),
+])
+def test_small_moe_eight_bit_shared(sv, E, k, hidden, inter, R, dt):
+    """The shared expert in eight-bit blocks (the head's kernels for its
+    three products) beside two-bit routed experts."""
+    (g, u, d), _ = _small_moe(E, hidden, inter, False, 107 + E)
+    sq = synth.shared_q8_weights(108 + E, hidden, inter)
+    sg, su, sd = (m.packed() for m in sq)
+    gen = synth.generator(109, E, R)
+    x = synth.normal_bf16(gen, (R, hidden)) if dt == "bf16" else synth.normal_f32(gen, (R, hidden))
+    logits = synth.normal_f32(synth.generator(110, E, R), (R, E))
+    tens = [dev(a) for a in (g, u, d, sg, su, sd)]
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, hidden, inter, E, k, *tens, shared_format=sv.SV_Q8)
+    y = empty((R, hidden), "f32")
+    ti = empty((R, k), "i32")
+    say("vq2_moe_gemm SWIGLU eight-bit shared", E, k, hidden, inter, R, dt)
+    sv.vq2_moe_gemm(desc, dev(x), dev(logits), y, ti)
+    want, widx, _ = oracle.moe_layer(g, u, d, sg, su, sd, E, k, hidden, inter, x, dt, logits,
+                                     shared_format="q8")
+    assert np.array_equal(host(ti), widx)
+    assert_close(host(y), want, what=f"small moe q8 shared E={E} k={k} {hidden}x{inter} R={R} {dt} y")
+
+
 # ------------------------------------------------------------ routing ties
 def _tie_logits(R, E, seed):
     """Router rows built to exercise the tie-breaking rule (equal logits: the

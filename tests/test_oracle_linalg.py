@@ -126,6 +126,40 @@ def test_moe_closed_form():
         assert np.allclose(y[r], val, rtol=1e-10, atol=1e-12)
 
 
+def _const_q8(n_out, k_in, d, q):
+    """An eight-bit matrix whose every weight is d*q."""
+    nblk = n_out * k_in // 32
+    return synth.pack_planes(np.full(nblk * 32, q, np.int8), np.full(nblk, d, np.float16))
+
+
+def test_moe_eight_bit_shared_closed_form():
+    """The shared expert in eight-bit blocks: constant matrices d*q, so
+    FFN_shared(x) = c * inter * silu(a S) * b S with a, b, c the products
+    d*q of gate, up and down; routed experts two-bit as before.  Also: the
+    two formats give the same layer when they hold the same weights."""
+    hidden, inter, E, k, R = 256, 256, 3, 1, 2
+    gate = np.concatenate([_const_q2(inter, hidden, 0.25 * (e + 1)) for e in range(E)])
+    up = np.concatenate([_const_q2(inter, hidden, -0.5 * (e + 1)) for e in range(E)])
+    down = np.concatenate([_const_q2(hidden, inter, 2.0 ** -(6 + e)) for e in range(E)])
+    a, b, c = 0.125 * 3, -0.0625 * 5, 2.0 ** -9 * 7
+    sg, su, sd = _const_q8(inter, hidden, 0.125, 3), _const_q8(inter, hidden, -0.0625, 5), _const_q8(hidden, inter, 2.0 ** -9, 7)
+    x = (synth.normal_f32(synth.generator(26, 0), (R, hidden)) * 0.05).astype(np.float32)
+    logits = np.array([[0.0, 1.0, -1.0], [2.0, 0.5, 0.25]], np.float32)
+    y, idx, w = oracle.moe_layer(gate, up, down, sg, su, sd, E, k, hidden, inter, x, "f32", logits,
+                                 shared_format="q8")
+    y0, _, _ = oracle.moe_layer(gate, up, down, None, None, None, E, k, hidden, inter, x, "f32", logits)
+    assert idx.tolist() == [[1], [0]]
+    for r in range(R):
+        S = math.fsum(float(v) for v in x[r])
+        g = a * S
+        shared = c * inter * (g / (1 + math.exp(-g))) * b * S
+        assert np.allclose(y[r] - y0[r], shared, rtol=1e-10, atol=1e-14)
+    # the same constant weights as two-bit blocks (d*sc*q with sc = 1, q = 1)
+    sg2, su2, sd2 = _const_q2(inter, hidden, a), _const_q2(inter, hidden, b), _const_q2(hidden, inter, c)
+    y2, _, _ = oracle.moe_layer(gate, up, down, sg2, su2, sd2, E, k, hidden, inter, x, "f32", logits)
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-15)
+
+
 def test_moe_single_expert_no_router():
     hidden, inter = 256, 256
     g, u, d = _const_q2(inter, hidden, 0.5), _const_q2(inter, hidden, 0.25), _const_q2(hidden, inter, 2.0 ** -6)
