@@ -539,19 +539,18 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
   double w = inv ? 0.0 : seg_weight(mode, P, pm, pz, Q, qm, qz, c, V);
   // 4. the last block of the sequence to get here samples.  The sums go out
   //    as device-scope stores (written through to the point of coherence of
-  //    all XCDs, not held in this XCD's L2); every thread then makes its
-  //    stores visible at device scope (a release fence, which also waits for
-  //    them to complete), the block meets, and one thread counts the block
-  //    done with a release increment.  The block that brings the count to
-  //    the total acquires before it reads the sums back (device-scope
-  //    loads): every other block's stores happen before its reads.
+  //    all XCDs, not held in this XCD's L2); the block meets (a workgroup
+  //    barrier: every thread's stores happen before what thread 0 does
+  //    next), and thread 0 counts the block done with an acquire-release
+  //    increment at device scope, whose release publishes them.  The block
+  //    that brings the count to the total acquires (every thread, after the
+  //    barrier) before it reads the sums back with device-scope loads, so
+  //    every other block's stores happen before those reads.
   __hip_atomic_store(&ws.tsum[((size_t)s * CHs + c) * ACC_T + tid], w, __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
   w = block_sum_d(w, sh);
   if (tid == 0)
     __hip_atomic_store(&ws.rsum[(size_t)s * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  wait_vmcnt_le(0);
   __syncthreads();
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -700,18 +699,16 @@ __global__ __launch_bounds__(ACC_T) void k_tsm_sample(int S, int K, int V, int C
   const double pm = s_m, pz = s_zr;
   const int bad = s_bad;
   // 2. this chunk's mass of p; the last block of the row to finish samples it
-  //    (publication as in k_acc_sample: device-scope stores, release fence,
-  //    release increment; the last block acquires)
+  //    (publication as in k_acc_sample: thread 0 stores the sum and counts
+  //    the block done with an acquire-release increment at device scope; the
+  //    last block acquires before its reads)
   double w = bad ? 0.0 : seg_weight(MODE_P, P, pm, pz, P, 0.0, 1.0, c, V);
   w = block_sum_d(w, sh);
-  if (tid == 0)
+  if (tid == 0) {
     __hip_atomic_store(&ws.rsum[(size_t)r * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  wait_vmcnt_le(0);
-  __syncthreads();
-  if (tid == 0)
     s_last = __hip_atomic_fetch_add(&ws.done[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
              (unsigned)(CHs - 1);
+  }
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -730,12 +727,14 @@ __global__ __launch_bounds__(ACC_T) void k_tsm_sample(int S, int K, int V, int C
       tok = seg_token(parts, s_base, s_found, (double)uf * s_z, s_hit, MODE_P, P, pm, pz, P, 0.0, 1.0, V);
   }
   if (tid >= 64) return;
-  // 4. publish it; the last row of the sequence to be sampled decides
-  if (lane == 0) __hip_atomic_store(&ws.tok[r], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  wait_vmcnt_le(0);
+  // 4. publish it (the same lane stores it and counts the row done with an
+  //    acquire-release increment); the last row of the sequence to be
+  //    sampled decides, after an acquire of its own wave
   unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&ws.done[rows + s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) {
+    __hip_atomic_store(&ws.tok[r], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __hip_atomic_fetch_add(&ws.done[rows + s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  }
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (unsigned)K) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
