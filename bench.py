@@ -17,8 +17,11 @@ Prints ONE JSON line (rank 0, N = 1).  Besides the headline (R = 5, S = 1)
 the line carries, unless --no-extras: one entry per R = 1..16 and the
 three-sequence cohort (R = 15, S = 3), single-expert calls at R = 1, 2, 4, 8
 beside an empty-launch floor, live per-kernel times of one R = 5 step with a
-roofline entry per expert kernel, the read-bandwidth probe, and SHA-256
-digests of the generated inputs.  --sweep prints one line per R instead.
+roofline entry per expert kernel, the layer with an eight-bit shared expert
+and target-sample matching timed beside the step's own calls, the step and a
+four-layer stack eagerly and as graph replays, the read-bandwidth probe, and
+SHA-256 digests of the generated inputs.  --sweep prints one line per R
+instead.
 """
 from __future__ import annotations
 
@@ -309,9 +312,55 @@ def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24, reps: int = 48):
             "rows": out}
 
 
+def event_median(call, reps: int = 40) -> float:
+    """Median event-timed duration of call() in microseconds."""
+    import torch
+    call()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)) * 1e3
+
+
+def next_rows(sv, step, wroute):
+    """The rows beyond the verifier step proper, timed at the step's shape:
+    the layer with its shared expert in eight-bit blocks beside the two-bit
+    one (the same routed experts and rows), and target-sample matching beside
+    the p/q rule on the step's own logits."""
+    import torch
+    wg, wu, wd = wroute
+    sq = [to_dev(m.packed()) for m in synth.shared_q8_weights()]
+    d8 = sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, synth.N_ROUTED, synth.TOP_K, wg, wu, wd,
+                     *sq, tiled=True, shared_format=sv.SV_Q8)
+    ws8 = torch.empty(sv.sv_moe_workspace_bytes(d8, step.R), dtype=torch.uint8, device="cuda")
+    bt = step.batches[0]
+    q2 = event_median(lambda: sv.vq2_moe_gemm(step.desc, bt["x"], bt["logits"], step.y, ws=step.ws_moe))
+    q8 = event_median(lambda: sv.vq2_moe_gemm(d8, bt["x"], bt["logits"], step.y, ws=ws8))
+    q8_bytes = 2 * sv.sv_q8_matrix_bytes(synth.INTER, synth.HIDDEN) + sv.sv_q8_matrix_bytes(synth.HIDDEN, synth.INTER)
+    V = synth.VOCAB
+    sv.vq8_lmhead_gemm(step.wq8, V, synth.HIDDEN, bt["h"], step.z, ws=step.ws_lm)
+    ws_t = torch.empty(sv.sv_accept_tsm_workspace_bytes(step.S, step.K, V), dtype=torch.uint8, device="cuda")
+    pq = event_median(lambda: sv.spec_accept(step.S, step.K, V, step.z, sv.SV_LOGITS, step.T, bt["draft"],
+                                             sv.SV_LOGITS, step.T, bt["drafts"], bt["u"], step.toks, step.nacc,
+                                             ws=step.ws_acc))
+    ts = event_median(lambda: sv.spec_accept_target_sample(step.S, step.K, V, step.z, sv.SV_LOGITS, step.T,
+                                                           bt["drafts"], bt["u"], step.toks, step.nacc, ws=ws_t))
+    return {"R": step.R, "S": step.S, "K": step.K,
+            "moe_layer_us": {"shared_q2": round(q2, 2), "shared_q8": round(q8, 2)},
+            "shared_expert_bytes": {"q2": Q2_EXPERT_BYTES, "q8": q8_bytes},
+            "accept_us": {"p_q_rule": round(pq, 2), "target_sample_matching": round(ts, 2)}}
+
+
 KERNEL_KEYS = {"gate/up": "k_gu8", "down": "k_dn8", "down input digits": "k_hdig", "routing": "k_moe_prep",
                "combine": "k_moe_combine", "head": "k_q8_lmhead", "head staging": "k_stage",
-               "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample"}
+               "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample",
+               "target-sample matching": "k_tsm_sample", "shared expert h staging": "k_stage_swiglu"}
 
 
 def kernel_times(step, steps: int = 10):
@@ -639,6 +688,8 @@ def main():
             if not args.no_extras:
                 log("kernel times of one step (profiler) ...")
                 line["kernel_times"] = kernel_times(step)
+                log("eight-bit shared expert and target-sample matching ...")
+                line["next_rows"] = next_rows(sv, step, (desc._keep[0], desc._keep[1], desc._keep[2]))
                 del step
                 ents = []
                 for r2, s2 in [(r, 1) for r in range(1, 17)] + [(15, 3)]:

@@ -132,6 +132,7 @@ int vq2_moe_gemm(const sv_moe_desc* d, const void* x, int32_t x_dtype, int32_t R
   st = hip_status(launch_moe_down(d, R, w, stream));
   if (st != SV_OK) return st;
   if (shared_q8(d)) {
+    plan_shared_q8(d, R, x_dtype, &w);
     st = hip_status(launch_shared_q8(d, R, x, x_dtype, w, stream));
     if (st != SV_OK) return st;
   }

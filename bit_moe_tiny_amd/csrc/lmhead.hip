@@ -347,13 +347,21 @@ static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
 }
 
 
+// Split over K (the products of small matrices, whose tiles alone would
+// occupy few compute units): block (x, y, z) takes the stages [y sp, (y+1)
+// sp) of matrix z (W, or W2 for z = 1) and writes its partial products to
+// logits + z zstride + y R vocab (one [R, vocab] slice per y).  The head
+// runs it with one slice (sp = all stages) and one matrix.
 template <bool USE_LO, int LD_WAVES>
-__global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W, int R, XImg img,
-                                                                               float* logits, int ncols) {
+__global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W1, Q8View W2, int R,
+                                                                               XImg img, float* logits,
+                                                                               int ncols, int sp, size_t zstride) {
   extern __shared__ __align__(16) uint8_t lds[];
+  const Q8View W = blockIdx.z ? W2 : W1;
   const int lane = threadIdx.x & 63, wv = wave_id();
   const int vocab = W.n_out, nb = W.nb, K = nb * 32;
-  const int tiles = (vocab + 15) / 16, ns = nb / LD_SB;
+  const int tiles = (vocab + 15) / 16, st0 = blockIdx.y * sp, ns = min(st0 + sp, nb / LD_SB);
+  logits += blockIdx.z * zstride + (size_t)blockIdx.y * R * vocab;
   const int rounds = (tiles + gridDim.x * LD_WAVES - 1) / (gridDim.x * LD_WAVES);
   const int nl = lane & 15, g = lane >> 4;
   const int kofs = 8 * (((g & 1) << 1) | (g >> 1));   // k offset of this lane's 8 values in a block
@@ -401,9 +409,9 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
   f4_t acc[LD_MAX_ROUNDS];
 #pragma unroll
   for (int r = 0; r < LD_MAX_ROUNDS; ++r) acc[r] = zero;
-  issue(0, 0, 0, 0);
+  issue(st0, 0, 0, st0 & 1);
   int k = 0;   // running step count: weight buffer k & 1
-  for (int st = 0; st < ns; ++st) {
+  for (int st = st0; st < ns; ++st) {
 #pragma unroll
     for (int r = 0; r < LD_MAX_ROUNDS; ++r) {
       if (r >= rounds) break;
@@ -486,12 +494,13 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
   if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX / 2 : LD_XMAX) && rounds <= LD_MAX_ROUNDS) {
     const size_t lb = ld_lds_bytes(waves, R, use_lo);
     const dim3 grid(two ? 2 * ncu : ncu), block(waves * 64);
+    const int ns = W.nb / LD_SB;
     if (use_lo) {
-      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<true, 4>), grid, block, lb, s, W, R, img, logits, R);
-      else hipLaunchKernelGGL((k_q8_lmhead_dma<true, 8>), grid, block, lb, s, W, R, img, logits, R);
+      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<true, 4>), grid, block, lb, s, W, W, R, img, logits, R, ns, (size_t)0);
+      else hipLaunchKernelGGL((k_q8_lmhead_dma<true, 8>), grid, block, lb, s, W, W, R, img, logits, R, ns, (size_t)0);
     } else {
-      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<false, 4>), grid, block, lb, s, W, R, img, logits, R);
-      else hipLaunchKernelGGL((k_q8_lmhead_dma<false, 8>), grid, block, lb, s, W, R, img, logits, R);
+      if (two) hipLaunchKernelGGL((k_q8_lmhead_dma<false, 4>), grid, block, lb, s, W, W, R, img, logits, R, ns, (size_t)0);
+      else hipLaunchKernelGGL((k_q8_lmhead_dma<false, 8>), grid, block, lb, s, W, W, R, img, logits, R, ns, (size_t)0);
     }
     return hipGetLastError();
   }
@@ -510,6 +519,32 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
     launch_lm<true, 2>(R, s, W, img, logits);
   else
     launch_lm<false, 2>(R, s, W, img, logits);
+  return hipGetLastError();
+}
+
+int q8_split_parts(int vocab, int hidden, int R, bool use_lo, int nmat) {
+  const int nb = hidden / 32, ns = nb / LD_SB, tiles = (vocab + 15) / 16;
+  if (nb % LD_SB || R > LD_XMAX || ld_lds_bytes(4, R, use_lo) > (size_t)160 * 1024) return 0;
+  // slices so that the launch has about two blocks per compute unit
+  const int bx = (tiles + 3) / 4, want = 2 * cu_count();
+  int sl = (want + bx * nmat - 1) / (bx * nmat);
+  sl = sl < 1 ? 1 : (sl > ns ? ns : sl);
+  const int sp = (ns + sl - 1) / sl;
+  return (ns + sp - 1) / sp;
+}
+
+hipError_t launch_q8_split(const void* w1, const void* w2, int vocab, int hidden, int R, bool use_lo, XImg img,
+                           float* part, hipStream_t s) {
+  const int nmat = w2 ? 2 : 1, parts = q8_split_parts(vocab, hidden, R, use_lo, nmat);
+  if (parts == 0) return hipErrorInvalidValue;
+  const Q8View W1 = q8_view(w1, vocab, hidden), W2 = w2 ? q8_view(w2, vocab, hidden) : W1;
+  const int ns = W1.nb / LD_SB, sp = (ns + parts - 1) / parts, tiles = (vocab + 15) / 16;
+  const dim3 grid((tiles + 3) / 4, parts, nmat), block(256);
+  const size_t lb = ld_lds_bytes(4, R, use_lo), zs = (size_t)parts * R * vocab;
+  if (use_lo)
+    hipLaunchKernelGGL((k_q8_lmhead_dma<true, 4>), grid, block, lb, s, W1, W2, R, img, part, R, sp, zs);
+  else
+    hipLaunchKernelGGL((k_q8_lmhead_dma<false, 4>), grid, block, lb, s, W1, W2, R, img, part, R, sp, zs);
   return hipGetLastError();
 }
 

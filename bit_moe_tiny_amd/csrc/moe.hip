@@ -66,9 +66,10 @@ size_t moe_ws_layout(const sv_moe_desc* d, int R, void* base, MoeWs* out) {
   const bool q8s = shared_q8(d);
   void* sxb = take(q8s ? ximg_bytes(R, d->hidden, XL_PLAIN) : 0);
   void* shb = take(q8s ? ximg_bytes(R, d->inter, XL_PLAIN) : 0);
-  w.sg = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
-  w.su = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
-  w.sh = (float*)take(q8s ? sizeof(float) * (size_t)R * d->inter : 0);
+  // at most one slice per 512-wide stage of K
+  w.sgu = (float*)take(q8s ? sizeof(float) * 2 * (size_t)(d->hidden / 512 + 1) * R * d->inter : 0);
+  w.sdn = (float*)take(q8s ? sizeof(float) * (size_t)(d->inter / 512 + 1) * R * d->hidden : 0);
+  w.sp_gu = w.sp_dn = 0;
   if (p) {
     if (!plain) w.xd = xdig_carve(xd, R, d->hidden);
     if (!plain) w.hd = xdig_carve(hd, max_assign, d->inter);
@@ -646,8 +647,10 @@ __device__ __forceinline__ void xl_img_dma(const XImg& img, const int* rows, int
 
 // --------------------------------------------------------------- combine
 // y[r, n] = sum_{s<k} w[r, s] * part[a(r, s), n] (+ part[a(r, shared), n]), in slot order.
-__global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_shared, MoeWs ws,
-                                                     float* y) {
+// The eight-bit shared expert's output is the sum of its down slices
+// (sdn_parts of them, in order; 0: a two-bit shared expert, in ws.part).
+__global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_shared, int sdn_parts, int R,
+                                                     MoeWs ws, float* y) {
   __shared__ int s_a[SV_MAX_TOPK + 1];
   __shared__ float s_w[SV_MAX_TOPK];
   const int r = blockIdx.y, tid = threadIdx.x;
@@ -660,7 +663,19 @@ __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_
   float4 v[SV_MAX_TOPK + 1];
 #pragma unroll
   for (int s = 0; s <= SV_MAX_TOPK; ++s)
-    if (s < ns) v[s] = *(const float4*)(ws.part + (size_t)s_a[s] * hidden + 4 * n4);
+    if (s < ns && !(s == k && sdn_parts > 0)) v[s] = *(const float4*)(ws.part + (size_t)s_a[s] * hidden + 4 * n4);
+  if (has_shared && sdn_parts > 0) {
+    const float* sp = ws.sdn + (size_t)r * hidden + 4 * n4;
+    float4 a = *(const float4*)sp;
+    for (int p = 1; p < sdn_parts; ++p) {
+      const float4 b = *(const float4*)(sp + (size_t)p * R * hidden);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    v[k] = a;
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int s = 0; s <= SV_MAX_TOPK; ++s) {
@@ -680,16 +695,41 @@ __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_
 }
 
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
+  const int sdn_parts = shared_q8(d) ? (ws.sp_dn > 0 ? ws.sp_dn : 1) : 0;
   hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden / 4 + 255) / 256, R), dim3(256), 0, s,
-                     d->hidden, d->top_k, d->s_gate ? 1 : 0, ws, y);
+                     d->hidden, d->top_k, d->s_gate ? 1 : 0, sdn_parts, R, ws, y);
   return hipGetLastError();
 }
 
 // ------------------------------------------------ eight-bit shared expert
-// h = silu(g) * u over the R x inter outputs of the shared gate / up products.
-__global__ __launch_bounds__(256) void k_swiglu_rows(const float* g, const float* u, float* h, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) h[i] = silu_mul(g[i], u[i]);
+// The products run on the vocabulary head's kernel split over K (the shared
+// expert's 2048-row matrices alone would occupy few compute units), or
+// unsplit where the split form does not take the shape (one slice).
+void plan_shared_q8(const sv_moe_desc* d, int R, int x_dtype, MoeWs* ws) {
+  ws->sp_gu = q8_split_parts(d->inter, d->hidden, R, x_dtype == SV_F32, 2);
+  ws->sp_dn = q8_split_parts(d->hidden, d->inter, R, true, 1);
+}
+
+// Stages h = silu(g) * u of the shared expert for the down product, g and u
+// summed over their K slices in order as they are loaded.
+__global__ __launch_bounds__(256) void k_stage_swiglu(const float* gu, int parts, int R, XImg img) {
+  __shared__ int sh[8];
+  const int I = img.K, row = blockIdx.x;
+  const size_t ps = (size_t)R * I;
+  const float* g = gu + (size_t)row * I;
+  const float* u = g + (size_t)parts * ps;
+  stage_row_l<256>(row, XL_PLAIN, img, sh, [&](int k, float* v) {
+    float4 a = *(const float4*)(g + k), b = *(const float4*)(u + k);
+    for (int p = 1; p < parts; ++p) {
+      const float4 a2 = *(const float4*)(g + p * ps + k), b2 = *(const float4*)(u + p * ps + k);
+      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+      b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+    }
+    v[0] = silu_mul(a.x, b.x);
+    v[1] = silu_mul(a.y, b.y);
+    v[2] = silu_mul(a.z, b.z);
+    v[3] = silu_mul(a.w, b.w);
+  });
 }
 
 hipError_t launch_shared_q8(const sv_moe_desc* d, int R, const void* x, int x_dtype, MoeWs ws,
@@ -698,14 +738,19 @@ hipError_t launch_shared_q8(const sv_moe_desc* d, int R, const void* x, int x_dt
   hipError_t e = launch_stage(x, x_dtype, R, H, XL_PLAIN, nullptr, ws.sx_img, s);
   if (e != hipSuccess) return e;
   const bool lo = x_dtype == SV_F32;   // bf16 rows are exact in the fp16 high part
-  if ((e = launch_q8_lmhead(d->s_gate, I, H, R, lo, ws.sx_img, ws.sg, s)) != hipSuccess) return e;
-  if ((e = launch_q8_lmhead(d->s_up, I, H, R, lo, ws.sx_img, ws.su, s)) != hipSuccess) return e;
-  const int n = R * I;
-  hipLaunchKernelGGL(k_swiglu_rows, dim3((n + 255) / 256), dim3(256), 0, s, ws.sg, ws.su, ws.sh, n);
+  int pg = ws.sp_gu;
+  if (pg > 0) {
+    e = launch_q8_split(d->s_gate, d->s_up, I, H, R, lo, ws.sx_img, ws.sgu, s);
+  } else {
+    pg = 1;
+    if ((e = launch_q8_lmhead(d->s_gate, I, H, R, lo, ws.sx_img, ws.sgu, s)) != hipSuccess) return e;
+    e = launch_q8_lmhead(d->s_up, I, H, R, lo, ws.sx_img, ws.sgu + (size_t)R * I, s);
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_stage_swiglu, dim3(R), dim3(256), 0, s, ws.sgu, pg, R, ws.sh_img);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_stage(ws.sh, SV_F32, R, I, XL_PLAIN, nullptr, ws.sh_img, s)) != hipSuccess) return e;
-  // the shared assignments are R*k .. R*k+R-1, row r at R*k + r
-  return launch_q8_lmhead(d->s_down, H, I, R, true, ws.sh_img, ws.part + (size_t)R * d->top_k * H, s);
+  if (ws.sp_dn > 0) return launch_q8_split(d->s_down, nullptr, H, I, R, true, ws.sh_img, ws.sdn, s);
+  return launch_q8_lmhead(d->s_down, H, I, R, true, ws.sh_img, ws.sdn, s);
 }
 
 // ----------------------------------------------------------------- plain

@@ -372,10 +372,12 @@ struct MoeWs {
   XDig hd;            // the down projection's input rows as digits  [max_assign, inter]
   XDig xd;            // x as digits  [R, hidden]
   XImg x_img;         // x staged for the one-matrix (PLAIN) path  [R, hidden]
-  // eight-bit shared expert: x and h staged for the head kernels, the
-  // gate / up outputs and h = silu(g) * u, all [R, *]
+  // eight-bit shared expert: x and h staged for the head kernels; the gate and
+  // up products as sums of sp_gu slices over K ([2][sp_gu][R, inter]), the
+  // down product as sp_dn slices ([sp_dn][R, hidden])
   XImg sx_img, sh_img;
-  float *sg, *su, *sh;
+  float *sgu, *sdn;
+  int sp_gu, sp_dn;
   int max_units, max_assign, max_work;
 };
 
@@ -407,10 +409,17 @@ hipError_t launch_moe_gateup(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t 
 hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
 hipError_t launch_moe_down(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s);
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s);
-// The eight-bit shared expert: its outputs into the shared assignments' rows
-// of ws.part.
+// The eight-bit shared expert: its K-slice counts (ws->sp_gu, sp_dn), then its
+// products into ws.sgu / ws.sdn (k_moe_combine adds the down slices).
+void plan_shared_q8(const sv_moe_desc* d, int R, int x_dtype, MoeWs* ws);
 hipError_t launch_shared_q8(const sv_moe_desc* d, int R, const void* x, int x_dtype, MoeWs ws,
                             hipStream_t s);
+// K slices of the head kernel's split form for [vocab x hidden] on R rows and
+// nmat matrices (0: the split form does not take this shape), and its launch
+// (w2 may be null): partial products [nmat][slices][R, vocab] into part.
+int q8_split_parts(int vocab, int hidden, int R, bool use_lo, int nmat);
+hipError_t launch_q8_split(const void* w1, const void* w2, int vocab, int hidden, int R, bool use_lo, XImg img,
+                           float* part, hipStream_t s);
 // Whether the streamed int8 expert kernels take this layer (LDS limits).
 bool moe_shape_ok(const sv_moe_desc* d);
 hipError_t launch_q2_tile(const void* src, void* dst, int n_out, int k_in, int parts, int count, hipStream_t s);

@@ -45,24 +45,23 @@ __device__ __forceinline__ int row_exponent(float mx, int bad) {
 
 constexpr int XIMG_MAX_K = 16384;   // longest row the staging routines take
 
-// The whole thread block (NT threads) stages row `row` of src ([rows, K],
-// row-major).  Every element is loaded once, into registers, with all loads
-// in flight together: half-wave h takes 256-element blocks h, h + NT/32, ...
+// The whole thread block (NT threads) stages row `row` of an activation
+// matrix [rows, K] whose elements load4(k, v) reads (4 consecutive elements of
+// the row from element k).  Every element is loaded once, into registers, with
+// all loads in flight together: half-wave h takes 256-element blocks h, h + NT/32, ...
 // (PERM: lane (t, g) holds elements 16 s + 4 hs + j and 16 s + 4 hs + 8 + j,
 // j = 0..3, of sub-block s = 4 g + t/2, hs = t & 1; PLAIN: lane l holds
 // elements 8 l .. 8 l + 7).  The row's largest magnitude is reduced over the
 // block (its power-of-two scale), then each lane converts its own elements;
 // a sub-block's 16-element sum is the lane's 8 plus those of lane l ^ 4.
-template <int DT, int NT>
-__device__ inline void stage_row(const void* src, int row, int layout, const XImg& img, int* sh) {
+template <int NT, class LOAD4>
+__device__ inline void stage_row_l(int row, int layout, const XImg& img, int* sh, LOAD4 load4) {
   constexpr int NHW = NT / 32, MAXB = (XIMG_MAX_K / 256 + NHW - 1) / NHW;
   const int K = img.K, nbk = (K + 255) / 256;
   const int l = threadIdx.x & 31, hw = threadIdx.x >> 5;
   const bool perm = layout == XL_PERM;
   const int t = l >> 2, g = l & 3, s = 4 * g + (t >> 1), hs = t & 1;
   const size_t base = (size_t)row * K;
-  const void* rs = DT == SV_BF16 ? (const void*)((const uint16_t*)src + base)
-                                 : (const void*)((const float*)src + base);
   float v[MAXB][8];
   float mx = 0.f;
   int bad = 0;
@@ -75,16 +74,16 @@ __device__ inline void stage_row(const void* src, int row, int layout, const XIm
       const int k0 = kb * 256;
       if (perm) {
         float a[4], b[4];
-        load4_act<DT>(rs, k0 + 16 * s + 4 * hs, a);
-        load4_act<DT>(rs, k0 + 16 * s + 4 * hs + 8, b);
+        load4(k0 + 16 * s + 4 * hs, a);
+        load4(k0 + 16 * s + 4 * hs + 8, b);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           v[i][2 * j] = a[j];
           v[i][2 * j + 1] = b[j];
         }
       } else if (k0 + 8 * l < K) {
-        load4_act<DT>(rs, k0 + 8 * l, v[i]);
-        load4_act<DT>(rs, k0 + 8 * l + 4, v[i] + 4);
+        load4(k0 + 8 * l, v[i]);
+        load4(k0 + 8 * l + 4, v[i] + 4);
       }
     }
   }
@@ -143,6 +142,15 @@ __device__ inline void stage_row(const void* src, int row, int layout, const XIm
     }
   }
   if (threadIdx.x == 0) img.rscale[row] = ldexpf(1.f, -esc);
+}
+
+// Row `row` of src ([rows, K] in element type DT).
+template <int DT, int NT>
+__device__ inline void stage_row(const void* src, int row, int layout, const XImg& img, int* sh) {
+  const size_t base = (size_t)row * img.K;
+  const void* rs = DT == SV_BF16 ? (const void*)((const uint16_t*)src + base)
+                                 : (const void*)((const float*)src + base);
+  stage_row_l<NT>(row, layout, img, sh, [&](int k, float* v) { load4_act<DT>(rs, k, v); });
 }
 
 }  // namespace sv
