@@ -29,10 +29,12 @@
 //                 from the chunk totals, the segment inside it from the
 //                 per-thread sums, and the token among that segment's
 //                 entries, then writes the outputs.
-//   k_tsm_sample  (target-sample matching) grid (512-entry chunk, target row):
-//                 the same chunk sums for p of one row; the last block of a row
-//                 samples it; the last row of a sequence to be sampled takes
-//                 the prefix of matching drafts and writes the outputs.
+//   k_tsm_pick    (target-sample matching) one block per target row: the
+//                 row's masses per statistics chunk (its chunk sums rescaled
+//                 to the row maximum) locate the chunk holding u Z, the block
+//                 finds the token among that chunk's 2048 entries; the last
+//                 row of a sequence to be sampled takes the prefix of
+//                 matching drafts and writes the outputs.
 #include "sv_internal.h"
 
 namespace sv {
@@ -426,11 +428,12 @@ __device__ inline void find_chunk(const double* cws, int CHs, double u, double* 
 // weights parts[0..ACC_T) of that chunk in LDS: the thread segment whose
 // running sum (from base) first exceeds tt, then the entry inside it, failing
 // that (rounding) the last entry with weight of the segment, of the chunk.
+template <int PER = SMP_PER>
 __device__ inline int seg_token(const double* parts, double base, bool found_chunk, double tt, int hit,
                                 int mode, const RowSrc& P, double pm, double pz, const RowSrc& Q, double qm,
                                 double qz, int V) {
   const int lane = threadIdx.x & 63;
-  constexpr int TPL = ACC_T / 64;
+  constexpr int TPL = ACC_T / 64, CHUNK = ACC_T * PER;
   double ptot;
   const double prun = base + wave_prefix(parts, ACC_T, TPL, &ptot);
   double tpre = 0.0;
@@ -443,8 +446,8 @@ __device__ inline int seg_token(const double* parts, double base, bool found_chu
     double run = tpre;
     int lp = -1;
 #pragma unroll
-    for (int i = 0; i < SMP_PER; ++i) {
-      const int x = hit * SMP_CHUNK + thr * SMP_PER + i;
+    for (int i = 0; i < PER; ++i) {
+      const int x = hit * CHUNK + thr * PER + i;
       if (x < V) {
         const double wi = sample_weight(mode, P, pm, pz, Q, qm, qz, x);
         run += wi;
@@ -458,8 +461,8 @@ __device__ inline int seg_token(const double* parts, double base, bool found_chu
     // (rounding put the crossing in a segment without weight) the chunk's
     // last entry with weight
     int lp = -1;
-    for (int i = lane; i < SMP_CHUNK; i += 64) {
-      const int x = hit * SMP_CHUNK + i;
+    for (int i = lane; i < CHUNK; i += 64) {
+      const int x = hit * CHUNK + i;
       if (x < V && sample_weight(mode, P, pm, pz, Q, qm, qz, x) > 0.0) lp = x;
     }
     for (int o = 32; o >= 1; o >>= 1) lp = max(lp, __shfl_xor(lp, o, 64));
@@ -615,13 +618,12 @@ struct TsmWs {
   double* cmax;     // [rows, CH]
   double* csum;     // [rows, CH]
   int* cbad;        // [rows, CH]
-  double* rsum;     // [rows, CHs]  p mass per sampling chunk
-  int* tok;         // [rows]       each row's sample (-1: invalid row or uniform)
-  unsigned* done;   // [rows + S]   blocks of each row done, then rows of each sequence done
+  int* tok;         // [rows]  each row's sample (-1: invalid row or uniform)
+  unsigned* done;   // [S]     rows of each sequence sampled
 };
 
 static TsmWs tsm_carve(void* base, int S, int K, int V) {
-  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
+  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V);
   uint8_t* p = (uint8_t*)base;
   TsmWs w;
   w.cmax = (double*)p;
@@ -630,8 +632,6 @@ static TsmWs tsm_carve(void* base, int S, int K, int V) {
   p += up256(rows * CH * 8);
   w.cbad = (int*)p;
   p += up256(rows * CH * 4);
-  w.rsum = (double*)p;
-  p += up256(rows * CHs * 8);
   w.tok = (int*)p;
   p += up256(rows * 4);
   w.done = (unsigned*)p;
@@ -639,9 +639,8 @@ static TsmWs tsm_carve(void* base, int S, int K, int V) {
 }
 
 size_t accept_tsm_ws_bytes(int S, int K, int V) {
-  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
-  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256(rows * CHs * 8) + up256(rows * 4) +
-         up256((rows + S) * 4);
+  const size_t rows = (size_t)S * (K + 1), CH = acc_chunks(V);
+  return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256(rows * 4) + up256((size_t)S * 4);
 }
 
 // Row r's statistics from its chunk statistics, by wave 0 (the same
@@ -667,24 +666,26 @@ __device__ inline void tsm_row_stats(int r, int CH, int kind, const TsmWs& ws, d
   *bad = (__any(cb) ? 1 : 0) | (kind == SV_PROBS ? !(*z > 0.0) : 0);
 }
 
-__global__ __launch_bounds__(ACC_T) void k_tsm_sample(int S, int K, int V, int CH, const float* target,
-                                                      int tkind, float Tp, const int32_t* drafts,
-                                                      const float* uni, int32_t* out_tokens, int32_t* out_n,
-                                                      TsmWs ws) {
-  __shared__ double sh[4];
-  __shared__ double cws[SMP_MAX_CH];   // the last block of the row: chunk totals
-  __shared__ double parts[ACC_T];      // the last block of the row: the hit chunk's segment totals
+__global__ __launch_bounds__(ACC_T) void k_tsm_pick(int S, int K, int V, int CH, const float* target,
+                                                    int tkind, float Tp, const int32_t* drafts, const float* uni,
+                                                    int32_t* out_tokens, int32_t* out_n, TsmWs ws) {
+  __shared__ double cws[ACC_MAX_CH];   // the row's mass per statistics chunk
+  __shared__ double parts[ACC_T];      // the hit chunk's mass per 8-entry thread segment
   __shared__ double s_m, s_zr, s_z, s_base;
-  __shared__ int s_bad, s_last, s_hit, s_found;
-  const int c = blockIdx.x, r = blockIdx.y, CHs = gridDim.x;
-  const int s = r / (K + 1), i = r - s * (K + 1);
+  __shared__ int s_bad, s_hit, s_found;
+  const int r = blockIdx.x, s = r / (K + 1), i = r - s * (K + 1);
   const int tid = threadIdx.x, lane = tid & 63;
-  const int rows = S * (K + 1);
-  // 1. the row's statistics
+  constexpr int PER = ACC_CHUNK / ACC_T;
+  // 1. the row's statistics and its mass per chunk: the chunk sums rescaled
+  //    to the row's maximum (unnormalised, like the entry weights below)
   if (tid < 64) {
     double m, z;
     int bad;
     tsm_row_stats(r, CH, tkind, ws, &m, &z, &bad);
+    for (int c = lane; c < CH; c += 64) {
+      const size_t o = (size_t)r * CH + c;
+      cws[c] = tkind == SV_LOGITS ? ws.csum[o] * exp(ws.cmax[o] - m) : ws.csum[o];
+    }
     if (lane == 0) {
       s_m = m;
       s_zr = z;
@@ -696,44 +697,34 @@ __global__ __launch_bounds__(ACC_T) void k_tsm_sample(int S, int K, int V, int C
   P.p = target + (size_t)r * V;
   P.kind = tkind;
   P.T = (double)Tp;
-  const double pm = s_m, pz = s_zr;
-  const int bad = s_bad;
-  // 2. this chunk's mass of p; the last block of the row to finish samples it
-  //    (publication as in k_acc_sample: thread 0 stores the sum and counts
-  //    the block done with an acquire-release increment at device scope; the
-  //    last block acquires before its reads)
-  double w = bad ? 0.0 : seg_weight(MODE_P, P, pm, pz, P, 0.0, 1.0, c, V);
-  w = block_sum_d(w, sh);
-  if (tid == 0) {
-    __hip_atomic_store(&ws.rsum[(size_t)r * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = __hip_atomic_fetch_add(&ws.done[r], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(CHs - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // 3. row r's sample at u_i (block-uniform branch)
+  // 2. row r's sample at u_i (block-uniform branches): a greedy row's token is
+  //    its first maximum; otherwise the chunk holding u Z, then the entry
   const float uf = uni[(size_t)s * (K + 1) + i];
-  const bool ok = !bad && uf >= 0.f && uf < 1.f;
+  const bool ok = !s_bad && uf >= 0.f && uf < 1.f;
   int tok = -1;
-  if (ok) {
-    for (int cc = tid; cc < CHs; cc += ACC_T)
-      cws[cc] = __hip_atomic_load(&ws.rsum[(size_t)r * CHs + cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    find_chunk(cws, CHs, (double)uf, &s_z, &s_found, &s_hit, &s_base);
-    parts[tid] = seg_weight(MODE_P, P, pm, pz, P, 0.0, 1.0, s_hit, V);
+  if (ok && tkind == ACC_ARGMAX) {
+    tok = (int)s_zr;
+  } else if (ok) {
+    find_chunk(cws, CH, (double)uf, &s_z, &s_found, &s_hit, &s_base);
+    double w = 0.0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int x = s_hit * ACC_CHUNK + tid * PER + e;
+      if (x < V) w += sample_weight(MODE_P, P, s_m, 1.0, P, 0.0, 1.0, x);
+    }
+    parts[tid] = w;
     __syncthreads();
     if (tid < 64)
-      tok = seg_token(parts, s_base, s_found, (double)uf * s_z, s_hit, MODE_P, P, pm, pz, P, 0.0, 1.0, V);
+      tok = seg_token<PER>(parts, s_base, s_found, (double)uf * s_z, s_hit, MODE_P, P, s_m, 1.0, P, 0.0, 1.0, V);
   }
   if (tid >= 64) return;
-  // 4. publish it (the same lane stores it and counts the row done with an
+  // 3. publish it (the same lane stores it and counts the row done with an
   //    acquire-release increment); the last row of the sequence to be
   //    sampled decides, after an acquire of its own wave
   unsigned prev = 0;
   if (lane == 0) {
     __hip_atomic_store(&ws.tok[r], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __hip_atomic_fetch_add(&ws.done[rows + s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
   }
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != (unsigned)K) return;
@@ -765,15 +756,15 @@ hipError_t launch_accept_tsm(int S, int K, int V, const float* target, int tkind
   aw.csum = tw.csum;
   aw.cbad = tw.cbad;
   aw.done = tw.done;
-  const int CH = acc_chunks(V), CHs = smp_chunks(V), rows = S * (K + 1);
+  const int CH = acc_chunks(V), rows = S * (K + 1);
   if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
   // target rows only (row index < S (K+1)); no draft rows are read
   hipLaunchKernelGGL(k_acc_stats, dim3(CH, rows), dim3(256), 0, s, S, K, V, target, tkind, Tp,
-                     (const float*)nullptr, tkind, Tp, aw, rows + S);
+                     (const float*)nullptr, tkind, Tp, aw, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_tsm_sample, dim3(CHs, rows), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind, Tp,
-                     drafts, u, out_tokens, out_n, tw);
+  hipLaunchKernelGGL(k_tsm_pick, dim3(rows), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind, Tp, drafts, u,
+                     out_tokens, out_n, tw);
   return hipGetLastError();
 }
 
