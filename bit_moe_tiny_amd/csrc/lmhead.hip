@@ -352,7 +352,7 @@ static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
 // sp) of matrix z (W, or W2 for z = 1) and writes its partial products to
 // logits + z zstride + y R vocab (one [R, vocab] slice per y).  The head
 // runs it with one slice (sp = all stages) and one matrix.
-template <bool USE_LO, int LD_WAVES>
+template <bool USE_LO, int LD_WAVES, int MAXR = LD_MAX_ROUNDS>
 __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W1, Q8View W2, int R,
                                                                                XImg img, float* logits,
                                                                                int ncols, int sp, size_t zstride) {
@@ -406,14 +406,14 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
   // Stage-major: for each 512-k stage, every round's tile in turn, so a
   // stage's activation columns are copied once per block (not once per
   // round); each round keeps its own accumulator.
-  f4_t acc[LD_MAX_ROUNDS];
+  f4_t acc[MAXR];
 #pragma unroll
-  for (int r = 0; r < LD_MAX_ROUNDS; ++r) acc[r] = zero;
+  for (int r = 0; r < MAXR; ++r) acc[r] = zero;
   issue(st0, 0, 0, st0 & 1);
   int k = 0;   // running step count: weight buffer k & 1
   for (int st = st0; st < ns; ++st) {
 #pragma unroll
-    for (int r = 0; r < LD_MAX_ROUNDS; ++r) {
+    for (int r = 0; r < MAXR; ++r) {
       if (r >= rounds) break;
       // this wave's copies of step k are done; after the barrier everyone's
       // are, and every wave is past step k-1 (whose buffers the next copies
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
     }
   }
 #pragma unroll
-  for (int r = 0; r < LD_MAX_ROUNDS; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     if (r >= rounds) break;
     const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
     const int n = tile * 16 + nl;
@@ -503,6 +503,26 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
       else hipLaunchKernelGGL((k_q8_lmhead_dma<false, 8>), grid, block, lb, s, W, W, R, img, logits, R, ns, (size_t)0);
     }
     return hipGetLastError();
+  }
+  // 9..16 rows (hi only; 5..8 with remainder planes): one block of seven
+  // waves per CU, its activation buffer taking the LDS of the eighth wave's
+  // weights; up to eight tiles per wave (the matrix-core tile has 16 columns,
+  // so the work per weight is that of 8 rows)
+  {
+    constexpr int W7 = 7;
+    const long rounds7 = ((vocab + 15) / 16 + (long)ncu * W7 - 1) / ((long)ncu * W7);
+    if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX : 2 * LD_XMAX) && rounds7 <= 2 * LD_MAX_ROUNDS &&
+        ld_lds_bytes(W7, R, use_lo) <= (size_t)160 * 1024) {
+      const size_t lb = ld_lds_bytes(W7, R, use_lo);
+      const int ns = W.nb / LD_SB;
+      if (use_lo)
+        hipLaunchKernelGGL((k_q8_lmhead_dma<true, W7, 2 * LD_MAX_ROUNDS>), dim3(ncu), dim3(W7 * 64), lb, s, W, W, R,
+                           img, logits, R, ns, (size_t)0);
+      else
+        hipLaunchKernelGGL((k_q8_lmhead_dma<false, W7, 2 * LD_MAX_ROUNDS>), dim3(ncu), dim3(W7 * 64), lb, s, W, W, R,
+                           img, logits, R, ns, (size_t)0);
+      return hipGetLastError();
+    }
   }
   // (groups in pairs; windows of LM_WIN_GROUPS groups when K does not fit)
   if (W.nb % (8 * LM_WIN_GROUPS) == 0) {
