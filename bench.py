@@ -360,7 +360,7 @@ def next_rows(sv, step, wroute):
 KERNEL_KEYS = {"gate/up": "k_gu8", "down": "k_dn8", "down input digits": "k_hdig", "routing": "k_moe_prep",
                "combine": "k_moe_combine", "head": "k_q8_lmhead", "head staging": "k_stage",
                "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample",
-               "target-sample matching": "k_tsm_sample", "shared expert h staging": "k_stage_swiglu"}
+               "target-sample matching": "k_tsm_pick", "shared expert h staging": "k_stage_swiglu"}
 
 
 def kernel_times(step, steps: int = 10):

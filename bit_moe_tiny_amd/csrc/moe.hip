@@ -647,8 +647,10 @@ __device__ __forceinline__ void xl_img_dma(const XImg& img, const int* rows, int
 
 // --------------------------------------------------------------- combine
 // y[r, n] = sum_{s<k} w[r, s] * part[a(r, s), n] (+ part[a(r, shared), n]), in slot order.
-// The eight-bit shared expert's output is the sum of its down slices
-// (sdn_parts of them, in order; 0: a two-bit shared expert, in ws.part).
+// SQ8: the shared expert is eight-bit and its output the sum of its
+// sdn_parts down slices (in order); otherwise it is in ws.part like the
+// routed ones.
+template <bool SQ8>
 __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_shared, int sdn_parts, int R,
                                                      MoeWs ws, float* y) {
   __shared__ int s_a[SV_MAX_TOPK + 1];
@@ -663,8 +665,8 @@ __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_
   float4 v[SV_MAX_TOPK + 1];
 #pragma unroll
   for (int s = 0; s <= SV_MAX_TOPK; ++s)
-    if (s < ns && !(s == k && sdn_parts > 0)) v[s] = *(const float4*)(ws.part + (size_t)s_a[s] * hidden + 4 * n4);
-  if (has_shared && sdn_parts > 0) {
+    if (s < (SQ8 ? k : ns)) v[s] = *(const float4*)(ws.part + (size_t)s_a[s] * hidden + 4 * n4);
+  if (SQ8) {
     const float* sp = ws.sdn + (size_t)r * hidden + 4 * n4;
     float4 a = *(const float4*)sp;
     for (int p = 1; p < sdn_parts; ++p) {
@@ -695,9 +697,13 @@ __global__ __launch_bounds__(256) void k_moe_combine(int hidden, int k, int has_
 }
 
 hipError_t launch_moe_combine(const sv_moe_desc* d, int R, MoeWs ws, float* y, hipStream_t s) {
-  const int sdn_parts = shared_q8(d) ? (ws.sp_dn > 0 ? ws.sp_dn : 1) : 0;
-  hipLaunchKernelGGL(k_moe_combine, dim3((d->hidden / 4 + 255) / 256, R), dim3(256), 0, s,
-                     d->hidden, d->top_k, d->s_gate ? 1 : 0, sdn_parts, R, ws, y);
+  const dim3 grid((d->hidden / 4 + 255) / 256, R);
+  if (shared_q8(d))
+    hipLaunchKernelGGL(k_moe_combine<true>, grid, dim3(256), 0, s, d->hidden, d->top_k, 1,
+                       ws.sp_dn > 0 ? ws.sp_dn : 1, R, ws, y);
+  else
+    hipLaunchKernelGGL(k_moe_combine<false>, grid, dim3(256), 0, s, d->hidden, d->top_k, d->s_gate ? 1 : 0, 0, R,
+                       ws, y);
   return hipGetLastError();
 }
 
