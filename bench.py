@@ -258,58 +258,37 @@ def entry(R, S, m):
             "moe_GB/s": round(float(m["moe_bytes"].sum() / (m["moe_ms"].sum() / 1e3) / 1e9), 1)}
 
 
-def launch_floor(n_launch: int, reps: int = 200):
-    """Time of n_launch back-to-back minimal kernel launches on the current
-    stream (a one-element fill each), median over reps: the fixed cost every
-    call of that many kernels pays whatever its size."""
-    import torch
-    t = torch.empty(1, dtype=torch.float32, device="cuda")
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(n_launch):
-            t.fill_(1.0)
-        e1.record()
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    return float(np.median(ts)) * 1e3
-
-
-def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24, reps: int = 48):
+def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24):
     """Config C1 shape: one SwiGLU expert (E = 1, no shared) with all R rows.
-    The calls rotate over `copies` resident experts (24 x 14.45 MB exceeds
-    the 256 MB last-level cache, so the weights stream from HBM); median of
-    the event-timed calls, beside the floor of the same number of empty
-    launches (the call is 5 kernels)."""
+    One timed unit is `copies` calls back to back, each on its own resident
+    expert (24 x 14.45 MB exceeds the 256 MB last-level cache, so the weights
+    stream from HBM), run eagerly and as a captured graph; the per-call time is
+    the unit's median over the copies.  Eager calls of this size are bound by
+    the host's launch rate, so `frac` is taken from the graph replay."""
     import torch
     wg, wu, wd = desc._keep[0], desc._keep[1], desc._keep[2]
     gu, dn = sv.sv_q2_tiled_bytes(synth.INTER, synth.HIDDEN), sv.sv_q2_tiled_bytes(synth.HIDDEN, synth.INTER)
     descs = [sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, 1, 1, wg[e * gu:(e + 1) * gu],
                          wu[e * gu:(e + 1) * gu], wd[e * dn:(e + 1) * dn], tiled=True)
              for e in range(copies)]
-    floor = launch_floor(5)
     out = []
     for R in Rs:
         x = to_dev(synth.expert(R).x_bf16)
         y = torch.empty((R, synth.HIDDEN), dtype=torch.float32, device="cuda")
         ws = torch.empty(sv.sv_moe_workspace_bytes(descs[0], R), dtype=torch.uint8, device="cuda")
-        for d in descs:   # warm-up
-            sv.vq2_moe_gemm(d, x, None, y, ws=ws)
+
+        def unit():
+            for d in descs:
+                sv.vq2_moe_gemm(d, x, None, y, ws=ws)
+
+        eager, graph = time_eager_and_graph(unit, reps=12)
+        us_e, us_g = eager / copies, graph / copies
+        out.append({"R": R, "us_eager": round(us_e, 2), "us": round(us_g, 2),
+                    "GB/s": round(Q2_EXPERT_BYTES / us_g / 1e3, 1),
+                    "frac": round(Q2_EXPERT_BYTES / us_g / 1e3 / PEAK_HBM_GBS, 4)})
+        del ws, x, y
         torch.cuda.synchronize()
-        ts = []
-        for i in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            sv.vq2_moe_gemm(descs[i % copies], x, None, y, ws=ws)
-            e1.record()
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        us = float(np.median(ts)) * 1e3
-        out.append({"R": R, "us": round(us, 2), "GB/s": round(Q2_EXPERT_BYTES / us / 1e3, 1),
-                    "frac": round(Q2_EXPERT_BYTES / us / 1e3 / PEAK_HBM_GBS, 4)})
-    return {"bytes": Q2_EXPERT_BYTES, "launches": 5, "empty_launch_floor_us": round(floor, 2),
-            "rows": out}
+    return {"bytes": Q2_EXPERT_BYTES, "launches": 5, "calls_per_unit": copies, "rows": out}
 
 
 def event_median(call, reps: int = 40) -> float:

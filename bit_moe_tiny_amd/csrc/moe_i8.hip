@@ -107,31 +107,32 @@ bool moe_shape_ok(const sv_moe_desc* d) {
 __device__ __forceinline__ bool m8_pair(int kb, int b1) { return !(kb & 1) && kb + 1 < b1; }
 
 // The M8_DMA wave instructions of one step: the chunk at p (1344 bytes per
-// block) into the slot at LDS byte address sa, lane l copying 16 bytes at
-// offset 16 l of each piece: pairs as pieces of 1024, 1024 and 640 bytes
-// (lanes < 40), single blocks as three pieces of 448 bytes (lanes < 28).
-// Every instruction has active lanes, so each one counts once in vmcnt.
-__device__ __forceinline__ void m8_issue(const uint8_t* p, bool pair, uint32_t voff, bool lt40, bool lt28,
-                                         uint32_t sa) {
+// block) into the slot at LDS byte address sa, every lane copying 16 bytes
+// at offset 16 lane of each 1 KB piece.  A pair (2688 bytes, whole 128-byte
+// lines, non-temporal) is read as the pieces at 0, 1024 and 1664, a single
+// block (1344 bytes) as the pieces at 0, 160 and 320: the last piece
+// overlaps the one before it inside the chunk (those bytes land twice, with
+// the same values), so every lane of every instruction copies bytes of the
+// chunk into the chunk's place in the slot, with no lane masked.
+__device__ __forceinline__ void m8_issue(const uint8_t* p, bool pair, uint32_t voff, uint32_t sa) {
   if (pair) {
     dma16s_nt(p, voff, sa);
     dma16s_nt(p + 1024, voff, sa + 1024);
-    if (lt40) dma16s_nt(p + 2048, voff, sa + 2048);
-  } else if (lt28) {
+    dma16s_nt(p + 1664, voff, sa + 1664);
+  } else {
     dma16s(p, voff, sa);
-    dma16s(p + 448, voff, sa + 448);
-    dma16s(p + 896, voff, sa + 896);
+    dma16s(p + 160, voff, sa + 160);
+    dma16s(p + 320, voff, sa + 320);
   }
 }
 
-// Placeholder for a step past the end of the wave's work: M8_DMA one-lane
-// loads of 16 valid bytes at p into the slot at sa, which is never read.
-__device__ __forceinline__ void m8_issue_none(const uint8_t* p, uint32_t voff, bool lane0, uint32_t sa) {
-  if (lane0) {
-    dma16s(p, voff, sa);
-    dma16s(p, voff, sa);
-    dma16s(p, voff, sa);
-  }
+// Placeholder for a step past the end of the wave's work: the M8_DMA loads
+// of a single-block step from p (any chunk's first 1344 bytes) into the slot
+// at sa, which is never read.
+__device__ __forceinline__ void m8_issue_none(const uint8_t* p, uint32_t voff, uint32_t sa) {
+  dma16s(p, voff, sa);
+  dma16s(p + 160, voff, sa + 160);
+  dma16s(p + 320, voff, sa + 320);
 }
 
 // The wait before computing a step: the oldest of M8_RING steps in flight is
@@ -257,28 +258,23 @@ __device__ __forceinline__ void m8_step_compute(const uint8_t* slot, int kbl, co
 
 
 // The same loads with one M0 and one base for all pieces of a step: the
-// instruction offset moves the global and the LDS address alike (the pieces
-// are the chunk's consecutive 1024- or 448-byte parts).
-__device__ __forceinline__ void m8_issue_o(const uint8_t* p, bool pair, uint32_t voff, bool lt40, bool lt28,
-                                           uint32_t sa) {
+// instruction offset moves the global and the LDS address alike.
+__device__ __forceinline__ void m8_issue_o(const uint8_t* p, bool pair, uint32_t voff, uint32_t sa) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(sa);
-  if (pair) {
+  if (pair)
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "global_load_lds_dwordx4 %0, %1 nt\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:1024 nt"
+        "global_load_lds_dwordx4 %0, %1 offset:1024 nt\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:1664 nt"
         :: "v"(voff), "s"(p), "s"(m0) : "memory", "m0");
-    if (lt40)
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 offset:2048 nt"
-                   :: "v"(voff), "s"(p), "s"(m0) : "memory", "m0");
-  } else if (lt28) {
+  else
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "global_load_lds_dwordx4 %0, %1\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:448\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:896"
+        "global_load_lds_dwordx4 %0, %1 offset:160\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:320"
         :: "v"(voff), "s"(p), "s"(m0) : "memory", "m0");
-  }
 }
 
 // Step patterns of the items whose block range is four steps long (the
@@ -422,7 +418,6 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8(ExpertPtrs P, int nb, int
   float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_RED;
   const uint32_t voff = 16u * (uint32_t)lane;
-  const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
   const uint8_t* const mroute = mm == 0 ? P.g : P.u;
   const uint8_t* const mshared = mm == 0 ? P.sg : P.su;
 
@@ -486,12 +481,12 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8(ExpertPtrs P, int nb, int
     const uint32_t sa = ring_la + (uint32_t)(lslot * M8_SLOT);
     if (lleft > 0) {
       const bool pair = m8_pair(lkb, lu.b1);
-      m8_issue(lp, pair, voff, lt40, lt28, sa);
+      m8_issue(lp, pair, voff, sa);
       lkb += pair ? 2 : 1;
       lp += pair ? M8_SLOT : M8_CHUNK;
       skip();
     } else {
-      m8_issue_none(pvalid, voff, lane0, sa);
+      m8_issue_none(pvalid, voff, sa);
     }
     lslot = lslot == M8_RING - 1 ? 0 : lslot + 1;
   };
@@ -568,7 +563,6 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8f(ExpertPtrs P, int inter,
   float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_RED;
   const uint32_t voff = 16u * (uint32_t)lane;
-  const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
   const uint8_t* const mroute = mm == 0 ? P.g : P.u;
   const uint8_t* const mshared = mm == 0 ? P.sg : P.su;
 
@@ -616,12 +610,12 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_gu8f(ExpertPtrs P, int inter,
     constexpr int j = decltype(J)::value;
     const uint32_t sa = ring_la + (uint32_t)(j * M8_SLOT);
     if (p == nullptr) {
-      m8_issue_none(P.sg ? P.sg : P.g, voff, lane0, sa);
+      m8_issue_none(P.sg ? P.sg : P.g, voff, sa);
       return;
     }
     const int off = odd ? PO::off(j) : PE::off(j);
     const bool pair = odd ? PO::nb(j) == 2 : PE::nb(j) == 2;
-    m8_issue_o(p + off, pair, voff, lt40, lt28, sa);
+    m8_issue_o(p + off, pair, voff, sa);
   };
 
   GuCur cc = cur_at(i0);
@@ -747,7 +741,6 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_dn8(ExpertPtrs P, int hidden,
   float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_MISC;
   const uint32_t voff = 16u * (uint32_t)lane;
-  const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
   const size_t tile_bytes = (size_t)M8_CHUNK * nbd;   // one 16-row tile
   auto chunk0 = [&](int dsc, int tg) {
     const int e = work[dsc].expert;
@@ -763,7 +756,7 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_dn8(ExpertPtrs P, int hidden,
     const uint32_t sa = ring_la + (uint32_t)(lslot * M8_SLOT);
     if (lleft > 0) {
       const bool pair = m8_pair(lkb, nbd);
-      m8_issue(lp, pair, voff, lt40, lt28, sa);
+      m8_issue(lp, pair, voff, sa);
       lkb += pair ? 2 : 1;
       lp += pair ? M8_SLOT : M8_CHUNK;
       if (lkb == nbd && --lleft > 0) {
@@ -775,7 +768,7 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_dn8(ExpertPtrs P, int hidden,
         lp = chunk0(ld, ltg);
       }
     } else {
-      m8_issue_none(pvalid, voff, lane0, sa);
+      m8_issue_none(pvalid, voff, sa);
     }
     lslot = lslot == M8_RING - 1 ? 0 : lslot + 1;
   };
@@ -829,7 +822,6 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_dn8f(ExpertPtrs P, int hidden
   float* s_rsc = (float*)(lds + M8_RINGS);   // row scales of the current descriptor's columns
   uint8_t* reg = lds + M8_RINGS + M8_MISC;
   const uint32_t voff = 16u * (uint32_t)lane;
-  const bool lt40 = lane < 40, lt28 = lane < 28, lane0 = lane == 0;
   constexpr size_t tile_bytes = (size_t)M8_CHUNK * NBD;   // one 16-row tile
   auto chunk0 = [&](int dsc, int tg) {
     const int e = work[dsc].expert;
@@ -839,8 +831,8 @@ __global__ __launch_bounds__(M8_THREADS, 1) void k_dn8f(ExpertPtrs P, int hidden
   auto issue = [&](auto J, const uint8_t* p) {
     constexpr int j = decltype(J)::value;
     const uint32_t sa = ring_la + (uint32_t)(j * M8_SLOT);
-    if (p == nullptr) m8_issue_none(P.dn, voff, lane0, sa);
-    else m8_issue_o(p + PD::off(j), PD::nb(j) == 2, voff, lt40, lt28, sa);
+    if (p == nullptr) m8_issue_none(P.dn, voff, sa);
+    else m8_issue_o(p + PD::off(j), PD::nb(j) == 2, voff, sa);
   };
 
   int cd = i0 / TG, ctg = i0 - cd * TG, key_d = -1, nc = 1, a0 = 0;

@@ -149,6 +149,8 @@ def _small_moe(E, hidden, inter, shared, seed):
     (12, 3, 768, 1024, 7, True, "bf16"),    # down: 4 blocks per row, 6 row groups
     (6, 2, 1280, 1536, 9, True, "f32"),     # down: 6 blocks per row; shared expert in 3 column groups
     (2, 1, 256, 9216, 3, True, "f32"),      # down: 36 blocks per row, one row per column group
+    (8, 2, 7168, 256, 6, True, "bf16"),     # gate/up: 28 blocks per row, parts of 4 and 3 blocks
+    (4, 2, 8192, 512, 9, True, "f32"),      # gate/up: 32 blocks per row, parts of 4 blocks
 ])
 def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
     (g, u, d), (sg, su, sd) = _small_moe(E, hidden, inter, shared, 104 + E)
