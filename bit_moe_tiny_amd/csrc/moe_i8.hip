@@ -19,11 +19,11 @@
 // Weights are streamed ("Roofline" of the ds4-on-spark README: decode is
 // bound by weight streaming): every wave keeps a ring of M8_RING slots, each
 // holding one step -- one chunk of the tiled layout, two blocks (2688 bytes)
-// or one (1344) of its 16 rows, read with three global-to-LDS wave
-// instructions (non-temporal for pairs, whose chunks are whole 128-byte
-// lines) -- and issues step j + M8_RING - 1 before computing step j.  When a
-// wave runs out of steps it issues one-lane placeholder loads instead, so
-// that every wait is the same constant vmcnt.  No block barrier is needed for
+// or one (1344) of its 16 rows, read with three full-wave global-to-LDS
+// instructions of 1 KB (non-temporal for pairs, whose chunks are whole
+// 128-byte lines) -- and issues step j + M8_RING - 1 before computing step j.
+// When a wave runs out of steps it issues placeholder loads of a chunk into a
+// slot it never reads, so that every wait is the same constant vmcnt.  No block barrier is needed for
 // weights: a wave only reads the slots its own loads filled.
 //
 // Work: persistent blocks of 8 waves, one per compute unit, each a contiguous
