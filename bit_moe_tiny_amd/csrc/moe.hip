@@ -280,18 +280,47 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
     for (int b = lane; b <= G; b += 64) blk[b] = 0;
     return;
   }
-  // block b starts in descriptor d when s_cost[d] <= floor(C b / G) <
-  // s_cost[d + 1], i.e. for b in [ceil(s_cost[d] G / C), ceil(s_cost[d+1] G / C)):
-  // each descriptor writes its own blocks (every product here is below 2^53,
-  // and a quotient that is not an integer is at least 1/C away from one, so
-  // the fp64 floor and ceil are exact)
+  // Block b starts at the first item whose cost offset is at least
+  // c = floor(C b / G): in the descriptor d with s_cost[d] <= c < s_cost[d+1],
+  // at item ceil((c - s_cost[d]) / w), w the descriptor's cost per item (an
+  // item past the descriptor's last is the next one's first).  Every product
+  // here is below 2^53, and a quotient that is not an integer is at least 1/C
+  // away from one, so the fp64 floors and ceilings are exact.
   const double dG = (double)G, dC = (double)C;
-  for (int d = lane; d < nd; d += 64) {
-    const int P0 = s_cost[d], P1 = s_cost[d + 1], w = (P1 - P0) / items;
-    const int b0 = (int)ceil((double)P0 * dG / dC), b1 = (int)ceil((double)P1 * dG / dC);
-    for (int b = b0; b < b1; ++b) {
+  if (nd < 16) {
+    // few descriptors, many blocks each: lane l takes blocks l, l + 64, ...
+    // and finds its descriptor by bisection (the offsets increase strictly)
+    for (int b = lane; b < G; b += 64) {
       const int c = (int)floor(dC * (double)b / dG);
-      blk[b] = d * items + (c - P0 + w - 1) / w;
+      int lo = 0, hi = nd - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cost[mid] <= c) lo = mid;
+        else hi = mid - 1;
+      }
+      const int P0 = s_cost[lo], w = (s_cost[lo + 1] - P0) / items;
+      blk[b] = lo * items + (c - P0 + w - 1) / w;
+    }
+  } else {
+    // lane l takes descriptors l, l + 64, ... and writes the blocks that
+    // start in them, b in [ceil(s_cost[d] G / C), ceil(s_cost[d+1] G / C));
+    // after the first, c steps by C = qG G + rG: c(b + 1) = c(b) + qG, plus
+    // one when the remainder C b - c G passes G
+    const int qG = C / G, rG = C - qG * G;
+    for (int d = lane; d < nd; d += 64) {
+      const int P0 = s_cost[d], P1 = s_cost[d + 1], w = (P1 - P0) / items;
+      const int b0 = (int)ceil((double)P0 * dG / dC), b1 = (int)ceil((double)P1 * dG / dC);
+      int c = (int)floor(dC * (double)b0 / dG);
+      int r = (int)((long long)C * b0 - (long long)c * G);
+      for (int b = b0; b < b1; ++b) {
+        blk[b] = d * items + (c - P0 + w - 1) / w;
+        c += qG;
+        r += rG;
+        if (r >= G) {
+          ++c;
+          r -= G;
+        }
+      }
     }
   }
   if (lane == 0) blk[G] = nd * items;
