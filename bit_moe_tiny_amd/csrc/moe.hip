@@ -104,14 +104,25 @@ __device__ inline uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-__device__ inline uint32_t wave_umax(uint32_t v) {
-  v = max(v, dpp_u32<0x111, 0xF>(v));   // row_shr:1
-  v = max(v, dpp_u32<0x112, 0xF>(v));   // row_shr:2
-  v = max(v, dpp_u32<0x114, 0xF>(v));   // row_shr:4
-  v = max(v, dpp_u32<0x118, 0xF>(v));   // row_shr:8   lane 15 of each row: the row's max
-  v = max(v, dpp_u32<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
-  v = max(v, dpp_u32<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+// Maximum of 64-bit values over the wave (both halves moved on the network).
+template <int CTRL, int ROWS>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ inline uint64_t wave_umax64(uint64_t v) {
+  v = umax64(v, dpp_u64<0x111, 0xF>(v));
+  v = umax64(v, dpp_u64<0x112, 0xF>(v));
+  v = umax64(v, dpp_u64<0x114, 0xF>(v));
+  v = umax64(v, dpp_u64<0x118, 0xF>(v));
+  v = umax64(v, dpp_u64<0x142, 0xA>(v));
+  v = umax64(v, dpp_u64<0x143, 0xC>(v));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Sum in a fixed order (run-to-run identical): zeros are shifted in at row
@@ -167,57 +178,53 @@ __device__ inline float key_logit(uint32_t k) {
 constexpr int PREP_THREADS = 1024;
 
 // One wave: top-k of one row of E logits (E <= 64 * PER), by logit, ties to
-// the lower index; weights = softmax probability over all E.
+// the lower index; weights = softmax probability over all E.  Every expert is
+// one 64-bit value, its logit's key above the complement of its index, so the
+// order of these values is the order of choice and no two are equal (slots
+// past E hold 0, below every expert).  Each lane sorts its PER values; in each
+// of k rounds the largest head over the wave is the next choice and the lane
+// holding it moves to its next value.
 template <int PER>
 __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, int32_t* idx_out,
                           float* w_out, MoeWs ws) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[PER];
   float v[PER];
-  unsigned taken = 0;
-  uint32_t lk0 = 0;
+  uint64_t c[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
     v[i] = e < E ? logits[(size_t)r * E + e] : -INFINITY;
-    key[i] = logit_key(v[i]);
-    if (e >= E) taken |= 1u << i;
-    else lk0 = max(lk0, key[i]);
+    c[i] = e < E ? ((uint64_t)logit_key(v[i]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
   }
-  const float mx = key_logit(wave_umax(lk0));   // the largest logit
+#pragma unroll
+  for (int i = 1; i < PER; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const uint64_t hi = umax64(c[j - 1], c[j]), lo = c[j - 1] ^ c[j] ^ hi;
+      c[j - 1] = hi;
+      c[j] = lo;
+    }
+  // lane s keeps the s-th choice; all k are written together afterwards
+  uint64_t mine = 0, first = 0;
+  for (int s = 0; s < k; ++s) {
+    const uint64_t g = wave_umax64(c[0]);
+    if (s == 0) first = g;
+    if (c[0] == g) {
+#pragma unroll
+      for (int j = 0; j + 1 < PER; ++j) c[j] = c[j + 1];
+      c[PER - 1] = 0;
+    }
+    if (lane == s) mine = g;
+  }
+  const float mx = key_logit((uint32_t)(first >> 32));   // the largest logit
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
-    if (!(taken >> i & 1)) sum += expf(v[i] - mx);
+    if (lane + 64 * i < E) sum += expf(v[i] - mx);
   sum = wave_sum(sum);
-  // k rounds of (largest key, then the lowest index holding it); lane s keeps
-  // the s-th choice, and all k are written together afterwards
-  uint32_t my_key = 0;
-  int my_idx = 0;
-  for (int s = 0; s < k; ++s) {
-    uint32_t lk = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (!(taken >> i & 1)) lk = max(lk, key[i]);
-    const uint32_t gk = wave_umax(lk);
-    // the lowest index holding gk: the first slot i with a match, then the
-    // lowest lane (index = lane + 64 i), from one ballot per slot
-    int bi = -1;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const unsigned long long m = __ballot(!(taken >> i & 1) && key[i] == gk);
-      if (bi < 0 && m) bi = 64 * i + (int)__builtin_ctzll(m);
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (lane + 64 * i == bi) taken |= 1u << i;
-    if (lane == s) {
-      my_key = gk;
-      my_idx = bi;
-    }
-  }
   if (lane < k) {
-    const float w = expf(key_logit(my_key) - mx) / sum;
+    const int my_idx = (int)~(uint32_t)mine;
+    const float w = expf(key_logit((uint32_t)(mine >> 32)) - mx) / sum;
     s_idx[r * k + lane] = my_idx;
     ws.topk_idx[r * k + lane] = my_idx;
     ws.topk_w[r * k + lane] = w;

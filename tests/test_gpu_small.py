@@ -260,6 +260,41 @@ def test_routing_ties_bit_exact(sv):
     assert_close(host(y)[ok], want, what="moe y (tie rows)")
 
 
+@pytest.mark.parametrize("E,k", [(100, 8), (500, 16), (1024, 8)])
+def test_routing_ties_wide_bit_exact(sv, E, k):
+    """Router widths of 2, 8 and 16 logits per lane (the routing kernel's other
+    instantiations): indices bit-exact with the oracle on integer-valued rows
+    (ties across lanes and slots), a row with NaNs and -infs, and plain normal
+    rows; weights close where finite.  The expert weights are zero blocks:
+    only the routing outputs are compared."""
+    hidden = inter = 256
+    R = 6
+    rng = np.random.default_rng(160 + E)
+    rows = [rng.integers(-3, 4, size=E).astype(np.float32) for _ in range(3)]
+    z = rng.integers(-2, 3, size=E).astype(np.float32)
+    z[rng.choice(E, E // 3, replace=False)] = np.nan
+    z[rng.choice(E, E // 3, replace=False)] = -np.inf
+    rows.append(z)
+    rows += [synth.normal_f32(synth.generator(161, E, i), (E,)) for i in range(2)]
+    lg = np.stack(rows).astype(np.float32)
+    nbytes = sv.sv_q2_matrix_bytes(inter, hidden) * E
+    wz = empty((nbytes,), "u8").zero_()
+    wd = empty((sv.sv_q2_matrix_bytes(hidden, inter) * E,), "u8").zero_()
+    desc = sv.moe_desc(sv.SV_FFN_SWIGLU, hidden, inter, E, k, wz, wz, wd)
+    x = synth.normal_bf16(synth.generator(162), (R, hidden))
+    y = empty((R, hidden), "f32")
+    ti = empty((R, k), "i32")
+    tw = empty((R, k), "f32")
+    say("vq2_moe_gemm routing", E, k, R)
+    sv.vq2_moe_gemm(desc, dev(x), dev(lg), y, ti, tw)
+    gi, gw = host(ti), host(tw)
+    widx, ww = oracle.route_topk(lg, k)
+    assert np.array_equal(gi, widx), f"routing differs:\n{gi}\n{widx}"
+    assert np.array_equal(np.isnan(gw), np.isnan(ww))
+    fin = np.isfinite(ww)
+    assert np.allclose(gw[fin], ww[fin], rtol=1e-5, atol=0)
+
+
 # ------------------------------------------------------------ lm head
 @pytest.mark.parametrize("vocab,hidden,R,dt", [(1000, 1024, 5, "bf16"), (77, 256, 3, "f32"),
                                               (4096, 7168, 16, "bf16"), (33, 32, 40, "f32"),
