@@ -264,13 +264,22 @@ def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24):
     expert (24 x 14.45 MB exceeds the 256 MB last-level cache, so the weights
     stream from HBM), run eagerly and as a captured graph; the per-call time is
     the unit's median over the copies.  Eager calls of this size are bound by
-    the host's launch rate, so `frac` is taken from the graph replay."""
+    the host's launch rate, so `frac` is taken from the graph replay.  Beside
+    it, the time of five minimal kernels (one-element fills), the floor of any
+    five-launch call, timed the same way."""
     import torch
     wg, wu, wd = desc._keep[0], desc._keep[1], desc._keep[2]
     gu, dn = sv.sv_q2_tiled_bytes(synth.INTER, synth.HIDDEN), sv.sv_q2_tiled_bytes(synth.HIDDEN, synth.INTER)
     descs = [sv.moe_desc(sv.SV_FFN_SWIGLU, synth.HIDDEN, synth.INTER, 1, 1, wg[e * gu:(e + 1) * gu],
                          wu[e * gu:(e + 1) * gu], wd[e * dn:(e + 1) * dn], tiled=True)
              for e in range(copies)]
+    t = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def empties():
+        for _ in range(5 * copies):
+            t.fill_(1.0)
+
+    floor_e, floor_g = time_eager_and_graph(empties, reps=12)
     out = []
     for R in Rs:
         x = to_dev(synth.expert(R).x_bf16)
@@ -288,7 +297,9 @@ def single_expert(sv, desc, Rs=(1, 2, 4, 8), copies: int = 24):
                     "frac": round(Q2_EXPERT_BYTES / us_g / 1e3 / PEAK_HBM_GBS, 4)})
         del ws, x, y
         torch.cuda.synchronize()
-    return {"bytes": Q2_EXPERT_BYTES, "launches": 5, "calls_per_unit": copies, "rows": out}
+    return {"bytes": Q2_EXPERT_BYTES, "launches": 5, "calls_per_unit": copies,
+            "empty_launch_floor_us": {"eager": round(floor_e / copies, 2), "graph": round(floor_g / copies, 2)},
+            "rows": out}
 
 
 def event_median(call, reps: int = 40) -> float:

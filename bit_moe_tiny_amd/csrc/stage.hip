@@ -11,7 +11,7 @@
 
 namespace sv {
 
-constexpr int STAGE_THREADS = 256;
+constexpr int STAGE_THREADS = 1024;
 
 template <int DT>
 __global__ __launch_bounds__(STAGE_THREADS) void k_stage(const void* src, int rows, int layout,
