@@ -516,24 +516,37 @@ __device__ void stage_digits(const void* x, int row, XDig xd) {
 
 // The down projection's input of assignment a as digits: silu(sum of the
 // gate quarters) * (sum of the up quarters), quarters summed in order (the
-// SwiGLU of the gate/up kernels' quarter sums).  One block per assignment.
+// SwiGLU of the gate/up kernels' quarter sums).  One block per assignment:
+// every thread first forms four of the row's values into LDS (so the loads
+// and the SwiGLU are spread over the whole block), then the row is turned
+// into digits one sub-block per thread.
 __global__ __launch_bounds__(PREP_THREADS) void k_hdig(MoeWs ws, int inter) {
+  extern __shared__ __align__(16) float s_h[];   // [inter]
   const int a = blockIdx.x;
-  const size_t qs = (size_t)ws.max_assign * inter;
+  const size_t qs = (size_t)ws.max_assign * inter, o = (size_t)a * inter;
+  for (int i = threadIdx.x; 4 * i < inter; i += PREP_THREADS) {
+    float4 gq[4], uq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      gq[q] = *(const float4*)(ws.gpart + (size_t)q * qs + o + 4 * i);
+      uq[q] = *(const float4*)(ws.gpart + (size_t)(4 + q) * qs + o + 4 * i);
+    }
+    float4 h;
+    h.x = silu_mul(((gq[0].x + gq[1].x) + gq[2].x) + gq[3].x, ((uq[0].x + uq[1].x) + uq[2].x) + uq[3].x);
+    h.y = silu_mul(((gq[0].y + gq[1].y) + gq[2].y) + gq[3].y, ((uq[0].y + uq[1].y) + uq[2].y) + uq[3].y);
+    h.z = silu_mul(((gq[0].z + gq[1].z) + gq[2].z) + gq[3].z, ((uq[0].z + uq[1].z) + uq[2].z) + uq[3].z);
+    h.w = silu_mul(((gq[0].w + gq[1].w) + gq[2].w) + gq[3].w, ((uq[0].w + uq[1].w) + uq[2].w) + uq[3].w);
+    *(float4*)(s_h + 4 * i) = h;
+  }
+  __syncthreads();
   stage_row_digits(a, ws.hd, [&](int sb, float (&v)[16]) {
-    const size_t o = (size_t)a * inter + 16 * sb;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float4 gq[4], uq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gq[q] = *(const float4*)(ws.gpart + (size_t)q * qs + o + 4 * j);
-        uq[q] = *(const float4*)(ws.gpart + (size_t)(4 + q) * qs + o + 4 * j);
-      }
-      v[4 * j] = silu_mul(((gq[0].x + gq[1].x) + gq[2].x) + gq[3].x, ((uq[0].x + uq[1].x) + uq[2].x) + uq[3].x);
-      v[4 * j + 1] = silu_mul(((gq[0].y + gq[1].y) + gq[2].y) + gq[3].y, ((uq[0].y + uq[1].y) + uq[2].y) + uq[3].y);
-      v[4 * j + 2] = silu_mul(((gq[0].z + gq[1].z) + gq[2].z) + gq[3].z, ((uq[0].z + uq[1].z) + uq[2].z) + uq[3].z);
-      v[4 * j + 3] = silu_mul(((gq[0].w + gq[1].w) + gq[2].w) + gq[3].w, ((uq[0].w + uq[1].w) + uq[2].w) + uq[3].w);
+      const float4 h = *(const float4*)(s_h + 16 * sb + 4 * j);
+      v[4 * j] = h.x;
+      v[4 * j + 1] = h.y;
+      v[4 * j + 2] = h.z;
+      v[4 * j + 3] = h.w;
     }
   });
 }
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(PREP_THREADS) void k_hdig(MoeWs ws, int inter) {
 hipError_t launch_hdig(const sv_moe_desc* d, int R, MoeWs ws, hipStream_t s) {
   // the eight-bit shared expert's assignments (the last R) have no quarter sums
   const int na = shared_q8(d) ? ws.max_assign - R : ws.max_assign;
-  hipLaunchKernelGGL(k_hdig, dim3(na), dim3(PREP_THREADS), 0, s, ws, d->inter);
+  hipLaunchKernelGGL(k_hdig, dim3(na), dim3(PREP_THREADS), (size_t)d->inter * sizeof(float), s, ws, d->inter);
   return hipGetLastError();
 }
 
