@@ -41,7 +41,9 @@ namespace sv {
 
 constexpr int ACC_T = 256;                    // threads per block
 constexpr int ACC_CHUNK = 2048;               // statistics chunk
-constexpr int ACC_PER = ACC_CHUNK / ACC_T;
+// threads per statistics block: 1024 for grids of fewer than STATS_WIDE
+// blocks (short per-thread chains), 256 beyond (more blocks per CU)
+constexpr int STATS_WIDE = 512;
 constexpr int ACC_MAX_CH = 256;               // V <= 524288
 constexpr int SMP_PER = 2;                    // sampling entries per thread
 constexpr int SMP_CHUNK = ACC_T * SMP_PER;    // sampling chunk
@@ -124,20 +126,29 @@ __device__ inline double wave_excl_scan_d(double v, double* total) {
   return (threadIdx.x & 63) == 0 ? 0.0 : ex;
 }
 
-// Block-wide fixed-order reductions (256 threads); `sh` holds 4 doubles.
+// Block-wide fixed-order reductions over NW waves (the per-wave results
+// folded left in wave order); `sh` holds NW doubles.
+template <int NW = ACC_T / 64>
 __device__ inline double block_sum_d(double v, double* sh) {
   v = wave_sum_d(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+  double t = sh[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) t += sh[w];
+  return t;
 }
+template <int NW = ACC_T / 64>
 __device__ inline double block_max_d(double v, double* sh) {
   v = wave_max_d(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
+  double t = sh[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) t = fmax(t, sh[w]);
+  return t;
 }
 
 // Block-wide exclusive prefix sum in a fixed order (256 threads); returns the
@@ -162,7 +173,7 @@ __device__ inline double block_excl_scan_d(double v, double* sh, double* total) 
 struct RowSrc {
   const float* p;   // row start
   int kind;         // SV_LOGITS / SV_PROBS
-  double T;
+  double rT;        // 1 / T: z / T is taken as z * rT everywhere
 };
 
 __device__ inline RowSrc row_src(int r, int S, int K, int V, const float* target, int tkind,
@@ -172,37 +183,39 @@ __device__ inline RowSrc row_src(int r, int S, int K, int V, const float* target
   if (r < nt) {
     s.p = target + (size_t)r * V;
     s.kind = tkind;
-    s.T = (double)Tp;
+    s.rT = 1.0 / (double)Tp;
   } else {
     s.p = draft + (size_t)(r - nt) * V;
     s.kind = dkind;
-    s.T = (double)Tq;
+    s.rT = 1.0 / (double)Tq;
   }
   return s;
 }
 
-__global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const float* target,
+template <int STATS_T>
+__global__ __launch_bounds__(STATS_T) void k_acc_stats(int S, int K, int V, const float* target,
                                                    int tkind, float Tp, const float* draft,
                                                    int dkind, float Tq, AccWs ws, int n_clear) {
-  __shared__ double sh[4];
-  __shared__ int shb[4];
+  constexpr int NW = STATS_T / 64, STATS_PER = ACC_CHUNK / STATS_T;
+  __shared__ double sh[NW];
+  __shared__ int shb[NW];
   const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
   if (c == 0 && r == 0)   // the sampling launch's counters
     for (int i = threadIdx.x; i < n_clear; i += blockDim.x) ws.done[i] = 0u;
   const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
   const int x0 = c * ACC_CHUNK;
-  double a[ACC_PER];
+  double a[STATS_PER];
   int bad = 0;
   double mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < ACC_PER; ++i) {
-    const int x = x0 + threadIdx.x + 256 * i;
+  for (int i = 0; i < STATS_PER; ++i) {
+    const int x = x0 + threadIdx.x + STATS_T * i;
     a[i] = -INFINITY;
     if (x < V) {
       const float v = src.p[x];
       if (src.kind != SV_PROBS) {
         bad |= !(fabsf(v) <= 3.402823466e38f);
-        a[i] = src.kind == SV_LOGITS ? (double)v / src.T : (double)v;
+        a[i] = src.kind == SV_LOGITS ? (double)v * src.rT : (double)v;
       } else {
         bad |= !(v >= 0.f && v <= 3.402823466e38f);
         a[i] = (double)v;
@@ -212,25 +225,25 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
   }
   double sum = 0.0;
   if (src.kind == SV_LOGITS) {
-    mx = block_max_d(mx, sh);
+    mx = block_max_d<NW>(mx, sh);
 #pragma unroll
-    for (int i = 0; i < ACC_PER; ++i)
-      if (x0 + threadIdx.x + 256 * i < V && !bad) sum += exp(a[i] - mx);
-    sum = block_sum_d(sum, sh);
+    for (int i = 0; i < STATS_PER; ++i)
+      if (x0 + threadIdx.x + STATS_T * i < V && !bad) sum += exp(a[i] - mx);
+    sum = block_sum_d<NW>(sum, sh);
   } else if (src.kind == ACC_ARGMAX) {
     // the chunk's first index holding its maximum (a maximum of -index)
-    mx = block_max_d(mx, sh);
+    mx = block_max_d<NW>(mx, sh);
     double fi = -INFINITY;
 #pragma unroll
-    for (int i = ACC_PER - 1; i >= 0; --i)
-      if (x0 + threadIdx.x + 256 * i < V && a[i] == mx) fi = -(double)(x0 + threadIdx.x + 256 * i);
-    sum = -block_max_d(fi, sh);
+    for (int i = STATS_PER - 1; i >= 0; --i)
+      if (x0 + threadIdx.x + STATS_T * i < V && a[i] == mx) fi = -(double)(x0 + threadIdx.x + STATS_T * i);
+    sum = -block_max_d<NW>(fi, sh);
   } else {
     mx = 0.0;
 #pragma unroll
-    for (int i = 0; i < ACC_PER; ++i)
-      if (x0 + threadIdx.x + 256 * i < V) sum += a[i];
-    sum = block_sum_d(sum, sh);
+    for (int i = 0; i < STATS_PER; ++i)
+      if (x0 + threadIdx.x + STATS_T * i < V) sum += a[i];
+    sum = block_sum_d<NW>(sum, sh);
   }
   bad = __any(bad) ? 1 : 0;
   if ((threadIdx.x & 63) == 0) shb[threadIdx.x >> 6] = bad;
@@ -239,15 +252,28 @@ __global__ __launch_bounds__(256) void k_acc_stats(int S, int K, int V, const fl
     const size_t o = (size_t)r * CH + c;
     ws.cmax[o] = mx;
     ws.csum[o] = sum;
-    ws.cbad[o] = shb[0] | shb[1] | shb[2] | shb[3];
+    int cb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cb |= shb[w];
+    ws.cbad[o] = cb;
   }
+}
+
+static void launch_acc_stats(dim3 grid, hipStream_t s, int S, int K, int V, const float* target, int tkind,
+                             float Tp, const float* draft, int dkind, float Tq, AccWs ws, int n_clear) {
+  if (grid.x * grid.y < (unsigned)STATS_WIDE)
+    hipLaunchKernelGGL(k_acc_stats<1024>, grid, dim3(1024), 0, s, S, K, V, target, tkind, Tp, draft, dkind, Tq,
+                       ws, n_clear);
+  else
+    hipLaunchKernelGGL(k_acc_stats<256>, grid, dim3(256), 0, s, S, K, V, target, tkind, Tp, draft, dkind, Tq, ws,
+                       n_clear);
 }
 
 // Distribution value of entry x of a row, given its recombined statistics.
 __device__ inline double dist_val(const RowSrc& s, double m, double z, int x) {
   if (s.kind == ACC_ARGMAX) return x == (int)z ? 1.0 : 0.0;
   const float v = s.p[x];
-  if (s.kind == SV_LOGITS) return exp((double)v / s.T - m) / z;
+  if (s.kind == SV_LOGITS) return exp((double)v * s.rT - m) / z;
   return (double)v;
 }
 
@@ -515,10 +541,10 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
     inv = __any(inv) ? 1 : 0;
     int rej = 1;   // lanes past K: rejected (K <= 31)
     if (!inv && lane < K) {
-      const double p = tkind == SV_LOGITS    ? exp((double)vp / (double)Tp - rm[lane]) / rz[lane]
+      const double p = tkind == SV_LOGITS    ? exp((double)vp * (1.0 / (double)Tp) - rm[lane]) / rz[lane]
                        : tkind == ACC_ARGMAX ? (dk == (int)rz[lane] ? 1.0 : 0.0)
                                              : (double)vp;
-      const double q = dkind == SV_LOGITS ? exp((double)vq / (double)Tq - rm[K + 1 + lane]) / rz[K + 1 + lane]
+      const double q = dkind == SV_LOGITS ? exp((double)vq * (1.0 / (double)Tq) - rm[K + 1 + lane]) / rz[K + 1 + lane]
                        : dkind == ACC_ARGMAX ? (dk == (int)rz[K + 1 + lane] ? 1.0 : 0.0)
                                              : (double)vq;
       rej = !(fma((double)uk, q, -p) < 0.0);   // reject: u*q >= p
@@ -604,8 +630,7 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
   const int CH = acc_chunks(V), CHs = smp_chunks(V);
   if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
   if (dkind == SV_LOGITS && Tq == 0.f) dkind = ACC_ARGMAX;
-  hipLaunchKernelGGL(k_acc_stats, dim3(CH, S * (2 * K + 1)), dim3(256), 0, s, S, K, V, target,
-                     tkind, Tp, draft, dkind, Tq, ws, S);
+  launch_acc_stats(dim3(CH, S * (2 * K + 1)), s, S, K, V, target, tkind, Tp, draft, dkind, Tq, ws, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_acc_sample, dim3(CHs, S), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind,
@@ -696,7 +721,7 @@ __global__ __launch_bounds__(ACC_T) void k_tsm_pick(int S, int K, int V, int CH,
   RowSrc P;
   P.p = target + (size_t)r * V;
   P.kind = tkind;
-  P.T = (double)Tp;
+  P.rT = 1.0 / (double)Tp;
   // 2. row r's sample at u_i (block-uniform branches): a greedy row's token is
   //    its first maximum; otherwise the chunk holding u Z, then the entry
   const float uf = uni[(size_t)s * (K + 1) + i];
@@ -759,8 +784,7 @@ hipError_t launch_accept_tsm(int S, int K, int V, const float* target, int tkind
   const int CH = acc_chunks(V), rows = S * (K + 1);
   if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
   // target rows only (row index < S (K+1)); no draft rows are read
-  hipLaunchKernelGGL(k_acc_stats, dim3(CH, rows), dim3(256), 0, s, S, K, V, target, tkind, Tp,
-                     (const float*)nullptr, tkind, Tp, aw, S);
+  launch_acc_stats(dim3(CH, rows), s, S, K, V, target, tkind, Tp, (const float*)nullptr, tkind, Tp, aw, S);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_tsm_pick, dim3(rows), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind, Tp, drafts, u,
