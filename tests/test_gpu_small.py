@@ -151,6 +151,7 @@ def _small_moe(E, hidden, inter, shared, seed):
     (2, 1, 256, 9216, 3, True, "f32"),      # down: 36 blocks per row, one row per column group
     (8, 2, 7168, 256, 6, True, "bf16"),     # gate/up: 28 blocks per row, parts of 4 and 3 blocks
     (4, 2, 8192, 512, 9, True, "f32"),      # gate/up: 32 blocks per row, parts of 4 blocks
+    (20, 16, 256, 256, 64, True, "bf16"),   # the limits: R = 64 rows, top-16 of 20 experts
 ])
 def test_small_moe_layer(sv, E, k, hidden, inter, R, shared, dt):
     (g, u, d), (sg, su, sd) = _small_moe(E, hidden, inter, shared, 104 + E)
@@ -299,7 +300,8 @@ def test_routing_ties_wide_bit_exact(sv, E, k):
 @pytest.mark.parametrize("vocab,hidden,R,dt", [(1000, 1024, 5, "bf16"), (77, 256, 3, "f32"),
                                               (4096, 7168, 16, "bf16"), (33, 32, 40, "f32"),
                                               (1999, 1024, 1, "f32"), (3001, 2048, 4, "bf16"),
-                                              (517, 3072, 2, "f32"), (700, 1024, 7, "bf16")])
+                                              (517, 3072, 2, "f32"), (700, 1024, 7, "bf16"),
+                                              (300, 512, 64, "bf16")])
 def test_small_lm_head(sv, vocab, hidden, R, dt):
     p = synth.q8_random(synth.generator(107, vocab, hidden), vocab, hidden, 0.01)
     buf = p.packed()
@@ -368,6 +370,32 @@ def test_accept_many_sequences_probs(sv):
              else p[s * (K + 1) + K].astype(np.float64))
         assert sample_flag(w, u[s, K]), s
     assert set(np.unique(wn).tolist()) > {0}      # the cases mix accepts and rejects
+
+
+def test_accept_most_drafts_probs(sv):
+    """K = 31 drafts (the limit) on probability rows, drafts drawn from q:
+    agreement with the oracle, with chains that stop early, deep into the
+    drafts, and after all 31 (q close to p)."""
+    rng = np.random.default_rng(12)
+    S, K, V = 6, 31, 40
+    w = rng.random((S * (K + 1), V)) + 0.05
+    p = (w / w.sum(1, keepdims=True)).astype(np.float32)
+    qw = p[np.arange(S * (K + 1)).reshape(S, K + 1)[:, :K].reshape(-1)].astype(np.float64)
+    qw = qw * (1.0 + 0.6 * rng.random(qw.shape))
+    q = (qw / qw.sum(1, keepdims=True)).astype(np.float32)
+    drafts = np.stack([[rng.choice(V, p=q[s * K + i] / q[s * K + i].sum()) for i in range(K)]
+                       for s in range(S)]).astype(np.int32)
+    u = synth.uniform24(synth.generator(111), S * (K + 1)).reshape(S, K + 1)
+    toks, nacc = _run_accept(sv, S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    wt, wn = oracle.spec_accept(S, K, V, p, PROBS, 1.0, q, PROBS, 1.0, drafts, u)
+    assert np.array_equal(nacc, wn)
+    for s in range(S):
+        if not np.array_equal(toks[s], wt[s]):
+            n = wn[s]
+            wr = (np.maximum(p[s * (K + 1) + n].astype(np.float64) - q[s * K + n], 0) if n < K
+                  else p[s * (K + 1) + K].astype(np.float64))
+            assert sample_flag(wr, u[s, K]), s
+    assert wn.max() == K and wn.min() < 8, wn   # chains stop early and run to the bonus
 
 
 def _check_accept(S, K, V, target, tk, tp, draft, dk, tq, drafts, u, toks, nacc):
@@ -530,6 +558,21 @@ def test_tsm_many_sequences_probs(sv):
     toks, nacc = _run_tsm(sv, S, K, V, p, PROBS, 1.0, drafts, u)
     wn, flagged = check_target_sample(S, K, V, p, PROBS, 1.0, drafts, u, toks, nacc)
     assert set(wn.tolist()) == set(range(K + 1)) and flagged <= 2
+
+
+def test_tsm_most_drafts_probs(sv):
+    """Target-sample matching with K = 31 drafts (the limit): agreement with
+    the oracle, prefixes of many lengths."""
+    rng = np.random.default_rng(32)
+    S, K, V = 8, 31, 40
+    w = rng.random((S * (K + 1), V)) * (rng.random((S * (K + 1), V)) > 0.2)
+    w[:, 0] += 1e-3
+    p = (w / w.sum(1, keepdims=True)).astype(np.float32)
+    u = synth.uniform24(synth.generator(151), S * (K + 1)).reshape(S, K + 1)
+    drafts = matching_drafts(S, K, V, p, PROBS, 1.0, u, 0.9, rng)
+    toks, nacc = _run_tsm(sv, S, K, V, p, PROBS, 1.0, drafts, u)
+    wn, flagged = check_target_sample(S, K, V, p, PROBS, 1.0, drafts, u, toks, nacc)
+    assert flagged <= 1 and wn.max() >= 4, wn
 
 
 def test_tsm_logits_ragged_and_invalid(sv):
