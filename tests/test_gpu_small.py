@@ -448,6 +448,25 @@ def test_accept_bonus_only(sv):
     assert np.all(wn == 0)
 
 
+def test_accept_one_token_vocabulary(sv):
+    """V = 1, the degenerate vocabulary: p = q = 1 at the only token, so every
+    draft is accepted and the bonus token is 0, under both rules and both
+    kinds of rows."""
+    S, K, V = 3, 4, 1
+    z = synth.normal(synth.generator(131), S * (K + 1), 1.0).astype(np.float32).reshape(S * (K + 1), V)
+    zq = synth.normal(synth.generator(132), S * K, 1.0).astype(np.float32).reshape(S * K, V)
+    drafts = np.zeros((S, K), np.int32)
+    u = synth.uniform24(synth.generator(133), S * (K + 1)).reshape(S, K + 1)
+    for tk, t, q in ((LOGITS, 0.8, zq), (PROBS, 1.0, np.ones((S * K, V), np.float32))):
+        tv = z if tk == LOGITS else np.ones((S * (K + 1), V), np.float32)
+        toks, nacc = _run_accept(sv, S, K, V, tv, tk, t, q, tk, t, drafts, u)
+        assert np.all(nacc == K) and np.all(toks == 0), (toks, nacc)
+        wt, wn = oracle.spec_accept(S, K, V, tv, tk, t, q, tk, t, drafts, u)
+        assert np.array_equal(wn, nacc) and np.array_equal(wt, toks)
+        toks, nacc = _run_tsm(sv, S, K, V, tv, tk, t, drafts, u)
+        assert np.all(nacc == K) and np.all(toks == 0), (toks, nacc)
+
+
 def test_accept_invalid_sequences(sv):
     """A token outside [0, V), a uniform of 1, a NaN draft value and an
     infinite target value each void their own sequence only."""
