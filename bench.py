@@ -349,7 +349,7 @@ def next_rows(sv, step, wroute):
 
 KERNEL_KEYS = {"gate/up": "k_gu8", "down": "k_dn8", "down input digits": "k_hdig", "routing": "k_moe_prep",
                "combine": "k_moe_combine", "head": "k_q8_lmhead", "head staging": "k_stage",
-               "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample",
+               "accept statistics": "k_acc_stats", "accept sample": "k_acc_sample", "accept pick": "k_acc_pick",
                "target-sample matching": "k_tsm_pick", "shared expert h staging": "k_stage_swiglu"}
 
 

@@ -13,7 +13,8 @@
 // inverse-CDF sample at its uniform; drafts stand while they equal these
 // samples, the first that differs (or row K's) is emitted last.
 //
-// Two launches per rule, no host sync, no block waiting on another:
+// Three launches for the p/q rule, two for target-sample matching; no host
+// sync, no block waiting on another:
 //   k_acc_stats   grid (chunk, row): per 2048-entry chunk of every target and
 //                 draft row, the chunk max of z/T and sum exp(z/T - max) in
 //                 fp64 (or the plain sum for probability rows), plus a
@@ -23,12 +24,14 @@
 //                 its sequence's row statistics (same order in every block, so
 //                 all agree bit for bit), replays the accept chain, and sums
 //                 the sampling weights of its chunk (residual, or p_K for the
-//                 bonus), per 2-entry thread segment and per chunk.  The last
-//                 block of the sequence to finish (a counter the first launch
-//                 clears) finds, with one wave, the chunk that holds u_K * Z
-//                 from the chunk totals, the segment inside it from the
-//                 per-thread sums, and the token among that segment's
-//                 entries, then writes the outputs.
+//                 bonus), per 2-entry thread segment and per chunk; block 0
+//                 also stores the sequence's decision (accepted drafts, u_K,
+//                 the sampled rows' statistics).
+//   k_acc_pick    one block per sequence: from those sums (published by the
+//                 kernel boundary, which costs less than a device-scope
+//                 release and counter per block) it finds the chunk that
+//                 holds u_K * Z, the segment inside it, and the token among
+//                 that segment's entries, then writes the outputs.
 //   k_tsm_pick    (target-sample matching) one block per target row: the
 //                 row's masses per statistics chunk (its chunk sums rescaled
 //                 to the row maximum) locate the chunk holding u Z, the block
@@ -60,7 +63,9 @@ struct AccWs {
   int* cbad;        // [rows, CH]
   double* rsum;     // [S, CHs]        sampling weight per sampling chunk
   double* tsum;     // [S, CHs, ACC_T] sampling weight per thread segment
-  unsigned* done;   // [S]            blocks of the sequence done sampling
+  unsigned* done;   // [S]            (target-sample matching only) rows sampled
+  int* sdec;        // [S, 2]         accepted drafts, invalid flag
+  double* sst;      // [S, 5]         u_K and the sampled rows' statistics pm, pz, qm, qz
 };
 
 static inline int acc_chunks(int V) { return (V + ACC_CHUNK - 1) / ACC_CHUNK; }
@@ -80,14 +85,17 @@ static AccWs acc_carve(void* base, int S, int K, int V) {
   p += up256((size_t)S * CHs * 8);
   w.tsum = (double*)p;
   p += up256((size_t)S * CHs * ACC_T * 8);
-  w.done = (unsigned*)p;
+  w.done = nullptr;
+  w.sdec = (int*)p;
+  p += up256((size_t)S * 8);
+  w.sst = (double*)p;
   return w;
 }
 
 size_t accept_ws_bytes(int S, int K, int V) {
   const size_t rows = (size_t)S * (2 * K + 1), CH = acc_chunks(V), CHs = smp_chunks(V);
   return 2 * up256(rows * CH * 8) + up256(rows * CH * 4) + up256((size_t)S * CHs * 8) +
-         up256((size_t)S * CHs * ACC_T * 8) + up256((size_t)S * 4);
+         up256((size_t)S * CHs * ACC_T * 8) + up256((size_t)S * 8) + up256((size_t)S * 40);
 }
 
 __device__ inline double wave_sum_d(double v) {
@@ -200,7 +208,7 @@ __global__ __launch_bounds__(STATS_T) void k_acc_stats(int S, int K, int V, cons
   __shared__ double sh[NW];
   __shared__ int shb[NW];
   const int c = blockIdx.x, r = blockIdx.y, CH = gridDim.x;
-  if (c == 0 && r == 0)   // the sampling launch's counters
+  if (c == 0 && r == 0)   // target-sample matching: its per-sequence counters
     for (int i = threadIdx.x; i < n_clear; i += blockDim.x) ws.done[i] = 0u;
   const RowSrc src = row_src(r, S, K, V, target, tkind, Tp, draft, dkind, Tq);
   const int x0 = c * ACC_CHUNK;
@@ -500,15 +508,12 @@ __device__ inline int seg_token(const double* parts, double base, bool found_chu
 __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int CH,
                                                       const float* target, int tkind, float Tp,
                                                       const float* draft, int dkind, float Tq,
-                                                      const int32_t* drafts, const float* uni,
-                                                      int32_t* out_tokens, int32_t* out_n, AccWs ws) {
+                                                      const int32_t* drafts, const float* uni, AccWs ws) {
   __shared__ double rm[2 * SV_MAX_DRAFTS + 1], rz[2 * SV_MAX_DRAFTS + 1];
   __shared__ int rbad[2 * SV_MAX_DRAFTS + 1];
   __shared__ double sh[4];
-  __shared__ double cws[SMP_MAX_CH];   // the last block: chunk totals
-  __shared__ double parts[ACC_T];      // the last block: the hit chunk's segment totals
-  __shared__ double s_uk, s_z, s_base;
-  __shared__ int s_nacc, s_invalid, s_last, s_hit, s_found;
+  __shared__ double s_uk;
+  __shared__ int s_nacc, s_invalid;
   const int c = blockIdx.x, s = blockIdx.y, CHs = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   // 0. wave 0, lane i: draft i's token and uniform and both rows' values at
@@ -566,38 +571,52 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
   const double qm = nacc < K ? rm[K + 1 + nacc] : 0.0, qz = nacc < K ? rz[K + 1 + nacc] : 1.0;
   const int mode = nacc < K ? MODE_RESID : MODE_P;
   double w = inv ? 0.0 : seg_weight(mode, P, pm, pz, Q, qm, qz, c, V);
-  // 4. the last block of the sequence to get here samples.  The sums go out
-  //    as device-scope stores (written through to the point of coherence of
-  //    all XCDs, not held in this XCD's L2); the block meets (a workgroup
-  //    barrier: every thread's stores happen before what thread 0 does
-  //    next), and thread 0 counts the block done with an acquire-release
-  //    increment at device scope, whose release publishes them.  The block
-  //    that brings the count to the total acquires (every thread, after the
-  //    barrier) before it reads the sums back with device-scope loads, so
-  //    every other block's stores happen before those reads.
-  __hip_atomic_store(&ws.tsum[((size_t)s * CHs + c) * ACC_T + tid], w, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  // 4. the chunk's sums for k_acc_pick (the kernel boundary publishes them),
+  //    and, from block 0, the sequence's decision
+  ws.tsum[((size_t)s * CHs + c) * ACC_T + tid] = w;
   w = block_sum_d(w, sh);
-  if (tid == 0)
-    __hip_atomic_store(&ws.rsum[(size_t)s * CHs + c], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) ws.rsum[(size_t)s * CHs + c] = w;
+  if (c == 0 && tid == 0) {
+    ws.sdec[2 * s] = nacc;
+    ws.sdec[2 * s + 1] = inv;
+    double* st = ws.sst + 5 * (size_t)s;
+    st[0] = s_uk;
+    st[1] = pm;
+    st[2] = pz;
+    st[3] = qm;
+    st[4] = qz;
+  }
+}
+
+// One block per sequence: from the chunk totals, the chunk that holds
+// u_K * Z, then the thread segment and the entry inside it (from the
+// segment sums), and the sequence's outputs.
+__global__ __launch_bounds__(ACC_T) void k_acc_pick(int S, int K, int V, const float* target, int tkind, float Tp,
+                                                    const float* draft, int dkind, float Tq, const int32_t* drafts,
+                                                    int CHs, int32_t* out_tokens, int32_t* out_n, AccWs ws) {
+  __shared__ double sh[4];
+  __shared__ double cws[SMP_MAX_CH];   // chunk totals
+  __shared__ double parts[ACC_T];      // the hit chunk's segment totals
+  __shared__ double s_z, s_base;
+  __shared__ int s_hit, s_found;
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int nacc = ws.sdec[2 * s], inv = ws.sdec[2 * s + 1];
+  const double* st = ws.sst + 5 * (size_t)s;
+  const double uk = st[0], pm = st[1], pz = st[2], qm = st[3], qz = st[4];
+  for (int cc = tid; cc < CHs; cc += ACC_T) cws[cc] = ws.rsum[(size_t)s * CHs + cc];
+  const int dk = lane < K && lane < nacc ? drafts[s * K + lane] : -1;
   __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&ws.done[s], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(CHs - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   int32_t* out = out_tokens + (size_t)s * (K + 1);
   if (inv) {
     if (tid <= K) out[tid] = -1;
     if (tid == 0) out_n[s] = -1;
     return;
   }
-  for (int cc = tid; cc < CHs; cc += ACC_T)
-    cws[cc] = __hip_atomic_load(&ws.rsum[(size_t)s * CHs + cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  RowSrc P, Q;
+  sample_rows(s, nacc, S, K, V, target, tkind, Tp, draft, dkind, Tq, P, Q);
+  const int mode = nacc < K ? MODE_RESID : MODE_P;
   // the chunk holding tt = u_K * Z
-  find_chunk(cws, CHs, s_uk, &s_z, &s_found, &s_hit, &s_base);
+  find_chunk(cws, CHs, uk, &s_z, &s_found, &s_hit, &s_base);
   const bool redo = !(s_z > 0.0);
   if (redo) {
     // the residual vanished (only through rounding): sample p itself
@@ -606,14 +625,13 @@ __global__ __launch_bounds__(ACC_T) void k_acc_sample(int S, int K, int V, int C
       if (tid == 0) cws[cc] = t;
     }
     __syncthreads();
-    find_chunk(cws, CHs, s_uk, &s_z, &s_found, &s_hit, &s_base);
+    find_chunk(cws, CHs, uk, &s_z, &s_found, &s_hit, &s_base);
   }
   const int smode = redo ? MODE_P : mode;
-  const double tt = s_uk * s_z;
+  const double tt = uk * s_z;
   const int hit = s_hit;
   parts[tid] = redo ? seg_weight(MODE_P, P, pm, pz, Q, qm, qz, hit, V)
-                    : __hip_atomic_load(&ws.tsum[((size_t)s * CHs + hit) * ACC_T + tid],
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    : ws.tsum[((size_t)s * CHs + hit) * ACC_T + tid];
   __syncthreads();
   if (tid >= 64) return;
   // the thread segment inside it, then the entry
@@ -630,11 +648,15 @@ hipError_t launch_accept(int S, int K, int V, const float* target, int tkind, fl
   const int CH = acc_chunks(V), CHs = smp_chunks(V);
   if (tkind == SV_LOGITS && Tp == 0.f) tkind = ACC_ARGMAX;   // greedy rows
   if (dkind == SV_LOGITS && Tq == 0.f) dkind = ACC_ARGMAX;
-  launch_acc_stats(dim3(CH, S * (2 * K + 1)), s, S, K, V, target, tkind, Tp, draft, dkind, Tq, ws, S);
+  launch_acc_stats(dim3(CH, S * (2 * K + 1)), s, S, K, V, target, tkind, Tp, draft, dkind, Tq, ws, 0);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(k_acc_sample, dim3(CHs, S), dim3(ACC_T), 0, s, S, K, V, CH, target, tkind,
-                     Tp, draft, dkind, Tq, drafts, u, out_tokens, out_n, ws);
+                     Tp, draft, dkind, Tq, drafts, u, ws);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_acc_pick, dim3(S), dim3(ACC_T), 0, s, S, K, V, target, tkind, Tp, draft, dkind, Tq, drafts,
+                     CHs, out_tokens, out_n, ws);
   return hipGetLastError();
 }
 
