@@ -323,7 +323,7 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 // 4 with fp32 inputs; at most LD_MAX_ROUNDS tiles per wave).  Blocks of
 // LD_WAVES (4 or 8) waves, persistent over tiles: in round r wave w of block
 // b owns tile (r G + b) LD_WAVES + w.  Two 4-wave blocks per CU where both
-// fit in LDS (each with its own step barrier, so a slow wave holds up 3
+// fit in LDS (each with its own stage barrier, so a slow wave holds up 3
 // others, not 7), else one of 8 waves.  K is swept in stages of 16 blocks
 // (512 k), stage-major: for each stage, the rounds' tiles one after another
 // (one accumulator per round), so the block copies a stage's activation
@@ -332,7 +332,9 @@ __global__ __launch_bounds__(LM_WAVES * 64, 4) void k_q8_lmhead_lds(Q8View W, in
 // 16 x 32 scale bytes into its own LDS buffer with global_load_lds (full
 // 128-byte lines, non-temporal: this is the pattern that streams fastest on
 // this part).  Everything is double buffered: step k+1 is in flight while
-// step k is computed; one barrier per step.  Code rows are stored rotated by
+// step k is computed.  A wave waits only for its own copies before a step;
+// the block meets once per stage, for the shared activation buffer.  Code
+// rows are stored rotated by
 // their row index in 16-byte units so that the 16 rows of an MFMA operand
 // read fall in distinct LDS banks.
 constexpr int LD_SB = 16;                                   // blocks (of 32) per stage
@@ -415,11 +417,13 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
       if (r >= rounds) break;
-      // this wave's copies of step k are done; after the barrier everyone's
-      // are, and every wave is past step k-1 (whose buffers the next copies
-      // reuse; the activation buffer of stage st+1 was last read in st-1)
+      // this wave's copies of step k are done.  Weight buffers are private
+      // to their wave, so only a stage's first step has a barrier: after it
+      // every wave's activation copies of the stage are done, and every wave
+      // is past stage st-1, whose activation buffer the copies of stage st+1
+      // (issued in this stage's last round) reuse
       wait_vmcnt_le(0);
-      barrier_lds();
+      if (r == 0) barrier_lds();
       if (r + 1 < rounds) issue(st, r + 1, (k + 1) & 1, st & 1);
       else if (st + 1 < ns) issue(st + 1, 0, (k + 1) & 1, (st + 1) & 1);
       const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
