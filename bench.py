@@ -9,9 +9,11 @@ One step = the whole verifier hot path on one batch of synthetic input:
                    of K = R/S - 1 drafts at T = 0.8.
 Inputs for several batches are generated up front (seeded, synth) and stay
 resident in HBM; steps rotate through them.  The timed region is K steps
-between two device synchronisations; value = algorithmic weight bytes of the
-timed steps (the routed experts each batch actually touches, the shared
-expert, the vocabulary head) / elapsed time.
+between two device synchronisations, by default each a replay of a captured
+HIP graph of the whole step on that batch (--launch eager: launched call by
+call; the other mode is timed too and reported beside); value = algorithmic
+weight bytes of the timed steps (the routed experts each batch actually
+touches, the shared expert, the vocabulary head) / elapsed time.
 
 Prints ONE JSON line (rank 0, N = 1).  Besides the headline (R = 5, S = 1)
 the line carries, unless --no-extras: one entry per R = 1..16 and the
@@ -70,6 +72,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline: no per-R entries, cohort, single-expert calls or kernel times")
     ap.add_argument("--extra-steps", type=int, default=20, help="timed steps of each per-R / cohort entry")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="timed steps as replays of one captured HIP graph per batch (default), or as "
+                         "eager launches; the other mode is timed too and reported beside")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, one plain device copy of this many MiB (fp32 x 1.0): "
                          "the known-size kernel that calibrates profiler byte counters")
@@ -173,26 +178,61 @@ class Step:
         return (len(np.unique(idx)) + 1) * Q2_EXPERT_BYTES
 
 
-def measure(step, steps, warmup):
+def capture_steps(step):
+    """One HIP graph per input batch, each holding one whole step (every
+    kernel of the three calls, on that batch's inputs)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for b in range(len(step.batches)):
+            step.run(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for b in range(len(step.batches)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run(b)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def measure(step, steps, warmup, launch="graph"):
     """Times `steps` steps with events at the two ends only (an event recorded
-    between kernels leaves a gap of several microseconds on the GPU timeline);
-    a second pass over the same batches, with events around each call, gives
-    the per-call breakdown."""
+    between kernels leaves a gap of several microseconds on the GPU timeline),
+    as graph replays (one captured graph per batch) or as eager launches, and
+    the other mode the same way for comparison; a further pass over the same
+    batches, eager with events around each call, gives the per-call
+    breakdown."""
     import torch
     for i in range(warmup):
         step.run(i)
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for i in range(steps):
-        step.run(i)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
+    graphs = capture_steps(step)
+    nb = len(step.batches)
+
+    def timed(graph):
+        for i in range(min(warmup, nb) if graph else 0):
+            graphs[i % nb].replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        t0.record()
+        for i in range(steps):
+            if graph:
+                graphs[i % nb].replay()
+            else:
+                step.run(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), time.perf_counter() - wall0
+
+    other_ms, _ = timed(launch != "graph")
+    total_ms, wall = timed(launch == "graph")
+    del graphs
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         step.run(i, evs[i])
@@ -203,7 +243,7 @@ def measure(step, steps, warmup):
     step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     moe_b = np.array([step.moe_bytes(i) for i in range(steps)], np.float64)
     return dict(total_ms=total_ms, wall_s=wall, moe_ms=moe, lm_ms=lm, acc_ms=acc, step_ms=step_ms,
-                moe_bytes=moe_b)
+                moe_bytes=moe_b, launch=launch, other_ms=other_ms)
 
 
 PROBE_MODES = {0: "plain loads to registers, full lines", 1: "global-to-LDS, non-temporal, full lines",
@@ -250,7 +290,9 @@ def entry(R, S, m):
     steps = len(m["step_ms"])
     total_s = m["total_ms"] / 1e3
     gbs = float((m["moe_bytes"] + Q8_HEAD_BYTES).sum() / total_s / 1e9)
+    other = "eager" if m["launch"] == "graph" else "graph"
     return {"R": R, "S": S, "K": R // S - 1, "ms_per_step": round(total_s * 1e3 / steps, 4),
+            f"{other}_ms_per_step": round(m["other_ms"] / steps, 4),
             "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
             "call_us": {"vq2_moe_gemm": round(float(m["moe_ms"].mean()) * 1e3, 2),
                         "vq8_lmhead_gemm": round(float(m["lm_ms"].mean()) * 1e3, 2),
@@ -596,6 +638,8 @@ def result_line(args, R, S, m, cpu=None):
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(total_s * 1e3 / steps, 4),
+        "launch": m["launch"],
+        ("eager" if m["launch"] == "graph" else "graph") + "_ms_per_step": round(m["other_ms"] / steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -665,7 +709,7 @@ def main():
         S = args.seqs if R % args.seqs == 0 else 1
         step = Step(sv, desc, wq8, R, S, args.batches, args.temperature)
         log(f"R={R} S={S}: {args.warmup} warmup + {args.steps} timed steps")
-        m = measure(step, args.steps, args.warmup)
+        m = measure(step, args.steps, args.warmup, args.launch)
         cpu = None
         if not args.no_cpu_baseline and not args.sweep:
             log("cpu_baseline: timing the oracle on a bounded sample ...")
@@ -684,7 +728,7 @@ def main():
                 ents = []
                 for r2, s2 in [(r, 1) for r in range(1, 17)] + [(15, 3)]:
                     st = Step(sv, desc, wq8, r2, s2, 3, args.temperature)
-                    ents.append(entry(r2, s2, measure(st, args.extra_steps, 3)))
+                    ents.append(entry(r2, s2, measure(st, args.extra_steps, 3, args.launch)))
                     log(f"entry R={r2} S={s2}: {ents[-1]['ms_per_step']} ms per step")
                     del st
                 line["per_R"] = [e for e in ents if e["S"] == 1]
