@@ -347,6 +347,10 @@ constexpr int LD_MAX_ROUNDS = 4;                            // tiles per wave (o
 static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
   return (size_t)waves * 2 * (LD_WBUF + LD_DBUF) + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_XRS * 2;
 }
+// SREG form: block scales in registers, activation rows unpadded (rotated)
+static size_t ld_lds_bytes_sreg(int waves, int ncols, bool use_lo) {
+  return (size_t)waves * 2 * LD_WBUF + (size_t)2 * (use_lo ? 2 : 1) * ncols * LD_SB * 32 * 2;
+}
 
 
 // Split over K (the products of small matrices, whose tiles alone would
@@ -354,23 +358,38 @@ static size_t ld_lds_bytes(int waves, int ncols, bool use_lo) {
 // sp) of matrix z (W, or W2 for z = 1) and writes its partial products to
 // logits + z zstride + y R vocab (one [R, vocab] slice per y).  The head
 // runs it with one slice (sp = all stages) and one matrix.
-template <bool USE_LO, int LD_WAVES, int MAXR = LD_MAX_ROUNDS>
+//
+// SREG (8 waves, 16 columns): each lane loads its row's 16 block scales of a
+// step into registers (two 16-byte loads, one step ahead, alternating
+// between two register sets by round parity, so rounds come in pairs) instead
+// of staging them in LDS, and an activation row of a stage is stored without
+// padding, its 16-byte pieces rotated by the column index (piece p of column
+// c at slot (p - c) mod 64) so that the 16 columns of an operand read still
+// fall in distinct banks.  Then 8 waves' double-buffered weights and the
+// activation buffers for 16 columns fit in the 160 KB of LDS, and the
+// vocabulary takes 4 rounds of 8 waves per CU instead of 5 of 7.
+template <bool USE_LO, int LD_WAVES, int MAXR = LD_MAX_ROUNDS, bool SREG = false>
 __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q8View W1, Q8View W2, int R,
                                                                                XImg img, float* logits,
                                                                                int ncols, int sp, size_t zstride) {
+  static_assert(!SREG || MAXR % 2 == 0, "SREG rounds come in pairs");
   extern __shared__ __align__(16) uint8_t lds[];
   const Q8View W = blockIdx.z ? W2 : W1;
   const int lane = threadIdx.x & 63, wv = wave_id();
   const int vocab = W.n_out, nb = W.nb, K = nb * 32;
   const int tiles = (vocab + 15) / 16, st0 = blockIdx.y * sp, ns = min(st0 + sp, nb / LD_SB);
   logits += blockIdx.z * zstride + (size_t)blockIdx.y * R * vocab;
-  const int rounds = (tiles + gridDim.x * LD_WAVES - 1) / (gridDim.x * LD_WAVES);
+  // (SREG: always MAXR rounds, whose tiles past the last are skipped, so that
+  // the scale registers take the same path through every stage)
+  const int rounds = SREG ? MAXR : (tiles + gridDim.x * LD_WAVES - 1) / (gridDim.x * LD_WAVES);
   const int nl = lane & 15, g = lane >> 4;
   const int kofs = 8 * (((g & 1) << 1) | (g >> 1));   // k offset of this lane's 8 values in a block
   const uint32_t lbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+  constexpr int DBUF = SREG ? 0 : LD_DBUF;          // scale bytes per wave and stage in LDS
+  constexpr int XRS = SREG ? LD_SB * 32 : LD_XRS;   // activation row stride (fp16)
   const uint32_t wbase = lbase + wv * 2 * LD_WBUF;
-  const uint32_t dbase = lbase + LD_WAVES * 2 * LD_WBUF + wv * 2 * LD_DBUF;
-  const uint32_t xbase = lbase + LD_WAVES * 2 * (LD_WBUF + LD_DBUF);
+  const uint32_t dbase = lbase + LD_WAVES * 2 * LD_WBUF + wv * 2 * DBUF;
+  const uint32_t xbase = lbase + LD_WAVES * 2 * (LD_WBUF + DBUF);
   const uint8_t* wl = lds + (wbase - lbase);
   const uint8_t* dl = lds + (dbase - lbase);
   const _Float16* xl16 = (const _Float16*)(lds + (xbase - lbase));
@@ -381,8 +400,19 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
   // code and scale rows of the round's tile) and, for the first round of a
   // stage, the stage's activation columns into activation buffer `xb`
   // (shared by the block; column c by wave c mod LD_WAVES)
-  auto issue = [&](int st, int r, int wb, int xb) {
+  // SREG: the scale registers of even and odd rounds
+  uint4 sr[2][2];
+  auto issue = [&](int st, int r, int wb, int xb, uint4 (&srn)[2]) {
     const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
+    if (SREG) {
+      // this lane's row: its 16 block scales of the stage (loaded for every
+      // tile, a row past the vocabulary reading the last one, so that the
+      // registers are written on every path and are never copied while the
+      // loads are in flight)
+      const uint16_t* ds = W.d + (size_t)min(tile * 16 + nl, vocab - 1) * nb + st * LD_SB;
+      srn[0] = *(const uint4*)ds;
+      srn[1] = *(const uint4*)(ds + 8);
+    }
     if (tile < tiles) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -391,17 +421,18 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
         const int8_t* src = W.qs + ((size_t)n * nb + st * LD_SB) * 32 + ((c + row) & 31) * 16;
         dma16_nt(src, wbase + wb * LD_WBUF + i * 1024);
       }
-      if (lane < 32) {   // scales: two 16-byte pieces per row, lanes 0..31
+      if (!SREG && lane < 32) {   // scales: two 16-byte pieces per row, lanes 0..31
         const int row = lane >> 1;
         const int n = min(tile * 16 + row, vocab - 1);
-        dma16(W.d + (size_t)n * nb + st * LD_SB + 8 * (lane & 1), dbase + wb * LD_DBUF);
+        dma16(W.d + (size_t)n * nb + st * LD_SB + 8 * (lane & 1), dbase + wb * DBUF);
       }
     }
     if (r == 0)
       for (int c = wv; c < ncols * (USE_LO ? 2 : 1); c += LD_WAVES) {
         const int pl = c >= ncols, cc = c - (pl ? ncols : 0);
-        const _Float16* src = (pl ? img.lo : img.hi) + (size_t)cc * K + st * LD_SB * 32 + 8 * lane;
-        dma16(src, xbase + (uint32_t)(((pl * 2 + xb) * ncols + cc) * LD_XRS * 2));
+        const int piece = SREG ? ((lane + cc) & 63) : lane;
+        const _Float16* src = (pl ? img.lo : img.hi) + (size_t)cc * K + st * LD_SB * 32 + 8 * piece;
+        dma16(src, xbase + (uint32_t)(((pl * 2 + xb) * ncols + cc) * XRS * 2));
       }
   };
 
@@ -411,7 +442,7 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
   f4_t acc[MAXR];
 #pragma unroll
   for (int r = 0; r < MAXR; ++r) acc[r] = zero;
-  issue(st0, 0, 0, st0 & 1);
+  issue(st0, 0, 0, st0 & 1, sr[0]);
   int k = 0;   // running step count: weight buffer k & 1
   for (int st = st0; st < ns; ++st) {
 #pragma unroll
@@ -424,18 +455,25 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
       // (issued in this stage's last round) reuse
       wait_vmcnt_le(0);
       if (r == 0) barrier_lds();
-      if (r + 1 < rounds) issue(st, r + 1, (k + 1) & 1, st & 1);
-      else if (st + 1 < ns) issue(st + 1, 0, (k + 1) & 1, (st + 1) & 1);
+      if (r + 1 < rounds) issue(st, r + 1, (k + 1) & 1, st & 1, sr[(r + 1) & 1]);
+      else if (st + 1 < ns) issue(st + 1, 0, (k + 1) & 1, (st + 1) & 1, sr[0]);
       const int tile = (r * gridDim.x + blockIdx.x) * LD_WAVES + wv;
       const int buf = k & 1, xbuf = st & 1;
       ++k;
       if (tile >= tiles) continue;
       const uint8_t* wb = wl + buf * LD_WBUF + nl * (LD_SB * 32);
-      const _Float16* xh = xl16 + (size_t)(xbuf * ncols + cr) * LD_XRS + kofs;
-      const _Float16* xo = xl16 + (size_t)((2 + xbuf) * ncols + cr) * LD_XRS + kofs;
+      const _Float16* xh = xl16 + (size_t)(xbuf * ncols + cr) * XRS + (SREG ? 0 : kofs);
+      const _Float16* xo = xl16 + (size_t)((2 + xbuf) * ncols + cr) * XRS + (SREG ? 0 : kofs);
+      // activation operand of block blk: at blk * 32 + kofs, or (SREG) in the
+      // rotated slot of that piece
+      auto xat = [&](const _Float16* x, int blk) {
+        return SREG ? *(const h8_t*)(x + 8 * ((4 * blk + (kofs >> 3) - cr) & 63))
+                    : *(const h8_t*)(x + blk * 32);
+      };
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint4 dv = *(const uint4*)(dl + buf * LD_DBUF + nl * 32 + 16 * j);   // 8 block scales of row nl
+        // 8 block scales of row nl
+        const uint4 dv = SREG ? sr[r & 1][j] : *(const uint4*)(dl + buf * DBUF + nl * 32 + 16 * j);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int k16 = 16 * j + 4 * p + g;   // 16-byte piece of the row's stage bytes
@@ -447,8 +485,8 @@ __global__ __launch_bounds__(LD_WAVES * 64, 8 / LD_WAVES) void k_q8_lmhead_dma(Q
           for (int h = 0; h < 2; ++h) {
             const int blk = j * 8 + 2 * p + h;
             const h8_t bw = q8_bop(h == 0 ? qa : qb);
-            f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xh + blk * 32), bw, zero, 0, 0, 0);
-            if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(*(const h8_t*)(xo + blk * 32), bw, dt, 0, 0, 0);
+            f4_t dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xat(xh, blk), bw, zero, 0, 0, 0);
+            if (USE_LO) dt = __builtin_amdgcn_mfma_f32_16x16x32_f16(xat(xo, blk), bw, dt, 0, 0, 0);
             const float d = f16b_to_f32((uint16_t)(w32 >> (16 * h)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(d, dt[e], acc[r][e]);
@@ -508,10 +546,26 @@ hipError_t launch_q8_lmhead(const void* w, int vocab, int hidden, int R, bool us
     }
     return hipGetLastError();
   }
-  // 9..16 rows (hi only; 5..8 with remainder planes): one block of seven
-  // waves per CU, its activation buffer taking the LDS of the eighth wave's
-  // weights; up to eight tiles per wave (the matrix-core tile has 16 columns,
-  // so the work per weight is that of 8 rows)
+  // 9..16 rows (hi only; 5..8 with remainder planes): one block of eight
+  // waves per CU with the scales in registers (the matrix-core tile has 16
+  // columns, so the work per weight is that of 8 rows) while 4 rounds cover
+  // the vocabulary, else seven waves, the activation buffer taking the LDS of
+  // the eighth wave's weights, with up to eight tiles per wave
+  {
+    const long rounds8 = ((vocab + 15) / 16 + (long)ncu * 8 - 1) / ((long)ncu * 8);
+    if (W.nb % LD_SB == 0 && R <= (use_lo ? LD_XMAX : 2 * LD_XMAX) && rounds8 <= LD_MAX_ROUNDS &&
+        ld_lds_bytes_sreg(8, R, use_lo) <= (size_t)160 * 1024) {
+      const size_t lb = ld_lds_bytes_sreg(8, R, use_lo);
+      const int ns = W.nb / LD_SB;
+      if (use_lo)
+        hipLaunchKernelGGL((k_q8_lmhead_dma<true, 8, LD_MAX_ROUNDS, true>), dim3(ncu), dim3(8 * 64), lb, s, W, W, R,
+                           img, logits, R, ns, (size_t)0);
+      else
+        hipLaunchKernelGGL((k_q8_lmhead_dma<false, 8, LD_MAX_ROUNDS, true>), dim3(ncu), dim3(8 * 64), lb, s, W, W,
+                           R, img, logits, R, ns, (size_t)0);
+      return hipGetLastError();
+    }
+  }
   {
     constexpr int W7 = 7;
     const long rounds7 = ((vocab + 15) / 16 + (long)ncu * W7 - 1) / ((long)ncu * W7);

@@ -301,7 +301,8 @@ def test_routing_ties_wide_bit_exact(sv, E, k):
                                               (4096, 7168, 16, "bf16"), (33, 32, 40, "f32"),
                                               (1999, 1024, 1, "f32"), (3001, 2048, 4, "bf16"),
                                               (517, 3072, 2, "f32"), (700, 1024, 7, "bf16"),
-                                              (300, 512, 64, "bf16")])
+                                              (300, 512, 64, "bf16"), (5000, 1024, 11, "bf16"),
+                                              (2000, 2048, 7, "f32"), (70000, 512, 13, "bf16")])
 def test_small_lm_head(sv, vocab, hidden, R, dt):
     p = synth.q8_random(synth.generator(107, vocab, hidden), vocab, hidden, 0.01)
     buf = p.packed()
