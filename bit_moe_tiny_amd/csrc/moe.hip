@@ -239,10 +239,11 @@ __device__ void route_row(const float* logits, int r, int E, int k, int* s_idx, 
 // descriptor, a larger one is cut into MOE_QUARTER descriptors of at most
 // cap_big rows; down: groups of at most cap_big rows, typed like the unit's
 // gate/up work.  Then the item ranges of the kernel's G persistent blocks:
-// every descriptor has `items` items, each costing MOE_COST_1 (at most four
-// rows) or MOE_COST_2_*; block b starts at the first item whose cost offset is
-// at least floor(C b / G) (C the total cost), so the ranges are contiguous,
-// cover every item once and carry about equal cost.
+// every descriptor costs MOE_SWITCH_* and then has `items` items, each costing
+// MOE_COST_1 (at most four rows) or MOE_COST_2_*; block b starts at the first
+// item whose cost offset is at least floor(C b / G) (C the total cost), so the
+// ranges are contiguous, cover every item once and carry about equal cost
+// (a block whose range crosses into another descriptor takes fewer items).
 __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucnt, int nu,
                           const int* s_arow, bool gateup, int cap_allk, int cap_big, int items, int G,
                           MoeWork* work, int* n_work, int* blk, int* s_cost) {
@@ -270,13 +271,15 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
   }
   const int nd = base;
   if (lane == 0) *n_work = nd;
-  // s_cost[d] becomes the cost offset of descriptor d's first item
+  // s_cost[d] becomes the cost offset of descriptor d (its change cost sw,
+  // then its items)
+  const int sw = gateup ? MOE_SWITCH_GU : MOE_SWITCH_DN;
   if (lane == 0) s_cost[0] = 0;
   __builtin_amdgcn_s_waitcnt(0xC07F);
   int run = 0;
   for (int d0 = 1; d0 <= nd; d0 += 64) {
     const int d = d0 + lane;
-    const int c = d <= nd ? s_cost[d] * items : 0;
+    const int c = d <= nd ? s_cost[d] * items + sw : 0;
     const int incl = wave_incl_scan(c);
     if (d <= nd) s_cost[d] = run + incl;
     run += __builtin_amdgcn_readlane(incl, 63);
@@ -289,11 +292,15 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
   }
   // Block b starts at the first item whose cost offset is at least
   // c = floor(C b / G): in the descriptor d with s_cost[d] <= c < s_cost[d+1],
-  // at item ceil((c - s_cost[d]) / w), w the descriptor's cost per item (an
-  // item past the descriptor's last is the next one's first).  Every product
-  // here is below 2^53, and a quotient that is not an integer is at least 1/C
-  // away from one, so the fp64 floors and ceilings are exact.
+  // at item ceil(max(0, c - s_cost[d] - sw) / w), w the descriptor's cost per
+  // item (an item past the descriptor's last is the next one's first).  Every
+  // product here is below 2^53, and a quotient that is not an integer is at
+  // least 1/C away from one, so the fp64 floors and ceilings are exact.
   const double dG = (double)G, dC = (double)C;
+  auto first = [&](int c, int P0, int w) {
+    const int t = c - P0 - sw;
+    return t <= 0 ? 0 : (t + w - 1) / w;
+  };
   if (nd < 16) {
     // few descriptors, many blocks each: lane l takes blocks l, l + 64, ...
     // and finds its descriptor by bisection (the offsets increase strictly)
@@ -305,8 +312,8 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
         if (s_cost[mid] <= c) lo = mid;
         else hi = mid - 1;
       }
-      const int P0 = s_cost[lo], w = (s_cost[lo + 1] - P0) / items;
-      blk[b] = lo * items + (c - P0 + w - 1) / w;
+      const int P0 = s_cost[lo], w = (s_cost[lo + 1] - P0 - sw) / items;
+      blk[b] = lo * items + first(c, P0, w);
     }
   } else {
     // lane l takes descriptors l, l + 64, ... and writes the blocks that
@@ -315,12 +322,12 @@ __device__ void emit_work(const int* s_uexp, const int* s_uoff, const int* s_ucn
     // one when the remainder C b - c G passes G
     const int qG = C / G, rG = C - qG * G;
     for (int d = lane; d < nd; d += 64) {
-      const int P0 = s_cost[d], P1 = s_cost[d + 1], w = (P1 - P0) / items;
+      const int P0 = s_cost[d], P1 = s_cost[d + 1], w = (P1 - P0 - sw) / items;
       const int b0 = (int)ceil((double)P0 * dG / dC), b1 = (int)ceil((double)P1 * dG / dC);
       int c = (int)floor(dC * (double)b0 / dG);
       int r = (int)((long long)C * b0 - (long long)c * G);
       for (int b = b0; b < b1; ++b) {
-        blk[b] = d * items + (c - P0 + w - 1) / w;
+        blk[b] = d * items + first(c, P0, w);
         c += qG;
         r += rG;
         if (r >= G) {

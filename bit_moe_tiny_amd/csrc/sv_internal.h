@@ -348,6 +348,12 @@ constexpr int MOE_MAX_GRID = 1024;   // persistent blocks of an expert kernel, a
 // weights.
 constexpr int MOE_COST_1 = 10;
 constexpr int MOE_COST_2_GU = 16, MOE_COST_2_DN = 19;
+// Cost of a block's change of descriptor inside its range (a barrier, at
+// which the waves that run ahead wait for the others, the new rows' copy,
+// and the load ring drained), on the same scale, charged at the start of
+// every descriptor: measured for gate/up (about 0.8 of an item); for down
+// (about 0.35) charging it made no difference.
+constexpr int MOE_SWITCH_GU = 8, MOE_SWITCH_DN = 0;
 enum { MOE_ALLK = 0, MOE_QUARTER = 1 };
 struct MoeWork {
   int expert, a0, ncols, type;
