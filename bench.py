@@ -9,9 +9,9 @@ One step = the whole verifier hot path on one batch of synthetic input:
                    of K = R/S - 1 drafts at T = 0.8.
 Inputs for several batches are generated up front (seeded, synth) and stay
 resident in HBM; steps rotate through them.  The timed region is K steps
-between two device synchronisations, by default each a replay of a captured
-HIP graph of the whole step on that batch (--launch eager: launched call by
-call; the other mode is timed too and reported beside); value = algorithmic
+between two device synchronisations, launched call by call (--launch graph:
+each step a replay of a captured HIP graph of the whole step on that batch;
+the other mode is timed too and reported beside); value = algorithmic
 weight bytes of the timed steps (the routed experts each batch actually
 touches, the shared expert, the vocabulary head) / elapsed time.
 
@@ -72,9 +72,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the headline: no per-R entries, cohort, single-expert calls or kernel times")
     ap.add_argument("--extra-steps", type=int, default=20, help="timed steps of each per-R / cohort entry")
-    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
-                    help="timed steps as replays of one captured HIP graph per batch (default), or as "
-                         "eager launches; the other mode is timed too and reported beside")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="timed steps launched call by call (default), or as replays of one captured HIP "
+                         "graph per batch; the other mode is timed too and reported beside")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the bench, one plain device copy of this many MiB (fp32 x 1.0): "
                          "the known-size kernel that calibrates profiler byte counters")
@@ -199,7 +199,7 @@ def capture_steps(step):
     return graphs
 
 
-def measure(step, steps, warmup, launch="graph"):
+def measure(step, steps, warmup, launch="eager"):
     """Times `steps` steps with events at the two ends only (an event recorded
     between kernels leaves a gap of several microseconds on the GPU timeline),
     as graph replays (one captured graph per batch) or as eager launches, and
@@ -214,8 +214,13 @@ def measure(step, steps, warmup, launch="graph"):
     nb = len(step.batches)
 
     def timed(graph):
-        for i in range(min(warmup, nb) if graph else 0):
-            graphs[i % nb].replay()
+        # each mode is warmed up by itself first (the first eager steps after
+        # a capture run slow)
+        for i in range(warmup):
+            if graph:
+                graphs[i % nb].replay()
+            else:
+                step.run(i)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
