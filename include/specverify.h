@@ -56,7 +56,7 @@ typedef struct ihipStream_t* hipStream_t;
 enum sv_status {
   SV_OK = 0,
   SV_EINVAL = 1,        /* invalid argument; nothing enqueued */
-  SV_EUNSUPPORTED = 2,  /* valid but outside what this build implements */
+  SV_EUNSUPPORTED = 2,  /* valid but outside what the library implements */
   SV_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() */
   SV_EHIP = 4,          /* a HIP launch failed */
   SV_ESCRATCH = 5       /* needs more than the library's static scratch buffer */
