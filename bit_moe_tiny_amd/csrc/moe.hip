@@ -104,25 +104,32 @@ __device__ inline uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-// Maximum of 64-bit values over the wave (both halves moved on the network).
+// (lanes a step does not reach read 0, the identity of the maximum, so the
+// move folds into the maximum)
 template <int CTRL, int ROWS>
-__device__ inline uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
+__device__ inline uint32_t dpp0_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+__device__ inline uint32_t wave_umax32(uint32_t v) {
+  v = max(v, dpp0_u32<0x111, 0xF>(v));
+  v = max(v, dpp0_u32<0x112, 0xF>(v));
+  v = max(v, dpp0_u32<0x114, 0xF>(v));
+  v = max(v, dpp0_u32<0x118, 0xF>(v));
+  v = max(v, dpp0_u32<0x142, 0xA>(v));
+  v = max(v, dpp0_u32<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// Maximum of 64-bit values over the wave: the largest high half, then the
+// largest low half among the lanes holding it (two 32-bit reductions, one
+// instruction per step each, instead of a 64-bit compare and two selects).
 __device__ inline uint64_t wave_umax64(uint64_t v) {
-  v = umax64(v, dpp_u64<0x111, 0xF>(v));
-  v = umax64(v, dpp_u64<0x112, 0xF>(v));
-  v = umax64(v, dpp_u64<0x114, 0xF>(v));
-  v = umax64(v, dpp_u64<0x118, 0xF>(v));
-  v = umax64(v, dpp_u64<0x142, 0xA>(v));
-  v = umax64(v, dpp_u64<0x143, 0xC>(v));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
+  const uint32_t hi = (uint32_t)(v >> 32), mh = wave_umax32(hi);
+  const uint32_t ml = wave_umax32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // Sum in a fixed order (run-to-run identical): zeros are shifted in at row
